@@ -1,0 +1,15 @@
+"""CPU oracle for paged decode attention -- TEST INFRASTRUCTURE ONLY.
+
+Only the test suite, the smoke check and the benchmark's CPU-baseline leg may
+import this package.  The GPU library shares no code with it and never calls
+it.  Every function is pinned by a check in the test suite; none is marked
+"parity unpinned".
+"""
+from .paged_attention import (ELEMENT_BYTES, attention_one, chunk_elems, combine_partitions,
+                              decode, empty_pools, gather_kv, gather_sequence,
+                              k_cache_shape, paged_attention, partition_stats,
+                              reshape_and_cache, v_cache_shape)
+
+__all__ = ["ELEMENT_BYTES", "attention_one", "chunk_elems", "combine_partitions", "decode",
+           "empty_pools", "gather_kv", "gather_sequence", "k_cache_shape",
+           "paged_attention", "partition_stats", "reshape_and_cache", "v_cache_shape"]

@@ -1,0 +1,221 @@
+"""Plain, slow CPU oracle for paged decode attention.
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+benchmark's CPU-baseline leg may import this module.  The GPU library never
+calls it, shares no code with it, and must fail loudly rather than fall back
+to it.
+
+What is computed, and where the pages define it
+-----------------------------------------------
+* KV cache in blocks: every sequence's keys and values are cut into
+  fixed-size blocks of ``block_size`` tokens; a logical block and a physical
+  block hold the same number of tokens; a per-sequence block table maps
+  logical block numbers to physical blocks, which may sit anywhere in the
+  pool ("core architecture" page, section 2.2.1 and its table;
+  "core features" page, section 4.1).
+* Attention over a paged cache: the result is attention of the query over the
+  complete K/V sequence put back together through the block table
+  ("core architecture" page, section 2.2.2, the sentence before the
+  pseudo-code).  The pages never write the formula out; this oracle takes the
+  standard scaled dot-product softmax attention with the caller's ``scale``,
+  and no mask other than the sequence length.  The pseudo-code's per-block
+  ``+=`` is read as the exact softmax over the whole sequence, since the same
+  section defines the result through the reassembled sequence.
+* Appending a token writes one slot: a newly generated token costs one more
+  entry in its sequence's mapping, nothing is moved ("core features" page,
+  section 4.1).  The slot of a token is physical_block * block_size +
+  offset_in_block, and reshape_and_cache scatters each new token's K and V
+  into its slot.
+* Grouped query heads: query head h reads KV head h // (Hq / Hkv).  The pages
+  are silent on grouping; contiguous groups are the plainest reading.
+
+Cache layout (the library's boundary format; the pages show only that a
+physical block yields its k and v):
+* k_cache: [num_blocks, Hkv, D // X, block_size, X] with X = 16 bytes / element
+  size (X = 8 for bfloat16, 4 for float32);
+* v_cache: [num_blocks, Hkv, D, block_size].
+Element (token t, kv head h, channel d) of sequence s lives at
+``k_cache[b, h, d // X, t % BS, d % X]`` and ``v_cache[b, h, d, t % BS]`` with
+``b = block_table[s, t // BS]``.
+
+Precision: inputs are float32 arrays or bfloat16 bit patterns (uint16);
+everything is decoded exactly to float64 and computed in float64 with NumPy's
+matmul, exp and sum as the only library steps.  Nothing is rounded back.
+
+Pins: the checks that tie these functions to the pages and to independent
+formulations live in the test suite (dense brute force over the never-paged
+sequence, block-permutation, sharing and block-size invariance, closed forms,
+a hand-worked fixture, and a per-element gather loop).  Every function below
+is pinned by at least one of them.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+ELEMENT_BYTES = {"f32": 4, "bf16": 2}
+
+
+# ---------------------------------------------------------------------------
+# element decoding and cache layout
+# ---------------------------------------------------------------------------
+def decode(x: np.ndarray, dtype: str) -> np.ndarray:
+    """Exact float64 value of each element.
+
+    bfloat16 is the upper half of an IEEE float32: widening the 16-bit pattern
+    to 32 bits with zeros below gives the same number as a float32.
+    """
+    if dtype == "bf16":
+        bits = np.ascontiguousarray(x, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+        return bits.view(np.float32).astype(np.float64)
+    if dtype == "f32":
+        return np.asarray(x, dtype=np.float32).astype(np.float64)
+    raise ValueError(f"unknown dtype {dtype!r}")
+
+
+def chunk_elems(dtype: str) -> int:
+    """X: elements in one 16-byte chunk of a K row."""
+    return 16 // ELEMENT_BYTES[dtype]
+
+
+def k_cache_shape(num_blocks: int, num_kv_heads: int, head_dim: int, block_size: int,
+                  dtype: str) -> tuple:
+    X = chunk_elems(dtype)
+    return (num_blocks, num_kv_heads, head_dim // X, block_size, X)
+
+
+def v_cache_shape(num_blocks: int, num_kv_heads: int, head_dim: int, block_size: int,
+                  dtype: str) -> tuple:
+    return (num_blocks, num_kv_heads, head_dim, block_size)
+
+
+# ---------------------------------------------------------------------------
+# write path: reshape_and_cache
+# ---------------------------------------------------------------------------
+def reshape_and_cache(key: np.ndarray, value: np.ndarray, slot_mapping: np.ndarray,
+                      k_cache: np.ndarray, v_cache: np.ndarray, inplace: bool = False):
+    """Pools with token i's K/V stored at slot_mapping[i] (copies unless ``inplace``).
+
+    key, value: [T, Hkv, D].  A negative slot means "no write" (padding).
+    Slots of one call must be distinct and inside the pool.
+    """
+    k_new = k_cache if inplace else k_cache.copy()
+    v_new = v_cache if inplace else v_cache.copy()
+    NB, Hkv, DX, BS, X = k_cache.shape
+    slots = np.asarray(slot_mapping, dtype=np.int64)
+    live = np.nonzero(slots >= 0)[0]
+    assert len(np.unique(slots[live])) == len(live), "slots of one call must be distinct"
+    assert (slots[live] < NB * BS).all(), "slot outside the pool"
+    blk, off = slots[live] // BS, slots[live] % BS
+    k_new[blk, :, :, off, :] = key[live].reshape(len(live), Hkv, DX, X)
+    v_new[blk, :, :, off] = value[live]
+    return k_new, v_new
+
+
+# ---------------------------------------------------------------------------
+# read path: reassemble through the block table
+# ---------------------------------------------------------------------------
+def gather_sequence(block_table_row: np.ndarray, context_len: int,
+                    k_cache: np.ndarray, v_cache: np.ndarray):
+    """Contiguous K and V ([L, Hkv, D], pool dtype, bit-exact) of one sequence."""
+    NB, Hkv, DX, BS, X = k_cache.shape
+    L = int(context_len)
+    n = -(-L // BS)
+    blocks = np.asarray(block_table_row[:n], dtype=np.int64)
+    k = k_cache[blocks].transpose(0, 3, 1, 2, 4).reshape(n * BS, Hkv, DX * X)[:L]
+    v = v_cache[blocks].transpose(0, 3, 1, 2).reshape(n * BS, Hkv, DX * X)[:L]
+    return k, v
+
+
+def gather_kv(block_table: np.ndarray, context_lens: np.ndarray,
+              k_cache: np.ndarray, v_cache: np.ndarray):
+    """All sequences' K/V concatenated along tokens: ([sum L, Hkv, D], same)."""
+    ks, vs = [], []
+    for s, L in enumerate(context_lens):
+        k, v = gather_sequence(block_table[s], int(L), k_cache, v_cache)
+        ks.append(k)
+        vs.append(v)
+    return np.concatenate(ks), np.concatenate(vs)
+
+
+# ---------------------------------------------------------------------------
+# attention
+# ---------------------------------------------------------------------------
+def attention_one(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float) -> np.ndarray:
+    """Softmax attention of queries q [G, D] over keys/values k, v [L, D] (float64)."""
+    if k.shape[0] == 0:
+        return np.zeros((q.shape[0], v.shape[1]))
+    z = scale * (k @ q.T)                     # [L, G] logits
+    w = np.exp(z - z.max(axis=0))             # unnormalised weights
+    return (w.T @ v) / w.sum(axis=0)[:, None]
+
+
+def paged_attention(query: np.ndarray, block_table: np.ndarray, context_lens: np.ndarray,
+                    k_cache: np.ndarray, v_cache: np.ndarray, scale: float,
+                    dtype: str, seqs=None) -> np.ndarray:
+    """Decode attention of each sequence's query over its paged K/V, in float64.
+
+    query: [S, Hq, D].  Returns [S, Hq, D] float64 (rows of sequences not in
+    ``seqs`` are left at zero).  A sequence of length 0 gives zeros.
+    """
+    S, Hq, D = query.shape
+    Hkv = k_cache.shape[1]
+    g = Hq // Hkv
+    out = np.zeros((S, Hq, D), dtype=np.float64)
+    for s in (range(S) if seqs is None else seqs):
+        k, v = gather_sequence(block_table[s], int(context_lens[s]), k_cache, v_cache)
+        kf, vf, qf = decode(k, dtype), decode(v, dtype), decode(query[s], dtype)
+        for kvh in range(Hkv):
+            heads = slice(kvh * g, (kvh + 1) * g)
+            out[s, heads] = attention_one(qf[heads], kf[:, kvh], vf[:, kvh], scale)
+    return out
+
+
+# ---------------------------------------------------------------------------
+# split context: per-partition statistics and their log-sum-exp combination
+# ---------------------------------------------------------------------------
+def partition_stats(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,
+                    partition_size: int):
+    """Per partition of ``partition_size`` tokens: running max m, weight sum l
+    and unnormalised weighted value sum acc (natural-log domain, float64).
+
+    q [G, D], k, v [L, D]; returns m [P, G], l [P, G], acc [P, G, D].
+    """
+    L = k.shape[0]
+    P = -(-L // partition_size)
+    m = np.empty((P, q.shape[0]))
+    l = np.empty((P, q.shape[0]))
+    acc = np.empty((P, q.shape[0], v.shape[1]))
+    for p in range(P):
+        kp = k[p * partition_size:(p + 1) * partition_size]
+        vp = v[p * partition_size:(p + 1) * partition_size]
+        z = scale * (kp @ q.T)
+        m[p] = z.max(axis=0)
+        w = np.exp(z - m[p])
+        l[p] = w.sum(axis=0)
+        acc[p] = w.T @ vp
+    return m, l, acc
+
+
+def combine_partitions(m: np.ndarray, l: np.ndarray, acc: np.ndarray) -> np.ndarray:
+    """Log-sum-exp combination: with M = max_p m_p,
+    out = sum_p e^(m_p - M) acc_p / sum_p e^(m_p - M) l_p."""
+    M = m.max(axis=0)
+    w = np.exp(m - M)
+    return (w[:, :, None] * acc).sum(axis=0) / (w * l).sum(axis=0)[:, None]
+
+
+# ---------------------------------------------------------------------------
+# helpers for building pools in tests
+# ---------------------------------------------------------------------------
+def empty_pools(num_blocks: int, num_kv_heads: int, head_dim: int, block_size: int,
+                dtype: str, fill: str = "nan"):
+    """Fresh pools filled with NaN (poison) or zeros."""
+    ks = k_cache_shape(num_blocks, num_kv_heads, head_dim, block_size, dtype)
+    vs = v_cache_shape(num_blocks, num_kv_heads, head_dim, block_size, dtype)
+    if dtype == "bf16":
+        val = np.uint16(0x7FC0) if fill == "nan" else np.uint16(0)
+        return np.full(ks, val, dtype=np.uint16), np.full(vs, val, dtype=np.uint16)
+    val = np.float32(math.nan) if fill == "nan" else np.float32(0)
+    return np.full(ks, val, dtype=np.float32), np.full(vs, val, dtype=np.float32)
