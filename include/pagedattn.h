@@ -1,0 +1,166 @@
+/*
+ * pagedattn.h -- C ABI of the MI355X (gfx950) paged-KV decode library.
+ *
+ * The operations follow the problem statement on the pages about vLLM's
+ * paged KV cache:
+ *   - the KV cache is cut into fixed-size blocks; a per-sequence block table
+ *     maps logical blocks to physical blocks that may sit anywhere in the pool
+ *     (page "vLLM core architecture: model loading, PagedAttention principle,
+ *     KV Cache management", section 2.2.1 and its table);
+ *   - decode attention reads each sequence's K/V back through its block table
+ *     (same page, section 2.2.2, the pseudo-code paged_attention(query,
+ *     block_table, physical_kv_cache));
+ *   - a new token only adds one entry to its sequence's mapping (page
+ *     "vLLM core features: PagedAttention, Continuous Batching, quantization,
+ *     distributed inference", section 4.1) -- here reshape_and_cache writes
+ *     that token's K and V into its slot.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - All array arguments are DEVICE pointers owned by the caller; the library
+ *   allocates nothing and keeps no device state between calls.
+ * - Every call is asynchronous on `stream` (a hipStream_t passed as void*;
+ *   NULL means the null stream) and never synchronises the host.
+ * - Arguments are checked on the host before anything is launched; a failed
+ *   check returns a status and launches nothing.  PA_ERR_HIP reports a failed
+ *   launch (hipGetLastError after the launch).
+ * - dtype names the element type of query, out, key, value and both caches:
+ *   PA_DTYPE_F32 (IEEE float32) or PA_DTYPE_BF16 (bfloat16).
+ * - Supported shapes: head_dim D in {64, 128}; block_size BS in {8, 16, 32};
+ *   num_heads a multiple of num_kv_heads with group size
+ *   g = num_heads / num_kv_heads <= 8 (bf16) or <= 16 (f32).
+ *   Other values return PA_ERR_UNSUPPORTED.
+ * - query/out/key/value/k_cache/v_cache must be 16-byte aligned; tables
+ *   4-byte aligned; slot_mapping and seq_offsets 8-byte aligned.
+ *
+ * Cache layout (one K pool and one V pool, X = 16 / element bytes, so X = 8
+ * for bf16 and X = 4 for f32):
+ *   k_cache: [num_blocks][num_kv_heads][D / X][BS][X]
+ *   v_cache: [num_blocks][num_kv_heads][D][BS]
+ * Token t of a sequence with block-table row `bt` lives in physical block
+ * b = bt[t / BS] at offset o = t % BS; its K channel d is
+ * k_cache[b][h][d / X][o][d % X] and its V channel d is v_cache[b][h][d][o].
+ * A slot is b * BS + o.
+ *
+ * Device-side preconditions (not checked by the library; violating them gives
+ * wrong results but no access outside the buffers passed in):
+ *   block ids in [0, num_blocks); context_lens[s] <= max_context_len;
+ *   slots of one reshape_and_cache call distinct; out aliases no input.
+ */
+#ifndef PAGEDATTN_H
+#define PAGEDATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PA_ABI_VERSION 1
+
+typedef enum {
+    PA_OK = 0,
+    PA_ERR_INVALID_ARG = 1,   /* null pointer, negative size, misalignment, bad length */
+    PA_ERR_UNSUPPORTED = 2,   /* well-formed but not built: D, BS, dtype, group size     */
+    PA_ERR_WORKSPACE = 3,     /* workspace missing or smaller than required              */
+    PA_ERR_HIP = 4            /* a HIP launch failed                                     */
+} pa_status;
+
+typedef enum {
+    PA_DTYPE_F32 = 0,
+    PA_DTYPE_BF16 = 1
+} pa_dtype;
+
+/* Version of this ABI (PA_ABI_VERSION of the build). */
+int pa_abi_version(void);
+
+/* Static, human-readable name of a status code. */
+const char* pa_status_string(pa_status status);
+
+/*
+ * Partition length (tokens) pa_paged_attention uses for these sizes when the
+ * caller passes partition_size = 0.  Always a multiple of 64.
+ */
+int pa_default_partition_size(int num_seqs, int num_kv_heads, int max_context_len,
+                              pa_dtype dtype);
+
+/*
+ * Bytes of workspace pa_paged_attention needs (0 when every sequence fits in
+ * one partition).  partition_size = 0 selects pa_default_partition_size.
+ * Returns 0 for arguments pa_paged_attention would reject.
+ */
+size_t pa_paged_attention_workspace_size(int num_seqs, int num_heads, int num_kv_heads,
+                                         int head_dim, int max_context_len,
+                                         int partition_size, pa_dtype dtype);
+
+/*
+ * Decode attention over a paged KV cache (one query token per sequence).
+ *
+ * For sequence s (length L = context_lens[s]) and query head h with KV head
+ * kvh = h / g:
+ *   z_t   = scale * sum_d query[s][h][d] * K_s[t][kvh][d],   t in [0, L)
+ *   out[s][h] = sum_t softmax(z)_t * V_s[t][kvh]
+ * where K_s/V_s is the sequence reassembled through block_table (the result
+ * is the attention over the whole reassembled sequence; the library combines
+ * block-wise partial results exactly with a running max and sum).  L = 0
+ * gives out = 0.  out is rounded to dtype (round to nearest even for bf16).
+ *
+ *   out, query     [num_seqs][num_heads][head_dim], contiguous
+ *   block_table    [num_seqs][max_blocks_per_seq] int32, row stride
+ *                  max_blocks_per_seq; entries past ceil(L / BS) are never read
+ *   context_lens   [num_seqs] int32
+ *   k_cache/v_cache  layouts above, num_blocks blocks
+ *   max_context_len  host-side upper bound of context_lens (sizes the grid;
+ *                  must be <= max_blocks_per_seq * block_size)
+ *   partition_size 0 = default, else a multiple of 64 in [64, 8192]: each
+ *                  sequence is split into partitions of this many tokens that
+ *                  run in parallel and are merged by a log-sum-exp reduce
+ *   workspace      device scratch of at least
+ *                  pa_paged_attention_workspace_size(...) bytes, 16-byte
+ *                  aligned; may be NULL when that size is 0.  Two calls in
+ *                  flight at once must not share a workspace.
+ */
+pa_status pa_paged_attention(void* out, const void* query, const int32_t* block_table,
+                             const int32_t* context_lens, const void* k_cache,
+                             const void* v_cache, int num_seqs, int num_heads,
+                             int num_kv_heads, int head_dim, int block_size,
+                             int max_blocks_per_seq, int num_blocks, int max_context_len,
+                             float scale, pa_dtype dtype, int partition_size,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Write path: store each new token's K and V into its slot.
+ *
+ *   key, value     [num_tokens][num_kv_heads][head_dim], contiguous
+ *   slot_mapping   [num_tokens] int64; slot = physical_block * BS + offset.
+ *                  A negative slot skips that token (padding); a slot at or
+ *                  past num_blocks * BS is skipped as well.
+ *   k_cache, v_cache  pools in the layouts above (written in place)
+ * The copy is bit-exact; nothing outside the written slots changes.
+ */
+pa_status pa_reshape_and_cache(const void* key, const void* value, const int64_t* slot_mapping,
+                               void* k_cache, void* v_cache, int num_tokens, int num_kv_heads,
+                               int head_dim, int block_size, int num_blocks, pa_dtype dtype,
+                               void* stream);
+
+/*
+ * Diagnostic read path: reassemble every sequence's K and V through its block
+ * table into contiguous token-major arrays (bit-exact copies).
+ *
+ *   k_out, v_out   [sum_s context_lens[s]][num_kv_heads][head_dim]
+ *   seq_offsets    [num_seqs] int64, row of k_out/v_out where sequence s
+ *                  starts (the exclusive prefix sum of context_lens)
+ *   other arguments as in pa_paged_attention
+ */
+pa_status pa_gather_kv(void* k_out, void* v_out, const int64_t* seq_offsets,
+                       const int32_t* block_table, const int32_t* context_lens,
+                       const void* k_cache, const void* v_cache, int num_seqs,
+                       int num_kv_heads, int head_dim, int block_size, int max_blocks_per_seq,
+                       int num_blocks, int max_context_len, pa_dtype dtype, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDATTN_H */

@@ -1,0 +1,12 @@
+"""MI355X (gfx950) paged-KV decode library: Python face of libpagedattn.so.
+
+The work runs in hand-written HIP kernels behind a C ABI (include/pagedattn.h);
+this package only marshals torch tensors to it.
+"""
+from .binding import (LIB_PATH, chunk_elems, default_partition_size, gather_kv, k_cache_shape,
+                      load_library, paged_attention, reshape_and_cache, v_cache_shape,
+                      workspace_size)
+
+__all__ = ["LIB_PATH", "chunk_elems", "default_partition_size", "gather_kv", "k_cache_shape",
+           "load_library", "paged_attention", "reshape_and_cache", "v_cache_shape",
+           "workspace_size"]

@@ -1,0 +1,178 @@
+// Write path and diagnostic read path of the paged KV cache (gfx950).
+//
+// reshape_and_cache: a new token only adds one entry to its sequence's
+// mapping (page "vLLM core features", section 4.1); here its K and V are
+// copied into the slot (physical block, offset) the scheduler chose for it.
+// gather_kv: the inverse, reassembling each sequence through its block table
+// (page "vLLM core architecture", section 2.2.2) as plain copies.
+//
+// Both are bit-exact copies; K moves in 16-byte chunks (one K chunk is
+// contiguous in both layouts), V element by element (its cache rows run
+// along tokens).
+#include "common.h"
+
+namespace pa {
+
+constexpr int kCopyThreads = 256;
+
+// One workgroup per token.
+template <typename T>
+__global__ void __launch_bounds__(kCopyThreads)
+reshape_and_cache_kernel(const T* __restrict__ key, const T* __restrict__ value,
+                         const int64_t* __restrict__ slot_mapping, T* __restrict__ k_cache,
+                         T* __restrict__ v_cache, int Hkv, int D, int BS, int NB) {
+  constexpr int X = ElemTraits<T>::kX;
+  const int i = blockIdx.x;
+  const int64_t slot = slot_mapping[i];
+  if (slot < 0 || slot >= (int64_t)NB * BS) return;
+  const int64_t blk = slot / BS;
+  const int off = (int)(slot % BS);
+  const int chunks = D / X;
+  const T* ksrc = key + (size_t)i * Hkv * D;
+  const T* vsrc = value + (size_t)i * Hkv * D;
+  for (int c = threadIdx.x; c < Hkv * chunks; c += kCopyThreads) {
+    const int h = c / chunks;
+    const int dc = c % chunks;
+    T* dst = k_cache + (((size_t)blk * Hkv + h) * chunks + dc) * BS * X + (size_t)off * X;
+    store16(dst, load16(ksrc + (size_t)h * D + dc * X));
+  }
+  for (int e = threadIdx.x; e < Hkv * D; e += kCopyThreads) {
+    const int h = e / D;
+    const int d = e % D;
+    v_cache[(((size_t)blk * Hkv + h) * D + d) * BS + off] = vsrc[e];
+  }
+}
+
+// One workgroup per (sequence, logical block).
+template <typename T>
+__global__ void __launch_bounds__(kCopyThreads)
+gather_kv_kernel(T* __restrict__ k_out, T* __restrict__ v_out,
+                 const int64_t* __restrict__ seq_offsets, const int32_t* __restrict__ block_table,
+                 const int32_t* __restrict__ context_lens, const T* __restrict__ k_cache,
+                 const T* __restrict__ v_cache, int Hkv, int D, int BS, int MB, int NB,
+                 int blocks_per_seq) {
+  constexpr int X = ElemTraits<T>::kX;
+  const int s = blockIdx.x / blocks_per_seq;
+  const int b = blockIdx.x % blocks_per_seq;
+  int L = context_lens[s];
+  L = L < 0 ? 0 : (L > MB * BS ? MB * BS : L);
+  const int t0 = b * BS;
+  if (t0 >= L) return;
+  const int nt = min(BS, L - t0);
+  const unsigned raw = static_cast<unsigned>(block_table[(size_t)s * MB + b]);
+  const size_t phys = min(raw, static_cast<unsigned>(NB - 1));
+  const size_t row0 = (size_t)seq_offsets[s] + t0;
+  const int chunks = D / X;
+  for (int c = threadIdx.x; c < nt * Hkv * chunks; c += kCopyThreads) {
+    const int o = c / (Hkv * chunks);
+    const int r = c % (Hkv * chunks);
+    const int h = r / chunks;
+    const int dc = r % chunks;
+    const T* src = k_cache + ((phys * Hkv + h) * chunks + dc) * BS * X + (size_t)o * X;
+    store16(k_out + ((row0 + o) * Hkv + h) * D + dc * X, load16(src));
+  }
+  for (int e = threadIdx.x; e < nt * Hkv * D; e += kCopyThreads) {
+    const int o = e / (Hkv * D);
+    const int r = e % (Hkv * D);
+    const int h = r / D;
+    const int d = r % D;
+    v_out[((row0 + o) * Hkv + h) * D + d] = v_cache[((phys * Hkv + h) * D + d) * BS + o];
+  }
+}
+
+}  // namespace pa
+
+namespace {
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+pa_status check_cache_shapes(int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                             pa_dtype dtype) {
+  if (dtype != PA_DTYPE_F32 && dtype != PA_DTYPE_BF16) return PA_ERR_UNSUPPORTED;
+  if (num_kv_heads <= 0 || num_blocks <= 0) return PA_ERR_INVALID_ARG;
+  if (head_dim != 64 && head_dim != 128) return PA_ERR_UNSUPPORTED;
+  if (block_size != 8 && block_size != 16 && block_size != 32) return PA_ERR_UNSUPPORTED;
+  return PA_OK;
+}
+
+}  // namespace
+
+extern "C" pa_status pa_reshape_and_cache(const void* key, const void* value,
+                                          const int64_t* slot_mapping, void* k_cache,
+                                          void* v_cache, int num_tokens, int num_kv_heads,
+                                          int head_dim, int block_size, int num_blocks,
+                                          pa_dtype dtype, void* stream) {
+  pa_status st = check_cache_shapes(num_kv_heads, head_dim, block_size, num_blocks, dtype);
+  if (st != PA_OK) return st;
+  if (num_tokens < 0) return PA_ERR_INVALID_ARG;
+  if (num_tokens == 0) return PA_OK;
+  if (!key || !value || !slot_mapping || !k_cache || !v_cache) return PA_ERR_INVALID_ARG;
+  if (!aligned(key, 16) || !aligned(value, 16) || !aligned(k_cache, 16) ||
+      !aligned(v_cache, 16) || !aligned(slot_mapping, 8))
+    return PA_ERR_INVALID_ARG;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (dtype == PA_DTYPE_BF16) {
+    hipLaunchKernelGGL(pa::reshape_and_cache_kernel<uint16_t>, dim3(num_tokens),
+                       dim3(pa::kCopyThreads), 0, s, static_cast<const uint16_t*>(key),
+                       static_cast<const uint16_t*>(value), slot_mapping,
+                       static_cast<uint16_t*>(k_cache), static_cast<uint16_t*>(v_cache),
+                       num_kv_heads, head_dim, block_size, num_blocks);
+  } else {
+    hipLaunchKernelGGL(pa::reshape_and_cache_kernel<float>, dim3(num_tokens),
+                       dim3(pa::kCopyThreads), 0, s, static_cast<const float*>(key),
+                       static_cast<const float*>(value), slot_mapping,
+                       static_cast<float*>(k_cache), static_cast<float*>(v_cache), num_kv_heads,
+                       head_dim, block_size, num_blocks);
+  }
+  return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+extern "C" pa_status pa_gather_kv(void* k_out, void* v_out, const int64_t* seq_offsets,
+                                  const int32_t* block_table, const int32_t* context_lens,
+                                  const void* k_cache, const void* v_cache, int num_seqs,
+                                  int num_kv_heads, int head_dim, int block_size,
+                                  int max_blocks_per_seq, int num_blocks, int max_context_len,
+                                  pa_dtype dtype, void* stream) {
+  pa_status st = check_cache_shapes(num_kv_heads, head_dim, block_size, num_blocks, dtype);
+  if (st != PA_OK) return st;
+  if (num_seqs < 0 || max_blocks_per_seq <= 0 || max_context_len < 0) return PA_ERR_INVALID_ARG;
+  if ((long)max_context_len > (long)max_blocks_per_seq * block_size) return PA_ERR_INVALID_ARG;
+  if (num_seqs == 0 || max_context_len == 0) return PA_OK;
+  if (!k_out || !v_out || !seq_offsets || !block_table || !context_lens || !k_cache || !v_cache)
+    return PA_ERR_INVALID_ARG;
+  if (!aligned(k_out, 16) || !aligned(v_out, 16) || !aligned(k_cache, 16) ||
+      !aligned(v_cache, 16) || !aligned(seq_offsets, 8) || !aligned(block_table, 4) ||
+      !aligned(context_lens, 4))
+    return PA_ERR_INVALID_ARG;
+  const int bps = (max_context_len + block_size - 1) / block_size;
+  const long grid = (long)num_seqs * bps;
+  if (grid > 0x7FFFFFFFL) return PA_ERR_INVALID_ARG;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (dtype == PA_DTYPE_BF16) {
+    hipLaunchKernelGGL(pa::gather_kv_kernel<uint16_t>, dim3((unsigned)grid), dim3(pa::kCopyThreads),
+                       0, s, static_cast<uint16_t*>(k_out), static_cast<uint16_t*>(v_out),
+                       seq_offsets, block_table, context_lens,
+                       static_cast<const uint16_t*>(k_cache), static_cast<const uint16_t*>(v_cache),
+                       num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks, bps);
+  } else {
+    hipLaunchKernelGGL(pa::gather_kv_kernel<float>, dim3((unsigned)grid), dim3(pa::kCopyThreads), 0,
+                       s, static_cast<float*>(k_out), static_cast<float*>(v_out), seq_offsets,
+                       block_table, context_lens, static_cast<const float*>(k_cache),
+                       static_cast<const float*>(v_cache), num_kv_heads, head_dim, block_size,
+                       max_blocks_per_seq, num_blocks, bps);
+  }
+  return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+extern "C" int pa_abi_version(void) { return PA_ABI_VERSION; }
+
+extern "C" const char* pa_status_string(pa_status status) {
+  switch (status) {
+    case PA_OK: return "PA_OK";
+    case PA_ERR_INVALID_ARG: return "PA_ERR_INVALID_ARG: invalid argument";
+    case PA_ERR_UNSUPPORTED: return "PA_ERR_UNSUPPORTED: shape or dtype not supported";
+    case PA_ERR_WORKSPACE: return "PA_ERR_WORKSPACE: workspace missing or too small";
+    case PA_ERR_HIP: return "PA_ERR_HIP: HIP launch failed";
+  }
+  return "unknown pa_status";
+}

@@ -1,0 +1,484 @@
+// Paged decode attention for gfx950 (MI355X).
+//
+// What is computed: each sequence's single query token attends over the K/V
+// reassembled through its block table (page "vLLM core architecture",
+// section 2.2.2: attention over the KV sequence put back together from the
+// block table).  The per-block loop there is made exact with a running max
+// and running sum (online softmax): every partial result is rescaled to the
+// largest logit seen so far, so the block-by-block accumulation equals the
+// softmax over the whole sequence.
+//
+// Work decomposition
+//   workgroup = (kv head, partition of P tokens, sequence); the kv head is the
+//     fastest-varying index so consecutive workgroups -- which the dispatcher
+//     spreads round-robin over the 8 XCDs -- carry equal work.
+//   NW waves per workgroup take the partition's steps round-robin.
+//   One step is 32 tokens (bf16) or 16 tokens (f32) of one KV head, shared by
+//     the whole query-head group (GQA): each K/V byte is fetched once per group.
+//   Sequences longer than one partition write (max, sum, unnormalised output)
+//     per partition to the workspace; a second kernel merges them with a
+//     log-sum-exp reduce.  Single-partition sequences write the output directly.
+//
+// Matrix cores
+//   Q.K^T for a step is [tokens x D] . [D x head-rows] and P.V is
+//   [D x tokens] . [tokens x head-rows]: dense contractions, run on
+//   v_mfma_f32_16x16x32_bf16 (bf16) or v_mfma_f32_16x16x4_f32 (f32).
+//   With the cache layout of pagedattn.h every MFMA operand is one 16-byte
+//   load per lane straight from HBM: K rows of 8 channels for Q.K^T, V rows of
+//   8 (bf16) or 4 (f32) consecutive tokens for P.V.
+//   For bf16 the softmax weights must enter the P.V product in bf16.  To keep
+//   float32 accuracy each weight is split p = hi + lo (both bf16, the error of
+//   the pair is ~2^-17 p) and the head group occupies 2g of the 16 MFMA rows:
+//   rows [0, g) carry hi, rows [g, 2g) carry lo, and the two are added at the
+//   end.  The rows are there anyway (g <= 8 < 16), so this costs no extra MFMA.
+//
+// Lane mapping of a 16x16 MFMA output: lane l holds rows 4*(l/16)..+3 of
+// column l%16.  Below, n = l%16 and j = l/16.
+#include <algorithm>
+
+#include "common.h"
+
+namespace pa {
+
+struct DecodeParams {
+  void* out;
+  float* part_ml;          // [S][Hq][Pmax][2]  (max in log2 units, weight sum)
+  float* part_acc;         // [S][Hq][Pmax][D]  unnormalised output
+  const void* q;
+  const int32_t* block_table;
+  const int32_t* context_lens;
+  const void* k_cache;
+  const void* v_cache;
+  int S, Hq, Hkv, g, MB, NB, P, Pmax;
+  float scale_log2;        // scale * log2(e): logits are kept in base-2 units
+};
+
+// Context length clamped to what the launch can address.
+__device__ __forceinline__ int clamped_len(const DecodeParams& a, int s, int BS) {
+  int L = a.context_lens[s];
+  const long cap = min((long)a.MB * BS, (long)a.P * a.Pmax);
+  L = L < 0 ? 0 : L;
+  return L > cap ? (int)cap : L;
+}
+
+template <int D, int NW, int ROWS_MAX>
+struct DecodeSmem {
+  static constexpr int kStride = D + 4;                  // padded row of one head-row
+  static constexpr int kWave = 32 + ROWS_MAX * kStride;  // m[16], l[16], acc[rows][D]
+  static constexpr int kBytes = NW * kWave * 4;
+};
+
+template <typename T, int D, int BS, int NW>
+__global__ void __launch_bounds__(NW * 64)
+paged_decode_kernel(const DecodeParams a) {
+  using Tr = ElemTraits<T>;
+  constexpr bool kBf16 = Tr::kBf16;
+  constexpr int kX = Tr::kX;
+  constexpr int kStep = kBf16 ? 32 : 16;   // tokens per step
+  constexpr int kTpl = kBf16 ? 8 : 4;      // logits per lane per step
+  constexpr int kNc = D / (kBf16 ? 32 : 16);  // 16-byte K chunks per lane per tile
+  constexpr int kNs = D / 16;              // 16-channel slices of the output
+  constexpr int kRowsMax = 16;
+  using Smem = DecodeSmem<D, NW, kRowsMax>;
+
+  extern __shared__ __align__(16) unsigned char smem[];
+  float* red = reinterpret_cast<float*>(smem);
+  int* tbl = reinterpret_cast<int*>(smem + Smem::kBytes);
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int n = lane & 15;
+  const int j = lane >> 4;
+
+  int id = blockIdx.x;
+  const int kvh = id % a.Hkv;
+  id /= a.Hkv;
+  const int p = id % a.Pmax;
+  const int s = id / a.Pmax;
+
+  const int L = clamped_len(a, s, BS);
+  const int nparts = max(1, (L + a.P - 1) / a.P);
+  if (p >= nparts) return;
+  const int tok0 = p * a.P;
+  const int tok1 = min(L, tok0 + a.P);
+  const int nblk = (tok1 - tok0 + BS - 1) / BS;
+
+  // Block-table window of this partition (clamped ids keep every read inside the pool).
+  for (int i = threadIdx.x; i < nblk; i += NW * 64) {
+    const unsigned b = static_cast<unsigned>(a.block_table[(size_t)s * a.MB + tok0 / BS + i]);
+    tbl[i] = static_cast<int>(min(b, static_cast<unsigned>(a.NB - 1)));
+  }
+
+  const int g = a.g;
+  const int rows = kBf16 ? 2 * g : g;
+  const int head = kvh * g + (n % g);
+  const bool row_live = n < rows;
+
+  // Query operand: lane (n, j) holds head-row n's channels of the chunks it multiplies.
+  const T* qrow = static_cast<const T*>(a.q) + ((size_t)s * a.Hq + head) * D;
+  u32x4 qop[kNc];
+#pragma unroll
+  for (int c = 0; c < kNc; ++c) {
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    qop[c] = row_live ? load16(qrow + kX * (4 * c + j)) : z;
+  }
+  __syncthreads();
+
+  const T* kc = static_cast<const T*>(a.k_cache);
+  const T* vc = static_cast<const T*>(a.v_cache);
+  const size_t head_elems = (size_t)D * BS;          // elements of one (block, kv head)
+
+  float m_run = kNegInf;
+  float l_run = 0.f;
+  f32x4 acc[kNs];
+#pragma unroll
+  for (int i = 0; i < kNs; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int nsteps = (tok1 - tok0 + kStep - 1) / kStep;
+  for (int st = wave; st < nsteps; st += NW) {
+    const int base = tok0 + st * kStep;
+    const bool tail = base + kStep > tok1;
+
+    // ---- issue all loads of the step -----------------------------------
+    constexpr int kTiles = kBf16 ? 2 : 1;
+    u32x4 kop[kTiles][kNc];
+#pragma unroll
+    for (int t = 0; t < kTiles; ++t) {
+      // K-tile row n: bf16 rows interleave the step as 8*(n/4) + 4*t + n%4 so that the
+      // score of lane (n, j), register e is token 8*j + 4*t + e; f32 rows are tokens n.
+      const int tok = kBf16 ? base + 8 * (n >> 2) + 4 * t + (n & 3) : base + n;
+      const bool ok = tok < tok1;
+      const int phys = ok ? tbl[(tok - tok0) / BS] : 0;
+      const T* kp = kc + ((size_t)phys * a.Hkv + kvh) * head_elems + (size_t)j * BS * kX +
+                    (size_t)(tok % BS) * kX;
+#pragma unroll
+      for (int c = 0; c < kNc; ++c) {
+        const u32x4 z = {0u, 0u, 0u, 0u};
+        kop[t][c] = ok ? load16(kp + (size_t)4 * c * BS * kX) : z;
+      }
+    }
+    // V operand of slice sl: channel 16*sl + n, tokens base + kTpl*j .. + kTpl - 1.
+    const int tokv = base + kTpl * j;
+    const bool okv = tokv < tok1;
+    const int physv = okv ? tbl[(tokv - tok0) / BS] : 0;
+    const T* vp = vc + ((size_t)physv * a.Hkv + kvh) * head_elems + (size_t)n * BS + (tokv % BS);
+    u32x4 vop[kNs];
+#pragma unroll
+    for (int sl = 0; sl < kNs; ++sl) {
+      const u32x4 z = {0u, 0u, 0u, 0u};
+      vop[sl] = okv ? load16(vp + (size_t)16 * sl * BS) : z;
+    }
+    if (tail) {
+      // zero V elements of tokens past the end (their weight is 0, and 0 * NaN is NaN)
+      const int nv = min(max(tok1 - tokv, 0), kTpl);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        uint32_t mask;
+        if (kBf16) {
+          mask = (2 * w + 1 < nv) ? 0xFFFFFFFFu : ((2 * w < nv) ? 0x0000FFFFu : 0u);
+        } else {
+          mask = (w < nv) ? 0xFFFFFFFFu : 0u;
+        }
+#pragma unroll
+        for (int sl = 0; sl < kNs; ++sl) vop[sl][w] &= mask;
+      }
+    }
+
+    // ---- scores ---------------------------------------------------------
+    float y[kTpl];
+    if constexpr (kBf16) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < kNc; ++c)
+          sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kop[t][c]),
+                                                       __builtin_bit_cast(bf16x8, qop[c]), sc,
+                                                       0, 0, 0);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) y[4 * t + e] = sc[e];
+      }
+    } else {
+      f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < kNc; ++c)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          sc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(kop[0][c][e]),
+                                                    __uint_as_float(qop[c][e]), sc, 0, 0, 0);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) y[e] = sc[e];
+    }
+
+    // ---- online softmax (base 2) ----------------------------------------
+    float mx = kNegInf;
+#pragma unroll
+    for (int v = 0; v < kTpl; ++v) {
+      const bool live = !tail || (base + kTpl * j + v < tok1);
+      y[v] = live ? y[v] * a.scale_log2 : kNegInf;
+      mx = fmaxf(mx, y[v]);
+    }
+    mx = fmaxf(mx, xor16(mx));
+    mx = fmaxf(mx, xor32(mx));
+    const float m_new = fmaxf(m_run, mx);
+    const float m_use = (m_new == kNegInf) ? 0.f : m_new;
+    const float alpha = exp2_fast(m_run - m_use);
+    float pw[kTpl];
+    float psum = 0.f;
+#pragma unroll
+    for (int v = 0; v < kTpl; ++v) {
+      pw[v] = exp2_fast(y[v] - m_use);
+      psum += pw[v];
+    }
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+#pragma unroll
+    for (int sl = 0; sl < kNs; ++sl) acc[sl] *= alpha;
+
+    // ---- P.V --------------------------------------------------------------
+    if constexpr (kBf16) {
+      const bool is_hi = n < g;
+      const bool is_lo = !is_hi && n < rows;
+      bf16x8 pop;
+#pragma unroll
+      for (int v = 0; v < 8; ++v) {
+        const __bf16 hi = f32_to_bf16(pw[v]);
+        const __bf16 lo = f32_to_bf16(pw[v] - bf16_to_f32(hi));
+        pop[v] = is_hi ? hi : (is_lo ? lo : f32_to_bf16(0.f));
+      }
+#pragma unroll
+      for (int sl = 0; sl < kNs; ++sl)
+        acc[sl] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vop[sl]), pop,
+                                                          acc[sl], 0, 0, 0);
+    } else {
+#pragma unroll
+      for (int sl = 0; sl < kNs; ++sl)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          acc[sl] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(vop[sl][e]), pw[e],
+                                                         acc[sl], 0, 0, 0);
+    }
+  }
+
+  // ---- merge the waves of the workgroup ------------------------------------
+  float lsum = l_run + xor16(l_run);
+  lsum += xor32(lsum);
+  float* wr = red + wave * Smem::kWave;
+  if (row_live) {
+    if (j == 0) {
+      wr[n] = m_run;
+      wr[16 + n] = lsum;
+    }
+#pragma unroll
+    for (int sl = 0; sl < kNs; ++sl)
+      *reinterpret_cast<f32x4*>(wr + 32 + n * Smem::kStride + 16 * sl + 4 * j) = acc[sl];
+  }
+  __syncthreads();
+
+  const bool single = nparts == 1;
+  for (int idx = threadIdx.x; idx < g * D; idx += NW * 64) {
+    const int h = idx / D;
+    const int d = idx % D;
+    float M = kNegInf;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, red[w * Smem::kWave + h]);
+    float num = 0.f, den = 0.f;
+    if (M != kNegInf) {
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        const float* r = red + w * Smem::kWave;
+        const float f = exp2_fast(r[h] - M);
+        den += f * r[16 + h];
+        float v = r[32 + h * Smem::kStride + d];
+        if (kBf16) v += r[32 + (h + g) * Smem::kStride + d];
+        num += f * v;
+      }
+    }
+    const size_t row = (size_t)s * a.Hq + kvh * g + h;
+    if (single) {
+      const float o = (M == kNegInf) ? 0.f : num / den;
+      if constexpr (kBf16)
+        static_cast<uint16_t*>(a.out)[row * D + d] = bf16_bits(o);
+      else
+        static_cast<float*>(a.out)[row * D + d] = o;
+    } else {
+      a.part_acc[(row * a.Pmax + p) * D + d] = num;
+      if (d == 0) {
+        a.part_ml[(row * a.Pmax + p) * 2 + 0] = M;
+        a.part_ml[(row * a.Pmax + p) * 2 + 1] = den;
+      }
+    }
+  }
+}
+
+// Log-sum-exp merge of the partitions of one (sequence, query head):
+//   M = max_p m_p,  out = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p.
+template <typename T, int D, int BS>
+__global__ void __launch_bounds__(64)
+reduce_partitions_kernel(const DecodeParams a) {
+  const int s = blockIdx.x / a.Hq;
+  const int h = blockIdx.x % a.Hq;
+  const int L = clamped_len(a, s, BS);
+  const int nparts = max(1, (L + a.P - 1) / a.P);
+  if (nparts <= 1) return;
+  const size_t row = (size_t)s * a.Hq + h;
+  const float* ml = a.part_ml + row * a.Pmax * 2;
+  const float* acc = a.part_acc + row * a.Pmax * D;
+  float M = kNegInf;
+  for (int q = 0; q < nparts; ++q) M = fmaxf(M, ml[2 * q]);
+  for (int d = threadIdx.x; d < D; d += 64) {
+    float num = 0.f, den = 0.f;
+    if (M != kNegInf) {
+      for (int q = 0; q < nparts; ++q) {
+        const float f = exp2_fast(ml[2 * q] - M);
+        den += f * ml[2 * q + 1];
+        num += f * acc[(size_t)q * D + d];
+      }
+    }
+    const float o = (M == kNegInf || den == 0.f) ? 0.f : num / den;
+    if constexpr (ElemTraits<T>::kBf16)
+      static_cast<uint16_t*>(a.out)[row * D + d] = bf16_bits(o);
+    else
+      static_cast<float*>(a.out)[row * D + d] = o;
+  }
+}
+
+constexpr int kWaves = 4;
+
+template <typename T, int D, int BS>
+hipError_t launch_decode(const DecodeParams& a, hipStream_t stream) {
+  using Smem = DecodeSmem<D, kWaves, 16>;
+  const int tbl_bytes = ((a.P / BS) * 4 + 15) / 16 * 16;
+  const size_t lds = Smem::kBytes + tbl_bytes;
+  const long grid = (long)a.Hkv * a.Pmax * a.S;
+  hipLaunchKernelGGL((paged_decode_kernel<T, D, BS, kWaves>), dim3((unsigned)grid),
+                     dim3(kWaves * 64), lds, stream, a);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess || a.Pmax == 1) return err;
+  hipLaunchKernelGGL((reduce_partitions_kernel<T, D, BS>), dim3((unsigned)((long)a.S * a.Hq)),
+                     dim3(64), 0, stream, a);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t dispatch_decode(const DecodeParams& a, int D, int BS, hipStream_t stream) {
+#define PA_CASE(DD, BB) \
+  if (D == DD && BS == BB) return launch_decode<T, DD, BB>(a, stream);
+  PA_CASE(64, 8) PA_CASE(64, 16) PA_CASE(64, 32)
+  PA_CASE(128, 8) PA_CASE(128, 16) PA_CASE(128, 32)
+#undef PA_CASE
+  return hipErrorInvalidValue;
+}
+
+}  // namespace pa
+
+// ---------------------------------------------------------------------------
+// host entry points
+// ---------------------------------------------------------------------------
+namespace {
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int group_limit(pa_dtype dt) { return dt == PA_DTYPE_BF16 ? 8 : 16; }
+
+pa_status check_shapes(int num_heads, int num_kv_heads, int head_dim, int block_size,
+                       pa_dtype dtype) {
+  if (dtype != PA_DTYPE_F32 && dtype != PA_DTYPE_BF16) return PA_ERR_UNSUPPORTED;
+  if (num_heads <= 0 || num_kv_heads <= 0) return PA_ERR_INVALID_ARG;
+  if (num_heads % num_kv_heads) return PA_ERR_INVALID_ARG;
+  if (head_dim != 64 && head_dim != 128) return PA_ERR_UNSUPPORTED;
+  if (block_size != 8 && block_size != 16 && block_size != 32) return PA_ERR_UNSUPPORTED;
+  if (num_heads / num_kv_heads > group_limit(dtype)) return PA_ERR_UNSUPPORTED;
+  return PA_OK;
+}
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+}  // namespace
+
+extern "C" int pa_default_partition_size(int num_seqs, int num_kv_heads, int max_context_len,
+                                         pa_dtype dtype) {
+  (void)num_seqs;
+  (void)num_kv_heads;
+  (void)max_context_len;
+  (void)dtype;
+  return 256;
+}
+
+extern "C" size_t pa_paged_attention_workspace_size(int num_seqs, int num_heads, int num_kv_heads,
+                                                    int head_dim, int max_context_len,
+                                                    int partition_size, pa_dtype dtype) {
+  if (num_seqs < 0 || max_context_len < 0) return 0;
+  if (check_shapes(num_heads, num_kv_heads, head_dim, 16, dtype) != PA_OK) return 0;
+  const int P = partition_size ? partition_size
+                               : pa_default_partition_size(num_seqs, num_kv_heads,
+                                                           max_context_len, dtype);
+  if (P < 64 || P > 8192 || P % 64) return 0;
+  const size_t pmax = std::max(1, (max_context_len + P - 1) / P);
+  if (pmax <= 1) return 0;
+  const size_t rows = (size_t)num_seqs * num_heads * pmax;
+  return round_up(rows * 2 * sizeof(float), 256) + round_up(rows * head_dim * sizeof(float), 256);
+}
+
+extern "C" pa_status pa_paged_attention(void* out, const void* query, const int32_t* block_table,
+                                        const int32_t* context_lens, const void* k_cache,
+                                        const void* v_cache, int num_seqs, int num_heads,
+                                        int num_kv_heads, int head_dim, int block_size,
+                                        int max_blocks_per_seq, int num_blocks,
+                                        int max_context_len, float scale, pa_dtype dtype,
+                                        int partition_size, void* workspace,
+                                        size_t workspace_bytes, void* stream) {
+  pa_status st = check_shapes(num_heads, num_kv_heads, head_dim, block_size, dtype);
+  if (st != PA_OK) return st;
+  if (num_seqs < 0 || max_blocks_per_seq <= 0 || num_blocks <= 0 || max_context_len < 0)
+    return PA_ERR_INVALID_ARG;
+  if ((long)max_context_len > (long)max_blocks_per_seq * block_size) return PA_ERR_INVALID_ARG;
+  if (partition_size != 0 && (partition_size < 64 || partition_size > 8192 || partition_size % 64))
+    return PA_ERR_INVALID_ARG;
+  if (num_seqs == 0) return PA_OK;
+  if (!out || !query || !block_table || !context_lens || !k_cache || !v_cache)
+    return PA_ERR_INVALID_ARG;
+  if (!aligned(out, 16) || !aligned(query, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
+      !aligned(block_table, 4) || !aligned(context_lens, 4))
+    return PA_ERR_INVALID_ARG;
+
+  const int P = partition_size ? partition_size
+                               : pa_default_partition_size(num_seqs, num_kv_heads,
+                                                           max_context_len, dtype);
+  const int pmax = std::max(1, (max_context_len + P - 1) / P);
+  const long grid = (long)num_kv_heads * pmax * num_seqs;
+  if (grid > 0x7FFFFFFFL || (long)num_seqs * num_heads > 0x7FFFFFFFL) return PA_ERR_INVALID_ARG;
+
+  const size_t need = pa_paged_attention_workspace_size(num_seqs, num_heads, num_kv_heads,
+                                                        head_dim, max_context_len, P, dtype);
+  if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 16)))
+    return PA_ERR_WORKSPACE;
+
+  pa::DecodeParams a;
+  a.out = out;
+  a.q = query;
+  a.block_table = block_table;
+  a.context_lens = context_lens;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.S = num_seqs;
+  a.Hq = num_heads;
+  a.Hkv = num_kv_heads;
+  a.g = num_heads / num_kv_heads;
+  a.MB = max_blocks_per_seq;
+  a.NB = num_blocks;
+  a.P = P;
+  a.Pmax = pmax;
+  a.scale_log2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
+  const size_t rows = (size_t)num_seqs * num_heads * pmax;
+  a.part_ml = need ? static_cast<float*>(workspace) : nullptr;
+  a.part_acc = need ? reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                               round_up(rows * 2 * sizeof(float), 256))
+                    : nullptr;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t err = dtype == PA_DTYPE_BF16
+                       ? pa::dispatch_decode<uint16_t>(a, head_dim, block_size, s)
+                       : pa::dispatch_decode<float>(a, head_dim, block_size, s);
+  return err == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
