@@ -1,0 +1,279 @@
+"""Decode-step benchmark of the paged-KV library on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 1]
+
+One step is the whole hot path over one batch: reshape_and_cache of the
+step's new tokens (one per sequence), then paged decode attention of every
+sequence over its paged K/V.  The default workload is the Llama-3-8B-shaped
+decode batch: 64 sequences, 32 query heads / 8 KV heads, head size 128,
+block size 16, context lengths uniform in [128, 2048], bfloat16.
+
+Inputs are resident in HBM before timing starts; the pools are written by the
+library's own reshape_and_cache.  To keep the 256 MB Infinity Cache from
+serving repeated steps, the step rotates over ``--replicas`` copies of the
+K/V pools (cold headline); a warm run over one copy is reported beside it.
+
+Prints ONE JSON line with the decode-step throughput (KV bytes read per
+second), the decode call's roofline (HIP events around every launch on the
+stream it runs on), and the CPU oracle's throughput on a bounded sample of
+the same workload (reported baseline).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "paged-attn decode KV GB/s (% of HBM peak) + µs/step, Llama-3-8B shape, 1 GPU"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, AMD's published peak
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
+KERNEL_SOURCE = os.path.join(ROOT, "paged_kv_cache_425_amd", "csrc", "paged_attention.hip")
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse_args():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", type=int, default=1, choices=[0, 1, 2, 3, 4])
+    ap.add_argument("--block-size", type=int, default=None, help="block size of config 2")
+    ap.add_argument("--variant", default=None, help="config 3: prefix | parallel-sampling")
+    ap.add_argument("--seed", type=int, default=None)
+    ap.add_argument("--partition-size", type=int, default=None,
+                    help="tokens per partition (0 = library default)")
+    ap.add_argument("--replicas", type=int, default=4,
+                    help="copies of the K/V pools the steps rotate over")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0,
+                    help="seconds of oracle work in the CPU baseline")
+    return ap.parse_args()
+
+
+# ---------------------------------------------------------------------------
+def algorithmic_bytes(w) -> dict:
+    """Bytes one decode step must move at the least.
+
+    kv: every context position's K and V row of its KV head, read once;
+    other: the query (read), the output (written), the block-table entries of
+    the blocks in use and the context lengths.
+    """
+    elt = 2 if w.dtype == "bf16" else 4
+    lens = w.context_lens.astype(np.int64)
+    kv = int(lens.sum()) * 2 * w.num_kv_heads * w.head_dim * elt
+    q = w.num_seqs * w.num_heads * w.head_dim * elt
+    table = int((-(-lens // w.block_size)).sum()) * 4
+    return {"kv": kv, "other": 2 * q + table + 4 * w.num_seqs, "total": kv + 2 * q + table + 4 * w.num_seqs}
+
+
+def source_digest() -> str:
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def load_traffic(workload: str):
+    """Measured HBM bytes per decode launch, if the counters were taken on the current kernel."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_sha256") != source_digest() or rec.get("workload") != workload:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+# ---------------------------------------------------------------------------
+def cpu_baseline(w, budget_s: float) -> dict:
+    """The CPU oracle on a bounded sample of the same step (reported baseline)."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        blas_threads = 1
+    hist, new = w.history_records, w.new_records
+    kc, vc = oracle.empty_pools(w.num_blocks, w.num_kv_heads, w.head_dim, w.block_size, w.dtype)
+    oracle.reshape_and_cache(w.rec_key[hist], w.rec_value[hist], w.rec_slot[hist], kc, vc,
+                             inplace=True)
+    elt = 2 if w.dtype == "bf16" else 4
+    per_token = 2 * w.num_kv_heads * w.head_dim * elt
+    t0 = time.perf_counter()
+    oracle.reshape_and_cache(w.rec_key[new], w.rec_value[new], w.rec_slot[new], kc, vc,
+                             inplace=True)
+    done, kv = 0, 0
+    for s in range(w.num_seqs):
+        oracle.paged_attention(w.query, w.block_table, w.context_lens, kc, vc, w.scale, w.dtype,
+                               seqs=[s])
+        done += 1
+        kv += int(w.context_lens[s]) * per_token
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": round(kv / dt / 1e9, 4), "unit": "GB/s", "cores": int(blas_threads),
+            "kind": "oracle",
+            "sample": (f"float64 NumPy oracle: scatter of the step's {len(new)} new tokens, then "
+                       f"decode of the first {done} of {w.num_seqs} sequences "
+                       f"({kv / 1e6:.1f} MB of KV) in {dt:.1f} s; "
+                       f"{len(os.sched_getaffinity(0))} cores visible, BLAS pool "
+                       f"{blas_threads} threads")}
+
+
+# ---------------------------------------------------------------------------
+def main() -> int:
+    args = parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the decode path runs on one GPU and has no multi-GPU mode)", file=sys.stderr)
+        return 2
+    import torch
+
+    import paged_kv_cache_425_amd as pk
+    from workloads import make_config
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU (no HIP device visible)", file=sys.stderr)
+        return 1
+    pk.load_library()          # raises if the HIP library was not built
+    dev = torch.device("cuda:0")
+
+    t = time.perf_counter()
+    w = make_config(args.config, seed=args.seed, block_size=args.block_size, variant=args.variant)
+    log(f"workload {w.name}: S={w.num_seqs} Hq={w.num_heads} Hkv={w.num_kv_heads} "
+        f"D={w.head_dim} BS={w.block_size} NB={w.num_blocks} max_len={w.max_context_len} "
+        f"({time.perf_counter() - t:.1f} s to draw)")
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+
+    def up(a):
+        if w.dtype == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(tdt).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev)
+
+    # ---- device inputs ------------------------------------------------------
+    hist, new = w.history_records, w.new_records
+    kshape = pk.k_cache_shape(w.num_blocks, w.num_kv_heads, w.head_dim, w.block_size, tdt)
+    vshape = pk.v_cache_shape(w.num_blocks, w.num_kv_heads, w.head_dim, w.block_size, tdt)
+    kc0 = torch.full(kshape, float("nan"), dtype=tdt, device=dev)
+    vc0 = torch.full(vshape, float("nan"), dtype=tdt, device=dev)
+    pk.reshape_and_cache(up(w.rec_key[hist]), up(w.rec_value[hist]),
+                         torch.from_numpy(w.rec_slot[hist]).to(dev), kc0, vc0)
+    pools = [(kc0, vc0)] + [(kc0.clone(), vc0.clone()) for _ in range(max(1, args.replicas) - 1)]
+    key_new, val_new = up(w.rec_key[new]), up(w.rec_value[new])
+    slot_new = torch.from_numpy(w.rec_slot[new]).to(dev)
+    query = up(w.query)
+    table = torch.from_numpy(w.block_table).to(dev)
+    lens = torch.from_numpy(w.context_lens).to(dev)
+    out = torch.empty_like(query)
+    part = args.partition_size if args.partition_size is not None else (w.partition_size or 0)
+    need = pk.workspace_size(w.num_seqs, w.num_heads, w.num_kv_heads, w.head_dim,
+                             w.max_context_len, part, tdt)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    writes = [pk.prepare_reshape_and_cache(key_new, val_new, slot_new, kc, vc) for kc, vc in pools]
+    decodes = [pk.prepare_paged_attention(query, table, lens, kc, vc, w.scale,
+                                          max_context_len=w.max_context_len, out=out,
+                                          partition_size=part, workspace=ws)
+               for kc, vc in pools]
+    nb = algorithmic_bytes(w)
+    K, W = args.steps, args.warmup
+
+    def run(n_rep: int, steps: int, timed: bool):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(steps)] if timed else None
+        for i in range(steps):
+            r = i % n_rep
+            writes[r]()
+            if timed:
+                ev[i][0].record()
+            decodes[r]()
+            if timed:
+                ev[i][1].record()
+        return ev
+
+    # ---- cold headline: rotate over the replicas ------------------------------
+    run(len(pools), W, False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev = run(len(pools), K, True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    decode_ms = np.array([a.elapsed_time(b) for a, b in ev])
+    log(f"cold: {wall / K * 1e6:.1f} us/step wall, decode call median "
+        f"{np.median(decode_ms) * 1e3:.1f} us")
+
+    # ---- warm: one pool, repeated ----------------------------------------------
+    run(1, W, False)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    evw = run(1, K, True)
+    torch.cuda.synchronize()
+    wall_w = time.perf_counter() - t1
+    decode_w = np.array([a.elapsed_time(b) for a, b in evw])
+    log(f"warm: {wall_w / K * 1e6:.1f} us/step wall, decode call median "
+        f"{np.median(decode_w) * 1e3:.1f} us")
+
+    ms_step = wall / K * 1e3
+    value = nb["kv"] / (ms_step * 1e-3) / 1e9
+    decode_avg_s = float(decode_ms.mean()) * 1e-3
+    achieved = nb["total"] / decode_avg_s / 1e9
+    traffic = load_traffic(w.name)
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(ms_step, 5),
+        "us_per_step": round(ms_step * 1e3, 2),
+        "hbm_frac": round(value / HBM_PEAK_GBS, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded N(0,1) q/K/V, random block tables)",
+        "config": {"workload": w.name, "num_seqs": w.num_seqs, "num_heads": w.num_heads,
+                   "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
+                   "block_size": w.block_size, "num_blocks": w.num_blocks,
+                   "max_context_len": w.max_context_len,
+                   "total_context_tokens": int(w.context_lens.astype(np.int64).sum()),
+                   "partition_size": part or pk.default_partition_size(
+                       w.num_seqs, w.num_kv_heads, w.max_context_len, tdt),
+                   "kv_bytes_per_step": nb["kv"], "seed": w.info["seed"],
+                   "pool_replicas": len(pools), "parallelism": "none (1 GPU)"},
+        "decode_us": {"mean": round(float(decode_ms.mean()) * 1e3, 2),
+                      "median": round(float(np.median(decode_ms)) * 1e3, 2),
+                      "p10": round(float(np.percentile(decode_ms, 10)) * 1e3, 2),
+                      "p90": round(float(np.percentile(decode_ms, 90)) * 1e3, 2)},
+        "warm": {"us_per_step": round(wall_w / K * 1e6, 2),
+                 "value": round(nb["kv"] / (wall_w / K) / 1e9, 2),
+                 "decode_us_mean": round(float(decode_w.mean()) * 1e3, 2)},
+        "roofline": {"kernel": "pa_paged_attention (paged_decode_kernel + reduce_partitions_kernel)",
+                     "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic,
+                     "algorithmic_bytes_per_launch": nb["total"]},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle) ...")
+        line["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -200,3 +200,55 @@ def gather_kv(block_table: torch.Tensor, context_lens: torch.Tensor, k_cache: to
                           NB, int(max_context_len), _dtype_code(k_cache), _stream(dev, stream))
     _check(st, "pa_gather_kv")
     return k_out, v_out
+
+
+# ---------------------------------------------------------------------------
+# prepared calls: validate once, then launch with fixed pointers (tight loops)
+# ---------------------------------------------------------------------------
+class PreparedCall:
+    """A library call whose tensors were checked once; calling it launches again.
+
+    The tensors are held so their memory stays valid; the stream is read at
+    preparation time.
+    """
+
+    def __init__(self, fn, args: tuple, what: str, keep: tuple):
+        self._fn, self._args, self._what, self._keep = fn, args, what, keep
+
+    def __call__(self) -> None:
+        st = self._fn(*self._args)
+        if st != PA_OK:
+            _check(st, self._what)
+
+
+def prepare_paged_attention(query, block_table, context_lens, k_cache, v_cache, scale, *,
+                            max_context_len: int, out, partition_size: int = 0,
+                            workspace=None, stream=None) -> PreparedCall:
+    """Check the arguments as paged_attention does and return a re-launchable call."""
+    lib = load_library()
+    dev = query.device
+    # one checked call validates every argument (and runs once)
+    paged_attention(query, block_table, context_lens, k_cache, v_cache, scale,
+                    max_context_len=max_context_len, out=out, partition_size=partition_size,
+                    workspace=workspace, stream=stream)
+    NB, Hkv, D, BS = _cache_dims(k_cache, v_cache)
+    S, Hq, _ = query.shape
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    args = (_ptr(out), _ptr(query), _ptr(block_table), _ptr(context_lens), _ptr(k_cache),
+            _ptr(v_cache), S, Hq, Hkv, D, BS, block_table.shape[1], NB, int(max_context_len),
+            float(scale), _dtype_code(query), int(partition_size), _ptr(workspace), ws_bytes,
+            _stream(dev, stream))
+    return PreparedCall(lib.pa_paged_attention, args, "pa_paged_attention",
+                        (query, block_table, context_lens, k_cache, v_cache, out, workspace))
+
+
+def prepare_reshape_and_cache(key, value, slot_mapping, k_cache, v_cache,
+                              stream=None) -> PreparedCall:
+    """Check the arguments as reshape_and_cache does and return a re-launchable call."""
+    lib = load_library()
+    reshape_and_cache(key, value, slot_mapping, k_cache, v_cache, stream=stream)
+    NB, Hkv, D, BS = _cache_dims(k_cache, v_cache)
+    args = (_ptr(key), _ptr(value), _ptr(slot_mapping), _ptr(k_cache), _ptr(v_cache),
+            key.shape[0], Hkv, D, BS, NB, _dtype_code(key), _stream(key.device, stream))
+    return PreparedCall(lib.pa_reshape_and_cache, args, "pa_reshape_and_cache",
+                        (key, value, slot_mapping, k_cache, v_cache))
