@@ -11,7 +11,7 @@ block size 16, context lengths uniform in [128, 2048], bfloat16.
 Inputs are resident in HBM before timing starts; the pools are written by the
 library's own reshape_and_cache.  To keep the 256 MB Infinity Cache from
 serving repeated steps, the step rotates over ``--replicas`` copies of the
-K/V pools (cold headline); a warm run over one copy is reported beside it.
+K/V pools (cold headline); ``--warm`` adds a run over one copy.
 
 Prints ONE JSON line with the decode-step throughput (KV bytes read per
 second), the decode call's roofline (HIP events around every launch on the
@@ -57,7 +57,9 @@ def parse_args():
     ap.add_argument("--replicas", type=int, default=4,
                     help="copies of the K/V pools the steps rotate over")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-budget", type=float, default=15.0,
+    ap.add_argument("--warm", action="store_true",
+                    help="also time K steps over one pool copy (Infinity Cache warm)")
+    ap.add_argument("--cpu-budget", type=float, default=10.0,
                     help="seconds of oracle work in the CPU baseline")
     return ap.parse_args()
 
@@ -110,23 +112,31 @@ def cpu_baseline(w, budget_s: float) -> dict:
                              inplace=True)
     elt = 2 if w.dtype == "bf16" else 4
     per_token = 2 * w.num_kv_heads * w.head_dim * elt
+    steps, done, kv = 0, 0, 0
     t0 = time.perf_counter()
-    oracle.reshape_and_cache(w.rec_key[new], w.rec_value[new], w.rec_slot[new], kc, vc,
-                             inplace=True)
-    done, kv = 0, 0
-    for s in range(w.num_seqs):
-        oracle.paged_attention(w.query, w.block_table, w.context_lens, kc, vc, w.scale, w.dtype,
-                               seqs=[s])
-        done += 1
-        kv += int(w.context_lens[s]) * per_token
-        if time.perf_counter() - t0 >= budget_s:
-            break
+    while True:
+        # one whole step: the scatter of the new tokens, then every sequence's decode
+        oracle.reshape_and_cache(w.rec_key[new], w.rec_value[new], w.rec_slot[new], kc, vc,
+                                 inplace=True)
+        for s in range(w.num_seqs):
+            oracle.paged_attention(w.query, w.block_table, w.context_lens, kc, vc, w.scale,
+                                   w.dtype, seqs=[s])
+            done += 1
+            kv += int(w.context_lens[s]) * per_token
+            if time.perf_counter() - t0 >= budget_s:
+                break
+        else:
+            steps += 1
+            if time.perf_counter() - t0 < budget_s:
+                continue
+        break
     dt = time.perf_counter() - t0
     return {"value": round(kv / dt / 1e9, 4), "unit": "GB/s", "cores": int(blas_threads),
             "kind": "oracle",
-            "sample": (f"float64 NumPy oracle: scatter of the step's {len(new)} new tokens, then "
-                       f"decode of the first {done} of {w.num_seqs} sequences "
-                       f"({kv / 1e6:.1f} MB of KV) in {dt:.1f} s; "
+            "sample": (f"float64 NumPy oracle, same workload: {steps} whole steps (scatter of "
+                       f"{len(new)} new tokens + decode of all {w.num_seqs} sequences) plus "
+                       f"{done - steps * w.num_seqs} sequences of a partial step, "
+                       f"{kv / 1e6:.1f} MB of KV in {dt:.1f} s; "
                        f"{len(os.sched_getaffinity(0))} cores visible, BLAS pool "
                        f"{blas_threads} threads")}
 
@@ -189,6 +199,8 @@ def main() -> int:
                for kc, vc in pools]
     nb = algorithmic_bytes(w)
     K, W = args.steps, args.warmup
+    part_used = part or pk.default_partition_size(w.num_seqs, w.num_kv_heads, w.max_context_len, tdt)
+    needs_reduce = w.max_context_len > part_used
 
     def run(n_rep: int, steps: int, timed: bool):
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -214,16 +226,21 @@ def main() -> int:
     log(f"cold: {wall / K * 1e6:.1f} us/step wall, decode call median "
         f"{np.median(decode_ms) * 1e3:.1f} us")
 
-    # ---- warm: one pool, repeated ----------------------------------------------
-    run(1, W, False)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    evw = run(1, K, True)
-    torch.cuda.synchronize()
-    wall_w = time.perf_counter() - t1
-    decode_w = np.array([a.elapsed_time(b) for a, b in evw])
-    log(f"warm: {wall_w / K * 1e6:.1f} us/step wall, decode call median "
-        f"{np.median(decode_w) * 1e3:.1f} us")
+    # ---- warm (optional): one pool, repeated ----------------------------------
+    warm = None
+    if args.warm:
+        run(1, W, False)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        evw = run(1, K, True)
+        torch.cuda.synchronize()
+        wall_w = time.perf_counter() - t1
+        decode_w = np.array([a.elapsed_time(b) for a, b in evw])
+        log(f"warm: {wall_w / K * 1e6:.1f} us/step wall, decode call median "
+            f"{np.median(decode_w) * 1e3:.1f} us")
+        warm = {"us_per_step": round(wall_w / K * 1e6, 2),
+                "value": round(nb["kv"] / (wall_w / K) / 1e9, 2),
+                "decode_us_mean": round(float(decode_w.mean()) * 1e3, 2)}
 
     ms_step = wall / K * 1e3
     value = nb["kv"] / (ms_step * 1e-3) / 1e9
@@ -250,18 +267,17 @@ def main() -> int:
                    "block_size": w.block_size, "num_blocks": w.num_blocks,
                    "max_context_len": w.max_context_len,
                    "total_context_tokens": int(w.context_lens.astype(np.int64).sum()),
-                   "partition_size": part or pk.default_partition_size(
-                       w.num_seqs, w.num_kv_heads, w.max_context_len, tdt),
+                   "partition_size": part_used,
                    "kv_bytes_per_step": nb["kv"], "seed": w.info["seed"],
+                   "pool_bytes_each": int(kc0.numel() * kc0.element_size()),
                    "pool_replicas": len(pools), "parallelism": "none (1 GPU)"},
         "decode_us": {"mean": round(float(decode_ms.mean()) * 1e3, 2),
                       "median": round(float(np.median(decode_ms)) * 1e3, 2),
                       "p10": round(float(np.percentile(decode_ms, 10)) * 1e3, 2),
                       "p90": round(float(np.percentile(decode_ms, 90)) * 1e3, 2)},
-        "warm": {"us_per_step": round(wall_w / K * 1e6, 2),
-                 "value": round(nb["kv"] / (wall_w / K) / 1e9, 2),
-                 "decode_us_mean": round(float(decode_w.mean()) * 1e3, 2)},
-        "roofline": {"kernel": "pa_paged_attention (paged_decode_kernel + reduce_partitions_kernel)",
+        "warm": warm,
+        "roofline": {"kernel": "pa_paged_attention: paged_decode_kernel" + (
+                         " + reduce_partitions_kernel" if needs_reduce else " (one partition, no reduce)"),
                      "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic,

@@ -80,7 +80,13 @@ const char* pa_status_string(pa_status status);
 
 /*
  * Partition length (tokens) pa_paged_attention uses for these sizes when the
- * caller passes partition_size = 0.  Always a multiple of 64.
+ * caller passes partition_size = 0.  Always a multiple of 64 in [64, 8192].
+ * When num_seqs * num_kv_heads gives every compute unit of the current
+ * device two workgroups and max_context_len <= 8192, one partition covers the
+ * longest sequence (no merge step); otherwise the context is split so that
+ * the grid holds about four workgroups per compute unit, with partitions of
+ * at least 512 tokens.  The value depends on the current device's compute
+ * unit count, so size the workspace on the device that runs the call.
  */
 int pa_default_partition_size(int num_seqs, int num_kv_heads, int max_context_len,
                               pa_dtype dtype);
@@ -115,11 +121,15 @@ size_t pa_paged_attention_workspace_size(int num_seqs, int num_heads, int num_kv
  *                  must be <= max_blocks_per_seq * block_size)
  *   partition_size 0 = default, else a multiple of 64 in [64, 8192]: each
  *                  sequence is split into partitions of this many tokens that
- *                  run in parallel and are merged by a log-sum-exp reduce
+ *                  run in parallel; sequences longer than one partition are
+ *                  merged by a second, log-sum-exp reduce kernel on the same
+ *                  stream
  *   workspace      device scratch of at least
  *                  pa_paged_attention_workspace_size(...) bytes, 16-byte
- *                  aligned; may be NULL when that size is 0.  Two calls in
- *                  flight at once must not share a workspace.
+ *                  aligned, any contents; may be NULL when that size is 0.
+ *                  It holds per-partition (max, sum, partial output) rows
+ *                  between the two kernels.  Two calls in flight at once must
+ *                  not share a workspace.
  */
 pa_status pa_paged_attention(void* out, const void* query, const int32_t* block_table,
                              const int32_t* context_lens, const void* k_cache,

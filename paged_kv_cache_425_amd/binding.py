@@ -227,6 +227,11 @@ def prepare_paged_attention(query, block_table, context_lens, k_cache, v_cache, 
     """Check the arguments as paged_attention does and return a re-launchable call."""
     lib = load_library()
     dev = query.device
+    need = workspace_size(query.shape[0], query.shape[1], k_cache.shape[1],
+                          k_cache.shape[2] * k_cache.shape[4], max_context_len, partition_size,
+                          query.dtype) if k_cache.dim() == 5 and query.dim() == 3 else 0
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     # one checked call validates every argument (and runs once)
     paged_attention(query, block_table, context_lens, k_cache, v_cache, scale,
                     max_context_len=max_context_len, out=out, partition_size=partition_size,

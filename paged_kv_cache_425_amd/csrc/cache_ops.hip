@@ -15,7 +15,11 @@ namespace pa {
 
 constexpr int kCopyThreads = 256;
 
-// One workgroup per token.
+// One workgroup per token.  Thread c moves 16-byte chunk c of the token's K
+// (c < Hkv*D/X) or V (the rest): K chunks land whole in the cache, V chunks
+// are split into X single-element stores along the cache's token axis.  The
+// source chunk is loaded before the slot is looked at, so the two loads are
+// in flight together.
 template <typename T>
 __global__ void __launch_bounds__(kCopyThreads)
 reshape_and_cache_kernel(const T* __restrict__ key, const T* __restrict__ value,
@@ -23,23 +27,27 @@ reshape_and_cache_kernel(const T* __restrict__ key, const T* __restrict__ value,
                          T* __restrict__ v_cache, int Hkv, int D, int BS, int NB) {
   constexpr int X = ElemTraits<T>::kX;
   const int i = blockIdx.x;
-  const int64_t slot = slot_mapping[i];
-  if (slot < 0 || slot >= (int64_t)NB * BS) return;
-  const int64_t blk = slot / BS;
-  const int off = (int)(slot % BS);
-  const int chunks = D / X;
-  const T* ksrc = key + (size_t)i * Hkv * D;
-  const T* vsrc = value + (size_t)i * Hkv * D;
-  for (int c = threadIdx.x; c < Hkv * chunks; c += kCopyThreads) {
-    const int h = c / chunks;
-    const int dc = c % chunks;
-    T* dst = k_cache + (((size_t)blk * Hkv + h) * chunks + dc) * BS * X + (size_t)off * X;
-    store16(dst, load16(ksrc + (size_t)h * D + dc * X));
-  }
-  for (int e = threadIdx.x; e < Hkv * D; e += kCopyThreads) {
-    const int h = e / D;
-    const int d = e % D;
-    v_cache[(((size_t)blk * Hkv + h) * D + d) * BS + off] = vsrc[e];
+  const int chunks = D / X;                 // 16-byte chunks per head
+  const int nchunk = Hkv * chunks;          // per token, for K and for V
+  const size_t src0 = (size_t)i * Hkv * D;
+  for (int c = threadIdx.x; c < 2 * nchunk; c += kCopyThreads) {
+    const bool is_v = c >= nchunk;
+    const int cc = is_v ? c - nchunk : c;
+    const u32x4 val = load16((is_v ? value : key) + src0 + (size_t)cc * X);
+    const int64_t slot = slot_mapping[i];
+    if (slot < 0 || slot >= (int64_t)NB * BS) continue;
+    const int64_t blk = slot / BS;
+    const int off = (int)(slot % BS);
+    const int h = cc / chunks;
+    const int dc = cc % chunks;
+    if (!is_v) {
+      store16(k_cache + (((size_t)blk * Hkv + h) * chunks + dc) * BS * X + (size_t)off * X, val);
+    } else {
+      T* dst = v_cache + (((size_t)blk * Hkv + h) * D + (size_t)dc * X) * BS + off;
+      const T* e = reinterpret_cast<const T*>(&val);
+#pragma unroll
+      for (int k = 0; k < X; ++k) dst[(size_t)k * BS] = e[k];
+    }
   }
 }
 

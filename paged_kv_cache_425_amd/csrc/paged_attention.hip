@@ -9,15 +9,26 @@
 // softmax over the whole sequence.
 //
 // Work decomposition
-//   workgroup = (kv head, partition of P tokens, sequence); the kv head is the
-//     fastest-varying index so consecutive workgroups -- which the dispatcher
-//     spreads round-robin over the 8 XCDs -- carry equal work.
-//   NW waves per workgroup take the partition's steps round-robin.
+//   workgroup = (kv head, sequence, partition of P tokens); the kv head is the
+//     fastest-varying index, so consecutive workgroups -- which the dispatcher
+//     spreads round-robin over the 8 XCDs -- carry equal work, and the
+//     partition index is the slowest, so the workgroups of partitions past a
+//     sequence's end (which exit at once) come last.
+//   NW waves per workgroup take the partition's 32-token steps round-robin;
+//     each wave keeps the loads of its next step in flight while it computes
+//     the current one (two register buffers; the prefetch is issued on every
+//     iteration -- past the last step it re-reads the current, cached step --
+//     so the compiler's wait counts never fall back to "wait for everything").
 //   One step is 32 tokens (bf16) or 16 tokens (f32) of one KV head, shared by
 //     the whole query-head group (GQA): each K/V byte is fetched once per group.
-//   Sequences longer than one partition write (max, sum, unnormalised output)
-//     per partition to the workspace; a second kernel merges them with a
-//     log-sum-exp reduce.  Single-partition sequences write the output directly.
+//   Sequences that fit in one partition write their output directly.  Longer
+//     ones write (max, sum, unnormalised output) per partition to the
+//     workspace and a second kernel merges the partitions with a log-sum-exp
+//     reduce.  When the batch has enough (sequence, kv head) pairs to fill the
+//     GPU the default partition covers the longest sequence, so no merge is
+//     needed; a merge inside the first kernel would need an agent-scope
+//     release per workgroup, which on this multi-XCD part writes back and
+//     invalidates the L2 and costs far more than a second launch.
 //
 // Matrix cores
 //   Q.K^T for a step is [tokens x D] . [D x head-rows] and P.V is
@@ -37,6 +48,16 @@
 #include <algorithm>
 
 #include "common.h"
+
+#ifndef PA_DECODE_WAVES
+#define PA_DECODE_WAVES 4
+#endif
+#ifndef PA_DECODE_PIPE
+#define PA_DECODE_PIPE 2
+#endif
+#ifndef PA_DECODE_OCC
+#define PA_DECODE_OCC 2
+#endif
 
 namespace pa {
 
@@ -61,40 +82,58 @@ __device__ __forceinline__ int clamped_len(const DecodeParams& a, int s, int BS)
   return L > cap ? (int)cap : L;
 }
 
-template <int D, int NW, int ROWS_MAX>
-struct DecodeSmem {
-  static constexpr int kStride = D + 4;                  // padded row of one head-row
-  static constexpr int kWave = 32 + ROWS_MAX * kStride;  // m[16], l[16], acc[rows][D]
-  static constexpr int kBytes = NW * kWave * 4;
+// Per-step shape constants for an element type.
+template <typename T, int D>
+struct StepShape {
+  static constexpr bool kBf16 = ElemTraits<T>::kBf16;
+  static constexpr int kX = ElemTraits<T>::kX;
+  static constexpr int kStep = kBf16 ? 32 : 16;     // tokens per step
+  static constexpr int kTpl = kBf16 ? 8 : 4;        // logits per lane per step
+  static constexpr int kTiles = kBf16 ? 2 : 1;      // 16-row K tiles per step
+  static constexpr int kNc = D / (kBf16 ? 32 : 16); // 16-byte K chunks per lane per tile
+  static constexpr int kNs = D / 16;                // 16-channel slices of the output
 };
 
-template <typename T, int D, int BS, int NW>
-__global__ void __launch_bounds__(NW * 64)
+// The K and V operands of one step, as loaded.
+template <typename T, int D>
+struct StepData {
+  using Sh = StepShape<T, D>;
+  u32x4 k[Sh::kTiles][Sh::kNc];
+  u32x4 v[Sh::kNs];
+};
+
+// LDS words per wave for the cross-wave merge: m[16], l[16], g rows of D (+4 pad).
+__host__ __device__ constexpr int merge_stride(int D) { return D + 4; }
+__host__ __device__ constexpr int merge_words(int D, int g) { return 32 + g * merge_stride(D); }
+
+template <typename T, int D, int BS, int NW, int PIPE>
+__global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(PA_DECODE_OCC)))
 paged_decode_kernel(const DecodeParams a) {
-  using Tr = ElemTraits<T>;
-  constexpr bool kBf16 = Tr::kBf16;
-  constexpr int kX = Tr::kX;
-  constexpr int kStep = kBf16 ? 32 : 16;   // tokens per step
-  constexpr int kTpl = kBf16 ? 8 : 4;      // logits per lane per step
-  constexpr int kNc = D / (kBf16 ? 32 : 16);  // 16-byte K chunks per lane per tile
-  constexpr int kNs = D / 16;              // 16-channel slices of the output
-  constexpr int kRowsMax = 16;
-  using Smem = DecodeSmem<D, NW, kRowsMax>;
+  using Sh = StepShape<T, D>;
+  constexpr bool kBf16 = Sh::kBf16;
+  constexpr int kX = Sh::kX;
+  constexpr int kStep = Sh::kStep;
+  constexpr int kTpl = Sh::kTpl;
+  constexpr int kNc = Sh::kNc;
+  constexpr int kNs = Sh::kNs;
+  constexpr int kThreads = NW * 64;
 
   extern __shared__ __align__(16) unsigned char smem[];
-  float* red = reinterpret_cast<float*>(smem);
-  int* tbl = reinterpret_cast<int*>(smem + Smem::kBytes);
+  int* tbl = reinterpret_cast<int*>(smem);                  // P / BS entries
+  const int tbl_bytes = ((a.P / BS) * 4 + 15) / 16 * 16;
+  float* red = reinterpret_cast<float*>(smem + tbl_bytes);
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  // wave index in a scalar register: the step loop below is then uniform per wave
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15;
   const int j = lane >> 4;
 
   int id = blockIdx.x;
   const int kvh = id % a.Hkv;
   id /= a.Hkv;
-  const int p = id % a.Pmax;
-  const int s = id / a.Pmax;
+  const int s = id % a.S;
+  const int p = id / a.S;
 
   const int L = clamped_len(a, s, BS);
   const int nparts = max(1, (L + a.P - 1) / a.P);
@@ -104,7 +143,7 @@ paged_decode_kernel(const DecodeParams a) {
   const int nblk = (tok1 - tok0 + BS - 1) / BS;
 
   // Block-table window of this partition (clamped ids keep every read inside the pool).
-  for (int i = threadIdx.x; i < nblk; i += NW * 64) {
+  for (int i = threadIdx.x; i < nblk; i += kThreads) {
     const unsigned b = static_cast<unsigned>(a.block_table[(size_t)s * a.MB + tok0 / BS + i]);
     tbl[i] = static_cast<int>(min(b, static_cast<unsigned>(a.NB - 1)));
   }
@@ -128,49 +167,46 @@ paged_decode_kernel(const DecodeParams a) {
   const T* vc = static_cast<const T*>(a.v_cache);
   const size_t head_elems = (size_t)D * BS;          // elements of one (block, kv head)
 
+  // ---- loads of one step ------------------------------------------------------
+  auto load_step = [&](int st, StepData<T, D>& b) {
+    const int base = tok0 + st * kStep;
+#pragma unroll
+    for (int t = 0; t < Sh::kTiles; ++t) {
+      // K-tile row n: bf16 rows interleave the step as 8*(n/4) + 4*t + n%4 so that the
+      // score of lane (n, j), register e is token 8*j + 4*t + e; f32 rows are tokens n.
+      // Rows past the partition's end read the last live token instead (in bounds; their
+      // logits are masked to -inf).
+      const int tok = min(kBf16 ? base + 8 * (n >> 2) + 4 * t + (n & 3) : base + n, tok1 - 1);
+      const int phys = tbl[(tok - tok0) / BS];
+      const T* kp = kc + ((size_t)phys * a.Hkv + kvh) * head_elems + (size_t)j * BS * kX +
+                    (size_t)(tok % BS) * kX;
+#pragma unroll
+      for (int c = 0; c < kNc; ++c) b.k[t][c] = load16(kp + (size_t)4 * c * BS * kX);
+    }
+    // V operand of slice sl: channel 16*sl + n, tokens base + kTpl*j .. + kTpl - 1.  A group
+    // wholly past the end reads the group of the last live token (in bounds; it is zeroed
+    // before use).
+    const int tokv = min(base + kTpl * j, (tok1 - 1) / kTpl * kTpl);
+    const int physv = tbl[(tokv - tok0) / BS];
+    const T* vp = vc + ((size_t)physv * a.Hkv + kvh) * head_elems + (size_t)n * BS + (tokv % BS);
+#pragma unroll
+    for (int sl = 0; sl < kNs; ++sl) b.v[sl] = load16(vp + (size_t)16 * sl * BS);
+  };
+
   float m_run = kNegInf;
   float l_run = 0.f;
   f32x4 acc[kNs];
 #pragma unroll
   for (int i = 0; i < kNs; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int nsteps = (tok1 - tok0 + kStep - 1) / kStep;
-  for (int st = wave; st < nsteps; st += NW) {
+  // ---- math of one step ---------------------------------------------------------
+  auto compute_step = [&](int st, StepData<T, D>& b) {
     const int base = tok0 + st * kStep;
     const bool tail = base + kStep > tok1;
-
-    // ---- issue all loads of the step -----------------------------------
-    constexpr int kTiles = kBf16 ? 2 : 1;
-    u32x4 kop[kTiles][kNc];
-#pragma unroll
-    for (int t = 0; t < kTiles; ++t) {
-      // K-tile row n: bf16 rows interleave the step as 8*(n/4) + 4*t + n%4 so that the
-      // score of lane (n, j), register e is token 8*j + 4*t + e; f32 rows are tokens n.
-      const int tok = kBf16 ? base + 8 * (n >> 2) + 4 * t + (n & 3) : base + n;
-      const bool ok = tok < tok1;
-      const int phys = ok ? tbl[(tok - tok0) / BS] : 0;
-      const T* kp = kc + ((size_t)phys * a.Hkv + kvh) * head_elems + (size_t)j * BS * kX +
-                    (size_t)(tok % BS) * kX;
-#pragma unroll
-      for (int c = 0; c < kNc; ++c) {
-        const u32x4 z = {0u, 0u, 0u, 0u};
-        kop[t][c] = ok ? load16(kp + (size_t)4 * c * BS * kX) : z;
-      }
-    }
-    // V operand of slice sl: channel 16*sl + n, tokens base + kTpl*j .. + kTpl - 1.
-    const int tokv = base + kTpl * j;
-    const bool okv = tokv < tok1;
-    const int physv = okv ? tbl[(tokv - tok0) / BS] : 0;
-    const T* vp = vc + ((size_t)physv * a.Hkv + kvh) * head_elems + (size_t)n * BS + (tokv % BS);
-    u32x4 vop[kNs];
-#pragma unroll
-    for (int sl = 0; sl < kNs; ++sl) {
-      const u32x4 z = {0u, 0u, 0u, 0u};
-      vop[sl] = okv ? load16(vp + (size_t)16 * sl * BS) : z;
-    }
-    if (tail) {
-      // zero V elements of tokens past the end (their weight is 0, and 0 * NaN is NaN)
-      const int nv = min(max(tok1 - tokv, 0), kTpl);
+    {
+      // zero V elements of tokens past the end (their weight is 0, and 0 * NaN is NaN);
+      // branch-free so the loads of the other buffer keep their wait counts
+      const int nv = min(max(tok1 - (base + kTpl * j), 0), kTpl);
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
         uint32_t mask;
@@ -180,11 +216,11 @@ paged_decode_kernel(const DecodeParams a) {
           mask = (w < nv) ? 0xFFFFFFFFu : 0u;
         }
 #pragma unroll
-        for (int sl = 0; sl < kNs; ++sl) vop[sl][w] &= mask;
+        for (int sl = 0; sl < kNs; ++sl) b.v[sl][w] &= mask;
       }
     }
 
-    // ---- scores ---------------------------------------------------------
+    // scores
     float y[kTpl];
     if constexpr (kBf16) {
 #pragma unroll
@@ -192,7 +228,7 @@ paged_decode_kernel(const DecodeParams a) {
         f32x4 sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int c = 0; c < kNc; ++c)
-          sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kop[t][c]),
+          sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, b.k[t][c]),
                                                        __builtin_bit_cast(bf16x8, qop[c]), sc,
                                                        0, 0, 0);
 #pragma unroll
@@ -204,13 +240,13 @@ paged_decode_kernel(const DecodeParams a) {
       for (int c = 0; c < kNc; ++c)
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          sc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(kop[0][c][e]),
+          sc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(b.k[0][c][e]),
                                                     __uint_as_float(qop[c][e]), sc, 0, 0, 0);
 #pragma unroll
       for (int e = 0; e < 4; ++e) y[e] = sc[e];
     }
 
-    // ---- online softmax (base 2) ----------------------------------------
+    // online softmax (base 2)
     float mx = kNegInf;
 #pragma unroll
     for (int v = 0; v < kTpl; ++v) {
@@ -235,7 +271,7 @@ paged_decode_kernel(const DecodeParams a) {
 #pragma unroll
     for (int sl = 0; sl < kNs; ++sl) acc[sl] *= alpha;
 
-    // ---- P.V --------------------------------------------------------------
+    // P.V
     if constexpr (kBf16) {
       const bool is_hi = n < g;
       const bool is_lo = !is_hi && n < rows;
@@ -248,50 +284,85 @@ paged_decode_kernel(const DecodeParams a) {
       }
 #pragma unroll
       for (int sl = 0; sl < kNs; ++sl)
-        acc[sl] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vop[sl]), pop,
+        acc[sl] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, b.v[sl]), pop,
                                                           acc[sl], 0, 0, 0);
     } else {
 #pragma unroll
       for (int sl = 0; sl < kNs; ++sl)
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          acc[sl] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(vop[sl][e]), pw[e],
+          acc[sl] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(b.v[sl][e]), pw[e],
                                                          acc[sl], 0, 0, 0);
+    }
+  };
+
+  // ---- the wave's steps: st = wave, wave + NW, ... ----------------------------------
+  const int nsteps = (tok1 - tok0 + kStep - 1) / kStep;
+  if constexpr (PIPE == 2) {
+    StepData<T, D> b0, b1;
+    int st = wave;
+    if (st < nsteps) {
+      load_step(st, b0);
+      for (;;) {
+        load_step(st + NW < nsteps ? st + NW : st, b1);
+        // keep the prefetch above the math: the scheduler would otherwise sink it to its use
+        __builtin_amdgcn_sched_barrier(0);
+        compute_step(st, b0);
+        st += NW;
+        if (st >= nsteps) break;
+        load_step(st + NW < nsteps ? st + NW : st, b0);
+        __builtin_amdgcn_sched_barrier(0);
+        compute_step(st, b1);
+        st += NW;
+        if (st >= nsteps) break;
+      }
+    }
+  } else {
+    for (int st = wave; st < nsteps; st += NW) {
+      StepData<T, D> b0;
+      load_step(st, b0);
+      compute_step(st, b0);
     }
   }
 
-  // ---- merge the waves of the workgroup ------------------------------------
+  // ---- merge the waves of the workgroup --------------------------------------------
+  if constexpr (kBf16) {
+    // add the lo rows [g, 2g) into the hi rows [0, g)
+#pragma unroll
+    for (int sl = 0; sl < kNs; ++sl)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[sl][e] += __shfl_down(acc[sl][e], g, 16);
+  }
   float lsum = l_run + xor16(l_run);
   lsum += xor32(lsum);
-  float* wr = red + wave * Smem::kWave;
-  if (row_live) {
+  const int wstride = merge_words(D, g);
+  float* wr = red + wave * wstride;
+  if (n < g) {
     if (j == 0) {
       wr[n] = m_run;
       wr[16 + n] = lsum;
     }
 #pragma unroll
     for (int sl = 0; sl < kNs; ++sl)
-      *reinterpret_cast<f32x4*>(wr + 32 + n * Smem::kStride + 16 * sl + 4 * j) = acc[sl];
+      *reinterpret_cast<f32x4*>(wr + 32 + n * merge_stride(D) + 16 * sl + 4 * j) = acc[sl];
   }
   __syncthreads();
 
   const bool single = nparts == 1;
-  for (int idx = threadIdx.x; idx < g * D; idx += NW * 64) {
+  for (int idx = threadIdx.x; idx < g * D; idx += kThreads) {
     const int h = idx / D;
     const int d = idx % D;
     float M = kNegInf;
 #pragma unroll
-    for (int w = 0; w < NW; ++w) M = fmaxf(M, red[w * Smem::kWave + h]);
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, red[w * wstride + h]);
     float num = 0.f, den = 0.f;
     if (M != kNegInf) {
 #pragma unroll
       for (int w = 0; w < NW; ++w) {
-        const float* r = red + w * Smem::kWave;
+        const float* r = red + w * wstride;
         const float f = exp2_fast(r[h] - M);
         den += f * r[16 + h];
-        float v = r[32 + h * Smem::kStride + d];
-        if (kBf16) v += r[32 + (h + g) * Smem::kStride + d];
-        num += f * v;
+        num += f * r[32 + h * merge_stride(D) + d];
       }
     }
     const size_t row = (size_t)s * a.Hq + kvh * g + h;
@@ -313,6 +384,7 @@ paged_decode_kernel(const DecodeParams a) {
 
 // Log-sum-exp merge of the partitions of one (sequence, query head):
 //   M = max_p m_p,  out = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p.
+// One wave per row; lane i handles channels i, i + 64, ...
 template <typename T, int D, int BS>
 __global__ void __launch_bounds__(64)
 reduce_partitions_kernel(const DecodeParams a) {
@@ -325,33 +397,46 @@ reduce_partitions_kernel(const DecodeParams a) {
   const float* ml = a.part_ml + row * a.Pmax * 2;
   const float* acc = a.part_acc + row * a.Pmax * D;
   float M = kNegInf;
-  for (int q = 0; q < nparts; ++q) M = fmaxf(M, ml[2 * q]);
-  for (int d = threadIdx.x; d < D; d += 64) {
-    float num = 0.f, den = 0.f;
-    if (M != kNegInf) {
-      for (int q = 0; q < nparts; ++q) {
-        const float f = exp2_fast(ml[2 * q] - M);
-        den += f * ml[2 * q + 1];
-        num += f * acc[(size_t)q * D + d];
-      }
+  for (int q = threadIdx.x; q < nparts; q += 64) M = fmaxf(M, ml[2 * q]);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
+  constexpr int kPer = D / 64;
+  float num[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) num[i] = 0.f;
+  float den = 0.f;
+  if (M != kNegInf) {
+    for (int q = 0; q < nparts; ++q) {
+      const float f = exp2_fast(ml[2 * q] - M);
+      den += f * ml[2 * q + 1];
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) num[i] += f * acc[(size_t)q * D + threadIdx.x + 64 * i];
     }
-    const float o = (M == kNegInf || den == 0.f) ? 0.f : num / den;
+  }
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const float o = (M == kNegInf || den == 0.f) ? 0.f : num[i] / den;
+    const size_t idx = row * D + threadIdx.x + 64 * i;
     if constexpr (ElemTraits<T>::kBf16)
-      static_cast<uint16_t*>(a.out)[row * D + d] = bf16_bits(o);
+      static_cast<uint16_t*>(a.out)[idx] = bf16_bits(o);
     else
-      static_cast<float*>(a.out)[row * D + d] = o;
+      static_cast<float*>(a.out)[idx] = o;
   }
 }
 
-constexpr int kWaves = 4;
+constexpr int kWaves = PA_DECODE_WAVES;
+constexpr int kPipe = PA_DECODE_PIPE;
+
+inline size_t decode_lds_bytes(int D, int BS, int P, int g) {
+  const size_t tbl_bytes = ((size_t)(P / BS) * 4 + 15) / 16 * 16;
+  return tbl_bytes + (size_t)kWaves * merge_words(D, g) * 4;
+}
 
 template <typename T, int D, int BS>
 hipError_t launch_decode(const DecodeParams& a, hipStream_t stream) {
-  using Smem = DecodeSmem<D, kWaves, 16>;
-  const int tbl_bytes = ((a.P / BS) * 4 + 15) / 16 * 16;
-  const size_t lds = Smem::kBytes + tbl_bytes;
+  const size_t lds = decode_lds_bytes(D, BS, a.P, a.g);
   const long grid = (long)a.Hkv * a.Pmax * a.S;
-  hipLaunchKernelGGL((paged_decode_kernel<T, D, BS, kWaves>), dim3((unsigned)grid),
+  hipLaunchKernelGGL((paged_decode_kernel<T, D, BS, kWaves, kPipe>), dim3((unsigned)grid),
                      dim3(kWaves * 64), lds, stream, a);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || a.Pmax == 1) return err;
@@ -394,15 +479,57 @@ pa_status check_shapes(int num_heads, int num_kv_heads, int head_dim, int block_
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+// Workspace layout: part_ml [rows][2] f32 | part_acc [rows][D] f32, rows = S * Hq * Pmax,
+// each region 256-byte aligned.
+struct WorkspaceLayout {
+  size_t ml, acc, total;
+};
+
+WorkspaceLayout workspace_layout(int S, int Hq, int D, int pmax) {
+  WorkspaceLayout w{0, 0, 0};
+  if (pmax <= 1) return w;
+  const size_t rows = (size_t)S * Hq * pmax;
+  w.ml = 0;
+  w.acc = round_up(rows * 2 * sizeof(float), 256);
+  w.total = w.acc + round_up(rows * D * sizeof(float), 256);
+  return w;
+}
+
+// Compute units of the current device (queried once per device).
+int device_cu_count() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+      n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
+constexpr int kMaxPartition = 8192;
+
 }  // namespace
 
+// Default partition: a single partition per sequence (no merge) when the
+// (sequence, kv head) pairs alone give every compute unit two workgroups;
+// otherwise split so that the grid holds about four workgroups per compute
+// unit, with partitions of at least 512 tokens.
 extern "C" int pa_default_partition_size(int num_seqs, int num_kv_heads, int max_context_len,
                                          pa_dtype dtype) {
-  (void)num_seqs;
-  (void)num_kv_heads;
-  (void)max_context_len;
   (void)dtype;
-  return 256;
+  const long units = std::max(1L, (long)num_seqs * std::max(1, num_kv_heads));
+  const long whole = std::max(64L, ((long)std::max(0, max_context_len) + 63) / 64 * 64);
+  const long cus = device_cu_count();
+  if (whole <= kMaxPartition && units >= 2 * cus) return (int)whole;
+  const long want_parts = std::max(1L, (4 * cus + units - 1) / units);
+  long P = ((long)std::max(0, max_context_len) + want_parts - 1) / want_parts;
+  P = (P + 63) / 64 * 64;
+  P = std::max(512L, std::min((long)kMaxPartition, P));
+  return (int)std::min(P, std::min(whole, (long)kMaxPartition));
 }
 
 extern "C" size_t pa_paged_attention_workspace_size(int num_seqs, int num_heads, int num_kv_heads,
@@ -413,11 +540,9 @@ extern "C" size_t pa_paged_attention_workspace_size(int num_seqs, int num_heads,
   const int P = partition_size ? partition_size
                                : pa_default_partition_size(num_seqs, num_kv_heads,
                                                            max_context_len, dtype);
-  if (P < 64 || P > 8192 || P % 64) return 0;
-  const size_t pmax = std::max(1, (max_context_len + P - 1) / P);
-  if (pmax <= 1) return 0;
-  const size_t rows = (size_t)num_seqs * num_heads * pmax;
-  return round_up(rows * 2 * sizeof(float), 256) + round_up(rows * head_dim * sizeof(float), 256);
+  if (P < 64 || P > kMaxPartition || P % 64) return 0;
+  const int pmax = std::max(1, (max_context_len + P - 1) / P);
+  return workspace_layout(num_seqs, num_heads, head_dim, pmax).total;
 }
 
 extern "C" pa_status pa_paged_attention(void* out, const void* query, const int32_t* block_table,
@@ -449,9 +574,8 @@ extern "C" pa_status pa_paged_attention(void* out, const void* query, const int3
   const long grid = (long)num_kv_heads * pmax * num_seqs;
   if (grid > 0x7FFFFFFFL || (long)num_seqs * num_heads > 0x7FFFFFFFL) return PA_ERR_INVALID_ARG;
 
-  const size_t need = pa_paged_attention_workspace_size(num_seqs, num_heads, num_kv_heads,
-                                                        head_dim, max_context_len, P, dtype);
-  if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 16)))
+  const WorkspaceLayout wl = workspace_layout(num_seqs, num_heads, head_dim, pmax);
+  if (wl.total > 0 && (!workspace || workspace_bytes < wl.total || !aligned(workspace, 16)))
     return PA_ERR_WORKSPACE;
 
   pa::DecodeParams a;
@@ -470,11 +594,9 @@ extern "C" pa_status pa_paged_attention(void* out, const void* query, const int3
   a.P = P;
   a.Pmax = pmax;
   a.scale_log2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
-  const size_t rows = (size_t)num_seqs * num_heads * pmax;
-  a.part_ml = need ? static_cast<float*>(workspace) : nullptr;
-  a.part_acc = need ? reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                               round_up(rows * 2 * sizeof(float), 256))
-                    : nullptr;
+  char* ws = static_cast<char*>(workspace);
+  a.part_ml = wl.total ? reinterpret_cast<float*>(ws + wl.ml) : nullptr;
+  a.part_acc = wl.total ? reinterpret_cast<float*>(ws + wl.acc) : nullptr;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t err = dtype == PA_DTYPE_BF16

@@ -53,6 +53,18 @@ def test_default_partition_is_a_multiple_of_64(lib):
         assert P >= 64 and P % 64 == 0
 
 
+def test_default_partition_policy(lib):
+    """Without a visible device the policy assumes 256 compute units."""
+    # 64 x 8 (sequence, kv head) pairs fill 256 units twice: one partition covers the longest
+    assert lib.pa_default_partition_size(64, 8, 2011, 1) == 2048
+    # 16 x 8 pairs do not: split into ~4 workgroups per unit, partitions >= 512 tokens
+    assert lib.pa_default_partition_size(16, 8, 32768, 1) == 4096
+    assert lib.pa_default_partition_size(16, 8, 3000, 1) == 512
+    # never longer than the longest sequence (rounded to 64), never past 8192
+    assert lib.pa_default_partition_size(1, 1, 10, 1) == 64
+    assert lib.pa_default_partition_size(4096, 8, 100000, 1) == 8192
+
+
 def test_workspace_size(lib):
     # one partition -> nothing needed
     assert lib.pa_paged_attention_workspace_size(64, 32, 8, 128, 256, 256, 1) == 0
