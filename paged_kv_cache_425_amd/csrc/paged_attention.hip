@@ -106,7 +106,15 @@ struct StepData {
 __host__ __device__ constexpr int merge_stride(int D) { return D + 4; }
 __host__ __device__ constexpr int merge_words(int D, int g) { return 32 + g * merge_stride(D); }
 
-template <typename T, int D, int BS, int NW, int PIPE>
+// Pair-balanced mode (PAIRED): a workgroup of NW waves takes two
+// (sequence, kv head) units -- the r-th longest and the r-th shortest
+// sequence -- and splits its waves between them in proportion to their steps,
+// so that every workgroup carries about the same number of tokens.  The order
+// of the sequences by length is computed from context_lens inside every
+// workgroup (identically), by counting for each sequence the sequences that
+// are longer (ties broken by index).  Used when each sequence is one
+// partition; otherwise a workgroup is one (kv head, sequence, partition).
+template <typename T, int D, int BS, int NW, int PIPE, bool PAIRED>
 __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(PA_DECODE_OCC)))
 paged_decode_kernel(const DecodeParams a) {
   using Sh = StepShape<T, D>;
@@ -118,10 +126,15 @@ paged_decode_kernel(const DecodeParams a) {
   constexpr int kNs = Sh::kNs;
   constexpr int kThreads = NW * 64;
 
+  // LDS: [ctrl: 16 ints][lens: S ints, PAIRED only][tables: 1 or 2 windows of P/BS][merge]
   extern __shared__ __align__(16) unsigned char smem[];
-  int* tbl = reinterpret_cast<int*>(smem);                  // P / BS entries
-  const int tbl_bytes = ((a.P / BS) * 4 + 15) / 16 * 16;
-  float* red = reinterpret_cast<float*>(smem + tbl_bytes);
+  int* ctrl = reinterpret_cast<int*>(smem);
+  const int win = a.P / BS;                                 // table entries per window
+  const int lens_words = PAIRED ? (a.S + 3) / 4 * 4 : 0;
+  int* lens = ctrl + 16;
+  int* tbl = lens + lens_words;
+  const int tbl_words = ((PAIRED ? 2 : 1) * win + 3) / 4 * 4;
+  float* red = reinterpret_cast<float*>(tbl + tbl_words);
 
   const int lane = threadIdx.x & 63;
   // wave index in a scalar register: the step loop below is then uniform per wave
@@ -132,20 +145,72 @@ paged_decode_kernel(const DecodeParams a) {
   int id = blockIdx.x;
   const int kvh = id % a.Hkv;
   id /= a.Hkv;
-  const int s = id % a.S;
-  const int p = id / a.S;
 
-  const int L = clamped_len(a, s, BS);
-  const int nparts = max(1, (L + a.P - 1) / a.P);
-  if (p >= nparts) return;
-  const int tok0 = p * a.P;
-  const int tok1 = min(L, tok0 + a.P);
-  const int nblk = (tok1 - tok0 + BS - 1) / BS;
-
-  // Block-table window of this partition (clamped ids keep every read inside the pool).
-  for (int i = threadIdx.x; i < nblk; i += kThreads) {
-    const unsigned b = static_cast<unsigned>(a.block_table[(size_t)s * a.MB + tok0 / BS + i]);
-    tbl[i] = static_cast<int>(min(b, static_cast<unsigned>(a.NB - 1)));
+  // ---- this wave's unit: sequence s, tokens [tok0, tok1), table window, wave slot ----
+  int s, tok0, tok1, lw, nw, p = 0, nparts = 1;
+  int sA = 0, sB = -1, nA = NW;                             // PAIRED: the two sequences
+  const int* tblw = tbl;
+  if constexpr (PAIRED) {
+    const int r = id;                                       // pair index
+    for (int t = threadIdx.x; t < a.S; t += kThreads) lens[t] = clamped_len(a, t, BS);
+    __syncthreads();
+    const int rB = a.S - 1 - r;
+    for (int t = threadIdx.x; t < a.S; t += kThreads) {
+      const int Lt = lens[t];
+      int rank = 0;
+      for (int u = 0; u < a.S; ++u) {
+        const int Lu = lens[u];
+        rank += (Lu > Lt) || (Lu == Lt && u < t);
+      }
+      if (rank == r) ctrl[0] = t;
+      if (rank == rB) ctrl[1] = t;
+    }
+    __syncthreads();
+    sA = __builtin_amdgcn_readfirstlane(ctrl[0]);
+    sB = r == rB ? -1 : __builtin_amdgcn_readfirstlane(ctrl[1]);
+    const int LA = lens[sA];
+    const int LB = sB >= 0 ? lens[sB] : 0;
+    // split the waves so that the busier unit's waves finish together
+    const int stA = (LA + kStep - 1) / kStep, stB = (LB + kStep - 1) / kStep;
+    if (stB > 0) {
+      int best = 1 << 30;
+      for (int c = 1; c < NW; ++c) {
+        const int t = max((stA + c - 1) / c, (stB + NW - c - 1) / (NW - c));
+        if (t < best) { best = t; nA = c; }
+      }
+    }
+    nA = __builtin_amdgcn_readfirstlane(nA);
+    const bool onA = wave < nA;
+    s = onA ? sA : sB;
+    tok0 = 0;
+    tok1 = __builtin_amdgcn_readfirstlane(onA ? LA : LB);
+    lw = onA ? wave : wave - nA;
+    nw = onA ? nA : NW - nA;
+    tblw = tbl + (onA ? 0 : win);
+    // both table windows (clamped ids keep every read inside the pool)
+    const int nbA = (LA + BS - 1) / BS, nbB = (LB + BS - 1) / BS;
+    for (int i = threadIdx.x; i < nbA + nbB; i += kThreads) {
+      const int us = i < nbA ? sA : sB;
+      const int li = i < nbA ? i : i - nbA;
+      const unsigned b = static_cast<unsigned>(a.block_table[(size_t)us * a.MB + li]);
+      tbl[(i < nbA ? 0 : win) + li] = static_cast<int>(min(b, static_cast<unsigned>(a.NB - 1)));
+    }
+  } else {
+    s = id % a.S;
+    p = id / a.S;
+    const int L = clamped_len(a, s, BS);
+    nparts = max(1, (L + a.P - 1) / a.P);
+    if (p >= nparts) return;
+    tok0 = p * a.P;
+    tok1 = min(L, tok0 + a.P);
+    lw = wave;
+    nw = NW;
+    const int nblk = (tok1 - tok0 + BS - 1) / BS;
+    // Block-table window of this partition (clamped ids keep every read inside the pool).
+    for (int i = threadIdx.x; i < nblk; i += kThreads) {
+      const unsigned b = static_cast<unsigned>(a.block_table[(size_t)s * a.MB + tok0 / BS + i]);
+      tbl[i] = static_cast<int>(min(b, static_cast<unsigned>(a.NB - 1)));
+    }
   }
 
   const int g = a.g;
@@ -159,7 +224,7 @@ paged_decode_kernel(const DecodeParams a) {
 #pragma unroll
   for (int c = 0; c < kNc; ++c) {
     const u32x4 z = {0u, 0u, 0u, 0u};
-    qop[c] = row_live ? load16(qrow + kX * (4 * c + j)) : z;
+    qop[c] = row_live && tok1 > tok0 ? load16(qrow + kX * (4 * c + j)) : z;
   }
   __syncthreads();
 
@@ -177,7 +242,7 @@ paged_decode_kernel(const DecodeParams a) {
       // Rows past the partition's end read the last live token instead (in bounds; their
       // logits are masked to -inf).
       const int tok = min(kBf16 ? base + 8 * (n >> 2) + 4 * t + (n & 3) : base + n, tok1 - 1);
-      const int phys = tbl[(tok - tok0) / BS];
+      const int phys = tblw[(tok - tok0) / BS];
       const T* kp = kc + ((size_t)phys * a.Hkv + kvh) * head_elems + (size_t)j * BS * kX +
                     (size_t)(tok % BS) * kX;
 #pragma unroll
@@ -187,7 +252,7 @@ paged_decode_kernel(const DecodeParams a) {
     // wholly past the end reads the group of the last live token (in bounds; it is zeroed
     // before use).
     const int tokv = min(base + kTpl * j, (tok1 - 1) / kTpl * kTpl);
-    const int physv = tbl[(tokv - tok0) / BS];
+    const int physv = tblw[(tokv - tok0) / BS];
     const T* vp = vc + ((size_t)physv * a.Hkv + kvh) * head_elems + (size_t)n * BS + (tokv % BS);
 #pragma unroll
     for (int sl = 0; sl < kNs; ++sl) b.v[sl] = load16(vp + (size_t)16 * sl * BS);
@@ -296,29 +361,29 @@ paged_decode_kernel(const DecodeParams a) {
     }
   };
 
-  // ---- the wave's steps: st = wave, wave + NW, ... ----------------------------------
+  // ---- the wave's steps: st = lw, lw + nw, ... ----------------------------------------
   const int nsteps = (tok1 - tok0 + kStep - 1) / kStep;
   if constexpr (PIPE == 2) {
     StepData<T, D> b0, b1;
-    int st = wave;
+    int st = lw;
     if (st < nsteps) {
       load_step(st, b0);
       for (;;) {
-        load_step(st + NW < nsteps ? st + NW : st, b1);
+        load_step(st + nw < nsteps ? st + nw : st, b1);
         // keep the prefetch above the math: the scheduler would otherwise sink it to its use
         __builtin_amdgcn_sched_barrier(0);
         compute_step(st, b0);
-        st += NW;
+        st += nw;
         if (st >= nsteps) break;
-        load_step(st + NW < nsteps ? st + NW : st, b0);
+        load_step(st + nw < nsteps ? st + nw : st, b0);
         __builtin_amdgcn_sched_barrier(0);
         compute_step(st, b1);
-        st += NW;
+        st += nw;
         if (st >= nsteps) break;
       }
     }
   } else {
-    for (int st = wave; st < nsteps; st += NW) {
+    for (int st = lw; st < nsteps; st += nw) {
       StepData<T, D> b0;
       load_step(st, b0);
       compute_step(st, b0);
@@ -348,24 +413,27 @@ paged_decode_kernel(const DecodeParams a) {
   }
   __syncthreads();
 
+  // unit 0 = waves [0, nA) (all waves outside the paired mode), unit 1 = waves [nA, NW)
+  const int nunits = (PAIRED && sB >= 0) ? 2 : 1;
   const bool single = nparts == 1;
-  for (int idx = threadIdx.x; idx < g * D; idx += kThreads) {
-    const int h = idx / D;
+  for (int idx = threadIdx.x; idx < nunits * g * D; idx += kThreads) {
+    const int u = idx / (g * D);
+    const int h = (idx % (g * D)) / D;
     const int d = idx % D;
+    const int w0 = u ? nA : 0, w1 = u ? NW : nA;
+    const int su = PAIRED ? (u ? sB : sA) : s;
     float M = kNegInf;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) M = fmaxf(M, red[w * wstride + h]);
+    for (int w = w0; w < w1; ++w) M = fmaxf(M, red[w * wstride + h]);
     float num = 0.f, den = 0.f;
     if (M != kNegInf) {
-#pragma unroll
-      for (int w = 0; w < NW; ++w) {
+      for (int w = w0; w < w1; ++w) {
         const float* r = red + w * wstride;
         const float f = exp2_fast(r[h] - M);
         den += f * r[16 + h];
         num += f * r[32 + h * merge_stride(D) + d];
       }
     }
-    const size_t row = (size_t)s * a.Hq + kvh * g + h;
+    const size_t row = (size_t)su * a.Hq + kvh * g + h;
     if (single) {
       const float o = (M == kNegInf) ? 0.f : num / den;
       if constexpr (kBf16)
@@ -424,19 +492,38 @@ reduce_partitions_kernel(const DecodeParams a) {
   }
 }
 
-constexpr int kWaves = PA_DECODE_WAVES;
+constexpr int kWaves = PA_DECODE_WAVES;     // waves per workgroup, partition mode
+constexpr int kPairWaves = 8;               // waves per workgroup, paired mode
 constexpr int kPipe = PA_DECODE_PIPE;
+constexpr int kMaxPairedSeqs = 512;         // the in-kernel ordering is O(S^2 / threads)
+constexpr size_t kMaxLds = 64 * 1024;
 
-inline size_t decode_lds_bytes(int D, int BS, int P, int g) {
-  const size_t tbl_bytes = ((size_t)(P / BS) * 4 + 15) / 16 * 16;
-  return tbl_bytes + (size_t)kWaves * merge_words(D, g) * 4;
+// Dynamic LDS of one workgroup; mirrors the layout at the top of paged_decode_kernel.
+inline size_t decode_lds_bytes(bool paired, int nw, int S, int D, int BS, int P, int g) {
+  const size_t lens_words = paired ? (size_t)(S + 3) / 4 * 4 : 0;
+  const size_t tbl_words = ((size_t)(paired ? 2 : 1) * (P / BS) + 3) / 4 * 4;
+  return 4 * (16 + lens_words + tbl_words + (size_t)nw * merge_words(D, g));
+}
+
+// Paired mode when every sequence is one partition, there are at least two
+// sequences, the ordering stays cheap and the workgroup's LDS fits.
+inline bool use_paired(const DecodeParams& a, int D, int BS) {
+  return a.Pmax == 1 && a.S >= 2 && a.S <= kMaxPairedSeqs &&
+         decode_lds_bytes(true, kPairWaves, a.S, D, BS, a.P, a.g) <= kMaxLds;
 }
 
 template <typename T, int D, int BS>
 hipError_t launch_decode(const DecodeParams& a, hipStream_t stream) {
-  const size_t lds = decode_lds_bytes(D, BS, a.P, a.g);
+  if (use_paired(a, D, BS)) {
+    const size_t lds = decode_lds_bytes(true, kPairWaves, a.S, D, BS, a.P, a.g);
+    const long grid = (long)a.Hkv * ((a.S + 1) / 2);
+    hipLaunchKernelGGL((paged_decode_kernel<T, D, BS, kPairWaves, kPipe, true>),
+                       dim3((unsigned)grid), dim3(kPairWaves * 64), lds, stream, a);
+    return hipGetLastError();
+  }
+  const size_t lds = decode_lds_bytes(false, kWaves, a.S, D, BS, a.P, a.g);
   const long grid = (long)a.Hkv * a.Pmax * a.S;
-  hipLaunchKernelGGL((paged_decode_kernel<T, D, BS, kWaves, kPipe>), dim3((unsigned)grid),
+  hipLaunchKernelGGL((paged_decode_kernel<T, D, BS, kWaves, kPipe, false>), dim3((unsigned)grid),
                      dim3(kWaves * 64), lds, stream, a);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || a.Pmax == 1) return err;

@@ -157,6 +157,25 @@ def test_variants_ragged(dtype, D, BS, g):
         check_close(to_f64(run_gpu(w, kc, vc, part)), ref, dtype, f"{dtype}/{D}/{BS}/{g}/{part}")
 
 
+def test_paired_mode_odd_count_and_uneven_pairs():
+    """One partition per sequence, few sequences: workgroups pair the r-th longest with the
+    r-th shortest sequence; with an odd count the middle sequence runs alone."""
+    w = tiny("bf16", (700, 3, 64, 1, 333, 129, 40), 32, 8, 128, 16, seed=21)
+    kc, vc = build_pools(w)
+    say("paired mode, 7 sequences")
+    check_close(to_f64(run_gpu(w, kc, vc, 768)), oracle_out(w, kc, vc), "bf16", "paired-odd")
+
+
+def test_many_sequences_single_partition_unpaired():
+    """More sequences than the in-kernel ordering handles: one workgroup per
+    (kv head, sequence) with no pairing."""
+    rng = np.random.default_rng(22)
+    w = tiny("bf16", rng.integers(1, 100, size=600), 8, 2, 128, 16, seed=22)
+    kc, vc = build_pools(w)
+    say("600 sequences, one partition each")
+    check_close(to_f64(run_gpu(w, kc, vc, 128)), oracle_out(w, kc, vc), "bf16", "unpaired")
+
+
 def test_group_of_sixteen_f32():
     w = tiny("f32", (5, 40, 129), 32, 2, 64, 16, seed=3)
     kc, vc = build_pools(w)
