@@ -2,9 +2,11 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 1]
 
-One step is the whole hot path over one batch: reshape_and_cache of the
-step's new tokens (one per sequence), then paged decode attention of every
-sequence over its paged K/V.  The default workload is the Llama-3-8B-shaped
+One step is the whole hot path over one batch: the scatter of the step's new
+tokens (one per sequence, at position L - 1) into their slots, then paged
+decode attention of every sequence over its paged K/V.  The headline runs the
+step as one launch (pa_decode_step); the same step as two calls
+(pa_reshape_and_cache, then pa_paged_attention) is timed beside it.  The default workload is the Llama-3-8B-shaped
 decode batch: 64 sequences, 32 query heads / 8 KV heads, head size 128,
 block size 16, context lengths uniform in [128, 2048], bfloat16.
 
@@ -13,10 +15,10 @@ library's own reshape_and_cache.  To keep the 256 MB Infinity Cache from
 serving repeated steps, the step rotates over ``--replicas`` copies of the
 K/V pools (cold headline); ``--warm`` adds a run over one copy.
 
-Prints ONE JSON line with the decode-step throughput (KV bytes read per
-second), the decode call's roofline (HIP events around every launch on the
-stream it runs on), and the CPU oracle's throughput on a bounded sample of
-the same workload (reported baseline).
+Prints ONE JSON line with the step throughput (KV bytes read per second), the
+step launch's roofline (HIP events around the timed steps on the stream the
+launches go to), and the CPU oracle's throughput on a bounded sample of the same workload
+(reported baseline).
 """
 from __future__ import annotations
 
@@ -35,7 +37,7 @@ if ROOT not in sys.path:
 
 METRIC = "paged-attn decode KV GB/s (% of HBM peak) + µs/step, Llama-3-8B shape, 1 GPU"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, AMD's published peak
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_step_traffic.json")
 KERNEL_SOURCE = os.path.join(ROOT, "paged_kv_cache_425_amd", "csrc", "paged_attention.hip")
 
 
@@ -172,7 +174,9 @@ def main() -> int:
         return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev)
 
     # ---- device inputs ------------------------------------------------------
-    hist, new = w.history_records, w.new_records
+    # the step's new token of each sequence is its record at position L - 1
+    new = np.array([w.seq_records[s][-1] for s in range(w.num_seqs)], dtype=np.int64)
+    hist = np.setdiff1d(np.arange(len(w.rec_slot)), new)
     kshape = pk.k_cache_shape(w.num_blocks, w.num_kv_heads, w.head_dim, w.block_size, tdt)
     vshape = pk.v_cache_shape(w.num_blocks, w.num_kv_heads, w.head_dim, w.block_size, tdt)
     kc0 = torch.full(kshape, float("nan"), dtype=tdt, device=dev)
@@ -192,61 +196,74 @@ def main() -> int:
     ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
 
+    # the step as one launch (pa_decode_step) and as the two calls
+    fused = [pk.prepare_decode_step(query, key_new, val_new, slot_new, table, lens, kc, vc,
+                                    w.scale, max_context_len=w.max_context_len, out=out,
+                                    partition_size=part, workspace=ws) for kc, vc in pools]
     writes = [pk.prepare_reshape_and_cache(key_new, val_new, slot_new, kc, vc) for kc, vc in pools]
     decodes = [pk.prepare_paged_attention(query, table, lens, kc, vc, w.scale,
                                           max_context_len=w.max_context_len, out=out,
                                           partition_size=part, workspace=ws)
                for kc, vc in pools]
     nb = algorithmic_bytes(w)
+    elt = 2 if w.dtype == "bf16" else 4
+    new_bytes = 2 * w.num_seqs * w.num_kv_heads * w.head_dim * elt     # new K and V
+    fused_bytes = nb["total"] + 2 * new_bytes + 8 * w.num_seqs          # read, written, slots
     K, W = args.steps, args.warmup
     part_used = part or pk.default_partition_size(w.num_seqs, w.num_kv_heads, w.max_context_len, tdt)
     needs_reduce = w.max_context_len > part_used
 
-    def run(n_rep: int, steps: int, timed: bool):
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(steps)] if timed else None
+    def run_fused(n_rep: int, steps: int) -> None:
         for i in range(steps):
-            r = i % n_rep
-            writes[r]()
-            if timed:
-                ev[i][0].record()
-            decodes[r]()
-            if timed:
-                ev[i][1].record()
-        return ev
+            fused[i % n_rep]()
 
-    # ---- cold headline: rotate over the replicas ------------------------------
-    run(len(pools), W, False)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    ev = run(len(pools), K, True)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    decode_ms = np.array([a.elapsed_time(b) for a, b in ev])
-    log(f"cold: {wall / K * 1e6:.1f} us/step wall, decode call median "
-        f"{np.median(decode_ms) * 1e3:.1f} us")
+    def run_two_calls(n_rep: int, steps: int) -> None:
+        for i in range(steps):
+            writes[i % n_rep]()
+            decodes[i % n_rep]()
+
+    def timed(fn, *a):
+        """Wall time and HIP-event time of fn, with synchronisation on both sides.
+
+        The events are recorded on the stream the launches go to (torch's current
+        stream), once before the first and once after the last step, so they add
+        no bubbles between launches."""
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        e0.record()
+        fn(*a)
+        e1.record()
+        torch.cuda.synchronize()
+        return time.perf_counter() - t0, e0.elapsed_time(e1) * 1e-3
+
+    R = len(pools)
+    # ---- cold headline: the fused step, rotating over the pool copies ----------
+    run_fused(R, W)
+    wall, ev_s = timed(run_fused, R, K)
+    log(f"cold fused step: {wall / K * 1e6:.1f} us/step wall, {ev_s / K * 1e6:.1f} us/launch "
+        "(events)")
+    # ---- the same step as two calls (reshape_and_cache, then paged_attention) --
+    run_two_calls(R, W)
+    wall2, ev2 = timed(run_two_calls, R, K)
+    log(f"cold two-call step: {wall2 / K * 1e6:.1f} us/step wall")
 
     # ---- warm (optional): one pool, repeated ----------------------------------
     warm = None
     if args.warm:
-        run(1, W, False)
-        torch.cuda.synchronize()
-        t1 = time.perf_counter()
-        evw = run(1, K, True)
-        torch.cuda.synchronize()
-        wall_w = time.perf_counter() - t1
-        decode_w = np.array([a.elapsed_time(b) for a, b in evw])
-        log(f"warm: {wall_w / K * 1e6:.1f} us/step wall, decode call median "
-            f"{np.median(decode_w) * 1e3:.1f} us")
+        run_fused(1, W)
+        wall_w, ev_w = timed(run_fused, 1, K)
+        log(f"warm fused step: {wall_w / K * 1e6:.1f} us/step wall")
         warm = {"us_per_step": round(wall_w / K * 1e6, 2),
                 "value": round(nb["kv"] / (wall_w / K) / 1e9, 2),
-                "decode_us_mean": round(float(decode_w.mean()) * 1e3, 2)}
+                "launch_us_events": round(ev_w / K * 1e6, 2)}
 
     ms_step = wall / K * 1e3
     value = nb["kv"] / (ms_step * 1e-3) / 1e9
-    decode_avg_s = float(decode_ms.mean()) * 1e-3
-    achieved = nb["total"] / decode_avg_s / 1e9
+    launch_avg_s = ev_s / K
+    achieved = fused_bytes / launch_avg_s / 1e9
     traffic = load_traffic(w.name)
+    kernels = "paged_decode_kernel" + (" + reduce_partitions_kernel" if needs_reduce else "")
     line = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -269,19 +286,19 @@ def main() -> int:
                    "total_context_tokens": int(w.context_lens.astype(np.int64).sum()),
                    "partition_size": part_used,
                    "kv_bytes_per_step": nb["kv"], "seed": w.info["seed"],
+                   "step": "pa_decode_step: scatter of the new tokens + paged decode, one launch",
                    "pool_bytes_each": int(kc0.numel() * kc0.element_size()),
-                   "pool_replicas": len(pools), "parallelism": "none (1 GPU)"},
-        "decode_us": {"mean": round(float(decode_ms.mean()) * 1e3, 2),
-                      "median": round(float(np.median(decode_ms)) * 1e3, 2),
-                      "p10": round(float(np.percentile(decode_ms, 10)) * 1e3, 2),
-                      "p90": round(float(np.percentile(decode_ms, 90)) * 1e3, 2)},
+                   "pool_replicas": R, "parallelism": "none (1 GPU)"},
+        "launch_us_events": round(launch_avg_s * 1e6, 2),
+        "two_call_step": {"us_per_step": round(wall2 / K * 1e6, 2),
+                          "us_per_step_events": round(ev2 / K * 1e6, 2),
+                          "value": round(nb["kv"] / (wall2 / K) / 1e9, 2)},
         "warm": warm,
-        "roofline": {"kernel": "pa_paged_attention: paged_decode_kernel" + (
-                         " + reduce_partitions_kernel" if needs_reduce else " (one partition, no reduce)"),
+        "roofline": {"kernel": f"pa_decode_step: {kernels}",
                      "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic,
-                     "algorithmic_bytes_per_launch": nb["total"]},
+                     "algorithmic_bytes_per_launch": fused_bytes},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

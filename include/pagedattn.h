@@ -155,6 +155,36 @@ pa_status pa_reshape_and_cache(const void* key, const void* value, const int64_t
                                void* stream);
 
 /*
+ * One decode step in a single launch: store each sequence's new token in its
+ * slot, then decode attention over the caches that now hold it.  The result
+ * (out and both caches) is the same as
+ *   pa_reshape_and_cache(key, value, slot_mapping, k_cache, v_cache, num_seqs, ...)
+ *   followed by pa_paged_attention(out, query, ...).
+ *
+ *   key, value     [num_seqs][num_kv_heads][head_dim], contiguous: the K and V
+ *                  of the token each sequence appends in this step
+ *   slot_mapping   [num_seqs] int64: slot of that token, which must be the
+ *                  slot of position context_lens[s] - 1 of sequence s (the
+ *                  block-table entry block_table[s][(L - 1) / BS] at offset
+ *                  (L - 1) % BS), or negative to write nothing for s
+ *   k_cache, v_cache  written in place (the new tokens' slots only)
+ *   other arguments as in pa_paged_attention
+ * Preconditions: a slot written for sequence s lies in a block that no other
+ * sequence of the call reads or writes (after copy-on-write a sequence's last
+ * block is its own); a slot other than position L - 1's is read by no sequence
+ * of the call.  The workgroup that reads position L - 1 of s writes s's new
+ * token: it uses the token for that position directly and stores it back
+ * together with the neighbouring tokens of the same 16-byte chunks, unchanged.
+ */
+pa_status pa_decode_step(void* out, const void* query, const void* key, const void* value,
+                         const int64_t* slot_mapping, const int32_t* block_table,
+                         const int32_t* context_lens, void* k_cache, void* v_cache,
+                         int num_seqs, int num_heads, int num_kv_heads, int head_dim,
+                         int block_size, int max_blocks_per_seq, int num_blocks,
+                         int max_context_len, float scale, pa_dtype dtype, int partition_size,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Diagnostic read path: reassemble every sequence's K and V through its block
  * table into contiguous token-major arrays (bit-exact copies).
  *

@@ -43,6 +43,8 @@ def load_library() -> ctypes.CDLL:
     lib.pa_paged_attention.argtypes = [vp] * 6 + [i32] * 8 + [f32, i32, i32, vp, sz, vp]
     lib.pa_reshape_and_cache.restype = i32
     lib.pa_reshape_and_cache.argtypes = [vp] * 5 + [i32] * 6 + [vp]
+    lib.pa_decode_step.restype = i32
+    lib.pa_decode_step.argtypes = [vp] * 9 + [i32] * 8 + [f32, i32, i32, vp, sz, vp]
     lib.pa_gather_kv.restype = i32
     lib.pa_gather_kv.argtypes = [vp] * 7 + [i32] * 8 + [vp]
     _lib = lib
@@ -161,6 +163,60 @@ def paged_attention(query: torch.Tensor, block_table: torch.Tensor, context_lens
     return out
 
 
+def _decode_step_args(query, key, value, slot_mapping, block_table, context_lens, k_cache,
+                      v_cache, scale, max_context_len, out, partition_size, workspace, stream):
+    """Checked argument tuple of pa_decode_step (allocates out/workspace when None)."""
+    dev = query.device
+    _require(query, "query", dev)
+    NB, Hkv, D, BS = _cache_dims(k_cache, v_cache)
+    for t, name in ((k_cache, "k_cache"), (v_cache, "v_cache"), (key, "key"), (value, "value")):
+        _require(t, name, dev, query.dtype)
+    _require(slot_mapping, "slot_mapping", dev, torch.int64)
+    _require(block_table, "block_table", dev, torch.int32)
+    _require(context_lens, "context_lens", dev, torch.int32)
+    if query.dim() != 3 or query.shape[2] != D:
+        raise ValueError(f"query must be [S, Hq, {D}], got {tuple(query.shape)}")
+    S, Hq, _ = query.shape
+    if tuple(key.shape) != (S, Hkv, D) or tuple(value.shape) != (S, Hkv, D) or \
+            tuple(slot_mapping.shape) != (S,):
+        raise ValueError(f"key/value must be [{S}, {Hkv}, {D}] and slot_mapping [{S}]")
+    if block_table.dim() != 2 or block_table.shape[0] != S or tuple(context_lens.shape) != (S,):
+        raise ValueError("block_table must be [S, MB] and context_lens [S]")
+    if out is None:
+        out = torch.empty_like(query)
+    _require(out, "out", dev, query.dtype)
+    if tuple(out.shape) != tuple(query.shape):
+        raise ValueError("out must have the shape of query")
+    need = workspace_size(S, Hq, Hkv, D, max_context_len, partition_size, query.dtype)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    if workspace is not None:
+        _require(workspace, "workspace", dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    args = (_ptr(out), _ptr(query), _ptr(key), _ptr(value), _ptr(slot_mapping), _ptr(block_table),
+            _ptr(context_lens), _ptr(k_cache), _ptr(v_cache), S, Hq, Hkv, D, BS,
+            block_table.shape[1], NB, int(max_context_len), float(scale), _dtype_code(query),
+            int(partition_size), _ptr(workspace), ws_bytes, _stream(dev, stream))
+    keep = (query, key, value, slot_mapping, block_table, context_lens, k_cache, v_cache, out,
+            workspace)
+    return args, out, keep
+
+
+def decode_step(query: torch.Tensor, key: torch.Tensor, value: torch.Tensor,
+                slot_mapping: torch.Tensor, block_table: torch.Tensor, context_lens: torch.Tensor,
+                k_cache: torch.Tensor, v_cache: torch.Tensor, scale: float, *,
+                max_context_len: int, out: torch.Tensor | None = None, partition_size: int = 0,
+                workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """One fused step: store key/value [S, Hkv, D] at slot_mapping [S], then decode
+    attention of query [S, Hq, D] (see pa_decode_step in pagedattn.h)."""
+    lib = load_library()
+    args, out, _ = _decode_step_args(query, key, value, slot_mapping, block_table, context_lens,
+                                     k_cache, v_cache, scale, max_context_len, out,
+                                     partition_size, workspace, stream)
+    _check(lib.pa_decode_step(*args), "pa_decode_step")
+    return out
+
+
 def reshape_and_cache(key: torch.Tensor, value: torch.Tensor, slot_mapping: torch.Tensor,
                       k_cache: torch.Tensor, v_cache: torch.Tensor, stream=None) -> None:
     """Store key/value [T, Hkv, D] at slot_mapping [T] (int64) in the caches, in place."""
@@ -257,3 +313,16 @@ def prepare_reshape_and_cache(key, value, slot_mapping, k_cache, v_cache,
             key.shape[0], Hkv, D, BS, NB, _dtype_code(key), _stream(key.device, stream))
     return PreparedCall(lib.pa_reshape_and_cache, args, "pa_reshape_and_cache",
                         (key, value, slot_mapping, k_cache, v_cache))
+
+
+def prepare_decode_step(query, key, value, slot_mapping, block_table, context_lens, k_cache,
+                        v_cache, scale, *, max_context_len: int, out, partition_size: int = 0,
+                        workspace=None, stream=None) -> PreparedCall:
+    """Check the arguments of decode_step once and return a re-launchable call."""
+    lib = load_library()
+    args, out, keep = _decode_step_args(query, key, value, slot_mapping, block_table,
+                                        context_lens, k_cache, v_cache, scale, max_context_len,
+                                        out, partition_size, workspace, stream)
+    call = PreparedCall(lib.pa_decode_step, args, "pa_decode_step", keep)
+    call()
+    return call

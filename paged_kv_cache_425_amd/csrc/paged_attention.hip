@@ -70,6 +70,11 @@ struct DecodeParams {
   const int32_t* context_lens;
   const void* k_cache;
   const void* v_cache;
+  // fused decode step (all null for plain decode): the step's new token of each
+  // sequence, [S][Hkv][D], and its slot, written into the caches before the reads
+  const void* new_k;
+  const void* new_v;
+  const int64_t* new_slot;
   int S, Hq, Hkv, g, MB, NB, P, Pmax;
   float scale_log2;        // scale * log2(e): logits are kept in base-2 units
 };
@@ -126,12 +131,14 @@ paged_decode_kernel(const DecodeParams a) {
   constexpr int kNs = Sh::kNs;
   constexpr int kThreads = NW * 64;
 
-  // LDS: [ctrl: 16 ints][lens: S ints, PAIRED only][tables: 1 or 2 windows of P/BS][merge]
+  // LDS: [ctrl: 16 ints][new K/V: 2 units x 2 x D elements][lens: S ints, PAIRED only]
+  //      [tables: 1 or 2 windows of P/BS][merge]
   extern __shared__ __align__(16) unsigned char smem[];
   int* ctrl = reinterpret_cast<int*>(smem);
+  T* newkv = reinterpret_cast<T*>(smem + 64);                // [unit][K, V][D]
   const int win = a.P / BS;                                 // table entries per window
   const int lens_words = PAIRED ? (a.S + 3) / 4 * 4 : 0;
-  int* lens = ctrl + 16;
+  int* lens = reinterpret_cast<int*>(smem + 64 + 4 * D * sizeof(T));
   int* tbl = lens + lens_words;
   const int tbl_words = ((PAIRED ? 2 : 1) * win + 3) / 4 * 4;
   float* red = reinterpret_cast<float*>(tbl + tbl_words);
@@ -147,7 +154,7 @@ paged_decode_kernel(const DecodeParams a) {
   id /= a.Hkv;
 
   // ---- this wave's unit: sequence s, tokens [tok0, tok1), table window, wave slot ----
-  int s, tok0, tok1, lw, nw, p = 0, nparts = 1;
+  int s, tok0, tok1, lw, nw, p = 0, nparts = 1, uidx = 0;
   int sA = 0, sB = -1, nA = NW;                             // PAIRED: the two sequences
   const int* tblw = tbl;
   if constexpr (PAIRED) {
@@ -181,6 +188,7 @@ paged_decode_kernel(const DecodeParams a) {
     }
     nA = __builtin_amdgcn_readfirstlane(nA);
     const bool onA = wave < nA;
+    uidx = onA ? 0 : 1;
     s = onA ? sA : sB;
     tok0 = 0;
     tok1 = __builtin_amdgcn_readfirstlane(onA ? LA : LB);
@@ -218,6 +226,33 @@ paged_decode_kernel(const DecodeParams a) {
   const int head = kvh * g + (n % g);
   const bool row_live = n < rows;
 
+  // Fused step: this workgroup's units' new tokens (kv head kvh).  Only the workgroup
+  // that reads a sequence's last position L - 1 handles its new token (the last
+  // partition, or the pair holding the sequence).  Thread t below 2 * kCh * units holds
+  // one 16-byte chunk of it and copies the chunk to LDS.  When the token's slot is where
+  // the decode reads position L - 1 (the usual case), the step covering that position
+  // substitutes the LDS copy for what the cache returned and writes the patched K row
+  // chunks and 8-token V chunks back -- after its own loads brought those lines in, so
+  // the stores do not miss.  Any other valid slot (read by no sequence of the call) is
+  // stored after the barrier below.
+  constexpr int kCh = D / kX;                               // 16-byte chunks per head
+  const bool fused = a.new_slot != nullptr;
+  const bool last_part = p == nparts - 1;
+  const int nun_new = !fused ? 0 : (PAIRED ? (sB >= 0 ? 2 : 1) : (last_part ? 1 : 0));
+  u32x4 new_val = {0u, 0u, 0u, 0u};
+  int64_t new_slot = -1;
+  int new_u = 0;
+  const bool new_is_v = (threadIdx.x % (2 * kCh)) >= kCh;
+  const int new_cc = threadIdx.x % kCh;
+  if ((int)threadIdx.x < nun_new * 2 * kCh) {
+    new_u = threadIdx.x / (2 * kCh);
+    const int su = PAIRED ? (new_u ? sB : sA) : s;
+    const size_t src = ((size_t)su * a.Hkv + kvh) * D + (size_t)new_cc * kX;
+    new_val = load16(static_cast<const T*>(new_is_v ? a.new_v : a.new_k) + src);
+    store16(newkv + (2 * new_u + (new_is_v ? 1 : 0)) * D + new_cc * kX, new_val);
+    new_slot = a.new_slot[su];
+  }
+
   // Query operand: lane (n, j) holds head-row n's channels of the chunks it multiplies.
   const T* qrow = static_cast<const T*>(a.q) + ((size_t)s * a.Hq + head) * D;
   u32x4 qop[kNc];
@@ -227,6 +262,41 @@ paged_decode_kernel(const DecodeParams a) {
     qop[c] = row_live && tok1 > tok0 ? load16(qrow + kX * (4 * c + j)) : z;
   }
   __syncthreads();
+
+  // slot of token `pos` of a unit whose table window `w` starts at token t0
+  auto slot_of = [&](const int* w, int t0, int pos) -> int64_t {
+    return (int64_t)w[(pos - t0) / BS] * BS + pos % BS;
+  };
+  const int64_t nslots = (int64_t)a.NB * BS;
+
+  // position this wave takes from LDS and writes back (-1: none)
+  int lm1 = -1;
+  if (uidx < nun_new && tok1 > tok0) {
+    const int64_t sl = a.new_slot[s];
+    if (sl >= 0 && sl < nslots && sl == slot_of(tblw, tok0, tok1 - 1)) lm1 = tok1 - 1;
+  }
+  lm1 = __builtin_amdgcn_readfirstlane(lm1);
+
+  // a new slot that is not where position L - 1 is read from: store it here
+  if (new_slot >= 0 && new_slot < nslots) {
+    const int Lu = PAIRED ? lens[new_u ? sB : sA] : tok1;
+    const int64_t loc =
+        Lu > 0 ? slot_of(PAIRED ? tbl + new_u * win : tbl, PAIRED ? 0 : tok0, Lu - 1) : -1;
+    if (new_slot != loc) {
+      T* kcw = const_cast<T*>(static_cast<const T*>(a.k_cache));
+      T* vcw = const_cast<T*>(static_cast<const T*>(a.v_cache));
+      const size_t blk = (size_t)(new_slot / BS);
+      const int off = (int)(new_slot % BS);
+      if (!new_is_v) {
+        store16(kcw + ((blk * a.Hkv + kvh) * kCh + new_cc) * BS * kX + (size_t)off * kX, new_val);
+      } else {
+        T* dst = vcw + ((blk * a.Hkv + kvh) * D + (size_t)new_cc * kX) * BS + off;
+        const T* e = reinterpret_cast<const T*>(&new_val);
+#pragma unroll
+        for (int k = 0; k < kX; ++k) dst[(size_t)k * BS] = e[k];
+      }
+    }
+  }
 
   const T* kc = static_cast<const T*>(a.k_cache);
   const T* vc = static_cast<const T*>(a.v_cache);
@@ -267,6 +337,49 @@ paged_decode_kernel(const DecodeParams a) {
   // ---- math of one step ---------------------------------------------------------
   auto compute_step = [&](int st, StepData<T, D>& b) {
     const int base = tok0 + st * kStep;
+    // fused step: position L - 1 takes the new token's K/V from LDS, and the patched
+    // chunks go back to the cache (their lines were just loaded)
+    if (lm1 >= base && lm1 < base + kStep) {
+      const T* nk = newkv + (2 * uidx) * D;
+      const T* nv = newkv + (2 * uidx + 1) * D;
+      T* kcw = const_cast<T*>(kc);
+      T* vcw = const_cast<T*>(vc);
+#pragma unroll
+      for (int t = 0; t < Sh::kTiles; ++t) {
+        const int tok = kBf16 ? base + 8 * (n >> 2) + 4 * t + (n & 3) : base + n;
+        if (tok == lm1) {
+          const int phys = tblw[(tok - tok0) / BS];
+          T* kp = kcw + ((size_t)phys * a.Hkv + kvh) * head_elems + (size_t)j * BS * kX +
+                  (size_t)(tok % BS) * kX;
+#pragma unroll
+          for (int c = 0; c < kNc; ++c) {
+            b.k[t][c] = *reinterpret_cast<const u32x4*>(nk + kX * (4 * c + j));
+            store16(kp + (size_t)4 * c * BS * kX, b.k[t][c]);
+          }
+        }
+      }
+      const int tokv = base + kTpl * j;
+      const int e = lm1 - tokv;
+      if (e >= 0 && e < kTpl) {
+        const int physv = tblw[(tokv - tok0) / BS];
+        T* vp = vcw + ((size_t)physv * a.Hkv + kvh) * head_elems + (size_t)n * BS + (tokv % BS);
+#pragma unroll
+        for (int sl = 0; sl < kNs; ++sl) {
+          const T val = nv[16 * sl + n];
+          if constexpr (kBf16) {
+            const uint32_t bitsv = __builtin_bit_cast(uint16_t, val);
+            const int w = e >> 1;
+            uint32_t word = b.v[sl][w];
+            word = (e & 1) ? ((word & 0x0000FFFFu) | (bitsv << 16)) : ((word & 0xFFFF0000u) | bitsv);
+            b.v[sl][w] = word;
+          } else {
+            b.v[sl][e] = __builtin_bit_cast(uint32_t, val);
+          }
+          store16(vp + (size_t)16 * sl * BS, b.v[sl]);
+        }
+      }
+    }
+
     const bool tail = base + kStep > tok1;
     {
       // zero V elements of tokens past the end (their weight is 0, and 0 * NaN is NaN);
@@ -499,29 +612,32 @@ constexpr int kMaxPairedSeqs = 512;         // the in-kernel ordering is O(S^2 /
 constexpr size_t kMaxLds = 64 * 1024;
 
 // Dynamic LDS of one workgroup; mirrors the layout at the top of paged_decode_kernel.
-inline size_t decode_lds_bytes(bool paired, int nw, int S, int D, int BS, int P, int g) {
+inline size_t decode_lds_bytes(bool paired, int nw, int S, int D, int BS, int P, int g,
+                               int elt) {
   const size_t lens_words = paired ? (size_t)(S + 3) / 4 * 4 : 0;
   const size_t tbl_words = ((size_t)(paired ? 2 : 1) * (P / BS) + 3) / 4 * 4;
-  return 4 * (16 + lens_words + tbl_words + (size_t)nw * merge_words(D, g));
+  return 64 + 4 * (size_t)D * elt +
+         4 * (lens_words + tbl_words + (size_t)nw * merge_words(D, g));
 }
 
 // Paired mode when every sequence is one partition, there are at least two
 // sequences, the ordering stays cheap and the workgroup's LDS fits.
-inline bool use_paired(const DecodeParams& a, int D, int BS) {
+inline bool use_paired(const DecodeParams& a, int D, int BS, int elt) {
   return a.Pmax == 1 && a.S >= 2 && a.S <= kMaxPairedSeqs &&
-         decode_lds_bytes(true, kPairWaves, a.S, D, BS, a.P, a.g) <= kMaxLds;
+         decode_lds_bytes(true, kPairWaves, a.S, D, BS, a.P, a.g, elt) <= kMaxLds;
 }
 
 template <typename T, int D, int BS>
 hipError_t launch_decode(const DecodeParams& a, hipStream_t stream) {
-  if (use_paired(a, D, BS)) {
-    const size_t lds = decode_lds_bytes(true, kPairWaves, a.S, D, BS, a.P, a.g);
+  constexpr int elt = sizeof(T);
+  if (use_paired(a, D, BS, elt)) {
+    const size_t lds = decode_lds_bytes(true, kPairWaves, a.S, D, BS, a.P, a.g, elt);
     const long grid = (long)a.Hkv * ((a.S + 1) / 2);
     hipLaunchKernelGGL((paged_decode_kernel<T, D, BS, kPairWaves, kPipe, true>),
                        dim3((unsigned)grid), dim3(kPairWaves * 64), lds, stream, a);
     return hipGetLastError();
   }
-  const size_t lds = decode_lds_bytes(false, kWaves, a.S, D, BS, a.P, a.g);
+  const size_t lds = decode_lds_bytes(false, kWaves, a.S, D, BS, a.P, a.g, elt);
   const long grid = (long)a.Hkv * a.Pmax * a.S;
   hipLaunchKernelGGL((paged_decode_kernel<T, D, BS, kWaves, kPipe, false>), dim3((unsigned)grid),
                      dim3(kWaves * 64), lds, stream, a);
@@ -632,26 +748,32 @@ extern "C" size_t pa_paged_attention_workspace_size(int num_seqs, int num_heads,
   return workspace_layout(num_seqs, num_heads, head_dim, pmax).total;
 }
 
-extern "C" pa_status pa_paged_attention(void* out, const void* query, const int32_t* block_table,
-                                        const int32_t* context_lens, const void* k_cache,
-                                        const void* v_cache, int num_seqs, int num_heads,
-                                        int num_kv_heads, int head_dim, int block_size,
-                                        int max_blocks_per_seq, int num_blocks,
-                                        int max_context_len, float scale, pa_dtype dtype,
-                                        int partition_size, void* workspace,
-                                        size_t workspace_bytes, void* stream) {
+namespace {
+
+// Checks shared by pa_paged_attention and pa_decode_step, then the launch.
+pa_status run_decode(void* out, const void* query, const int32_t* block_table,
+                     const int32_t* context_lens, const void* k_cache, const void* v_cache,
+                     const void* new_k, const void* new_v, const int64_t* new_slot,
+                     int num_seqs, int num_heads, int num_kv_heads, int head_dim, int block_size,
+                     int max_blocks_per_seq, int num_blocks, int max_context_len, float scale,
+                     pa_dtype dtype, int partition_size, void* workspace, size_t workspace_bytes,
+                     void* stream) {
   pa_status st = check_shapes(num_heads, num_kv_heads, head_dim, block_size, dtype);
   if (st != PA_OK) return st;
   if (num_seqs < 0 || max_blocks_per_seq <= 0 || num_blocks <= 0 || max_context_len < 0)
     return PA_ERR_INVALID_ARG;
   if ((long)max_context_len > (long)max_blocks_per_seq * block_size) return PA_ERR_INVALID_ARG;
-  if (partition_size != 0 && (partition_size < 64 || partition_size > 8192 || partition_size % 64))
+  if (partition_size != 0 &&
+      (partition_size < 64 || partition_size > kMaxPartition || partition_size % 64))
     return PA_ERR_INVALID_ARG;
   if (num_seqs == 0) return PA_OK;
   if (!out || !query || !block_table || !context_lens || !k_cache || !v_cache)
     return PA_ERR_INVALID_ARG;
   if (!aligned(out, 16) || !aligned(query, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
       !aligned(block_table, 4) || !aligned(context_lens, 4))
+    return PA_ERR_INVALID_ARG;
+  if (new_slot && (!new_k || !new_v || !aligned(new_k, 16) || !aligned(new_v, 16) ||
+                   !aligned(new_slot, 8)))
     return PA_ERR_INVALID_ARG;
 
   const int P = partition_size ? partition_size
@@ -672,6 +794,9 @@ extern "C" pa_status pa_paged_attention(void* out, const void* query, const int3
   a.context_lens = context_lens;
   a.k_cache = k_cache;
   a.v_cache = v_cache;
+  a.new_k = new_k;
+  a.new_v = new_v;
+  a.new_slot = new_slot;
   a.S = num_seqs;
   a.Hq = num_heads;
   a.Hkv = num_kv_heads;
@@ -690,4 +815,35 @@ extern "C" pa_status pa_paged_attention(void* out, const void* query, const int3
                        ? pa::dispatch_decode<uint16_t>(a, head_dim, block_size, s)
                        : pa::dispatch_decode<float>(a, head_dim, block_size, s);
   return err == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" pa_status pa_paged_attention(void* out, const void* query, const int32_t* block_table,
+                                        const int32_t* context_lens, const void* k_cache,
+                                        const void* v_cache, int num_seqs, int num_heads,
+                                        int num_kv_heads, int head_dim, int block_size,
+                                        int max_blocks_per_seq, int num_blocks,
+                                        int max_context_len, float scale, pa_dtype dtype,
+                                        int partition_size, void* workspace,
+                                        size_t workspace_bytes, void* stream) {
+  return run_decode(out, query, block_table, context_lens, k_cache, v_cache, nullptr, nullptr,
+                    nullptr, num_seqs, num_heads, num_kv_heads, head_dim, block_size,
+                    max_blocks_per_seq, num_blocks, max_context_len, scale, dtype,
+                    partition_size, workspace, workspace_bytes, stream);
+}
+
+extern "C" pa_status pa_decode_step(void* out, const void* query, const void* key,
+                                    const void* value, const int64_t* slot_mapping,
+                                    const int32_t* block_table, const int32_t* context_lens,
+                                    void* k_cache, void* v_cache, int num_seqs, int num_heads,
+                                    int num_kv_heads, int head_dim, int block_size,
+                                    int max_blocks_per_seq, int num_blocks, int max_context_len,
+                                    float scale, pa_dtype dtype, int partition_size,
+                                    void* workspace, size_t workspace_bytes, void* stream) {
+  if (num_seqs > 0 && (!key || !value || !slot_mapping)) return PA_ERR_INVALID_ARG;
+  return run_decode(out, query, block_table, context_lens, k_cache, v_cache, key, value,
+                    num_seqs > 0 ? slot_mapping : nullptr, num_seqs, num_heads, num_kv_heads,
+                    head_dim, block_size, max_blocks_per_seq, num_blocks, max_context_len, scale,
+                    dtype, partition_size, workspace, workspace_bytes, stream);
 }

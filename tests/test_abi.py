@@ -32,7 +32,7 @@ def test_header_declares_the_boundary():
     assert declared_functions() == sorted([
         "pa_abi_version", "pa_status_string", "pa_default_partition_size",
         "pa_paged_attention_workspace_size", "pa_paged_attention", "pa_reshape_and_cache",
-        "pa_gather_kv"])
+        "pa_gather_kv", "pa_decode_step"])
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -113,6 +113,24 @@ def test_f32_allows_larger_groups(lib):
     # i.e. the group check passed
     assert call_attention(lib, Hq=128, Hkv=8, dtype=0, q=None) == 1
     assert call_attention(lib, Hq=136, Hkv=8, dtype=0) == 2
+
+
+def test_decode_step_rejects_before_launch(lib):
+    f = lib.pa_decode_step
+    base = [FAKE] * 9 + [4, 32, 8, 128, 16, 8, 64, 128, 0.1, 1, 0, None, 0, None]
+
+    def call(over):
+        a = list(base)
+        for k, v in over.items():
+            a[k] = v
+        return f(*a)
+    assert call({2: None}) == 1                 # key missing
+    assert call({4: FAKE + 4}) == 1             # slot_mapping misaligned
+    assert call({3: FAKE + 8}) == 1             # value misaligned
+    assert call({12: 96}) == 2                  # head size
+    assert call({16: 129}) == 1                 # max_context_len past the table
+    assert call({9: 0, 2: None, 3: None, 4: None}) == 0   # empty batch
+    assert call({16: 128, 19: 64}) == 3         # two partitions, no workspace
 
 
 def test_reshape_and_cache_rejects_before_launch(lib):

@@ -127,6 +127,76 @@ def test_decode_step_matches_oracle(name, make):
     say(f"  {name}: {stats}")
 
 
+# ---------------------------------------------------------------------------
+# fused step (pa_decode_step): same caches and output as the two calls
+# ---------------------------------------------------------------------------
+FUSED_CASES = [("cfg0", lambda: make_config(0), 0),
+               ("cfg1", lambda: make_config(1), 0),
+               ("cfg2-bs8", lambda: make_config(2, block_size=8), 0),
+               ("cfg2-bs32-P1024", lambda: make_config(2, block_size=32), 1024),
+               ("cfg3-prefix", lambda: make_config(3), 0),
+               ("cfg3-parallel-sampling", lambda: make_config(3, variant="parallel-sampling"), 0),
+               ("cfg4", lambda: make_config(4), 512),
+               ("tiny-f32-P64", lambda: tiny("f32", LENS, 8, 2, 128, 16, seed=31), 64),
+               ("tiny-bf16-bs8-P128", lambda: tiny("bf16", LENS, 16, 2, 64, 8, seed=32), 128),
+               ("tiny-bf16-paired", lambda: tiny("bf16", LENS, 16, 2, 64, 32, seed=33), 0),
+               ("many-seqs-unpaired", lambda: tiny("bf16", np.random.default_rng(34).integers(
+                   1, 90, size=600), 8, 2, 128, 16, seed=34), 128)]
+
+
+def fused_inputs(w):
+    """The new token of every sequence: its record at position L - 1."""
+    new = np.array([w.seq_records[s][-1] for s in range(w.num_seqs)], dtype=np.int64)
+    return new, w.rec_slot[new].copy()
+
+
+@pytest.mark.parametrize("name,make,part", FUSED_CASES, ids=[c[0] for c in FUSED_CASES])
+def test_fused_decode_step_matches_two_calls_and_oracle(name, make, part):
+    w = make()
+    say(f"fused step {name} S={w.num_seqs} BS={w.block_size} P={part}")
+    new, slots = fused_inputs(w)
+    assert set(new.tolist()) == set(w.new_records.tolist())
+    hist_k, hist_v = build_pools(w, include_new=False)
+    ref_k, ref_v = oracle.reshape_and_cache(w.rec_key[new], w.rec_value[new], slots, hist_k, hist_v)
+    ref = oracle_out(w, ref_k, ref_v)
+    inp = upload_inputs(w, DEV)
+    key, val = to_dev(w.rec_key[new], w.dtype, DEV), to_dev(w.rec_value[new], w.dtype, DEV)
+    slot_t = torch.from_numpy(slots).to(DEV)
+    kc, vc = to_dev(hist_k, w.dtype, DEV), to_dev(hist_v, w.dtype, DEV)
+    out = pk.decode_step(inp["query"], key, val, slot_t, inp["block_table"], inp["context_lens"],
+                         kc, vc, w.scale, max_context_len=w.max_context_len, partition_size=part)
+    kc2, vc2 = to_dev(hist_k, w.dtype, DEV), to_dev(hist_v, w.dtype, DEV)
+    pk.reshape_and_cache(key, val, slot_t, kc2, vc2)
+    out2 = pk.paged_attention(inp["query"], inp["block_table"], inp["context_lens"], kc2, vc2,
+                              w.scale, max_context_len=w.max_context_len, partition_size=part)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(kc), ref_k.view(bits(kc).dtype))
+    assert np.array_equal(bits(vc), ref_v.view(bits(vc).dtype))
+    assert np.array_equal(bits(out), bits(out2))
+    stats = check_close(to_f64(out), ref, w.dtype, name)
+    say(f"  {name}: {stats}")
+
+
+def test_fused_decode_step_skips_negative_slots():
+    """A negative slot writes nothing: the cache keeps what it held."""
+    w = tiny("bf16", (5, 40, 17, 64), 8, 2, 128, 16, seed=35)
+    kc_np, vc_np = build_pools(w)                     # every token already stored
+    new, slots = fused_inputs(w)
+    slots[1] = -1
+    key = w.rec_key[new].copy()
+    key[1] = 0                                        # would change the result if written
+    inp = upload_inputs(w, DEV)
+    kc, vc = to_dev(kc_np, w.dtype, DEV), to_dev(vc_np, w.dtype, DEV)
+    say("fused step with a negative slot")
+    out = pk.decode_step(inp["query"], to_dev(key, w.dtype, DEV),
+                         to_dev(w.rec_value[new], w.dtype, DEV), torch.from_numpy(slots).to(DEV),
+                         inp["block_table"], inp["context_lens"], kc, vc, w.scale,
+                         max_context_len=w.max_context_len)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(kc), kc_np.view(np.uint16))
+    check_close(to_f64(out), oracle_out(w, kc_np, vc_np), "bf16", "negative-slot")
+
+
 def test_cfg1_shape_in_f32_is_exact_to_1e5():
     """The Llama-3-8B decode shape with f32 data: a tighter check of indexing."""
     base = make_config(1)
