@@ -159,15 +159,20 @@ paged_decode_kernel(const DecodeParams a) {
   const int* tblw = tbl;
   if constexpr (PAIRED) {
     const int r = id;                                       // pair index
-    for (int t = threadIdx.x; t < a.S; t += kThreads) lens[t] = clamped_len(a, t, BS);
+    // lengths, padded with -1 to a multiple of 4 (a pad never counts as longer)
+    for (int t = threadIdx.x; t < lens_words; t += kThreads)
+      lens[t] = t < a.S ? clamped_len(a, t, BS) : -1;
     __syncthreads();
     const int rB = a.S - 1 - r;
     for (int t = threadIdx.x; t < a.S; t += kThreads) {
       const int Lt = lens[t];
       int rank = 0;
-      for (int u = 0; u < a.S; ++u) {
-        const int Lu = lens[u];
-        rank += (Lu > Lt) || (Lu == Lt && u < t);
+#pragma unroll 4
+      for (int u4 = 0; u4 < lens_words / 4; ++u4) {
+        const int4 v = reinterpret_cast<const int4*>(lens)[u4];   // same address in every lane
+        const int u = 4 * u4;
+        rank += (v.x > Lt) + (v.x == Lt && u < t) + (v.y > Lt) + (v.y == Lt && u + 1 < t) +
+                (v.z > Lt) + (v.z == Lt && u + 2 < t) + (v.w > Lt) + (v.w == Lt && u + 3 < t);
       }
       if (rank == r) ctrl[0] = t;
       if (rank == rB) ctrl[1] = t;

@@ -52,7 +52,7 @@ def kernel_durations_ordered(db: str) -> dict:
     return out
 
 
-def trace_table(db: str, last: int = 0) -> str:
+def trace_table(db: str, last: int = 0, slices: list | None = None) -> str:
     durs = kernel_durations_ordered(db)
     lines = ["| kernel | launches | mean us | median us | min us | max us |",
              "|---|---|---|---|---|---|"]
@@ -70,6 +70,20 @@ def trace_table(db: str, last: int = 0) -> str:
             d = ds[-last:]
             lines.append(f"| `{short(name)}` | {len(d)} | {statistics.fmean(d):.2f} | "
                          f"{statistics.median(d):.2f} | {min(d):.2f} | {max(d):.2f} |")
+    for spec in slices or []:
+        # KERNEL_SUBSTRING:START:COUNT:LABEL -- launches START .. START+COUNT-1 of that kernel
+        sub, start, count, label = spec.split(":", 3)
+        start, count = int(start), int(count)
+        for name, ds in durs.items():
+            if sub not in name:
+                continue
+            d = ds[start:start + count]
+            if not d:
+                continue
+            lines += ["", f"{label}: launches {start}..{start + len(d) - 1} of `{short(name)}`:", "",
+                      "| launches | mean us | median us | min us | max us |", "|---|---|---|---|---|",
+                      f"| {len(d)} | {statistics.fmean(d):.2f} | {statistics.median(d):.2f} | "
+                      f"{min(d):.2f} | {max(d):.2f} |"]
     return "\n".join(lines)
 
 
@@ -97,6 +111,8 @@ def main() -> None:
     t.add_argument("--title", default="Kernel trace")
     t.add_argument("--last", type=int, default=0,
                    help="also tabulate the last N launches of each kernel")
+    t.add_argument("--slice", action="append", default=[],
+                   help="KERNEL_SUBSTRING:START:COUNT:LABEL, stats of a window of launches")
     t.add_argument("--out", required=True)
     f = sub.add_parser("traffic")
     f.add_argument("--fetch", required=True)
@@ -107,13 +123,15 @@ def main() -> None:
     f.add_argument("--workload", required=True)
     f.add_argument("--command-fetch", required=True)
     f.add_argument("--command-write", required=True)
+    f.add_argument("--start", type=int, default=0, help="first launch of the kernel to use")
+    f.add_argument("--count", type=int, default=0, help="launches to use (0: all from start)")
     f.add_argument("--out", required=True)
     f.add_argument("--out-json", required=True)
     a = ap.parse_args()
 
     if a.cmd == "trace":
         text = (f"# {a.title}\n\nCommand (from the repository root on the GPU box):\n\n"
-                f"```\n{a.command}\n```\n\n{trace_table(a.db, a.last)}\n")
+                f"```\n{a.command}\n```\n\n{trace_table(a.db, a.last, a.slice)}\n")
         with open(a.out, "w") as fh:
             fh.write(text)
         print(text)
@@ -123,8 +141,9 @@ def main() -> None:
     wr = counter_values(a.write, "WRITE_SIZE")
     ff, fread, fn = copy_factor(fr, a.copy_bytes)
     wf, wread, wn = copy_factor(wr, a.copy_bytes)
-    fk = kernel_counter(fr, a.kernel)
-    wk = kernel_counter(wr, a.kernel)
+    end = a.start + a.count if a.count else None
+    fk = kernel_counter(fr, a.kernel)[a.start:end]
+    wk = kernel_counter(wr, a.kernel)[a.start:end]
     if not fk or not wk:
         raise SystemExit(f"kernel {a.kernel} not found in the counter runs")
     fetch_b = statistics.median(fk) * 1024.0 * ff
@@ -156,10 +175,10 @@ K/V pools, {a.copy_bytes} bytes each.  FETCH_SIZE reads {fread:.1f} KiB for them
 
 | per launch of `{a.kernel}` | bytes |
 |---|---|
-| FETCH_SIZE x scale (median of {len(fk)} launches) | {fetch_b:,.0f} |
-| WRITE_SIZE x scale (median of {len(wk)} launches) | {write_b:,.0f} |
+| FETCH_SIZE x scale (median of launches {a.start}..{a.start + len(fk) - 1}) | {fetch_b:,.0f} |
+| WRITE_SIZE x scale (median of launches {a.start}..{a.start + len(wk) - 1}) | {write_b:,.0f} |
 | measured HBM traffic | {total:,.0f} |
-| algorithmic bytes (KV + q + out + table entries + lengths) | {a.algorithmic_bytes:,} |
+| algorithmic bytes per launch | {a.algorithmic_bytes:,} |
 | measured / algorithmic | {total / a.algorithmic_bytes:.4f} |
 
 Kernel source SHA-256: `{sha}`.
