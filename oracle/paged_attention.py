@@ -114,6 +114,31 @@ def reshape_and_cache(key: np.ndarray, value: np.ndarray, slot_mapping: np.ndarr
 
 
 # ---------------------------------------------------------------------------
+# copy-on-write: whole physical blocks
+# ---------------------------------------------------------------------------
+def copy_blocks(k_cache: np.ndarray, v_cache: np.ndarray, block_mapping: np.ndarray,
+                inplace: bool = False):
+    """Pools where physical block dst holds a copy of block src, for every (src, dst).
+
+    Several sequences may point at one physical block (parallel samples of one
+    prompt, beams, a shared system prompt: "core features" page, section 4.1;
+    "core architecture" page, section 2.2.1).  A sharer that appends into such
+    a block first gets a private copy of it; this is that copy, every kv head
+    of K and V.  Destinations must be distinct and none may be a source, so the
+    order of the copies does not matter.
+    """
+    pairs = np.asarray(block_mapping, dtype=np.int64).reshape(-1, 2)
+    src, dst = pairs[:, 0], pairs[:, 1]
+    assert len(np.unique(dst)) == len(dst), "destinations must be distinct"
+    assert not (set(dst.tolist()) & set(src.tolist())), "a destination is also a source"
+    k_new = k_cache if inplace else k_cache.copy()
+    v_new = v_cache if inplace else v_cache.copy()
+    k_new[dst] = k_cache[src]
+    v_new[dst] = v_cache[src]
+    return k_new, v_new
+
+
+# ---------------------------------------------------------------------------
 # read path: reassemble through the block table
 # ---------------------------------------------------------------------------
 def gather_sequence(block_table_row: np.ndarray, context_len: int,

@@ -386,3 +386,54 @@ def test_one_partition_covering_everything_is_softmax_numerator_and_denominator(
     np.testing.assert_allclose(m[0], z.max(axis=0), rtol=1e-15)
     np.testing.assert_allclose(acc[0] / l[0][:, None], scipy.special.softmax(z, axis=0).T @ v,
                                rtol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# copy-on-write block copies
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype,BS,D", [("f32", 8, 16), ("bf16", 16, 64), ("bf16", 32, 128)])
+def test_copy_blocks_matches_element_loop(dtype, BS, D):
+    rng = np.random.default_rng(40)
+    NB, Hkv = 12, 2
+    kc, vc = oracle.empty_pools(NB, Hkv, D, BS, dtype, fill="zero")
+    if dtype == "bf16":
+        kc[:] = rng.integers(0, 1 << 16, size=kc.shape, dtype=np.uint16)
+        vc[:] = rng.integers(0, 1 << 16, size=vc.shape, dtype=np.uint16)
+    else:
+        kc[:] = rng.standard_normal(kc.shape, dtype=np.float32)
+        vc[:] = rng.standard_normal(vc.shape, dtype=np.float32)
+    pairs = np.array([[3, 7], [3, 9], [0, 11], [5, 2]], dtype=np.int64)
+    k2, v2 = oracle.copy_blocks(kc, vc, pairs)
+    kf, vf = kc.reshape(NB, -1), vc.reshape(NB, -1)
+    k2f, v2f = k2.reshape(NB, -1), v2.reshape(NB, -1)
+    dsts = {int(d): int(s) for s, d in pairs}
+    for b in range(NB):
+        sb = dsts.get(b, b)
+        for i in range(kf.shape[1]):
+            assert kf[sb, i].tobytes() == k2f[b, i].tobytes()
+            assert vf[sb, i].tobytes() == v2f[b, i].tobytes()
+
+
+def test_copy_blocks_rejects_overlapping_pairs():
+    kc, vc = oracle.empty_pools(8, 1, 16, 8, "f32")
+    with pytest.raises(AssertionError):
+        oracle.copy_blocks(kc, vc, np.array([[1, 2], [3, 2]]))
+    with pytest.raises(AssertionError):
+        oracle.copy_blocks(kc, vc, np.array([[1, 2], [2, 4]]))
+
+
+def test_copy_blocks_reproduces_the_copy_on_write_records():
+    """Parallel sampling: the pools before the copies plus copy_blocks equal the pools
+    that hold the workload's per-token duplicate records (NaN where nothing is stored)."""
+    w = make_config(3, variant="parallel-sampling")
+    assert len(w.cow_pairs) > 0
+    keep_after = np.setdiff1d(np.arange(len(w.rec_slot)), w.new_records)
+    keep_before = np.setdiff1d(keep_after, w.cow_records)
+    kb, vb = oracle.empty_pools(w.num_blocks, w.num_kv_heads, w.head_dim, w.block_size, w.dtype)
+    oracle.reshape_and_cache(w.rec_key[keep_before], w.rec_value[keep_before],
+                             w.rec_slot[keep_before], kb, vb, inplace=True)
+    ka, va = oracle.empty_pools(w.num_blocks, w.num_kv_heads, w.head_dim, w.block_size, w.dtype)
+    oracle.reshape_and_cache(w.rec_key[keep_after], w.rec_value[keep_after],
+                             w.rec_slot[keep_after], ka, va, inplace=True)
+    kc, vc = oracle.copy_blocks(kb, vb, w.cow_pairs)
+    assert np.array_equal(kc, ka) and np.array_equal(vc, va)

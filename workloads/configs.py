@@ -88,6 +88,11 @@ class Workload:
     seq_records: list               # S arrays of int64, length L_s
     new_records: np.ndarray         # [T] int64, written by the decode step
     partition_size: int | None = None
+    # copy-on-write block copies, [n, 2] int64 (source block, destination block): the
+    # records that duplicate a source block's tokens into its copy are listed in
+    # cow_records (they exist before the step only once the blocks are copied)
+    cow_pairs: np.ndarray = field(default_factory=lambda: np.zeros((0, 2), dtype=np.int64))
+    cow_records: np.ndarray = field(default_factory=lambda: np.zeros(0, dtype=np.int64))
     blocks_allocated: int = 0
     info: dict = field(default_factory=dict)
 
@@ -192,6 +197,7 @@ def make_workload(*, name: str, context_lens, num_heads: int, num_kv_heads: int,
     # copy-on-write duplicate of an existing record.
     rec_slot: list = []
     rec_src: list = []
+    cow_pairs: list = []
     seqs: list = []
     seq_records: list = []
     new_records: list = []
@@ -213,6 +219,7 @@ def make_workload(*, name: str, context_lens, num_heads: int, num_kv_heads: int,
         for i, seq in enumerate(seqs):
             w = append_token(seq, pool, BS)
             if w.copy_from >= 0:
+                cow_pairs.append((w.copy_from, w.copy_to))
                 # duplicate the stored tokens of the shared block into the copy
                 stored = seq.num_tokens - 1 - (seq.num_tokens - 1) // BS * BS
                 logical = (seq.num_tokens - 1) // BS
@@ -298,6 +305,8 @@ def make_workload(*, name: str, context_lens, num_heads: int, num_kv_heads: int,
         partition_size=partition_size,
         blocks_allocated=int(np.count_nonzero(pool.refcount)),
         info={"seed": seed},
+        cow_pairs=np.asarray(cow_pairs, dtype=np.int64).reshape(-1, 2),
+        cow_records=np.nonzero(src >= 0)[0].astype(np.int64),
     )
 
 
