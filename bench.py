@@ -50,6 +50,9 @@ def parse_args():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--op", default="step", choices=["step", "copy_blocks"],
+                    help="step: the decode step (default); copy_blocks: the copy-on-write "
+                         "copies of the parallel-sampling workload")
     ap.add_argument("--config", type=int, default=1, choices=[0, 1, 2, 3, 4])
     ap.add_argument("--block-size", type=int, default=None, help="block size of config 2")
     ap.add_argument("--variant", default=None, help="config 3: prefix | parallel-sampling")
@@ -144,6 +147,79 @@ def cpu_baseline(w, budget_s: float) -> dict:
 
 
 # ---------------------------------------------------------------------------
+def bench_copy_blocks(args) -> int:
+    """Copy-on-write block copies of the parallel-sampling layout (32 prompts x 4 samples)."""
+    import torch
+
+    import paged_kv_cache_425_amd as pk
+    from workloads import make_config
+
+    dev = torch.device("cuda:0")
+    w = make_config(3, seed=args.seed, variant="parallel-sampling")
+    tdt = torch.bfloat16
+    pairs = w.cow_pairs
+    log(f"workload {w.name}: {len(pairs)} block copies, NB={w.num_blocks}")
+    up = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(tdt).to(dev)  # noqa: E731
+    keep = np.setdiff1d(np.setdiff1d(np.arange(len(w.rec_slot)), w.new_records), w.cow_records)
+    kshape = pk.k_cache_shape(w.num_blocks, w.num_kv_heads, w.head_dim, w.block_size, tdt)
+    vshape = pk.v_cache_shape(w.num_blocks, w.num_kv_heads, w.head_dim, w.block_size, tdt)
+    kc0 = torch.full(kshape, float("nan"), dtype=tdt, device=dev)
+    vc0 = torch.full(vshape, float("nan"), dtype=tdt, device=dev)
+    pk.reshape_and_cache(up(w.rec_key[keep]), up(w.rec_value[keep]),
+                         torch.from_numpy(w.rec_slot[keep]).to(dev), kc0, vc0)
+    # enough pool copies that a rotation spans well past the 256 MB Infinity Cache
+    pool_bytes = 2 * kc0.numel() * kc0.element_size()
+    R = max(args.replicas, int(np.ceil(1.2e9 / pool_bytes)))
+    pools = [(kc0, vc0)] + [(kc0.clone(), vc0.clone()) for _ in range(R - 1)]
+    pt = torch.from_numpy(pairs).to(dev)
+    calls = [pk.prepare_copy_blocks(kc, vc, pt) for kc, vc in pools]
+    elt = 2
+    moved = 2 * len(pairs) * 2 * w.num_kv_heads * w.head_dim * w.block_size * elt  # read + write
+    K, W = args.steps, args.warmup
+    for i in range(W):
+        calls[i % R]()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for i in range(K):
+        calls[i % R]()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ev = e0.elapsed_time(e1) * 1e-3
+    value = moved / (wall / K) / 1e9
+    achieved = moved / (ev / K) / 1e9
+    log(f"copy_blocks: {wall / K * 1e6:.2f} us/call wall, {ev / K * 1e6:.2f} us/call events")
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        kh = kc0.view(torch.int16).cpu().numpy().view(np.uint16)
+        vh = vc0.view(torch.int16).cpu().numpy().view(np.uint16)
+        n, t1 = 0, time.perf_counter()
+        while time.perf_counter() - t1 < min(args.cpu_budget, 5.0):
+            oracle.copy_blocks(kh, vh, pairs, inplace=True)
+            n += 1
+        dt = time.perf_counter() - t1
+        cpu = {"value": round(n * moved / dt / 1e9, 4), "unit": "GB/s", "cores": 1,
+               "kind": "oracle",
+               "sample": f"NumPy oracle copy_blocks of the same {len(pairs)} pairs, {n} calls "
+                         f"in {dt:.1f} s (one thread)"}
+    print(json.dumps({
+        "metric": "copy-on-write copy_blocks GB/s moved (read + write), 1 GPU",
+        "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": W,
+        "ms_per_step": round(wall / K * 1e3, 6), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name, "pairs": int(len(pairs)), "bytes_moved_per_call": moved,
+                   "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
+                   "block_size": w.block_size, "pool_replicas": R},
+        "roofline": {"kernel": "copy_blocks_kernel", "bound": "hbm", "achieved": round(achieved, 2),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": None, "algorithmic_bytes_per_launch": moved},
+        "cpu_baseline": cpu}), flush=True)
+    return 0
+
+
 def main() -> int:
     args = parse_args()
     if args.gpus != 1:
@@ -159,6 +235,8 @@ def main() -> int:
         print("bench.py needs a GPU (no HIP device visible)", file=sys.stderr)
         return 1
     pk.load_library()          # raises if the HIP library was not built
+    if args.op == "copy_blocks":
+        return bench_copy_blocks(args)
     dev = torch.device("cuda:0")
 
     t = time.perf_counter()

@@ -185,6 +185,24 @@ pa_status pa_decode_step(void* out, const void* query, const void* key, const vo
                          void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Copy-on-write: make physical block dst a copy of physical block src (every
+ * kv head, K and V), for each pair of block_mapping.  A sequence that appends
+ * into a block it shares with others (parallel samples, beams, a common prompt:
+ * page "vLLM core features", section 4.1; page "vLLM core architecture",
+ * section 2.2.1) first gets a private copy of it.
+ *
+ *   block_mapping  [num_pairs][2] int64: (src, dst).  Destinations must be
+ *                  distinct and none may be a source of the same call (the
+ *                  copies run in parallel).  A pair with a block outside
+ *                  [0, num_blocks) is skipped.
+ *   k_cache, v_cache  pools in the layouts above (written in place)
+ * The copy is bit-exact; blocks that are not destinations do not change.
+ */
+pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_mapping,
+                         int num_pairs, int num_kv_heads, int head_dim, int block_size,
+                         int num_blocks, pa_dtype dtype, void* stream);
+
+/*
  * Diagnostic read path: reassemble every sequence's K and V through its block
  * table into contiguous token-major arrays (bit-exact copies).
  *

@@ -3,12 +3,14 @@
 The work runs in hand-written HIP kernels behind a C ABI (include/pagedattn.h);
 this package only marshals torch tensors to it.
 """
-from .binding import (LIB_PATH, PreparedCall, chunk_elems, decode_step, default_partition_size,
+from .binding import (LIB_PATH, PreparedCall, chunk_elems, copy_blocks, decode_step,
+                      default_partition_size, prepare_copy_blocks,
                       gather_kv, k_cache_shape, load_library, paged_attention,
                       prepare_decode_step, prepare_paged_attention, prepare_reshape_and_cache,
                       reshape_and_cache, v_cache_shape, workspace_size)
 
-__all__ = ["LIB_PATH", "PreparedCall", "decode_step", "prepare_decode_step",
+__all__ = ["LIB_PATH", "PreparedCall", "copy_blocks", "prepare_copy_blocks", "decode_step",
+           "prepare_decode_step",
            "prepare_paged_attention", "prepare_reshape_and_cache",
            "chunk_elems", "default_partition_size", "gather_kv", "k_cache_shape",
            "load_library", "paged_attention", "reshape_and_cache", "v_cache_shape",

@@ -45,6 +45,8 @@ def load_library() -> ctypes.CDLL:
     lib.pa_reshape_and_cache.argtypes = [vp] * 5 + [i32] * 6 + [vp]
     lib.pa_decode_step.restype = i32
     lib.pa_decode_step.argtypes = [vp] * 9 + [i32] * 8 + [f32, i32, i32, vp, sz, vp]
+    lib.pa_copy_blocks.restype = i32
+    lib.pa_copy_blocks.argtypes = [vp] * 3 + [i32] * 6 + [vp]
     lib.pa_gather_kv.restype = i32
     lib.pa_gather_kv.argtypes = [vp] * 7 + [i32] * 8 + [vp]
     _lib = lib
@@ -234,6 +236,35 @@ def reshape_and_cache(key: torch.Tensor, value: torch.Tensor, slot_mapping: torc
                                   _ptr(v_cache), T, Hkv, D, BS, NB, _dtype_code(key),
                                   _stream(dev, stream))
     _check(st, "pa_reshape_and_cache")
+
+
+def copy_blocks(k_cache: torch.Tensor, v_cache: torch.Tensor, block_mapping: torch.Tensor,
+                stream=None) -> None:
+    """Copy physical block src to dst for every (src, dst) row of block_mapping [n, 2]
+    (int64), in place (see pa_copy_blocks)."""
+    lib = load_library()
+    dev = k_cache.device
+    NB, Hkv, D, BS = _cache_dims(k_cache, v_cache)
+    _require(k_cache, "k_cache", dev)
+    _require(v_cache, "v_cache", dev, k_cache.dtype)
+    _require(block_mapping, "block_mapping", dev, torch.int64)
+    if block_mapping.dim() != 2 or block_mapping.shape[1] != 2:
+        raise ValueError("block_mapping must be [n, 2] (src, dst)")
+    st = lib.pa_copy_blocks(_ptr(k_cache), _ptr(v_cache), _ptr(block_mapping),
+                            block_mapping.shape[0], Hkv, D, BS, NB, _dtype_code(k_cache),
+                            _stream(dev, stream))
+    _check(st, "pa_copy_blocks")
+
+
+def prepare_copy_blocks(k_cache, v_cache, block_mapping, stream=None) -> PreparedCall:
+    """Check the arguments of copy_blocks once and return a re-launchable call."""
+    lib = load_library()
+    copy_blocks(k_cache, v_cache, block_mapping, stream=stream)
+    NB, Hkv, D, BS = _cache_dims(k_cache, v_cache)
+    args = (_ptr(k_cache), _ptr(v_cache), _ptr(block_mapping), block_mapping.shape[0], Hkv, D,
+            BS, NB, _dtype_code(k_cache), _stream(k_cache.device, stream))
+    return PreparedCall(lib.pa_copy_blocks, args, "pa_copy_blocks",
+                        (k_cache, v_cache, block_mapping))
 
 
 def gather_kv(block_table: torch.Tensor, context_lens: torch.Tensor, k_cache: torch.Tensor,

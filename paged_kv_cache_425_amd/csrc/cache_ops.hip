@@ -1,4 +1,4 @@
-// Write path and diagnostic read path of the paged KV cache (gfx950).
+// Write path, copy-on-write and diagnostic read path of the paged KV cache (gfx950).
 //
 // reshape_and_cache: a new token only adds one entry to its sequence's
 // mapping (page "vLLM core features", section 4.1); here its K and V are
@@ -88,6 +88,30 @@ gather_kv_kernel(T* __restrict__ k_out, T* __restrict__ v_out,
   }
 }
 
+// Copy-on-write: block dst becomes a copy of block src.  One workgroup per
+// (pair, kv head, K or V): a (block, kv head) tile of D * BS elements is
+// contiguous in both pools, so the copy is a run of 16-byte chunks.  Pairs
+// naming a block outside the pool are skipped.
+template <typename T>
+__global__ void __launch_bounds__(kCopyThreads)
+copy_blocks_kernel(T* __restrict__ k_cache, T* __restrict__ v_cache,
+                   const int64_t* __restrict__ pairs, int Hkv, int D, int BS, int NB) {
+  constexpr int X = ElemTraits<T>::kX;
+  const int id = blockIdx.x;
+  const int is_v = id & 1;
+  const int h = (id >> 1) % Hkv;
+  const int pr = (id >> 1) / Hkv;
+  const int64_t src = pairs[2 * (size_t)pr], dst = pairs[2 * (size_t)pr + 1];
+  if (src < 0 || src >= NB || dst < 0 || dst >= NB) return;
+  T* pool = is_v ? v_cache : k_cache;
+  const size_t tile = (size_t)D * BS;
+  const T* from = pool + ((size_t)src * Hkv + h) * tile;
+  T* to = pool + ((size_t)dst * Hkv + h) * tile;
+  const int chunks = (int)(tile / X);
+  for (int c = threadIdx.x; c < chunks; c += kCopyThreads)
+    store16(to + (size_t)c * X, load16(from + (size_t)c * X));
+}
+
 }  // namespace pa
 
 namespace {
@@ -168,6 +192,32 @@ extern "C" pa_status pa_gather_kv(void* k_out, void* v_out, const int64_t* seq_o
                        block_table, context_lens, static_cast<const float*>(k_cache),
                        static_cast<const float*>(v_cache), num_kv_heads, head_dim, block_size,
                        max_blocks_per_seq, num_blocks, bps);
+  }
+  return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+extern "C" pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_mapping,
+                                    int num_pairs, int num_kv_heads, int head_dim, int block_size,
+                                    int num_blocks, pa_dtype dtype, void* stream) {
+  pa_status st = check_cache_shapes(num_kv_heads, head_dim, block_size, num_blocks, dtype);
+  if (st != PA_OK) return st;
+  if (num_pairs < 0) return PA_ERR_INVALID_ARG;
+  if (num_pairs == 0) return PA_OK;
+  if (!k_cache || !v_cache || !block_mapping) return PA_ERR_INVALID_ARG;
+  if (!aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(block_mapping, 8))
+    return PA_ERR_INVALID_ARG;
+  const long grid = (long)num_pairs * num_kv_heads * 2;
+  if (grid > 0x7FFFFFFFL) return PA_ERR_INVALID_ARG;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (dtype == PA_DTYPE_BF16) {
+    hipLaunchKernelGGL(pa::copy_blocks_kernel<uint16_t>, dim3((unsigned)grid),
+                       dim3(pa::kCopyThreads), 0, s, static_cast<uint16_t*>(k_cache),
+                       static_cast<uint16_t*>(v_cache), block_mapping, num_kv_heads, head_dim,
+                       block_size, num_blocks);
+  } else {
+    hipLaunchKernelGGL(pa::copy_blocks_kernel<float>, dim3((unsigned)grid), dim3(pa::kCopyThreads),
+                       0, s, static_cast<float*>(k_cache), static_cast<float*>(v_cache),
+                       block_mapping, num_kv_heads, head_dim, block_size, num_blocks);
   }
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
 }

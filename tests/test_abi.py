@@ -32,7 +32,7 @@ def test_header_declares_the_boundary():
     assert declared_functions() == sorted([
         "pa_abi_version", "pa_status_string", "pa_default_partition_size",
         "pa_paged_attention_workspace_size", "pa_paged_attention", "pa_reshape_and_cache",
-        "pa_gather_kv", "pa_decode_step"])
+        "pa_gather_kv", "pa_decode_step", "pa_copy_blocks"])
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -141,6 +141,15 @@ def test_reshape_and_cache_rejects_before_launch(lib):
     assert f(FAKE, FAKE, FAKE + 4, FAKE, FAKE, 4, 8, 128, 16, 64, 1, None) == 1
     assert f(FAKE, FAKE, FAKE, FAKE, FAKE, -1, 8, 128, 16, 64, 1, None) == 1
     assert f(None, None, None, None, None, 0, 8, 128, 16, 64, 1, None) == 0
+
+
+def test_copy_blocks_rejects_before_launch(lib):
+    f = lib.pa_copy_blocks
+    assert f(None, FAKE, FAKE, 4, 8, 128, 16, 64, 1, None) == 1
+    assert f(FAKE, FAKE, FAKE + 4, 4, 8, 128, 16, 64, 1, None) == 1
+    assert f(FAKE, FAKE, FAKE, -1, 8, 128, 16, 64, 1, None) == 1
+    assert f(FAKE, FAKE, FAKE, 4, 8, 96, 16, 64, 1, None) == 2
+    assert f(None, None, None, 0, 8, 128, 16, 64, 1, None) == 0
 
 
 def test_gather_rejects_before_launch(lib):

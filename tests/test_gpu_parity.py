@@ -360,3 +360,58 @@ def test_binding_rejects_bad_inputs():
     with pytest.raises(ValueError):
         pk.paged_attention(inp["query"], inp["block_table"], inp["context_lens"], kd, vd, 0.1,
                            max_context_len=64, partition_size=100)
+
+
+# ---------------------------------------------------------------------------
+# copy-on-write block copies
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype,BS,D", [("f32", 8, 64), ("f32", 32, 128), ("bf16", 16, 128),
+                                        ("bf16", 8, 64), ("bf16", 32, 128)])
+def test_copy_blocks_bit_exact(dtype, BS, D):
+    rng = np.random.default_rng(50 + BS + D)
+    NB, Hkv = 40, 4
+    kc, vc = oracle.empty_pools(NB, Hkv, D, BS, dtype, fill="zero")
+    if dtype == "bf16":
+        kc[:] = rng.integers(0, 1 << 16, size=kc.shape, dtype=np.uint16)
+        vc[:] = rng.integers(0, 1 << 16, size=vc.shape, dtype=np.uint16)
+    else:
+        kc[:] = rng.standard_normal(kc.shape, dtype=np.float32)
+        vc[:] = rng.standard_normal(vc.shape, dtype=np.float32)
+    perm = rng.permutation(NB)
+    valid = np.stack([perm[:10], perm[10:20]], axis=1).astype(np.int64)
+    bad = np.array([[-1, perm[30]], [perm[31], NB], [NB + 5, perm[32]]], dtype=np.int64)
+    pairs = np.concatenate([valid, bad])
+    ref_k, ref_v = oracle.copy_blocks(kc, vc, valid)
+    say(f"copy_blocks {dtype} BS={BS} D={D} pairs={len(pairs)}")
+    kd, vd = to_dev(kc, dtype, DEV), to_dev(vc, dtype, DEV)
+    pk.copy_blocks(kd, vd, torch.from_numpy(pairs).to(DEV))
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(kd), ref_k.view(bits(kd).dtype))
+    assert np.array_equal(bits(vd), ref_v.view(bits(vd).dtype))
+
+
+def test_copy_on_write_step_parallel_sampling():
+    """Prompts shared by 4 samples: copy the shared partial last blocks, then run the
+    fused decode step; caches bit-exact and output within tolerance of the oracle."""
+    w = make_config(3, variant="parallel-sampling")
+    keep_after = np.setdiff1d(np.arange(len(w.rec_slot)), w.new_records)
+    keep_before = np.setdiff1d(keep_after, w.cow_records)
+    kb, vb = oracle.empty_pools(w.num_blocks, w.num_kv_heads, w.head_dim, w.block_size, w.dtype)
+    oracle.reshape_and_cache(w.rec_key[keep_before], w.rec_value[keep_before],
+                             w.rec_slot[keep_before], kb, vb, inplace=True)
+    ref_k, ref_v = oracle.copy_blocks(kb, vb, w.cow_pairs)
+    new, slots = fused_inputs(w)
+    ref_k, ref_v = oracle.reshape_and_cache(w.rec_key[new], w.rec_value[new], slots, ref_k, ref_v)
+    ref = oracle_out(w, ref_k, ref_v)
+    say(f"copy-on-write step: {len(w.cow_pairs)} copies, {w.num_seqs} sequences")
+    kd, vd = to_dev(kb, w.dtype, DEV), to_dev(vb, w.dtype, DEV)
+    pk.copy_blocks(kd, vd, torch.from_numpy(w.cow_pairs).to(DEV))
+    inp = upload_inputs(w, DEV)
+    out = pk.decode_step(inp["query"], to_dev(w.rec_key[new], w.dtype, DEV),
+                         to_dev(w.rec_value[new], w.dtype, DEV), torch.from_numpy(slots).to(DEV),
+                         inp["block_table"], inp["context_lens"], kd, vd, w.scale,
+                         max_context_len=w.max_context_len)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(kd), ref_k.view(np.uint16))
+    assert np.array_equal(bits(vd), ref_v.view(np.uint16))
+    check_close(to_f64(out), ref, "bf16", "cow-step")
