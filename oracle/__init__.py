@@ -7,10 +7,10 @@ it.  Every function is pinned by a check in the test suite; none is marked
 """
 from .paged_attention import (ELEMENT_BYTES, attention_one, chunk_elems, combine_partitions,
                               copy_blocks, decode, empty_pools, gather_kv, gather_sequence,
-                              k_cache_shape, paged_attention, partition_stats,
+                              k_cache_shape, paged_attention, paged_prefill, partition_stats,
                               reshape_and_cache, v_cache_shape)
 
 __all__ = ["ELEMENT_BYTES", "attention_one", "chunk_elems", "combine_partitions", "copy_blocks",
            "decode",
            "empty_pools", "gather_kv", "gather_sequence", "k_cache_shape",
-           "paged_attention", "partition_stats", "reshape_and_cache", "v_cache_shape"]
+           "paged_attention", "paged_prefill", "partition_stats", "reshape_and_cache", "v_cache_shape"]

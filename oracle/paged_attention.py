@@ -197,6 +197,44 @@ def paged_attention(query: np.ndarray, block_table: np.ndarray, context_lens: np
     return out
 
 
+def paged_prefill(query: np.ndarray, query_start_loc: np.ndarray, block_table: np.ndarray,
+                  context_lens: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray,
+                  scale: float, dtype: str, seqs=None) -> np.ndarray:
+    """Causal attention of a chunk of new query tokens per sequence over its paged K/V.
+
+    Sequence s owns query rows query_start_loc[s] .. query_start_loc[s+1] - 1; with
+    n = that count and L = context_lens[s] (the chunk included), row i is the
+    token at position p = L - n + i and attends to positions 0 .. p.  The chunk's
+    own K/V are already in the pool.  This is what a request's prompt needs when
+    an earlier part of its context is cached in blocks (a shared system prompt,
+    "core inference engine" page, section 2.2; prefix caching, "core features"
+    page, sections 4.2 and 4.6): only the new tokens are computed, attending to
+    the cached prefix through the block table ("core architecture" page,
+    section 2.2.2).  One new token (n = 1) is the decode step.
+
+    query: [T, Hq, D]; returns [T, Hq, D] float64.
+    """
+    T, Hq, D = query.shape
+    Hkv = k_cache.shape[1]
+    g = Hq // Hkv
+    qsl = np.asarray(query_start_loc, dtype=np.int64)
+    out = np.zeros((T, Hq, D), dtype=np.float64)
+    for s in (range(len(qsl) - 1) if seqs is None else seqs):
+        r0, r1 = int(qsl[s]), int(qsl[s + 1])
+        L = int(context_lens[s])
+        n = r1 - r0
+        assert 0 <= n <= L, "a chunk cannot be longer than its context"
+        k, v = gather_sequence(block_table[s], L, k_cache, v_cache)
+        kf, vf, qf = decode(k, dtype), decode(v, dtype), decode(query[r0:r1], dtype)
+        for i in range(n):
+            p = L - n + i
+            for kvh in range(Hkv):
+                heads = slice(kvh * g, (kvh + 1) * g)
+                out[r0 + i, heads] = attention_one(qf[i, heads], kf[:p + 1, kvh],
+                                                   vf[:p + 1, kvh], scale)
+    return out
+
+
 # ---------------------------------------------------------------------------
 # split context: per-partition statistics and their log-sum-exp combination
 # ---------------------------------------------------------------------------

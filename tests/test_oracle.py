@@ -437,3 +437,92 @@ def test_copy_blocks_reproduces_the_copy_on_write_records():
                              w.rec_slot[keep_after], ka, va, inplace=True)
     kc, vc = oracle.copy_blocks(kb, vb, w.cow_pairs)
     assert np.array_equal(kc, ka) and np.array_equal(vc, va)
+
+
+# ---------------------------------------------------------------------------
+# paged prefill (causal chunks over the paged context)
+# ---------------------------------------------------------------------------
+from workloads import make_prefill  # noqa: E402
+
+
+def test_prefill_of_one_token_is_the_decode():
+    w = tiny("bf16", lens=(1, 9, 30, 64), Hq=8, Hkv=2, D=32, BS=8, seed=60)
+    pb = make_prefill(w, [1, 1, 1, 1], 60)
+    kc, vc = build_pools(w)
+    a = oracle.paged_prefill(pb.query, pb.query_start_loc, w.block_table, w.context_lens, kc, vc,
+                             w.scale, w.dtype)
+    b = oracle.paged_attention(pb.query, w.block_table, w.context_lens, kc, vc, w.scale, w.dtype)
+    assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_prefill_matches_causal_bruteforce(dtype):
+    w = tiny(dtype, lens=(3, 17, 26), Hq=4, Hkv=2, D=16, BS=8, seed=61)
+    pb = make_prefill(w, [3, 5, 9], 61)
+    kc, vc = build_pools(w)
+    got = oracle.paged_prefill(pb.query, pb.query_start_loc, w.block_table, w.context_lens, kc, vc,
+                               w.scale, dtype)
+    g = w.num_heads // w.num_kv_heads
+    for s in range(w.num_seqs):
+        r0, r1 = pb.query_start_loc[s], pb.query_start_loc[s + 1]
+        L = int(w.context_lens[s])
+        for i in range(r1 - r0):
+            p = L - (r1 - r0) + i
+            recs = w.seq_records[s][:p + 1]
+            for h in range(w.num_heads):
+                K = torch_decode(w.rec_key[recs][:, h // g], dtype)
+                V = torch_decode(w.rec_value[recs][:, h // g], dtype)
+                q = torch_decode(pb.query[r0 + i, h], dtype)
+                z = [w.scale * math.fsum(float(q[d]) * float(K[t, d]) for d in range(K.shape[1]))
+                     for t in range(p + 1)]
+                m = max(z)
+                e = [math.exp(zt - m) for zt in z]
+                den = math.fsum(e)
+                ref = [math.fsum(e[t] * float(V[t, d]) for t in range(p + 1)) / den
+                       for d in range(K.shape[1])]
+                np.testing.assert_allclose(got[r0 + i, h], ref, rtol=1e-12, atol=1e-13)
+
+
+def test_prefill_chunk_split_in_two_calls_is_identical():
+    """A chunk of n tokens equals its first half (context shortened to end there) followed
+    by its second half: each token only sees positions up to its own."""
+    w = tiny("bf16", lens=(40, 64, 25), Hq=8, Hkv=2, D=32, BS=16, seed=62)
+    n = np.array([12, 20, 8])
+    pb = make_prefill(w, n, 62)
+    kc, vc = build_pools(w)
+    whole = oracle.paged_prefill(pb.query, pb.query_start_loc, w.block_table, w.context_lens,
+                                 kc, vc, w.scale, w.dtype)
+    half = n // 2
+    rows_a = np.concatenate([np.arange(pb.query_start_loc[s], pb.query_start_loc[s] + half[s])
+                             for s in range(3)])
+    rows_b = np.concatenate([np.arange(pb.query_start_loc[s] + half[s], pb.query_start_loc[s + 1])
+                             for s in range(3)])
+    qa = np.concatenate([[0], np.cumsum(half)]).astype(np.int32)
+    qb = np.concatenate([[0], np.cumsum(n - half)]).astype(np.int32)
+    part_a = oracle.paged_prefill(pb.query[rows_a], qa, w.block_table, w.context_lens - (n - half),
+                                  kc, vc, w.scale, w.dtype)
+    part_b = oracle.paged_prefill(pb.query[rows_b], qb, w.block_table, w.context_lens, kc, vc,
+                                  w.scale, w.dtype)
+    assert np.array_equal(whole[rows_a], part_a) and np.array_equal(whole[rows_b], part_b)
+
+
+def test_prefill_is_block_permutation_invariant():
+    w = tiny("bf16", lens=(33, 50), Hq=4, Hkv=4, D=16, BS=8, seed=63)
+    pb = make_prefill(w, [10, 30], 63)
+    kc, vc = build_pools(w)
+    a = oracle.paged_prefill(pb.query, pb.query_start_loc, w.block_table, w.context_lens, kc, vc,
+                             w.scale, w.dtype)
+    perm = np.random.default_rng(3).permutation(w.num_blocks)
+    kc2, vc2 = np.empty_like(kc), np.empty_like(vc)
+    kc2[perm], vc2[perm] = kc, vc
+    b = oracle.paged_prefill(pb.query, pb.query_start_loc, perm[w.block_table], w.context_lens,
+                             kc2, vc2, w.scale, w.dtype)
+    assert np.array_equal(a, b)
+
+
+def test_prefill_chunks_are_the_last_positions():
+    w = tiny("bf16", lens=(5, 9, 1), Hq=4, Hkv=2, D=16, BS=8, seed=64)
+    pb = make_prefill(w, [2, 9, 3], 64)
+    assert list(pb.query_start_loc) == [0, 2, 11, 12]        # the last chunk is clipped to L
+    assert list(pb.chunk_records[:2]) == list(w.seq_records[0][3:5])
+    assert list(pb.chunk_records[2:11]) == list(w.seq_records[1])

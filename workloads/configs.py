@@ -367,3 +367,57 @@ def make_config(index: int, *, seed: int | None = None, block_size: int | None =
                              seed=seed, rng=rng, max_blocks_per_seq=32768 // 32,
                              partition_size=512)
     raise ValueError(f"no config {index}")
+
+
+# ---------------------------------------------------------------------------
+# prefill chunks: the last n tokens of each sequence are new query tokens
+# ---------------------------------------------------------------------------
+@dataclass
+class PrefillBatch:
+    """New query tokens of a workload's sequences (their K/V records are in the workload).
+
+    Sequence s owns rows query_start_loc[s] .. query_start_loc[s+1] - 1 of ``query``; they
+    are its last n_s context positions, whose K/V records are ``chunk_records`` (in row
+    order).  Every other record is history already in the pool.
+    """
+    query: np.ndarray               # [T, Hq, D]
+    query_start_loc: np.ndarray     # [S + 1] int32
+    chunk_records: np.ndarray       # [T] int64
+    max_query_len: int
+
+    def history_records(self, w: Workload) -> np.ndarray:
+        mask = np.ones(len(w.rec_slot), dtype=bool)
+        mask[self.chunk_records] = False
+        return np.nonzero(mask)[0]
+
+
+def make_prefill(w: Workload, chunk_lens, seed: int) -> PrefillBatch:
+    """Chunks of chunk_lens[s] new tokens at the end of each sequence of ``w``."""
+    n = np.minimum(np.asarray(chunk_lens, dtype=np.int64), w.context_lens.astype(np.int64))
+    qsl = np.zeros(w.num_seqs + 1, dtype=np.int32)
+    qsl[1:] = np.cumsum(n)
+    recs = np.concatenate([w.seq_records[s][len(w.seq_records[s]) - n[s]:]
+                           for s in range(w.num_seqs)]) if w.num_seqs else np.zeros(0, np.int64)
+    rng = np.random.default_rng([seed, 7919])
+    query = _draw(rng, (int(qsl[-1]), w.num_heads, w.head_dim), w.dtype)
+    return PrefillBatch(query=query, query_start_loc=qsl, chunk_records=recs.astype(np.int64),
+                        max_query_len=int(n.max()) if len(n) else 0)
+
+
+PREFILL_NAMES = {
+    "prefix-cache-prefill": "the prefix-sharing batch; each sequence's private suffix "
+                            "(32..512 tokens) is prefilled over the cached 1024-token prefix",
+    "chunked-prefill-llama3-8b": "the Llama-3-8B-shaped batch; the last min(L, 512) tokens of "
+                                 "each sequence are one prefill chunk",
+}
+
+
+def make_prefill_config(name: str, seed: int | None = None):
+    """(workload, prefill batch) of a named prefill case."""
+    if name == "prefix-cache-prefill":
+        w = make_config(3, seed=seed)
+        return w, make_prefill(w, w.context_lens.astype(np.int64) - 1024, w.info["seed"])
+    if name == "chunked-prefill-llama3-8b":
+        w = make_config(1, seed=seed)
+        return w, make_prefill(w, np.minimum(w.context_lens, 512), w.info["seed"])
+    raise ValueError(f"no prefill case {name!r}")
