@@ -50,9 +50,11 @@ def parse_args():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--op", default="step", choices=["step", "copy_blocks"],
+    ap.add_argument("--op", default="step", choices=["step", "copy_blocks", "prefill"],
                     help="step: the decode step (default); copy_blocks: the copy-on-write "
-                         "copies of the parallel-sampling workload")
+                         "copies of the parallel-sampling workload; prefill: paged prefill")
+    ap.add_argument("--prefill-case", default="prefix-cache-prefill",
+                    choices=["prefix-cache-prefill", "chunked-prefill-llama3-8b"])
     ap.add_argument("--config", type=int, default=1, choices=[0, 1, 2, 3, 4])
     ap.add_argument("--block-size", type=int, default=None, help="block size of config 2")
     ap.add_argument("--variant", default=None, help="config 3: prefix | parallel-sampling")
@@ -220,6 +222,95 @@ def bench_copy_blocks(args) -> int:
     return 0
 
 
+def bench_prefill(args) -> int:
+    """Paged prefill of a named batch (default: prefix-cache prefill of the prefix-sharing
+    batch's private suffixes over the cached 1024-token prefix)."""
+    import torch
+
+    import paged_kv_cache_425_amd as pk
+    from workloads import make_prefill_config
+
+    dev = torch.device("cuda:0")
+    w, pb = make_prefill_config(args.prefill_case, seed=args.seed)
+    tdt = torch.bfloat16
+    up = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(tdt).to(dev)  # noqa: E731
+    kshape = pk.k_cache_shape(w.num_blocks, w.num_kv_heads, w.head_dim, w.block_size, tdt)
+    vshape = pk.v_cache_shape(w.num_blocks, w.num_kv_heads, w.head_dim, w.block_size, tdt)
+    kc = torch.full(kshape, float("nan"), dtype=tdt, device=dev)
+    vc = torch.full(vshape, float("nan"), dtype=tdt, device=dev)
+    pk.reshape_and_cache(up(w.rec_key), up(w.rec_value), torch.from_numpy(w.rec_slot).to(dev),
+                         kc, vc)
+    query = up(pb.query)
+    qsl = torch.from_numpy(pb.query_start_loc).to(dev)
+    table = torch.from_numpy(w.block_table).to(dev)
+    lens = torch.from_numpy(w.context_lens).to(dev)
+    out = torch.empty_like(query)
+    torch.cuda.synchronize()
+    n = np.diff(pb.query_start_loc).astype(np.int64)
+    L = w.context_lens.astype(np.int64)
+    keys = int(sum(int(((L[s] - n[s] + 1) + L[s]) * n[s] // 2) for s in range(w.num_seqs)))
+    flops = 4 * w.num_heads * w.head_dim * keys              # Q.K^T and P.V, 2 flops per MAC
+    bytes_q = 2 * query.numel() * 2                          # query read, output written
+    log(f"prefill {args.prefill_case}: S={w.num_seqs} T={query.shape[0]} "
+        f"attention pairs={keys * w.num_heads / 1e6:.0f} M, {flops / 1e12:.3f} TFLOP")
+
+    def call():
+        pk.paged_prefill(query, qsl, table, lens, kc, vc, w.scale,
+                         max_query_len=pb.max_query_len, out=out)
+
+    K, W = max(1, args.steps // 10), max(1, args.warmup // 10)
+    for _ in range(W):
+        call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(K):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ev = e0.elapsed_time(e1) * 1e-3
+    tflops = flops / (ev / K) / 1e12
+    log(f"prefill: {wall / K * 1e6:.1f} us/call wall, {ev / K * 1e6:.1f} us/call events, "
+        f"{tflops:.1f} TFLOP/s")
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        kh = kc.view(torch.int16).cpu().numpy().view(np.uint16)
+        vh = vc.view(torch.int16).cpu().numpy().view(np.uint16)
+        done, kdone, t1 = 0, 0, time.perf_counter()
+        for s in range(w.num_seqs):
+            oracle.paged_prefill(pb.query, pb.query_start_loc, w.block_table, w.context_lens,
+                                 kh, vh, w.scale, w.dtype, seqs=[s])
+            done += 1
+            kdone += int(((L[s] - n[s] + 1) + L[s]) * n[s] // 2)
+            if time.perf_counter() - t1 >= args.cpu_budget:
+                break
+        dt = time.perf_counter() - t1
+        cpu = {"value": round(4 * w.num_heads * w.head_dim * kdone / dt / 1e12, 6),
+               "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
+               "sample": f"float64 NumPy oracle prefill of the first {done} of {w.num_seqs} "
+                         f"sequences in {dt:.1f} s"}
+    print(json.dumps({
+        "metric": "paged prefill TFLOP/s (causal, bf16), 1 GPU",
+        "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": K, "warmup": W,
+        "ms_per_step": round(wall / K * 1e3, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": args.prefill_case, "num_seqs": w.num_seqs,
+                   "query_tokens": int(query.shape[0]), "max_chunk": pb.max_query_len,
+                   "num_heads": w.num_heads, "num_kv_heads": w.num_kv_heads,
+                   "head_dim": w.head_dim, "block_size": w.block_size,
+                   "attention_pairs": keys * w.num_heads},
+        "roofline": {"kernel": "paged_prefill_kernel", "bound": "mfma",
+                     "achieved": round(tflops, 2), "peak": 2500.0, "unit": "TFLOP/s",
+                     "frac": round(tflops / 2500.0, 4), "traffic": None,
+                     "algorithmic_flops_per_launch": flops,
+                     "query_and_output_bytes": bytes_q},
+        "cpu_baseline": cpu}), flush=True)
+    return 0
+
+
 def main() -> int:
     args = parse_args()
     if args.gpus != 1:
@@ -237,6 +328,8 @@ def main() -> int:
     pk.load_library()          # raises if the HIP library was not built
     if args.op == "copy_blocks":
         return bench_copy_blocks(args)
+    if args.op == "prefill":
+        return bench_prefill(args)
     dev = torch.device("cuda:0")
 
     t = time.perf_counter()

@@ -185,6 +185,36 @@ pa_status pa_decode_step(void* out, const void* query, const void* key, const vo
                          void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Paged prefill: causal attention of a chunk of new query tokens per sequence
+ * over the sequence's paged K/V (the chunk's own K/V already stored, e.g. by
+ * pa_reshape_and_cache).  A request's earlier context -- a system prompt kept
+ * in shared blocks, a cached prefix (page "vLLM core inference engine",
+ * section 2.2; page "vLLM core features", sections 4.2 and 4.6) -- is read
+ * through the block table and only the new tokens are computed.
+ *
+ * Sequence s owns query rows query_start_loc[s] .. query_start_loc[s+1] - 1
+ * (n tokens, n <= L = context_lens[s]); row i is the token at position
+ * p = L - n + i and
+ *   out[row][h] = sum_{t <= p} softmax_t(scale * query[row][h] . K_s[t][kvh]) V_s[t][kvh]
+ * with kvh = h / g.  n = 1 gives the decode result.
+ *
+ *   out, query       [num_query_tokens][num_heads][head_dim], contiguous
+ *   query_start_loc  [num_seqs + 1] int32, non-decreasing, query_start_loc[0] = 0,
+ *                    query_start_loc[num_seqs] = num_query_tokens
+ *   max_query_len    host-side upper bound of the chunk lengths (sizes the grid)
+ *   other arguments as in pa_paged_attention; group size g = num_heads /
+ *   num_kv_heads must divide 128 (1, 2, 4, 8, 16)
+ * Values outside these ranges are clamped on the device (rows that fall outside
+ * [0, num_query_tokens) are not written).
+ */
+pa_status pa_paged_prefill(void* out, const void* query, const int32_t* query_start_loc,
+                           const int32_t* block_table, const int32_t* context_lens,
+                           const void* k_cache, const void* v_cache, int num_seqs, int num_heads,
+                           int num_kv_heads, int head_dim, int block_size, int max_blocks_per_seq,
+                           int num_blocks, int num_query_tokens, int max_query_len, float scale,
+                           pa_dtype dtype, void* stream);
+
+/*
  * Copy-on-write: make physical block dst a copy of physical block src (every
  * kv head, K and V), for each pair of block_mapping.  A sequence that appends
  * into a block it shares with others (parallel samples, beams, a common prompt:

@@ -5,7 +5,7 @@ this package only marshals torch tensors to it.
 """
 from .binding import (LIB_PATH, PreparedCall, chunk_elems, copy_blocks, decode_step,
                       default_partition_size, prepare_copy_blocks,
-                      gather_kv, k_cache_shape, load_library, paged_attention,
+                      gather_kv, k_cache_shape, load_library, paged_attention, paged_prefill,
                       prepare_decode_step, prepare_paged_attention, prepare_reshape_and_cache,
                       reshape_and_cache, v_cache_shape, workspace_size)
 
@@ -13,5 +13,5 @@ __all__ = ["LIB_PATH", "PreparedCall", "copy_blocks", "prepare_copy_blocks", "de
            "prepare_decode_step",
            "prepare_paged_attention", "prepare_reshape_and_cache",
            "chunk_elems", "default_partition_size", "gather_kv", "k_cache_shape",
-           "load_library", "paged_attention", "reshape_and_cache", "v_cache_shape",
+           "load_library", "paged_attention", "paged_prefill", "reshape_and_cache", "v_cache_shape",
            "workspace_size"]

@@ -45,6 +45,8 @@ def load_library() -> ctypes.CDLL:
     lib.pa_reshape_and_cache.argtypes = [vp] * 5 + [i32] * 6 + [vp]
     lib.pa_decode_step.restype = i32
     lib.pa_decode_step.argtypes = [vp] * 9 + [i32] * 8 + [f32, i32, i32, vp, sz, vp]
+    lib.pa_paged_prefill.restype = i32
+    lib.pa_paged_prefill.argtypes = [vp] * 7 + [i32] * 9 + [f32, i32, vp]
     lib.pa_copy_blocks.restype = i32
     lib.pa_copy_blocks.argtypes = [vp] * 3 + [i32] * 6 + [vp]
     lib.pa_gather_kv.restype = i32
@@ -236,6 +238,41 @@ def reshape_and_cache(key: torch.Tensor, value: torch.Tensor, slot_mapping: torc
                                   _ptr(v_cache), T, Hkv, D, BS, NB, _dtype_code(key),
                                   _stream(dev, stream))
     _check(st, "pa_reshape_and_cache")
+
+
+def paged_prefill(query: torch.Tensor, query_start_loc: torch.Tensor, block_table: torch.Tensor,
+                  context_lens: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                  scale: float, *, max_query_len: int, out: torch.Tensor | None = None,
+                  stream=None) -> torch.Tensor:
+    """Causal attention of each sequence's chunk of new tokens (query [T, Hq, D], rows
+    query_start_loc[s] .. query_start_loc[s+1] - 1) over its paged K/V (pa_paged_prefill)."""
+    lib = load_library()
+    dev = query.device
+    _require(query, "query", dev)
+    NB, Hkv, D, BS = _cache_dims(k_cache, v_cache)
+    _require(k_cache, "k_cache", dev, query.dtype)
+    _require(v_cache, "v_cache", dev, query.dtype)
+    _require(query_start_loc, "query_start_loc", dev, torch.int32)
+    _require(block_table, "block_table", dev, torch.int32)
+    _require(context_lens, "context_lens", dev, torch.int32)
+    if query.dim() != 3 or query.shape[2] != D:
+        raise ValueError(f"query must be [T, Hq, {D}], got {tuple(query.shape)}")
+    T, Hq, _ = query.shape
+    S = context_lens.shape[0]
+    if tuple(query_start_loc.shape) != (S + 1,) or block_table.dim() != 2 or \
+            block_table.shape[0] != S:
+        raise ValueError("query_start_loc must be [S + 1] and block_table [S, MB]")
+    if out is None:
+        out = torch.empty_like(query)
+    _require(out, "out", dev, query.dtype)
+    if tuple(out.shape) != tuple(query.shape):
+        raise ValueError("out must have the shape of query")
+    st = lib.pa_paged_prefill(_ptr(out), _ptr(query), _ptr(query_start_loc), _ptr(block_table),
+                              _ptr(context_lens), _ptr(k_cache), _ptr(v_cache), S, Hq, Hkv, D,
+                              BS, block_table.shape[1], NB, T, int(max_query_len), float(scale),
+                              _dtype_code(query), _stream(dev, stream))
+    _check(st, "pa_paged_prefill")
+    return out
 
 
 def copy_blocks(k_cache: torch.Tensor, v_cache: torch.Tensor, block_mapping: torch.Tensor,

@@ -1,0 +1,438 @@
+// Paged prefill for gfx950 (MI355X): causal attention of a chunk of new query
+// tokens per sequence over the sequence's paged K/V.
+//
+// What is computed: sequence s owns query rows query_start_loc[s] ..
+// query_start_loc[s+1] - 1 (n tokens); with L = context_lens[s], row i is the
+// token at position p = L - n + i and attends to positions 0 .. p of the K/V
+// reassembled through the block table (page "vLLM core architecture", section
+// 2.2.2).  Only the new tokens of a request are computed; its earlier, cached
+// context -- e.g. a system prompt shared in physical blocks (page "core
+// inference engine", section 2.2; prefix caching, page "core features",
+// sections 4.2 and 4.6) -- is read through the table.  n = 1 is a decode step.
+//
+// Work decomposition
+//   workgroup = (kv head, sequence, query tile).  A tile holds 128 query rows:
+//     128 / g tokens x the g query heads of the kv head (row r = token r / g,
+//     head r % g).  4 waves; wave w owns rows [32 w, 32 w + 32) as two 16-row
+//     column blocks.
+//   The workgroup streams the keys 0 .. (last position of the tile) in steps of
+//   32 keys (bf16) or 16 keys (f32).  Each step's K and V tiles are loaded once
+//   into LDS (every thread one 16-byte chunk of K and of V per 256 chunks) and
+//   read by all waves; the next step's chunks are loaded into registers while the
+//   current step is computed.
+//   Q.K^T per column block is [keys x D] . [D x 16 rows] on MFMA (the K tile is the
+//   A operand, the query rows the B operand), P.V is [D x keys] . [keys x 16 rows]
+//   -- the same lane mapping as the decode kernel.  For bf16 the softmax weights
+//   enter P.V as two bf16 MFMAs, p = hi + lo, accumulated into one output.
+//   Rows keep a running max and sum (online softmax); key t counts for a row at
+//   position p only if t <= p.  V rows at positions >= L are zeroed in LDS (their
+//   weight is 0, and 0 * NaN is NaN).
+#include <algorithm>
+
+#include "common.h"
+
+namespace pa {
+
+struct PrefillParams {
+  void* out;
+  const void* q;
+  const int32_t* qsl;            // query_start_loc [S + 1]
+  const int32_t* block_table;
+  const int32_t* context_lens;
+  const void* k_cache;
+  const void* v_cache;
+  int S, Hq, Hkv, g, MB, NB, T, tiles;
+  float scale_log2;
+};
+
+template <typename T, int D>
+struct PrefillShape {
+  static constexpr bool kBf16 = ElemTraits<T>::kBf16;
+  static constexpr int kX = ElemTraits<T>::kX;               // elements per 16-byte chunk
+  static constexpr int kStep = kBf16 ? 32 : 16;              // keys per step
+  static constexpr int kTpl = kBf16 ? 8 : 4;                 // logits per lane per step
+  static constexpr int kTiles = kBf16 ? 2 : 1;               // 16-key K tiles per step
+  static constexpr int kNc = D / (kBf16 ? 32 : 16);          // K chunks per lane per tile
+  static constexpr int kNs = D / 16;                         // 16-channel output slices
+  static constexpr int kKChunks = kStep * (D / kX);          // 16-byte K chunks per step
+  static constexpr int kVChunks = D * (kStep / kX);          // 16-byte V chunks per step
+  // LDS rows: K [key][chunk] with a 16-byte pad, V [channel][keys] with a 16-byte pad
+  static constexpr int kKRow = D / kX + 1;                   // in 16-byte units
+  static constexpr int kVRow = kStep / kX + 1;               // in 16-byte units
+  static constexpr int kKBytes = kStep * kKRow * 16;
+  static constexpr int kVBytes = D * kVRow * 16;
+};
+
+constexpr int kPrefillWaves = 4;
+constexpr int kPrefillRows = 128;                            // query rows per workgroup
+constexpr int kPrefillBlocks = 2;                            // 16-row column blocks per wave
+
+template <typename T, int D, int BS>
+__global__ void __launch_bounds__(kPrefillWaves * 64)
+paged_prefill_kernel(const PrefillParams a) {
+  using Sh = PrefillShape<T, D>;
+  constexpr bool kBf16 = Sh::kBf16;
+  constexpr int kX = Sh::kX;
+  constexpr int kStep = Sh::kStep;
+  constexpr int kTpl = Sh::kTpl;
+  constexpr int kNc = Sh::kNc;
+  constexpr int kNs = Sh::kNs;
+  constexpr int kThreads = kPrefillWaves * 64;
+  constexpr int kLoadsK = (Sh::kKChunks + kThreads - 1) / kThreads;
+  constexpr int kLoadsV = (Sh::kVChunks + kThreads - 1) / kThreads;
+
+  __shared__ __align__(16) unsigned char kt[Sh::kKBytes];
+  __shared__ __align__(16) unsigned char vt[Sh::kVBytes];
+  __shared__ int tbl_lds[1024];                              // block-table window (<= 1024)
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n = lane & 15;
+  const int j = lane >> 4;
+
+  int id = blockIdx.x;
+  const int kvh = id % a.Hkv;
+  id /= a.Hkv;
+  const int s = id % a.S;
+  const int tile = id / a.S;
+
+  const int g = a.g;
+  const int tile_tokens = kPrefillRows / g;
+  int L = a.context_lens[s];
+  L = L < 0 ? 0 : (L > a.MB * BS ? a.MB * BS : L);
+  const int r0 = min(max(a.qsl[s], 0), a.T);
+  int nq = min(max(a.qsl[s + 1], 0), a.T) - r0;
+  nq = nq < 0 ? 0 : (nq > L ? L : nq);
+  const int t0 = tile * tile_tokens;                         // first token of the tile
+  if (t0 >= nq) return;
+  const int t1 = min(nq, t0 + tile_tokens);
+  const int pos0 = L - nq;                                   // position of chunk token 0
+  const int kmax = pos0 + t1;                                // keys 0 .. kmax - 1 are seen
+  const int nsteps = (kmax + kStep - 1) / kStep;
+  const int nblk = (kmax + BS - 1) / BS;                     // <= MB
+
+  // block-table window 0 .. nblk - 1, in chunks of 1024 entries (refilled per 1024 blocks)
+  const int* bt = a.block_table + (size_t)s * a.MB;
+  auto load_table = [&](int first) {
+    for (int i = threadIdx.x; i < 1024 && first + i < nblk; i += kThreads) {
+      const unsigned b = static_cast<unsigned>(bt[first + i]);
+      tbl_lds[i] = static_cast<int>(min(b, static_cast<unsigned>(a.NB - 1)));
+    }
+  };
+
+  // ---- this wave's query rows: operand, position, output row -------------------------
+  // column block cb (0, 1) of this wave: row = 32 * wave + 16 * cb + n
+  u32x4 qop[kPrefillBlocks][kNc];
+  int pos[kPrefillBlocks];                                   // row's position (-1: no row)
+  size_t orow[kPrefillBlocks];
+  const T* qbase = static_cast<const T*>(a.q);
+#pragma unroll
+  for (int cb = 0; cb < kPrefillBlocks; ++cb) {
+    const int row = 32 * wave + 16 * cb + n;
+    const int tok = t0 + row / g;
+    const int head = kvh * g + row % g;
+    const bool live = tok < t1;
+    pos[cb] = live ? pos0 + tok : -1;
+    orow[cb] = ((size_t)(r0 + (live ? tok : 0)) * a.Hq + head) * D;
+#pragma unroll
+    for (int c = 0; c < kNc; ++c) {
+      const u32x4 z = {0u, 0u, 0u, 0u};
+      qop[cb][c] = live ? load16(qbase + orow[cb] + kX * (4 * c + j)) : z;
+    }
+  }
+
+  // last position of each column block (the same in every lane of the wave)
+  int pend[kPrefillBlocks];
+#pragma unroll
+  for (int cb = 0; cb < kPrefillBlocks; ++cb) {
+    int pm = pos[cb];
+    pm = max(pm, __shfl_xor(pm, 1, 64));
+    pm = max(pm, __shfl_xor(pm, 2, 64));
+    pm = max(pm, __shfl_xor(pm, 4, 64));
+    pm = max(pm, __shfl_xor(pm, 8, 64));
+    pend[cb] = __builtin_amdgcn_readfirstlane(pm);
+  }
+
+  // ---- cooperative K/V tile loads (global -> registers -> LDS) -------------------------
+  const T* kc = static_cast<const T*>(a.k_cache);
+  const T* vc = static_cast<const T*>(a.v_cache);
+  const size_t head_elems = (size_t)D * BS;
+  u32x4 kreg[kLoadsK], vreg[kLoadsV];
+
+  // chunk ids: K id = q * kStep + key (q = 16-byte chunk of the row), V id = channel *
+  // (kStep / kX) + group; consecutive threads read consecutive addresses within a block
+  auto fetch = [&](int st) {
+    const int base = st * kStep;
+    const int tb0 = (base / BS) / 1024 * 1024;               // table chunk of this step
+#pragma unroll
+    for (int i = 0; i < kLoadsK; ++i) {
+      const int cid = threadIdx.x + i * kThreads;
+      const int q = cid / kStep;
+      const int key = min(base + cid % kStep, kmax - 1);      // past kmax: a seen key (masked)
+      const int phys = tbl_lds[key / BS - tb0];
+      const T* src = kc + ((size_t)phys * a.Hkv + kvh) * head_elems +
+                     ((size_t)q * BS + key % BS) * kX;
+      const u32x4 z = {0u, 0u, 0u, 0u};
+      kreg[i] = cid < Sh::kKChunks ? load16(src) : z;
+    }
+#pragma unroll
+    for (int i = 0; i < kLoadsV; ++i) {
+      const int cid = threadIdx.x + i * kThreads;
+      const int ch = cid / (kStep / kX);
+      const int grp = cid % (kStep / kX);
+      const int key = min(base + grp * kX, (kmax - 1) / kX * kX);
+      const int phys = tbl_lds[key / BS - tb0];
+      const T* src = vc + ((size_t)phys * a.Hkv + kvh) * head_elems + (size_t)ch * BS + key % BS;
+      const u32x4 z = {0u, 0u, 0u, 0u};
+      vreg[i] = cid < Sh::kVChunks ? load16(src) : z;
+    }
+  };
+  auto stage = [&](int st) {
+    const int base = st * kStep;
+#pragma unroll
+    for (int i = 0; i < kLoadsK; ++i) {
+      const int cid = threadIdx.x + i * kThreads;
+      if (cid < Sh::kKChunks) {
+        const int q = cid / kStep, key = cid % kStep;
+        *reinterpret_cast<u32x4*>(kt + (key * Sh::kKRow + q) * 16) = kreg[i];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kLoadsV; ++i) {
+      const int cid = threadIdx.x + i * kThreads;
+      if (cid < Sh::kVChunks) {
+        const int ch = cid / (kStep / kX), grp = cid % (kStep / kX);
+        // zero positions >= L (kmax <= L): weight 0 must not meet NaN
+        const int nv = min(max(kmax - (base + grp * kX), 0), kX);
+        u32x4 v = vreg[i];
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          uint32_t mask;
+          if (kBf16)
+            mask = (2 * w + 1 < nv) ? 0xFFFFFFFFu : ((2 * w < nv) ? 0x0000FFFFu : 0u);
+          else
+            mask = (w < nv) ? 0xFFFFFFFFu : 0u;
+          v[w] &= mask;
+        }
+        *reinterpret_cast<u32x4*>(vt + (ch * Sh::kVRow + grp) * 16) = v;
+      }
+    }
+  };
+
+  float m_run[kPrefillBlocks], l_run[kPrefillBlocks];
+  f32x4 acc[kPrefillBlocks][kNs];
+#pragma unroll
+  for (int cb = 0; cb < kPrefillBlocks; ++cb) {
+    m_run[cb] = kNegInf;
+    l_run[cb] = 0.f;
+#pragma unroll
+    for (int i = 0; i < kNs; ++i) acc[cb][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  load_table(0);
+  __syncthreads();
+  if (nsteps > 0) fetch(0);
+  for (int st = 0; st < nsteps; ++st) {
+    __syncthreads();                                         // previous step's reads done
+    stage(st);
+    if (st + 1 < nsteps && ((st + 1) * kStep / BS) / 1024 != (st * kStep / BS) / 1024) {
+      __syncthreads();                                       // table window moves on
+      load_table((st + 1) * kStep / BS / 1024 * 1024);
+    }
+    __syncthreads();
+    if (st + 1 < nsteps) fetch(st + 1);                      // next step in flight
+    const int base = st * kStep;
+
+#pragma unroll
+    for (int cb = 0; cb < kPrefillBlocks; ++cb) {
+      if (base > pend[cb]) continue;                         // every row of the block ended
+      // scores: K tile rows from LDS (A), query rows (B)
+      float y[kTpl];
+      if constexpr (kBf16) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const int key = 8 * (n >> 2) + 4 * t + (n & 3);
+          f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int c = 0; c < kNc; ++c) {
+            const u32x4 kk =
+                *reinterpret_cast<const u32x4*>(kt + (key * Sh::kKRow + 4 * c + j) * 16);
+            sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kk),
+                                                         __builtin_bit_cast(bf16x8, qop[cb][c]),
+                                                         sc, 0, 0, 0);
+          }
+#pragma unroll
+          for (int e = 0; e < 4; ++e) y[4 * t + e] = sc[e];
+        }
+      } else {
+        f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < kNc; ++c) {
+          const u32x4 kk = *reinterpret_cast<const u32x4*>(kt + (n * Sh::kKRow + 4 * c + j) * 16);
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            sc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(kk[e]),
+                                                      __uint_as_float(qop[cb][c][e]), sc, 0, 0, 0);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) y[e] = sc[e];
+      }
+
+      // online softmax (base 2); key base + kTpl*j + v counts if <= the row's position
+      float mx = kNegInf;
+#pragma unroll
+      for (int v = 0; v < kTpl; ++v) {
+        const bool live = base + kTpl * j + v <= pos[cb];
+        y[v] = live ? y[v] * a.scale_log2 : kNegInf;
+        mx = fmaxf(mx, y[v]);
+      }
+      mx = fmaxf(mx, xor16(mx));
+      mx = fmaxf(mx, xor32(mx));
+      const float m_new = fmaxf(m_run[cb], mx);
+      const float m_use = (m_new == kNegInf) ? 0.f : m_new;
+      const float alpha = exp2_fast(m_run[cb] - m_use);
+      float pw[kTpl];
+      float psum = 0.f;
+#pragma unroll
+      for (int v = 0; v < kTpl; ++v) {
+        pw[v] = exp2_fast(y[v] - m_use);
+        psum += pw[v];
+      }
+      l_run[cb] = l_run[cb] * alpha + psum;
+      m_run[cb] = m_new;
+#pragma unroll
+      for (int sl = 0; sl < kNs; ++sl) acc[cb][sl] *= alpha;
+
+      // P.V: V tile from LDS (A), weights (B)
+      if constexpr (kBf16) {
+        bf16x8 phi, plo;
+#pragma unroll
+        for (int v = 0; v < 8; ++v) {
+          const __bf16 hi = f32_to_bf16(pw[v]);
+          phi[v] = hi;
+          plo[v] = f32_to_bf16(pw[v] - bf16_to_f32(hi));
+        }
+#pragma unroll
+        for (int sl = 0; sl < kNs; ++sl) {
+          const u32x4 vv =
+              *reinterpret_cast<const u32x4*>(vt + ((16 * sl + n) * Sh::kVRow + j) * 16);
+          acc[cb][sl] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vv),
+                                                                phi, acc[cb][sl], 0, 0, 0);
+          acc[cb][sl] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vv),
+                                                                plo, acc[cb][sl], 0, 0, 0);
+        }
+      } else {
+#pragma unroll
+        for (int sl = 0; sl < kNs; ++sl) {
+          const u32x4 vv =
+              *reinterpret_cast<const u32x4*>(vt + ((16 * sl + n) * Sh::kVRow + j) * 16);
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            acc[cb][sl] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(vv[e]), pw[e],
+                                                               acc[cb][sl], 0, 0, 0);
+        }
+      }
+    }
+  }
+
+  // ---- normalise and write the rows -----------------------------------------------------
+#pragma unroll
+  for (int cb = 0; cb < kPrefillBlocks; ++cb) {
+    float lsum = l_run[cb] + xor16(l_run[cb]);
+    lsum += xor32(lsum);
+    if (pos[cb] < 0) continue;
+    const float inv = (m_run[cb] == kNegInf || lsum == 0.f) ? 0.f : 1.f / lsum;
+#pragma unroll
+    for (int sl = 0; sl < kNs; ++sl) {
+      const size_t o = orow[cb] + 16 * sl + 4 * j;
+      if constexpr (kBf16) {
+        uint16_t* op = static_cast<uint16_t*>(a.out) + o;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) op[e] = bf16_bits(acc[cb][sl][e] * inv);
+      } else {
+        float* op = static_cast<float*>(a.out) + o;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) op[e] = acc[cb][sl][e] * inv;
+      }
+    }
+  }
+}
+
+template <typename T, int D, int BS>
+hipError_t launch_prefill(const PrefillParams& a, hipStream_t stream) {
+  const long grid = (long)a.Hkv * a.S * a.tiles;
+  hipLaunchKernelGGL((paged_prefill_kernel<T, D, BS>), dim3((unsigned)grid),
+                     dim3(kPrefillWaves * 64), 0, stream, a);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t dispatch_prefill(const PrefillParams& a, int D, int BS, hipStream_t stream) {
+#define PA_CASE(DD, BB) \
+  if (D == DD && BS == BB) return launch_prefill<T, DD, BB>(a, stream);
+  PA_CASE(64, 8) PA_CASE(64, 16) PA_CASE(64, 32)
+  PA_CASE(128, 8) PA_CASE(128, 16) PA_CASE(128, 32)
+#undef PA_CASE
+  return hipErrorInvalidValue;
+}
+
+}  // namespace pa
+
+namespace {
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+}  // namespace
+
+extern "C" pa_status pa_paged_prefill(void* out, const void* query, const int32_t* query_start_loc,
+                                      const int32_t* block_table, const int32_t* context_lens,
+                                      const void* k_cache, const void* v_cache, int num_seqs,
+                                      int num_heads, int num_kv_heads, int head_dim,
+                                      int block_size, int max_blocks_per_seq, int num_blocks,
+                                      int num_query_tokens, int max_query_len, float scale,
+                                      pa_dtype dtype, void* stream) {
+  if (dtype != PA_DTYPE_F32 && dtype != PA_DTYPE_BF16) return PA_ERR_UNSUPPORTED;
+  if (num_heads <= 0 || num_kv_heads <= 0 || num_heads % num_kv_heads) return PA_ERR_INVALID_ARG;
+  if (head_dim != 64 && head_dim != 128) return PA_ERR_UNSUPPORTED;
+  if (block_size != 8 && block_size != 16 && block_size != 32) return PA_ERR_UNSUPPORTED;
+  const int g = num_heads / num_kv_heads;
+  if (g > 16 || pa::kPrefillRows % g != 0) return PA_ERR_UNSUPPORTED;
+  if (num_seqs < 0 || max_blocks_per_seq <= 0 || num_blocks <= 0 || num_query_tokens < 0 ||
+      max_query_len < 0)
+    return PA_ERR_INVALID_ARG;
+  if (num_seqs == 0 || num_query_tokens == 0 || max_query_len == 0) return PA_OK;
+  if (!out || !query || !query_start_loc || !block_table || !context_lens || !k_cache ||
+      !v_cache)
+    return PA_ERR_INVALID_ARG;
+  if (!aligned(out, 16) || !aligned(query, 16) || !aligned(k_cache, 16) ||
+      !aligned(v_cache, 16) || !aligned(block_table, 4) || !aligned(context_lens, 4) ||
+      !aligned(query_start_loc, 4))
+    return PA_ERR_INVALID_ARG;
+  const int tile_tokens = pa::kPrefillRows / g;
+  const long tiles = ((long)max_query_len + tile_tokens - 1) / tile_tokens;
+  const long grid = (long)num_kv_heads * num_seqs * tiles;
+  if (grid > 0x7FFFFFFFL) return PA_ERR_INVALID_ARG;
+
+  pa::PrefillParams a;
+  a.out = out;
+  a.q = query;
+  a.qsl = query_start_loc;
+  a.block_table = block_table;
+  a.context_lens = context_lens;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.S = num_seqs;
+  a.Hq = num_heads;
+  a.Hkv = num_kv_heads;
+  a.g = g;
+  a.MB = max_blocks_per_seq;
+  a.NB = num_blocks;
+  a.T = num_query_tokens;
+  a.tiles = (int)tiles;
+  a.scale_log2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t err = dtype == PA_DTYPE_BF16
+                       ? pa::dispatch_prefill<uint16_t>(a, head_dim, block_size, s)
+                       : pa::dispatch_prefill<float>(a, head_dim, block_size, s);
+  return err == hipSuccess ? PA_OK : PA_ERR_HIP;
+}

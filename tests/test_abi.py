@@ -32,7 +32,7 @@ def test_header_declares_the_boundary():
     assert declared_functions() == sorted([
         "pa_abi_version", "pa_status_string", "pa_default_partition_size",
         "pa_paged_attention_workspace_size", "pa_paged_attention", "pa_reshape_and_cache",
-        "pa_gather_kv", "pa_decode_step", "pa_copy_blocks"])
+        "pa_gather_kv", "pa_decode_step", "pa_copy_blocks", "pa_paged_prefill"])
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -141,6 +141,25 @@ def test_reshape_and_cache_rejects_before_launch(lib):
     assert f(FAKE, FAKE, FAKE + 4, FAKE, FAKE, 4, 8, 128, 16, 64, 1, None) == 1
     assert f(FAKE, FAKE, FAKE, FAKE, FAKE, -1, 8, 128, 16, 64, 1, None) == 1
     assert f(None, None, None, None, None, 0, 8, 128, 16, 64, 1, None) == 0
+
+
+def test_prefill_rejects_before_launch(lib):
+    f = lib.pa_paged_prefill
+    base = [FAKE] * 7 + [4, 32, 8, 128, 16, 8, 64, 100, 40, 0.1, 1, None]
+
+    def call(over):
+        a = list(base)
+        for k, v in over.items():
+            a[k] = v
+        return f(*a)
+    assert call({1: None}) == 1                  # query missing
+    assert call({2: FAKE + 2}) == 1              # query_start_loc misaligned
+    assert call({10: 96}) == 2                   # head size
+    assert call({11: 24}) == 2                   # block size
+    assert call({8: 24, 9: 8}) == 2              # group of 3 does not divide 128
+    assert call({8: 36}) == 1                    # heads not a multiple of kv heads
+    assert call({14: 0}) == 0                    # no query tokens: nothing to do
+    assert call({7: 0}) == 0                     # no sequences
 
 
 def test_copy_blocks_rejects_before_launch(lib):
