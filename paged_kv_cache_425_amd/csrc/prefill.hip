@@ -28,6 +28,7 @@
 //   position p only if t <= p.  V rows at positions >= L are zeroed in LDS (their
 //   weight is 0, and 0 * NaN is NaN).
 #include <algorithm>
+#include <type_traits>
 
 #include "common.h"
 
@@ -66,9 +67,10 @@ struct PrefillShape {
 constexpr int kPrefillWaves = 4;
 constexpr int kPrefillRows = 128;                            // query rows per workgroup
 constexpr int kPrefillBlocks = 2;                            // 16-row column blocks per wave
+constexpr float kLazy = 8.f;                                 // lazy-rescale threshold (log2)
 
 template <typename T, int D, int BS>
-__global__ void __launch_bounds__(kPrefillWaves * 64)
+__global__ void __launch_bounds__(kPrefillWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 paged_prefill_kernel(const PrefillParams a) {
   using Sh = PrefillShape<T, D>;
   constexpr bool kBf16 = Sh::kBf16;
@@ -81,8 +83,10 @@ paged_prefill_kernel(const PrefillParams a) {
   constexpr int kLoadsK = (Sh::kKChunks + kThreads - 1) / kThreads;
   constexpr int kLoadsV = (Sh::kVChunks + kThreads - 1) / kThreads;
 
-  __shared__ __align__(16) unsigned char kt[Sh::kKBytes];
-  __shared__ __align__(16) unsigned char vt[Sh::kVBytes];
+  // two K/V tile buffers: step st is computed from buffer st % 2 while step st + 1 is
+  // staged into the other
+  __shared__ __align__(16) unsigned char kt[2 * Sh::kKBytes];
+  __shared__ __align__(16) unsigned char vt[2 * Sh::kVBytes];
   __shared__ int tbl_lds[1024];                              // block-table window (<= 1024)
 
   const int lane = threadIdx.x & 63;
@@ -141,23 +145,18 @@ paged_prefill_kernel(const PrefillParams a) {
     }
   }
 
-  // last position of each column block (the same in every lane of the wave)
-  int pend[kPrefillBlocks];
-#pragma unroll
-  for (int cb = 0; cb < kPrefillBlocks; ++cb) {
-    int pm = pos[cb];
-    pm = max(pm, __shfl_xor(pm, 1, 64));
-    pm = max(pm, __shfl_xor(pm, 2, 64));
-    pm = max(pm, __shfl_xor(pm, 4, 64));
-    pm = max(pm, __shfl_xor(pm, 8, 64));
-    pend[cb] = __builtin_amdgcn_readfirstlane(pm);
-  }
-
   // ---- cooperative K/V tile loads (global -> registers -> LDS) -------------------------
   const T* kc = static_cast<const T*>(a.k_cache);
   const T* vc = static_cast<const T*>(a.v_cache);
   const size_t head_elems = (size_t)D * BS;
   u32x4 kreg[kLoadsK], vreg[kLoadsV];
+
+  // LDS row of a key within the step: the MFMA row that reads it (bf16: tile t = (key/4)%2,
+  // row (key%4) + 4 * (key/8)), so the 16 lanes of a read pass take consecutive rows and
+  // the 17-chunk row stride spreads them over distinct banks
+  auto krow = [](int key) -> int {
+    return kBf16 ? ((key >> 2) & 1) * 16 + (key & 3) + 4 * ((key >> 3) & 3) : key;
+  };
 
   // chunk ids: K id = q * kStep + key (q = 16-byte chunk of the row), V id = channel *
   // (kStep / kX) + group; consecutive threads read consecutive addresses within a block
@@ -187,14 +186,16 @@ paged_prefill_kernel(const PrefillParams a) {
       vreg[i] = cid < Sh::kVChunks ? load16(src) : z;
     }
   };
-  auto stage = [&](int st) {
+  auto stage = [&](int st, int buf) {
     const int base = st * kStep;
+    unsigned char* kb = kt + buf * Sh::kKBytes;
+    unsigned char* vb = vt + buf * Sh::kVBytes;
 #pragma unroll
     for (int i = 0; i < kLoadsK; ++i) {
       const int cid = threadIdx.x + i * kThreads;
       if (cid < Sh::kKChunks) {
         const int q = cid / kStep, key = cid % kStep;
-        *reinterpret_cast<u32x4*>(kt + (key * Sh::kKRow + q) * 16) = kreg[i];
+        *reinterpret_cast<u32x4*>(kb + (krow(key) * Sh::kKRow + q) * 16) = kreg[i];
       }
     }
 #pragma unroll
@@ -214,7 +215,7 @@ paged_prefill_kernel(const PrefillParams a) {
             mask = (w < nv) ? 0xFFFFFFFFu : 0u;
           v[w] &= mask;
         }
-        *reinterpret_cast<u32x4*>(vt + (ch * Sh::kVRow + grp) * 16) = v;
+        *reinterpret_cast<u32x4*>(vb + (ch * Sh::kVRow + grp) * 16) = v;
       }
     }
   };
@@ -229,111 +230,160 @@ paged_prefill_kernel(const PrefillParams a) {
     for (int i = 0; i < kNs; ++i) acc[cb][i] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
+  // table window of a step (a window of 1024 blocks spans >= 8192 keys, many steps)
+  auto window = [&](int st) { return (st * kStep / BS) / 1024; };
   load_table(0);
   __syncthreads();
-  if (nsteps > 0) fetch(0);
-  for (int st = 0; st < nsteps; ++st) {
-    __syncthreads();                                         // previous step's reads done
-    stage(st);
-    if (st + 1 < nsteps && ((st + 1) * kStep / BS) / 1024 != (st * kStep / BS) / 1024) {
-      __syncthreads();                                       // table window moves on
-      load_table((st + 1) * kStep / BS / 1024 * 1024);
-    }
-    __syncthreads();
-    if (st + 1 < nsteps) fetch(st + 1);                      // next step in flight
+  if (nsteps > 0) {
+    fetch(0);
+    stage(0, 0);
+  }
+  __syncthreads();
+  if (nsteps > 1) fetch(1);                                  // same window as step 0
+  auto run_step = [&](const int st, auto masked) {
+    constexpr bool kMasked = decltype(masked)::value;
     const int base = st * kStep;
+    const unsigned char* ktc = kt + (st & 1) * Sh::kKBytes;
+    const unsigned char* vtc = vt + (st & 1) * Sh::kVBytes;
 
+    // scores of both column blocks; each K fragment is read from LDS once and used by
+    // both blocks' MFMAs (K tile rows are the A operand, query rows the B operand)
+    float y[kPrefillBlocks][kTpl];
+    if constexpr (kBf16) {
 #pragma unroll
-    for (int cb = 0; cb < kPrefillBlocks; ++cb) {
-      if (base > pend[cb]) continue;                         // every row of the block ended
-      // scores: K tile rows from LDS (A), query rows (B)
-      float y[kTpl];
-      if constexpr (kBf16) {
+      for (int t = 0; t < 2; ++t) {
+        // row n of tile t holds key 8 * (n / 4) + 4 * t + n % 4 (stored at LDS row 16 t + n)
+        f32x4 sc[kPrefillBlocks];
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const int key = 8 * (n >> 2) + 4 * t + (n & 3);
-          f32x4 sc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int c = 0; c < kNc; ++c) {
-            const u32x4 kk =
-                *reinterpret_cast<const u32x4*>(kt + (key * Sh::kKRow + 4 * c + j) * 16);
-            sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kk),
-                                                         __builtin_bit_cast(bf16x8, qop[cb][c]),
-                                                         sc, 0, 0, 0);
-          }
-#pragma unroll
-          for (int e = 0; e < 4; ++e) y[4 * t + e] = sc[e];
-        }
-      } else {
-        f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+        for (int cb = 0; cb < kPrefillBlocks; ++cb) sc[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int c = 0; c < kNc; ++c) {
-          const u32x4 kk = *reinterpret_cast<const u32x4*>(kt + (n * Sh::kKRow + 4 * c + j) * 16);
+          const u32x4 kk =
+              *reinterpret_cast<const u32x4*>(ktc + ((16 * t + n) * Sh::kKRow + 4 * c + j) * 16);
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            sc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(kk[e]),
-                                                      __uint_as_float(qop[cb][c][e]), sc, 0, 0, 0);
+          for (int cb = 0; cb < kPrefillBlocks; ++cb)
+            sc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kk),
+                                                             __builtin_bit_cast(bf16x8, qop[cb][c]),
+                                                             sc[cb], 0, 0, 0);
         }
 #pragma unroll
-        for (int e = 0; e < 4; ++e) y[e] = sc[e];
+        for (int cb = 0; cb < kPrefillBlocks; ++cb)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) y[cb][4 * t + e] = sc[cb][e];
       }
+    } else {
+      f32x4 sc[kPrefillBlocks];
+#pragma unroll
+      for (int cb = 0; cb < kPrefillBlocks; ++cb) sc[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < kNc; ++c) {
+        const u32x4 kk = *reinterpret_cast<const u32x4*>(ktc + (n * Sh::kKRow + 4 * c + j) * 16);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+#pragma unroll
+          for (int cb = 0; cb < kPrefillBlocks; ++cb)
+            sc[cb] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(kk[e]),
+                                                          __uint_as_float(qop[cb][c][e]), sc[cb],
+                                                          0, 0, 0);
+      }
+#pragma unroll
+      for (int cb = 0; cb < kPrefillBlocks; ++cb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) y[cb][e] = sc[cb][e];
+    }
 
-      // online softmax (base 2); key base + kTpl*j + v counts if <= the row's position
+    // online softmax (base 2).  Masked steps: key base + kTpl*j + v counts if <= the
+    // row's position.  A row's running max moves only when a step raises it by more
+    // than kLazy (its weights then stay below 2^kLazy), so the accumulators are
+    // rescaled on few steps; the result is the same sum with another common factor.
+    float pw[kPrefillBlocks][kTpl];
+    float alpha[kPrefillBlocks];
+    bool moved = false;
+#pragma unroll
+    for (int cb = 0; cb < kPrefillBlocks; ++cb) {
       float mx = kNegInf;
 #pragma unroll
       for (int v = 0; v < kTpl; ++v) {
-        const bool live = base + kTpl * j + v <= pos[cb];
-        y[v] = live ? y[v] * a.scale_log2 : kNegInf;
-        mx = fmaxf(mx, y[v]);
+        if constexpr (kMasked) {
+          const bool live = base + kTpl * j + v <= pos[cb];
+          y[cb][v] = live ? y[cb][v] * a.scale_log2 : kNegInf;
+        } else {
+          y[cb][v] *= a.scale_log2;
+        }
+        mx = fmaxf(mx, y[cb][v]);
       }
       mx = fmaxf(mx, xor16(mx));
       mx = fmaxf(mx, xor32(mx));
-      const float m_new = fmaxf(m_run[cb], mx);
+      const float m_old = m_run[cb];
+      const float m_new = (mx > m_old + kLazy) ? mx : m_old;    // -inf + kLazy = -inf
       const float m_use = (m_new == kNegInf) ? 0.f : m_new;
-      const float alpha = exp2_fast(m_run[cb] - m_use);
-      float pw[kTpl];
+      alpha[cb] = exp2_fast(m_old - m_use);                    // 1 unless the max moved
       float psum = 0.f;
 #pragma unroll
       for (int v = 0; v < kTpl; ++v) {
-        pw[v] = exp2_fast(y[v] - m_use);
-        psum += pw[v];
+        pw[cb][v] = exp2_fast(y[cb][v] - m_use);
+        psum += pw[cb][v];
       }
-      l_run[cb] = l_run[cb] * alpha + psum;
+      l_run[cb] = l_run[cb] * alpha[cb] + psum;
       m_run[cb] = m_new;
+      // while a row's max is -inf its weights were all 0 and its accumulators are 0
+      moved = moved || (m_new != m_old && m_old != kNegInf);
+    }
+    if (__builtin_amdgcn_ballot_w64(moved) != 0) {
 #pragma unroll
-      for (int sl = 0; sl < kNs; ++sl) acc[cb][sl] *= alpha;
+      for (int cb = 0; cb < kPrefillBlocks; ++cb)
+#pragma unroll
+        for (int sl = 0; sl < kNs; ++sl) acc[cb][sl] *= alpha[cb];
+    }
 
-      // P.V: V tile from LDS (A), weights (B)
-      if constexpr (kBf16) {
-        bf16x8 phi, plo;
+    // P.V: each V fragment (A operand) is read once and used by both blocks' weights (B)
+    if constexpr (kBf16) {
+      bf16x8 phi[kPrefillBlocks], plo[kPrefillBlocks];
+#pragma unroll
+      for (int cb = 0; cb < kPrefillBlocks; ++cb)
 #pragma unroll
         for (int v = 0; v < 8; ++v) {
-          const __bf16 hi = f32_to_bf16(pw[v]);
-          phi[v] = hi;
-          plo[v] = f32_to_bf16(pw[v] - bf16_to_f32(hi));
+          const __bf16 hi = f32_to_bf16(pw[cb][v]);
+          phi[cb][v] = hi;
+          plo[cb][v] = f32_to_bf16(pw[cb][v] - bf16_to_f32(hi));
         }
 #pragma unroll
-        for (int sl = 0; sl < kNs; ++sl) {
-          const u32x4 vv =
-              *reinterpret_cast<const u32x4*>(vt + ((16 * sl + n) * Sh::kVRow + j) * 16);
-          acc[cb][sl] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vv),
-                                                                phi, acc[cb][sl], 0, 0, 0);
-          acc[cb][sl] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vv),
-                                                                plo, acc[cb][sl], 0, 0, 0);
-        }
-      } else {
+      for (int sl = 0; sl < kNs; ++sl) {
+        const bf16x8 vv = __builtin_bit_cast(
+            bf16x8, *reinterpret_cast<const u32x4*>(vtc + ((16 * sl + n) * Sh::kVRow + j) * 16));
 #pragma unroll
-        for (int sl = 0; sl < kNs; ++sl) {
-          const u32x4 vv =
-              *reinterpret_cast<const u32x4*>(vt + ((16 * sl + n) * Sh::kVRow + j) * 16);
+        for (int cb = 0; cb < kPrefillBlocks; ++cb)
+          acc[cb][sl] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vv, phi[cb], acc[cb][sl], 0, 0, 0);
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            acc[cb][sl] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(vv[e]), pw[e],
+        for (int cb = 0; cb < kPrefillBlocks; ++cb)
+          acc[cb][sl] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vv, plo[cb], acc[cb][sl], 0, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int sl = 0; sl < kNs; ++sl) {
+        const u32x4 vv =
+            *reinterpret_cast<const u32x4*>(vtc + ((16 * sl + n) * Sh::kVRow + j) * 16);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+#pragma unroll
+          for (int cb = 0; cb < kPrefillBlocks; ++cb)
+            acc[cb][sl] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(vv[e]), pw[cb][e],
                                                                acc[cb][sl], 0, 0, 0);
-        }
       }
     }
-  }
+    // stage the next step into the other buffer, then one barrier for both
+    if (st + 1 < nsteps) stage(st + 1, (st + 1) & 1);
+    if (st + 2 < nsteps && window(st + 2) != window(st + 1)) {
+      __syncthreads();                                       // every fetch of step st+1 done
+      load_table(window(st + 2) * 1024);
+    }
+    __syncthreads();
+    if (st + 2 < nsteps) fetch(st + 2);
+  };
+  // steps below the tile's first position need no causal mask
+  const int nfull = min(nsteps, (pos0 + t0 + 1) / kStep);
+  for (int st = 0; st < nfull; ++st) run_step(st, std::false_type{});
+  for (int st = nfull; st < nsteps; ++st) run_step(st, std::true_type{});
 
   // ---- normalise and write the rows -----------------------------------------------------
 #pragma unroll

@@ -7,6 +7,12 @@
 
 ``trace`` tabulates kernel durations (count, mean, median, min, max).
 
+``counters`` tabulates the per-dispatch value of every counter of one or more
+``--pmc`` runs for one kernel (median over a window of its launches) and, when
+SQ_VALU_MFMA_BUSY_CYCLES and GRBM_GUI_ACTIVE were both collected, the MFMA
+utilisation: busy cycles summed over all SIMDs / (GUI-active cycles of one XCD x
+256 CUs x 4 SIMDs).
+
 ``traffic`` turns the FETCH_SIZE / WRITE_SIZE counters (KiB per dispatch)
 into HBM bytes per launch of one kernel.  Each counter is scaled by what it
 reads for a plain device copy of known size recorded in the same run: the
@@ -87,6 +93,47 @@ def trace_table(db: str, last: int = 0, slices: list | None = None) -> str:
     return "\n".join(lines)
 
 
+N_CU = 256
+SIMD_PER_CU = 4
+
+
+def dispatch_counters(db: str, kernel: str) -> dict:
+    """counter -> list over the kernel's dispatches (in order) of (sum, instances)."""
+    con = sqlite3.connect(db)
+    out: dict = {}
+    for cname, _d, total, inst in con.execute(
+            "select counter_name, dispatch_id, sum(counter_value), count(*) from pmc_events "
+            "where name like ? group by dispatch_id, counter_name order by dispatch_id",
+            (f"%{kernel}%",)):
+        out.setdefault(cname, []).append((float(total), int(inst)))
+    return out
+
+
+def counters_table(dbs: list, kernel: str, start: int, count: int) -> tuple:
+    merged: dict = {}
+    for db in dbs:
+        for cname, vals in dispatch_counters(db, kernel).items():
+            end = start + count if count else None
+            merged[cname] = vals[start:end]
+    if not merged:
+        raise SystemExit(f"kernel {kernel} not found in the counter runs")
+    lines = ["| counter | dispatches | instances | median per dispatch (sum over instances) |",
+             "|---|---|---|---|"]
+    med = {}
+    for cname in sorted(merged):
+        vals = merged[cname]
+        med[cname] = (statistics.median(v for v, _ in vals), vals[0][1])
+        lines.append(f"| {cname} | {len(vals)} | {vals[0][1]} | {med[cname][0]:,.0f} |")
+    derived = {}
+    if "SQ_VALU_MFMA_BUSY_CYCLES" in med and "GRBM_GUI_ACTIVE" in med:
+        gui, inst = med["GRBM_GUI_ACTIVE"]
+        per_xcd = gui / inst
+        derived["mfma_util"] = med["SQ_VALU_MFMA_BUSY_CYCLES"][0] / (per_xcd * N_CU * SIMD_PER_CU)
+        lines += ["", f"MFMA utilisation = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / {inst} "
+                  f"x {N_CU} CUs x {SIMD_PER_CU} SIMDs) = {derived['mfma_util']:.3f}"]
+    return "\n".join(lines), derived
+
+
 def copy_factor(rows: list, copy_bytes: int) -> tuple:
     """Scale factor from the largest copy dispatches (those within 5% of the largest)."""
     vals = [v for n, _, v in rows if n.startswith(COPY_KERNEL)]
@@ -114,6 +161,15 @@ def main() -> None:
     t.add_argument("--slice", action="append", default=[],
                    help="KERNEL_SUBSTRING:START:COUNT:LABEL, stats of a window of launches")
     t.add_argument("--out", required=True)
+    c = sub.add_parser("counters")
+    c.add_argument("dbs", nargs="+")
+    c.add_argument("--kernel", required=True)
+    c.add_argument("--title", required=True)
+    c.add_argument("--command", action="append", required=True,
+                   help="the command of each run, in the order of the databases")
+    c.add_argument("--start", type=int, default=0)
+    c.add_argument("--count", type=int, default=0)
+    c.add_argument("--out", required=True)
     f = sub.add_parser("traffic")
     f.add_argument("--fetch", required=True)
     f.add_argument("--write", required=True)
@@ -132,6 +188,18 @@ def main() -> None:
     if a.cmd == "trace":
         text = (f"# {a.title}\n\nCommand (from the repository root on the GPU box):\n\n"
                 f"```\n{a.command}\n```\n\n{trace_table(a.db, a.last, a.slice)}\n")
+        with open(a.out, "w") as fh:
+            fh.write(text)
+        print(text)
+        return
+
+    if a.cmd == "counters":
+        table, _ = counters_table(a.dbs, a.kernel, a.start, a.count)
+        cmds = "\n".join(a.command)
+        end = f"{a.start + a.count - 1}" if a.count else "last"
+        text = (f"# {a.title}\n\nCommands (from the repository root on the GPU box), one "
+                f"counter set per run:\n\n```\n{cmds}\n```\n\nKernel `{a.kernel}`, launches "
+                f"{a.start}..{end} of each run.\n\n{table}\n")
         with open(a.out, "w") as fh:
             fh.write(text)
         print(text)

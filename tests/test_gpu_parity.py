@@ -467,6 +467,28 @@ def test_prefill_long_context_reloads_the_table_window():
     check_close(to_f64(got), ref, "bf16", "prefill-long")
 
 
+def test_prefill_rising_scores_move_the_running_max():
+    """Keys of one sign grow along the sequence (x(1 + t/35) at position t) and the
+    queries have one sign too, so each row's maximum score climbs by about 9.5 (log2
+    units) per 32-key step: the running max moves on most steps and the accumulators
+    are rescaled, which random keys of one scale almost never cause.  bf16 only: at
+    these logits (up to ~100) fp32 rounding of the score alone nears the f32 bar."""
+    from workloads.configs import f32_to_bf16_bits
+    w = tiny("bf16", (300, 130, 77), 8, 2, 128, 16, seed=81, scale=1.0 / np.sqrt(128))
+    for recs in w.seq_records:
+        f = 1.0 + np.arange(len(recs)) / 35.0
+        kf = (w.rec_key[recs].astype(np.uint32) << 16).view(np.float32)
+        w.rec_key[recs] = f32_to_bf16_bits(np.abs(kf) * f[:, None, None].astype(np.float32))
+    pb = make_prefill(w, [300, 64, 77], 81)
+    pb.query = pb.query & np.uint16(0x7FFF)
+    kc, vc = build_pools(w)
+    say("prefill rising scores")
+    got = run_prefill(w, pb, kc, vc)
+    ref = oracle.paged_prefill(pb.query, pb.query_start_loc, w.block_table, w.context_lens,
+                               kc, vc, w.scale, "bf16")
+    check_close(to_f64(got), ref, "bf16", "prefill-rising")
+
+
 @pytest.mark.parametrize("name", ["prefix-cache-prefill", "chunked-prefill-llama3-8b"])
 def test_prefill_named_cases_on_sampled_sequences(name):
     """Full-size batches; the oracle checks every row of a sample of sequences."""
