@@ -38,6 +38,7 @@ if ROOT not in sys.path:
 METRIC = "paged-attn decode KV GB/s (% of HBM peak) + µs/step, Llama-3-8B shape, 1 GPU"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, AMD's published peak
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_step_traffic.json")
+FP8_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_fp8_traffic.json")
 KERNEL_SOURCE = os.path.join(ROOT, "paged_kv_cache_425_amd", "csrc", "paged_attention.hip")
 
 
@@ -50,9 +51,10 @@ def parse_args():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--op", default="step", choices=["step", "copy_blocks", "prefill"],
+    ap.add_argument("--op", default="step", choices=["step", "copy_blocks", "prefill", "fp8"],
                     help="step: the decode step (default); copy_blocks: the copy-on-write "
-                         "copies of the parallel-sampling workload; prefill: paged prefill")
+                         "copies of the parallel-sampling workload; prefill: paged prefill; "
+                         "fp8: the decode step over FP8 (E4M3) K/V pools")
     ap.add_argument("--prefill-case", default="prefix-cache-prefill",
                     choices=["prefix-cache-prefill", "chunked-prefill-llama3-8b"])
     ap.add_argument("--config", type=int, default=1, choices=[0, 1, 2, 3, 4])
@@ -92,10 +94,10 @@ def source_digest() -> str:
         return hashlib.sha256(f.read()).hexdigest()
 
 
-def load_traffic(workload: str):
+def load_traffic(workload: str, path: str = TRAFFIC_FILE):
     """Measured HBM bytes per decode launch, if the counters were taken on the current kernel."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(path) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
@@ -105,14 +107,19 @@ def load_traffic(workload: str):
 
 
 # ---------------------------------------------------------------------------
+def blas_thread_count() -> int:
+    """Threads of the BLAS pool the oracle's matmuls run on."""
+    try:
+        from threadpoolctl import threadpool_info
+        return int(max([p.get("num_threads", 1) for p in threadpool_info()] or [1]))
+    except Exception:  # pragma: no cover
+        return 1
+
+
 def cpu_baseline(w, budget_s: float) -> dict:
     """The CPU oracle on a bounded sample of the same step (reported baseline)."""
     import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        blas_threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        blas_threads = 1
+    blas_threads = blas_thread_count()
     hist, new = w.history_records, w.new_records
     kc, vc = oracle.empty_pools(w.num_blocks, w.num_kv_heads, w.head_dim, w.block_size, w.dtype)
     oracle.reshape_and_cache(w.rec_key[hist], w.rec_value[hist], w.rec_slot[hist], kc, vc,
@@ -311,6 +318,167 @@ def bench_prefill(args) -> int:
     return 0
 
 
+FP8_K_SCALE = 0.0135           # about 6 / 448 for N(0, 1) records
+FP8_V_SCALE = 0.0121
+
+
+def cpu_baseline_fp8(w, budget_s: float, n_seqs: int = 8) -> dict:
+    """The oracle's FP8 step on the first n_seqs sequences (their history quantised first,
+    outside the timed budget): scatter of their new tokens, then their decode."""
+    import oracle
+    seqs = list(range(min(n_seqs, w.num_seqs)))
+    new = np.array([w.seq_records[s][-1] for s in seqs], dtype=np.int64)
+    hist = np.concatenate([w.seq_records[s][:-1] for s in seqs])
+    kc, vc = oracle.empty_fp8_pools(w.num_blocks, w.num_kv_heads, w.head_dim, w.block_size)
+    oracle.reshape_and_cache_fp8(w.rec_key[hist], w.rec_value[hist], w.rec_slot[hist], kc, vc,
+                                 w.dtype, FP8_K_SCALE, FP8_V_SCALE, inplace=True)
+    per_token = 2 * w.num_kv_heads * w.head_dim
+    rounds, kv = 0, 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < budget_s:
+        oracle.reshape_and_cache_fp8(w.rec_key[new], w.rec_value[new], w.rec_slot[new], kc, vc,
+                                     w.dtype, FP8_K_SCALE, FP8_V_SCALE, inplace=True)
+        oracle.paged_attention_fp8(w.query, w.block_table, w.context_lens, kc, vc, w.scale,
+                                   FP8_K_SCALE, FP8_V_SCALE, w.dtype, seqs=seqs)
+        kv += int(w.context_lens[seqs].astype(np.int64).sum()) * per_token
+        rounds += 1
+    dt = time.perf_counter() - t0
+    threads = blas_thread_count()
+    return {"value": round(kv / dt / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": (f"float64 NumPy oracle, FP8 step of the first {len(seqs)} sequences "
+                       f"(quantised scatter of their new tokens + their decode) repeated "
+                       f"{rounds} times, {kv / 1e6:.1f} MB of FP8 KV in {dt:.1f} s; "
+                       f"{len(os.sched_getaffinity(0))} cores visible, BLAS pool {threads} "
+                       "threads")}
+
+
+def bench_fp8(args) -> int:
+    """The decode step over FP8 pools on the Llama-3-8B-shaped batch: pa_decode_step_fp8
+    (one launch) as the headline, and the same step as pa_reshape_and_cache_fp8 followed by
+    pa_paged_attention_fp8 beside it."""
+    import torch
+
+    import paged_kv_cache_425_amd as pk
+    from workloads import make_config
+    dev = torch.device("cuda:0")
+    w = make_config(args.config, seed=args.seed, block_size=args.block_size, variant=args.variant)
+    if w.dtype != "bf16":
+        print("the FP8 step needs a bf16 workload", file=sys.stderr)
+        return 2
+    log(f"workload {w.name} (FP8 K/V): S={w.num_seqs} Hq={w.num_heads} Hkv={w.num_kv_heads} "
+        f"D={w.head_dim} BS={w.block_size} NB={w.num_blocks} max_len={w.max_context_len}")
+
+    def up(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    new = np.array([w.seq_records[s][-1] for s in range(w.num_seqs)], dtype=np.int64)
+    hist = np.setdiff1d(np.arange(len(w.rec_slot)), new)
+    kshape = (w.num_blocks, w.num_kv_heads, w.head_dim // 16, w.block_size, 16)
+    vshape = (w.num_blocks, w.num_kv_heads, w.head_dim, w.block_size)
+    kc0 = torch.full(kshape, 0x7F, dtype=torch.uint8, device=dev)     # NaN codes
+    vc0 = torch.full(vshape, 0x7F, dtype=torch.uint8, device=dev)
+    pk.reshape_and_cache_fp8(up(w.rec_key[hist]), up(w.rec_value[hist]),
+                             torch.from_numpy(w.rec_slot[hist]).to(dev), kc0, vc0,
+                             FP8_K_SCALE, FP8_V_SCALE)
+    pools = [(kc0, vc0)] + [(kc0.clone(), vc0.clone()) for _ in range(max(1, args.replicas) - 1)]
+    key_new, val_new = up(w.rec_key[new]), up(w.rec_value[new])
+    slot_new = torch.from_numpy(w.rec_slot[new]).to(dev)
+    query = up(w.query)
+    table = torch.from_numpy(w.block_table).to(dev)
+    lens = torch.from_numpy(w.context_lens).to(dev)
+    out = torch.empty_like(query)
+    part = args.partition_size if args.partition_size is not None else (w.partition_size or 0)
+    need = pk.workspace_size(w.num_seqs, w.num_heads, w.num_kv_heads, w.head_dim,
+                             w.max_context_len, part, torch.bfloat16)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+    fused = [pk.prepare_decode_step_fp8(query, key_new, val_new, slot_new, table, lens, kc, vc,
+                                        w.scale, FP8_K_SCALE, FP8_V_SCALE,
+                                        max_context_len=w.max_context_len, out=out,
+                                        partition_size=part, workspace=ws) for kc, vc in pools]
+    writes = [pk.prepare_reshape_and_cache_fp8(key_new, val_new, slot_new, kc, vc, FP8_K_SCALE,
+                                               FP8_V_SCALE) for kc, vc in pools]
+    decodes = [pk.prepare_paged_attention_fp8(query, table, lens, kc, vc, w.scale, FP8_K_SCALE,
+                                              FP8_V_SCALE, max_context_len=w.max_context_len,
+                                              out=out, partition_size=part, workspace=ws)
+               for kc, vc in pools]
+    R, K, W = len(pools), args.steps, args.warmup
+
+    def run_fused(steps: int) -> None:
+        for i in range(steps):
+            fused[i % R]()
+
+    def run_two_calls(steps: int) -> None:
+        for i in range(steps):
+            writes[i % R]()
+            decodes[i % R]()
+
+    def timed(fn, steps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        e0.record()
+        fn(steps)
+        e1.record()
+        torch.cuda.synchronize()
+        return time.perf_counter() - t0, e0.elapsed_time(e1) * 1e-3
+
+    run_fused(W)
+    wall, ev = timed(run_fused, K)
+    log(f"FP8 fused step: {wall / K * 1e6:.1f} us/step wall, {ev / K * 1e6:.1f} us/launch "
+        "(events)")
+    run_two_calls(W)
+    wall2, ev2 = timed(run_two_calls, K)
+    log(f"FP8 two-call step: {wall2 / K * 1e6:.1f} us/step wall")
+
+    lens64 = w.context_lens.astype(np.int64)
+    kv = int(lens64.sum()) * 2 * w.num_kv_heads * w.head_dim            # 1 byte per element
+    q = w.num_seqs * w.num_heads * w.head_dim * 2
+    table_b = int((-(-lens64 // w.block_size)).sum()) * 4
+    new_in = w.num_seqs * 2 * w.num_kv_heads * w.head_dim * 2            # bf16 new K and V
+    new_out = w.num_seqs * 2 * w.num_kv_heads * w.head_dim               # their codes
+    fused_bytes = kv + 2 * q + table_b + 4 * w.num_seqs + new_in + new_out + 8 * w.num_seqs
+    ms_step = wall / K * 1e3
+    value = kv / (ms_step * 1e-3) / 1e9
+    achieved = fused_bytes / (ev / K) / 1e9
+    part_used = part or pk.default_partition_size(w.num_seqs, w.num_kv_heads, w.max_context_len,
+                                                  torch.bfloat16)
+    line = {
+        "metric": "paged-attn decode over FP8 (E4M3) K/V: KV GB/s + µs/step, "
+                  "Llama-3-8B shape, 1 GPU",
+        "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": W,
+        "ms_per_step": round(ms_step, 5), "us_per_step": round(ms_step * 1e3, 2),
+        "hbm_frac": round(value / HBM_PEAK_GBS, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp8-e4m3 K/V, bf16 query/out, f32 accumulation",
+        "data": "synthetic (seeded N(0,1) q/K/V, random block tables)",
+        "config": {"workload": w.name + "-fp8", "num_seqs": w.num_seqs,
+                   "num_heads": w.num_heads, "num_kv_heads": w.num_kv_heads,
+                   "head_dim": w.head_dim, "block_size": w.block_size,
+                   "max_context_len": w.max_context_len, "partition_size": part_used,
+                   "k_scale": FP8_K_SCALE, "v_scale": FP8_V_SCALE, "kv_bytes_per_step": kv,
+                   "step": "pa_decode_step_fp8: quantised scatter of the new tokens + paged "
+                           "decode, one launch",
+                   "pool_bytes_each": int(kc0.numel()), "pool_replicas": R,
+                   "parallelism": "none (1 GPU)"},
+        "launch_us_events": round(ev / K * 1e6, 2),
+        "two_call_step": {"us_per_step": round(wall2 / K * 1e6, 2),
+                          "us_per_step_events": round(ev2 / K * 1e6, 2),
+                          "value": round(kv / (wall2 / K) / 1e9, 2)},
+        "roofline": {"kernel": "pa_decode_step_fp8: paged_decode_kernel<bf16, e4m3>",
+                     "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": load_traffic(w.name + "-fp8", FP8_TRAFFIC_FILE),
+                     "algorithmic_bytes_per_launch": fused_bytes},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle, FP8) ...")
+        line["cpu_baseline"] = cpu_baseline_fp8(w, args.cpu_budget)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def main() -> int:
     args = parse_args()
     if args.gpus != 1:
@@ -330,6 +498,8 @@ def main() -> int:
         return bench_copy_blocks(args)
     if args.op == "prefill":
         return bench_prefill(args)
+    if args.op == "fp8":
+        return bench_fp8(args)
     dev = torch.device("cuda:0")
 
     t = time.perf_counter()

@@ -233,6 +233,73 @@ pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_mapp
                          int num_blocks, pa_dtype dtype, void* stream);
 
 /*
+ * FP8 K/V cache.  The pages list FP8 E4M3 as an 8-bit float precision that
+ * needs about half the memory of 16-bit formats (page "vLLM core features",
+ * section 4.3, the table of quantisation formats); here it is the storage
+ * format of the K/V pools, which halves the bytes a decode step reads.
+ *
+ * Format: OCP FP8 E4M3 codes, one byte per element (bias 7, subnormals
+ * m * 2^-9, S.1111.111 = NaN, no infinities, largest finite 448).  One scale
+ * per tensor: the stored code of a K element x is the E4M3 value nearest to
+ * the float32 quotient x / k_scale (ties to the even code; magnitudes above
+ * 448 and infinities saturate to +-448; a NaN x gives the NaN code with the
+ * sign of x), and it reads back as
+ * E4M3(code) * k_scale; likewise V with v_scale.  k_scale and v_scale must be
+ * finite and > 0 (else PA_ERR_INVALID_ARG).
+ *
+ * Layout: the pools above with 1-byte elements, so X = 16:
+ *   k_cache: [num_blocks][num_kv_heads][D / 16][BS][16] uint8
+ *   v_cache: [num_blocks][num_kv_heads][D][BS] uint8
+ */
+
+/*
+ * Write path into FP8 pools: quantise each new token's K and V (given in
+ * dtype, f32 or bf16) with k_scale / v_scale and store the codes in its slot.
+ * Slots as in pa_reshape_and_cache (negative or past the pool: skipped).
+ * The codes are bit-exact functions of the inputs and scales.
+ */
+pa_status pa_reshape_and_cache_fp8(const void* key, const void* value,
+                                   const int64_t* slot_mapping, void* k_cache, void* v_cache,
+                                   int num_tokens, int num_kv_heads, int head_dim,
+                                   int block_size, int num_blocks, pa_dtype dtype,
+                                   float k_scale, float v_scale, void* stream);
+
+/*
+ * Decode attention over FP8 pools: the result of pa_paged_attention over the
+ * dequantised K and V.  query and out are bf16 (dtype must be PA_DTYPE_BF16;
+ * f32 returns PA_ERR_UNSUPPORTED).  The codes are widened to bf16 exactly on
+ * load; k_scale joins the softmax scale and v_scale multiplies the output.
+ * partition_size, when not 0, must also be a multiple of 64; the workspace is
+ * sized by pa_paged_attention_workspace_size with dtype PA_DTYPE_BF16.  Other
+ * arguments as in pa_paged_attention.
+ */
+pa_status pa_paged_attention_fp8(void* out, const void* query, const int32_t* block_table,
+                                 const int32_t* context_lens, const void* k_cache,
+                                 const void* v_cache, int num_seqs, int num_heads,
+                                 int num_kv_heads, int head_dim, int block_size,
+                                 int max_blocks_per_seq, int num_blocks, int max_context_len,
+                                 float scale, float k_scale, float v_scale, pa_dtype dtype,
+                                 int partition_size, void* workspace, size_t workspace_bytes,
+                                 void* stream);
+
+/*
+ * One decode step over FP8 pools in a single launch: quantise each sequence's
+ * new token (bf16 key/value, with k_scale / v_scale, codes identical to
+ * pa_reshape_and_cache_fp8) into its slot, then decode attention as
+ * pa_paged_attention_fp8 over the pools that now hold it.  The result is the
+ * same as those two calls in a row.  Slot rules and preconditions as in
+ * pa_decode_step; other arguments as in pa_paged_attention_fp8.
+ */
+pa_status pa_decode_step_fp8(void* out, const void* query, const void* key, const void* value,
+                             const int64_t* slot_mapping, const int32_t* block_table,
+                             const int32_t* context_lens, void* k_cache, void* v_cache,
+                             int num_seqs, int num_heads, int num_kv_heads, int head_dim,
+                             int block_size, int max_blocks_per_seq, int num_blocks,
+                             int max_context_len, float scale, float k_scale, float v_scale,
+                             pa_dtype dtype, int partition_size, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
+/*
  * Diagnostic read path: reassemble every sequence's K and V through its block
  * table into contiguous token-major arrays (bit-exact copies).
  *

@@ -21,8 +21,9 @@ plainest reading of an FP8 K/V cache:
 * Writing (quantising) element x: q = x / scale rounded to float32 (the
   precision the write kernel divides in), then the E4M3 value nearest to q,
   ties to the code with the even last bit.  Magnitudes above 448 and
-  infinities saturate to +-448; NaN stays NaN (code 0x7F or 0xFF by sign);
-  -0 keeps its sign.
+  infinities saturate to +-448; -0 keeps its sign.  A NaN element stays NaN
+  with the sign of the element itself (code 0x7F or 0xFF): IEEE 754 leaves
+  the sign of a NaN quotient open, so the code is fixed before the division.
 * Reading (dequantising) code c: E4M3(c) * scale.  The product has at most
   4 + 24 significant bits, so float64 holds it exactly.
 * Attention over an FP8 cache is attention over the dequantised K and V.
@@ -65,7 +66,6 @@ def e4m3_values() -> np.ndarray:
 
 _VALUES = e4m3_values()
 # the non-negative finite codes 0x00 .. 0x7E in increasing value order
-_POS_CODES = np.arange(0x7F, dtype=np.int64)
 _POS_VALUES = _VALUES[:0x7F]
 
 
@@ -77,37 +77,31 @@ def e4m3_decode(codes: np.ndarray) -> np.ndarray:
 def e4m3_encode(q: np.ndarray) -> np.ndarray:
     """E4M3 codes (uint8) of float32 values: nearest, ties to even code, saturating."""
     q = np.asarray(q, dtype=np.float32).astype(np.float64)
-    flat = q.reshape(-1)
-    out = np.empty(flat.shape, dtype=np.uint8)
-    for i, x in enumerate(flat):
-        neg = bool(np.signbit(x))
-        if np.isnan(x):
-            out[i] = 0xFF if neg else 0x7F
-            continue
-        a = abs(x)
-        if a >= FP8_MAX:                               # includes +-inf
-            code = 0x7E
-        else:
-            # the two codes around a: lo with value <= a < value of lo + 1
-            lo = int(np.searchsorted(_POS_VALUES, a, side="right")) - 1
-            hi = lo + 1
-            dlo = a - _POS_VALUES[lo]
-            dhi = _POS_VALUES[hi] - a
-            if dlo < dhi:
-                code = lo
-            elif dhi < dlo:
-                code = hi
-            else:
-                code = lo if lo % 2 == 0 else hi       # tie: the even code
-        out[i] = code | (0x80 if neg else 0)
-    return out.reshape(q.shape)
+    neg = np.signbit(q)
+    nan = np.isnan(q)
+    a = np.where(nan, 0.0, np.abs(q))
+    # the two codes around a: lo with value <= a < value of lo + 1 (a < 448 here)
+    lo = np.clip(np.searchsorted(_POS_VALUES, a, side="right") - 1, 0, 0x7D)
+    hi = lo + 1
+    dlo = a - _POS_VALUES[lo]
+    dhi = _POS_VALUES[hi] - a
+    tie_code = np.where(lo % 2 == 0, lo, hi)               # tie: the even code
+    code = np.where(dlo < dhi, lo, np.where(dhi < dlo, hi, tie_code))
+    code = np.where(a >= FP8_MAX, 0x7E, code)              # saturate (and +-inf)
+    code = np.where(nan, 0x7F, code)
+    code = code | np.where(neg, 0x80, 0)
+    return code.astype(np.uint8)
 
 
 def quantize(x: np.ndarray, dtype: str, scale: float) -> np.ndarray:
     """Codes of elements x (float32 array or bfloat16 bits) stored with ``scale``."""
     xf = decode(x, dtype).astype(np.float32)           # exact: the inputs are float32 or bf16
-    q = xf / np.float32(scale)                         # float32 division, correctly rounded
-    return e4m3_encode(q)
+    with np.errstate(invalid="ignore", over="ignore"):
+        q = xf / np.float32(scale)                     # float32 division, correctly rounded
+    codes = e4m3_encode(q)
+    nan = np.isnan(xf)
+    codes[nan] = np.where(np.signbit(xf[nan]), 0xFF, 0x7F)   # the element's own sign
+    return codes
 
 
 def empty_fp8_pools(num_blocks: int, num_kv_heads: int, head_dim: int, block_size: int,

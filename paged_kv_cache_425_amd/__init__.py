@@ -4,14 +4,16 @@ The work runs in hand-written HIP kernels behind a C ABI (include/pagedattn.h);
 this package only marshals torch tensors to it.
 """
 from .binding import (LIB_PATH, PreparedCall, chunk_elems, copy_blocks, decode_step,
-                      default_partition_size, prepare_copy_blocks,
-                      gather_kv, k_cache_shape, load_library, paged_attention, paged_prefill,
-                      prepare_decode_step, prepare_paged_attention, prepare_reshape_and_cache,
-                      reshape_and_cache, v_cache_shape, workspace_size)
+                      decode_step_fp8, default_partition_size, gather_kv, k_cache_shape,
+                      load_library, prepare_decode_step_fp8, paged_attention, paged_attention_fp8, paged_prefill, prepare_copy_blocks,
+                      prepare_decode_step, prepare_paged_attention, prepare_paged_attention_fp8,
+                      prepare_reshape_and_cache, prepare_reshape_and_cache_fp8, reshape_and_cache,
+                      reshape_and_cache_fp8, v_cache_shape, workspace_size)
 
-__all__ = ["LIB_PATH", "PreparedCall", "copy_blocks", "prepare_copy_blocks", "decode_step",
-           "prepare_decode_step",
-           "prepare_paged_attention", "prepare_reshape_and_cache",
-           "chunk_elems", "default_partition_size", "gather_kv", "k_cache_shape",
-           "load_library", "paged_attention", "paged_prefill", "reshape_and_cache", "v_cache_shape",
-           "workspace_size"]
+__all__ = ["LIB_PATH", "PreparedCall", "chunk_elems", "copy_blocks", "decode_step",
+           "decode_step_fp8", "prepare_decode_step_fp8",
+           "default_partition_size", "gather_kv", "k_cache_shape", "load_library",
+           "paged_attention", "paged_attention_fp8", "paged_prefill", "prepare_copy_blocks",
+           "prepare_decode_step", "prepare_paged_attention", "prepare_paged_attention_fp8",
+           "prepare_reshape_and_cache", "prepare_reshape_and_cache_fp8", "reshape_and_cache",
+           "reshape_and_cache_fp8", "v_cache_shape", "workspace_size"]

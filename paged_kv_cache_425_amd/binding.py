@@ -51,6 +51,13 @@ def load_library() -> ctypes.CDLL:
     lib.pa_copy_blocks.argtypes = [vp] * 3 + [i32] * 6 + [vp]
     lib.pa_gather_kv.restype = i32
     lib.pa_gather_kv.argtypes = [vp] * 7 + [i32] * 8 + [vp]
+    lib.pa_reshape_and_cache_fp8.restype = i32
+    lib.pa_reshape_and_cache_fp8.argtypes = [vp] * 5 + [i32] * 6 + [f32, f32, vp]
+    lib.pa_decode_step_fp8.restype = i32
+    lib.pa_decode_step_fp8.argtypes = [vp] * 9 + [i32] * 8 + [f32] * 3 + [i32, i32, vp, sz, vp]
+    lib.pa_paged_attention_fp8.restype = i32
+    lib.pa_paged_attention_fp8.argtypes = [vp] * 6 + [i32] * 8 + [f32] * 3 + [i32, i32, vp, sz,
+                                                                              vp]
     _lib = lib
     return lib
 
@@ -240,6 +247,121 @@ def reshape_and_cache(key: torch.Tensor, value: torch.Tensor, slot_mapping: torc
     _check(st, "pa_reshape_and_cache")
 
 
+# ---------------------------------------------------------------------------
+# FP8 (E4M3) pools: uint8 tensors of codes, one scale per tensor (see pagedattn.h)
+# ---------------------------------------------------------------------------
+def _fp8_cache_dims(k_cache: torch.Tensor, v_cache: torch.Tensor):
+    if k_cache.dtype != torch.uint8 or v_cache.dtype != torch.uint8:
+        raise TypeError("FP8 pools are uint8 tensors of E4M3 codes")
+    return _cache_dims(k_cache, v_cache)
+
+
+def _reshape_fp8_args(key, value, slot_mapping, k_cache, v_cache, k_scale, v_scale, stream):
+    dev = key.device
+    NB, Hkv, D, BS = _fp8_cache_dims(k_cache, v_cache)
+    _require(key, "key", dev)
+    _require(value, "value", dev, key.dtype)
+    _require(k_cache, "k_cache", dev)
+    _require(v_cache, "v_cache", dev)
+    _require(slot_mapping, "slot_mapping", dev, torch.int64)
+    T = key.shape[0]
+    if tuple(key.shape) != (T, Hkv, D) or tuple(value.shape) != (T, Hkv, D) or \
+            tuple(slot_mapping.shape) != (T,):
+        raise ValueError(f"key/value must be [T, {Hkv}, {D}] and slot_mapping [T]")
+    return (_ptr(key), _ptr(value), _ptr(slot_mapping), _ptr(k_cache), _ptr(v_cache), T, Hkv,
+            D, BS, NB, _dtype_code(key), float(k_scale), float(v_scale), _stream(dev, stream))
+
+
+def reshape_and_cache_fp8(key: torch.Tensor, value: torch.Tensor, slot_mapping: torch.Tensor,
+                          k_cache: torch.Tensor, v_cache: torch.Tensor, k_scale: float,
+                          v_scale: float, stream=None) -> None:
+    """Quantise key/value [T, Hkv, D] (f32 or bf16) into the FP8 pools at slot_mapping [T]."""
+    args = _reshape_fp8_args(key, value, slot_mapping, k_cache, v_cache, k_scale, v_scale,
+                             stream)
+    _check(load_library().pa_reshape_and_cache_fp8(*args), "pa_reshape_and_cache_fp8")
+
+
+def _attention_fp8_args(query, block_table, context_lens, k_cache, v_cache, scale, k_scale,
+                        v_scale, max_context_len, out, partition_size, workspace, stream):
+    dev = query.device
+    NB, Hkv, D, BS = _fp8_cache_dims(k_cache, v_cache)
+    _require(query, "query", dev)
+    _require(k_cache, "k_cache", dev)
+    _require(v_cache, "v_cache", dev)
+    _require(block_table, "block_table", dev, torch.int32)
+    _require(context_lens, "context_lens", dev, torch.int32)
+    if query.dim() != 3 or query.shape[2] != D:
+        raise ValueError(f"query must be [S, Hq, {D}], got {tuple(query.shape)}")
+    S, Hq, _ = query.shape
+    if block_table.dim() != 2 or block_table.shape[0] != S or tuple(context_lens.shape) != (S,):
+        raise ValueError("block_table must be [S, MB] and context_lens [S]")
+    if out is None:
+        out = torch.empty_like(query)
+    _require(out, "out", dev, query.dtype)
+    if tuple(out.shape) != tuple(query.shape):
+        raise ValueError("out must have the shape of query")
+    need = workspace_size(S, Hq, Hkv, D, max_context_len, partition_size, torch.bfloat16)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    if workspace is not None:
+        _require(workspace, "workspace", dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    args = (_ptr(out), _ptr(query), _ptr(block_table), _ptr(context_lens), _ptr(k_cache),
+            _ptr(v_cache), S, Hq, Hkv, D, BS, block_table.shape[1], NB, int(max_context_len),
+            float(scale), float(k_scale), float(v_scale), _dtype_code(query),
+            int(partition_size), _ptr(workspace), ws_bytes, _stream(dev, stream))
+    keep = (query, block_table, context_lens, k_cache, v_cache, out, workspace)
+    return args, out, keep
+
+
+def paged_attention_fp8(query: torch.Tensor, block_table: torch.Tensor,
+                        context_lens: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                        scale: float, k_scale: float, v_scale: float, *, max_context_len: int,
+                        out: torch.Tensor | None = None, partition_size: int = 0,
+                        workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Decode attention of bf16 query [S, Hq, D] over FP8 pools (see pagedattn.h)."""
+    args, out, _ = _attention_fp8_args(query, block_table, context_lens, k_cache, v_cache, scale,
+                                       k_scale, v_scale, max_context_len, out, partition_size,
+                                       workspace, stream)
+    _check(load_library().pa_paged_attention_fp8(*args), "pa_paged_attention_fp8")
+    return out
+
+
+def _decode_step_fp8_args(query, key, value, slot_mapping, block_table, context_lens, k_cache,
+                          v_cache, scale, k_scale, v_scale, max_context_len, out,
+                          partition_size, workspace, stream):
+    dev = query.device
+    NB, Hkv, D, BS = _fp8_cache_dims(k_cache, v_cache)
+    S = query.shape[0] if query.dim() == 3 else -1
+    for t, name in ((key, "key"), (value, "value")):
+        _require(t, name, dev, query.dtype)
+    _require(slot_mapping, "slot_mapping", dev, torch.int64)
+    if tuple(key.shape) != (S, Hkv, D) or tuple(value.shape) != (S, Hkv, D) or \
+            tuple(slot_mapping.shape) != (S,):
+        raise ValueError(f"key/value must be [{S}, {Hkv}, {D}] and slot_mapping [{S}]")
+    args, out, keep = _attention_fp8_args(query, block_table, context_lens, k_cache, v_cache,
+                                          scale, k_scale, v_scale, max_context_len, out,
+                                          partition_size, workspace, stream)
+    # pa_decode_step_fp8 takes key, value and slot_mapping after query
+    args = args[:2] + (_ptr(key), _ptr(value), _ptr(slot_mapping)) + args[2:]
+    return args, out, keep + (key, value, slot_mapping)
+
+
+def decode_step_fp8(query: torch.Tensor, key: torch.Tensor, value: torch.Tensor,
+                    slot_mapping: torch.Tensor, block_table: torch.Tensor,
+                    context_lens: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                    scale: float, k_scale: float, v_scale: float, *, max_context_len: int,
+                    out: torch.Tensor | None = None, partition_size: int = 0,
+                    workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """One fused step over FP8 pools: quantise key/value [S, Hkv, D] (bf16) into
+    slot_mapping [S], then decode attention of query [S, Hq, D] (see pa_decode_step_fp8)."""
+    args, out, _ = _decode_step_fp8_args(query, key, value, slot_mapping, block_table,
+                                         context_lens, k_cache, v_cache, scale, k_scale, v_scale,
+                                         max_context_len, out, partition_size, workspace, stream)
+    _check(load_library().pa_decode_step_fp8(*args), "pa_decode_step_fp8")
+    return out
+
+
 def paged_prefill(query: torch.Tensor, query_start_loc: torch.Tensor, block_table: torch.Tensor,
                   context_lens: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                   scale: float, *, max_query_len: int, out: torch.Tensor | None = None,
@@ -392,5 +514,44 @@ def prepare_decode_step(query, key, value, slot_mapping, block_table, context_le
                                         context_lens, k_cache, v_cache, scale, max_context_len,
                                         out, partition_size, workspace, stream)
     call = PreparedCall(lib.pa_decode_step, args, "pa_decode_step", keep)
+    call()
+    return call
+
+
+def prepare_reshape_and_cache_fp8(key, value, slot_mapping, k_cache, v_cache, k_scale, v_scale,
+                                  stream=None) -> PreparedCall:
+    """Check the arguments of reshape_and_cache_fp8 once and return a re-launchable call."""
+    args = _reshape_fp8_args(key, value, slot_mapping, k_cache, v_cache, k_scale, v_scale,
+                             stream)
+    call = PreparedCall(load_library().pa_reshape_and_cache_fp8, args,
+                        "pa_reshape_and_cache_fp8", (key, value, slot_mapping, k_cache, v_cache))
+    call()
+    return call
+
+
+def prepare_paged_attention_fp8(query, block_table, context_lens, k_cache, v_cache, scale,
+                                k_scale, v_scale, *, max_context_len: int, out,
+                                partition_size: int = 0, workspace=None,
+                                stream=None) -> PreparedCall:
+    """Check the arguments of paged_attention_fp8 once and return a re-launchable call."""
+    args, out, keep = _attention_fp8_args(query, block_table, context_lens, k_cache, v_cache,
+                                          scale, k_scale, v_scale, max_context_len, out,
+                                          partition_size, workspace, stream)
+    call = PreparedCall(load_library().pa_paged_attention_fp8, args, "pa_paged_attention_fp8",
+                        keep)
+    call()
+    return call
+
+
+def prepare_decode_step_fp8(query, key, value, slot_mapping, block_table, context_lens, k_cache,
+                            v_cache, scale, k_scale, v_scale, *, max_context_len: int, out,
+                            partition_size: int = 0, workspace=None,
+                            stream=None) -> PreparedCall:
+    """Check the arguments of decode_step_fp8 once and return a re-launchable call."""
+    args, out, keep = _decode_step_fp8_args(query, key, value, slot_mapping, block_table,
+                                            context_lens, k_cache, v_cache, scale, k_scale,
+                                            v_scale, max_context_len, out, partition_size,
+                                            workspace, stream)
+    call = PreparedCall(load_library().pa_decode_step_fp8, args, "pa_decode_step_fp8", keep)
     call()
     return call

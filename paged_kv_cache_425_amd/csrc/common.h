@@ -57,4 +57,44 @@ struct ElemTraits<float> {
   static constexpr bool kBf16 = false;
 };
 
+template <>
+struct ElemTraits<uint8_t> {             // OCP FP8 E4M3 codes (K/V cache storage only)
+  static constexpr int kBytes = 1;
+  static constexpr int kX = 16;
+  static constexpr bool kBf16 = false;
+};
+
+// ---- FP8 E4M3 (OCP): 1 sign, 4 exponent bits (bias 7), 3 mantissa bits; exponent field 0
+// holds subnormals m * 2^-9; S.1111.111 is NaN; no infinities; largest finite 448. ----
+
+// Code of a float32 value: nearest E4M3 value, ties to the even code; magnitudes above 448
+// and infinities saturate to +-448; NaN keeps its sign as S.1111.111.  Branch-free: both
+// the subnormal and the normal candidate are formed (clamped, so no conversion leaves its
+// range) and the right one is selected.
+__device__ __forceinline__ uint32_t e4m3_code(float q) {
+  const uint32_t sign = (__float_as_uint(q) >> 24) & 0x80u;
+  const float a = fabsf(q);
+  // below 2^-6 the grid is 2^-9: code = round(a * 2^9), 0 .. 8 (8 = smallest normal)
+  const uint32_t sub = static_cast<uint32_t>(fminf(rintf(a * 512.f), 8.f));
+  // normal: a = 2^e * (m / 8) with m in [8, 16]; m = 16 carries into the exponent
+  const int e = min(max(static_cast<int>((__float_as_uint(a) >> 23) & 0xFFu) - 127, -6), 8);
+  const uint32_t m = static_cast<uint32_t>(fminf(rintf(ldexpf(a, 3 - e)), 16.f));
+  const uint32_t nrm = static_cast<uint32_t>(e + 7) * 8u + m - 8u;
+  uint32_t code = a < 0.015625f ? sub : nrm;
+  code = a >= 448.f ? 0x7Eu : code;                      // saturate (and +-inf)
+  code = (a == a) ? code : 0x7Fu;                        // NaN
+  return sign | code;
+}
+
+// Eight E4M3 codes (bytes of w0 then w1, lowest byte first) as an MFMA bf16 operand.
+// Every E4M3 value is a bfloat16 value, so the conversion (scale 1) is exact.
+__device__ __forceinline__ bf16x8 e4m3x8_to_bf16x8(uint32_t w0, uint32_t w1) {
+  u32x4 r;
+  r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.f, false));
+  r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.f, true));
+  r[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.f, false));
+  r[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.f, true));
+  return __builtin_bit_cast(bf16x8, r);
+}
+
 }  // namespace pa

@@ -76,7 +76,9 @@ struct DecodeParams {
   const void* new_v;
   const int64_t* new_slot;
   int S, Hq, Hkv, g, MB, NB, P, Pmax;
-  float scale_log2;        // scale * log2(e): logits are kept in base-2 units
+  float scale_log2;        // scale * log2(e) (* k_scale for FP8 K): base-2 logits
+  float v_scale;           // output multiplier: 1, or the FP8 V scale
+  float k_quant, v_quant;  // FP8 fused step: the scales the new token is quantised with
 };
 
 // Context length clamped to what the launch can address.
@@ -87,22 +89,27 @@ __device__ __forceinline__ int clamped_len(const DecodeParams& a, int s, int BS)
   return L > cap ? (int)cap : L;
 }
 
-// Per-step shape constants for an element type.
-template <typename T, int D>
+// Per-step shape constants for a query/output type T and a cache element type C (C = T,
+// or uint8_t for FP8 E4M3 codes, which need bf16 queries).
+template <typename T, typename C, int D>
 struct StepShape {
   static constexpr bool kBf16 = ElemTraits<T>::kBf16;
-  static constexpr int kX = ElemTraits<T>::kX;
-  static constexpr int kStep = kBf16 ? 32 : 16;     // tokens per step
-  static constexpr int kTpl = kBf16 ? 8 : 4;        // logits per lane per step
-  static constexpr int kTiles = kBf16 ? 2 : 1;      // 16-row K tiles per step
-  static constexpr int kNc = D / (kBf16 ? 32 : 16); // 16-byte K chunks per lane per tile
+  static constexpr bool kFp8 = sizeof(C) == 1;
+  static constexpr int kX = ElemTraits<C>::kX;      // cache elements per 16-byte chunk
+  static constexpr int kStep = kFp8 ? 64 : (kBf16 ? 32 : 16);   // tokens per step
+  static constexpr int kTpl = kStep / 4;            // logits per lane per step
+  static constexpr int kTiles = kStep / 16;         // 16-row K tiles per step
+  // 16-byte K chunks per lane per tile, and Q operands (MFMAs per tile)
+  static constexpr int kNc = kFp8 ? D / 64 : D / (kBf16 ? 32 : 16);
+  static constexpr int kNq = kFp8 ? D / 32 : kNc;
   static constexpr int kNs = D / 16;                // 16-channel slices of the output
+  static_assert(!kFp8 || kBf16, "an FP8 cache is read with bf16 queries");
 };
 
 // The K and V operands of one step, as loaded.
-template <typename T, int D>
+template <typename T, typename C, int D>
 struct StepData {
-  using Sh = StepShape<T, D>;
+  using Sh = StepShape<T, C, D>;
   u32x4 k[Sh::kTiles][Sh::kNc];
   u32x4 v[Sh::kNs];
 };
@@ -119,15 +126,17 @@ __host__ __device__ constexpr int merge_words(int D, int g) { return 32 + g * me
 // workgroup (identically), by counting for each sequence the sequences that
 // are longer (ties broken by index).  Used when each sequence is one
 // partition; otherwise a workgroup is one (kv head, sequence, partition).
-template <typename T, int D, int BS, int NW, int PIPE, bool PAIRED>
+template <typename T, typename C, int D, int BS, int NW, int PIPE, bool PAIRED>
 __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(PA_DECODE_OCC)))
 paged_decode_kernel(const DecodeParams a) {
-  using Sh = StepShape<T, D>;
+  using Sh = StepShape<T, C, D>;
   constexpr bool kBf16 = Sh::kBf16;
+  constexpr bool kFp8 = Sh::kFp8;
   constexpr int kX = Sh::kX;
   constexpr int kStep = Sh::kStep;
   constexpr int kTpl = Sh::kTpl;
   constexpr int kNc = Sh::kNc;
+  constexpr int kNq = Sh::kNq;
   constexpr int kNs = Sh::kNs;
   constexpr int kThreads = NW * 64;
 
@@ -234,13 +243,15 @@ paged_decode_kernel(const DecodeParams a) {
   // Fused step: this workgroup's units' new tokens (kv head kvh).  Only the workgroup
   // that reads a sequence's last position L - 1 handles its new token (the last
   // partition, or the pair holding the sequence).  Thread t below 2 * kCh * units holds
-  // one 16-byte chunk of it and copies the chunk to LDS.  When the token's slot is where
-  // the decode reads position L - 1 (the usual case), the step covering that position
-  // substitutes the LDS copy for what the cache returned and writes the patched K row
-  // chunks and 8-token V chunks back -- after its own loads brought those lines in, so
-  // the stores do not miss.  Any other valid slot (read by no sequence of the call) is
-  // stored after the barrier below.
-  constexpr int kCh = D / kX;                               // 16-byte chunks per head
+  // one 16-byte chunk of it and copies the chunk to LDS (FP8 pools: it quantises the
+  // chunk's 8 elements to E4M3 codes first, exactly as the FP8 write kernel does, and
+  // LDS holds the codes).  When the token's slot is where the decode reads position
+  // L - 1 (the usual case), the step covering that position substitutes the LDS copy for
+  // what the cache returned and writes the patched K row chunks and V token chunks back
+  // -- after its own loads brought those lines in, so the stores do not miss.  Any other
+  // valid slot (read by no sequence of the call) is stored after the barrier below.
+  constexpr int kSx = ElemTraits<T>::kX;                    // new-token elements per 16 bytes
+  constexpr int kCh = D / kSx;                              // 16-byte new-token chunks per head
   const bool fused = a.new_slot != nullptr;
   const bool last_part = p == nparts - 1;
   const int nun_new = !fused ? 0 : (PAIRED ? (sB >= 0 ? 2 : 1) : (last_part ? 1 : 0));
@@ -252,19 +263,38 @@ paged_decode_kernel(const DecodeParams a) {
   if ((int)threadIdx.x < nun_new * 2 * kCh) {
     new_u = threadIdx.x / (2 * kCh);
     const int su = PAIRED ? (new_u ? sB : sA) : s;
-    const size_t src = ((size_t)su * a.Hkv + kvh) * D + (size_t)new_cc * kX;
+    const size_t src = ((size_t)su * a.Hkv + kvh) * D + (size_t)new_cc * kSx;
     new_val = load16(static_cast<const T*>(new_is_v ? a.new_v : a.new_k) + src);
-    store16(newkv + (2 * new_u + (new_is_v ? 1 : 0)) * D + new_cc * kX, new_val);
+    if constexpr (kFp8) {
+      // 8 bf16 elements -> 8 codes (words 0 and 1 of new_val); a NaN keeps its sign
+      const float sc = new_is_v ? a.v_quant : a.k_quant;
+      uint32_t w[2] = {0u, 0u};
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const uint32_t h = new_val[k >> 1];
+        const float x = __uint_as_float((k & 1) ? (h & 0xFFFF0000u) : (h << 16));
+        const uint32_t code = x != x ? (((__float_as_uint(x) >> 24) & 0x80u) | 0x7Fu)
+                                     : e4m3_code(__fdiv_rn(x, sc));
+        w[k >> 2] |= code << (8 * (k & 3));
+      }
+      new_val = u32x4{w[0], w[1], 0u, 0u};
+      *reinterpret_cast<uint2*>(smem + 64 + (2 * new_u + (new_is_v ? 1 : 0)) * D + new_cc * 8) =
+          make_uint2(w[0], w[1]);
+    } else {
+      store16(newkv + (2 * new_u + (new_is_v ? 1 : 0)) * D + new_cc * kX, new_val);
+    }
     new_slot = a.new_slot[su];
   }
 
   // Query operand: lane (n, j) holds head-row n's channels of the chunks it multiplies.
+  // FP8: K chunk j + 4c' (16 channels) feeds MFMAs 2c' and 2c' + 1 (8 channels each).
   const T* qrow = static_cast<const T*>(a.q) + ((size_t)s * a.Hq + head) * D;
-  u32x4 qop[kNc];
+  u32x4 qop[kNq];
 #pragma unroll
-  for (int c = 0; c < kNc; ++c) {
+  for (int c = 0; c < kNq; ++c) {
     const u32x4 z = {0u, 0u, 0u, 0u};
-    qop[c] = row_live && tok1 > tok0 ? load16(qrow + kX * (4 * c + j)) : z;
+    const int off = kFp8 ? 16 * (j + 4 * (c >> 1)) + 8 * (c & 1) : kX * (4 * c + j);
+    qop[c] = row_live && tok1 > tok0 ? load16(qrow + off) : z;
   }
   __syncthreads();
 
@@ -276,7 +306,7 @@ paged_decode_kernel(const DecodeParams a) {
 
   // position this wave takes from LDS and writes back (-1: none)
   int lm1 = -1;
-  if (uidx < nun_new && tok1 > tok0) {
+  if (fused && uidx < nun_new && tok1 > tok0) {
     const int64_t sl = a.new_slot[s];
     if (sl >= 0 && sl < nslots && sl == slot_of(tblw, tok0, tok1 - 1)) lm1 = tok1 - 1;
   }
@@ -287,7 +317,23 @@ paged_decode_kernel(const DecodeParams a) {
     const int Lu = PAIRED ? lens[new_u ? sB : sA] : tok1;
     const int64_t loc =
         Lu > 0 ? slot_of(PAIRED ? tbl + new_u * win : tbl, PAIRED ? 0 : tok0, Lu - 1) : -1;
-    if (new_slot != loc) {
+    if (new_slot != loc && kFp8) {
+      uint8_t* kcw = static_cast<uint8_t*>(const_cast<void*>(a.k_cache));
+      uint8_t* vcw = static_cast<uint8_t*>(const_cast<void*>(a.v_cache));
+      const size_t blk = (size_t)(new_slot / BS);
+      const int off = (int)(new_slot % BS);
+      const int d0 = new_cc * 8;                           // first channel of the 8 codes
+      if (!new_is_v) {
+        uint8_t* dst = kcw + (((blk * a.Hkv + kvh) * (D / 16) + d0 / 16) * BS + off) * 16 +
+                       d0 % 16;
+        *reinterpret_cast<uint2*>(dst) = make_uint2(new_val[0], new_val[1]);
+      } else {
+        uint8_t* dst = vcw + ((blk * a.Hkv + kvh) * D + (size_t)d0) * BS + off;
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+          dst[(size_t)k * BS] = static_cast<uint8_t>(new_val[k >> 2] >> (8 * (k & 3)));
+      }
+    } else if (new_slot != loc) {
       T* kcw = const_cast<T*>(static_cast<const T*>(a.k_cache));
       T* vcw = const_cast<T*>(static_cast<const T*>(a.v_cache));
       const size_t blk = (size_t)(new_slot / BS);
@@ -303,22 +349,23 @@ paged_decode_kernel(const DecodeParams a) {
     }
   }
 
-  const T* kc = static_cast<const T*>(a.k_cache);
-  const T* vc = static_cast<const T*>(a.v_cache);
+  const C* kc = static_cast<const C*>(a.k_cache);
+  const C* vc = static_cast<const C*>(a.v_cache);
   const size_t head_elems = (size_t)D * BS;          // elements of one (block, kv head)
 
   // ---- loads of one step ------------------------------------------------------
-  auto load_step = [&](int st, StepData<T, D>& b) {
+  auto load_step = [&](int st, StepData<T, C, D>& b) {
     const int base = tok0 + st * kStep;
 #pragma unroll
     for (int t = 0; t < Sh::kTiles; ++t) {
-      // K-tile row n: bf16 rows interleave the step as 8*(n/4) + 4*t + n%4 so that the
-      // score of lane (n, j), register e is token 8*j + 4*t + e; f32 rows are tokens n.
-      // Rows past the partition's end read the last live token instead (in bounds; their
-      // logits are masked to -inf).
-      const int tok = min(kBf16 ? base + 8 * (n >> 2) + 4 * t + (n & 3) : base + n, tok1 - 1);
+      // K-tile row n: bf16/FP8 rows interleave the step as kTpl*(n/4) + 4*t + n%4 so
+      // that the score of lane (n, j), register 4t + e is token kTpl*j + 4*t + e; f32
+      // rows are tokens n.  Rows past the partition's end read the last live token
+      // instead (in bounds; their logits are masked to -inf).
+      const int tok =
+          min(Sh::kTiles == 1 ? base + n : base + kTpl * (n >> 2) + 4 * t + (n & 3), tok1 - 1);
       const int phys = tblw[(tok - tok0) / BS];
-      const T* kp = kc + ((size_t)phys * a.Hkv + kvh) * head_elems + (size_t)j * BS * kX +
+      const C* kp = kc + ((size_t)phys * a.Hkv + kvh) * head_elems + (size_t)j * BS * kX +
                     (size_t)(tok % BS) * kX;
 #pragma unroll
       for (int c = 0; c < kNc; ++c) b.k[t][c] = load16(kp + (size_t)4 * c * BS * kX);
@@ -328,9 +375,22 @@ paged_decode_kernel(const DecodeParams a) {
     // before use).
     const int tokv = min(base + kTpl * j, (tok1 - 1) / kTpl * kTpl);
     const int physv = tblw[(tokv - tok0) / BS];
-    const T* vp = vc + ((size_t)physv * a.Hkv + kvh) * head_elems + (size_t)n * BS + (tokv % BS);
+    const C* vp = vc + ((size_t)physv * a.Hkv + kvh) * head_elems + (size_t)n * BS + (tokv % BS);
+    if constexpr (kFp8 && BS < 16) {
+      // 16 tokens span two blocks of 8: two 8-byte halves (the second clamped like tokv)
+      const int tokv2 = min(tokv + 8, (tok1 - 1) / 8 * 8);
+      const int physv2 = tblw[(tokv2 - tok0) / BS];
+      const C* vp2 = vc + ((size_t)physv2 * a.Hkv + kvh) * head_elems + (size_t)n * BS;
 #pragma unroll
-    for (int sl = 0; sl < kNs; ++sl) b.v[sl] = load16(vp + (size_t)16 * sl * BS);
+      for (int sl = 0; sl < kNs; ++sl) {
+        const uint2 lo = *reinterpret_cast<const uint2*>(vp + (size_t)16 * sl * BS);
+        const uint2 hi = *reinterpret_cast<const uint2*>(vp2 + (size_t)16 * sl * BS);
+        b.v[sl] = u32x4{lo.x, lo.y, hi.x, hi.y};
+      }
+    } else {
+#pragma unroll
+      for (int sl = 0; sl < kNs; ++sl) b.v[sl] = load16(vp + (size_t)16 * sl * BS);
+    }
   };
 
   float m_run = kNegInf;
@@ -340,10 +400,54 @@ paged_decode_kernel(const DecodeParams a) {
   for (int i = 0; i < kNs; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // ---- math of one step ---------------------------------------------------------
-  auto compute_step = [&](int st, StepData<T, D>& b) {
+  auto compute_step = [&](int st, StepData<T, C, D>& b) {
     const int base = tok0 + st * kStep;
     // fused step: position L - 1 takes the new token's K/V from LDS, and the patched
     // chunks go back to the cache (their lines were just loaded)
+    if constexpr (kFp8) {
+      if (lm1 >= base && lm1 < base + kStep) {
+        const uint8_t* nk = smem + 64 + (2 * uidx) * D;
+        const uint8_t* nv = smem + 64 + (2 * uidx + 1) * D;
+        uint8_t* kcw = static_cast<uint8_t*>(const_cast<void*>(a.k_cache));
+        uint8_t* vcw = static_cast<uint8_t*>(const_cast<void*>(a.v_cache));
+#pragma unroll
+        for (int t = 0; t < Sh::kTiles; ++t) {
+          const int tok = base + kTpl * (n >> 2) + 4 * t + (n & 3);
+          if (tok == lm1) {
+            const int phys = tblw[(tok - tok0) / BS];
+            uint8_t* kp = kcw + ((size_t)phys * a.Hkv + kvh) * head_elems +
+                          (size_t)j * BS * kX + (size_t)(tok % BS) * kX;
+#pragma unroll
+            for (int c = 0; c < kNc; ++c) {
+              b.k[t][c] = *reinterpret_cast<const u32x4*>(nk + 16 * (j + 4 * c));
+              store16(kp + (size_t)4 * c * BS * kX, b.k[t][c]);
+            }
+          }
+        }
+        const int tokv = base + kTpl * j;
+        const int e = lm1 - tokv;
+        if (e >= 0 && e < kTpl) {
+          // 16 tokens per lane; at BS 8 they are two 8-byte halves in two blocks
+          const int half_tok = BS < 16 ? tokv + (e & 8) : tokv;
+          const int physv = tblw[(half_tok - tok0) / BS];
+          uint8_t* vp = vcw + ((size_t)physv * a.Hkv + kvh) * head_elems + (size_t)n * BS +
+                        (BS < 16 ? 0 : tokv % BS);
+#pragma unroll
+          for (int sl = 0; sl < kNs; ++sl) {
+            const uint32_t code = nv[16 * sl + n];
+            const int sh = 8 * (e & 3);
+            b.v[sl][e >> 2] = (b.v[sl][e >> 2] & ~(0xFFu << sh)) | (code << sh);
+            if constexpr (BS < 16) {
+              const int h = e >> 3;
+              *reinterpret_cast<uint2*>(vp + (size_t)16 * sl * BS) =
+                  make_uint2(b.v[sl][2 * h], b.v[sl][2 * h + 1]);
+            } else {
+              store16(vp + (size_t)16 * sl * BS, b.v[sl]);
+            }
+          }
+        }
+      }
+    } else
     if (lm1 >= base && lm1 < base + kStep) {
       const T* nk = newkv + (2 * uidx) * D;
       const T* nv = newkv + (2 * uidx + 1) * D;
@@ -393,7 +497,10 @@ paged_decode_kernel(const DecodeParams a) {
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
         uint32_t mask;
-        if (kBf16) {
+        if (kFp8) {
+          const int r = nv - 4 * w;                          // live bytes of word w
+          mask = r >= 4 ? 0xFFFFFFFFu : (r <= 0 ? 0u : (0xFFFFFFFFu >> (32 - 8 * r)));
+        } else if (kBf16) {
           mask = (2 * w + 1 < nv) ? 0xFFFFFFFFu : ((2 * w < nv) ? 0x0000FFFFu : 0u);
         } else {
           mask = (w < nv) ? 0xFFFFFFFFu : 0u;
@@ -405,7 +512,24 @@ paged_decode_kernel(const DecodeParams a) {
 
     // scores
     float y[kTpl];
-    if constexpr (kBf16) {
+    if constexpr (kFp8) {
+#pragma unroll
+      for (int t = 0; t < Sh::kTiles; ++t) {
+        f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < kNc; ++c) {
+          const u32x4 kk = b.k[t][c];
+          sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(e4m3x8_to_bf16x8(kk[0], kk[1]),
+                                                       __builtin_bit_cast(bf16x8, qop[2 * c]), sc,
+                                                       0, 0, 0);
+          sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(e4m3x8_to_bf16x8(kk[2], kk[3]),
+                                                       __builtin_bit_cast(bf16x8, qop[2 * c + 1]),
+                                                       sc, 0, 0, 0);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) y[4 * t + e] = sc[e];
+      }
+    } else if constexpr (kBf16) {
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         f32x4 sc = {0.f, 0.f, 0.f, 0.f};
@@ -455,7 +579,26 @@ paged_decode_kernel(const DecodeParams a) {
     for (int sl = 0; sl < kNs; ++sl) acc[sl] *= alpha;
 
     // P.V
-    if constexpr (kBf16) {
+    if constexpr (kFp8) {
+      // V bytes 8h .. 8h + 7 of lane j are tokens kTpl*j + 8h + i, whose weights are
+      // pw[8h + i]; hi/lo rows as for bf16
+      const bool is_hi = n < g;
+      const bool is_lo = !is_hi && n < rows;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        bf16x8 pop;
+#pragma unroll
+        for (int v = 0; v < 8; ++v) {
+          const __bf16 hi = f32_to_bf16(pw[8 * h + v]);
+          const __bf16 lo = f32_to_bf16(pw[8 * h + v] - bf16_to_f32(hi));
+          pop[v] = is_hi ? hi : (is_lo ? lo : f32_to_bf16(0.f));
+        }
+#pragma unroll
+        for (int sl = 0; sl < kNs; ++sl)
+          acc[sl] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              e4m3x8_to_bf16x8(b.v[sl][2 * h], b.v[sl][2 * h + 1]), pop, acc[sl], 0, 0, 0);
+      }
+    } else if constexpr (kBf16) {
       const bool is_hi = n < g;
       const bool is_lo = !is_hi && n < rows;
       bf16x8 pop;
@@ -482,7 +625,7 @@ paged_decode_kernel(const DecodeParams a) {
   // ---- the wave's steps: st = lw, lw + nw, ... ----------------------------------------
   const int nsteps = (tok1 - tok0 + kStep - 1) / kStep;
   if constexpr (PIPE == 2) {
-    StepData<T, D> b0, b1;
+    StepData<T, C, D> b0, b1;
     int st = lw;
     if (st < nsteps) {
       load_step(st, b0);
@@ -502,14 +645,14 @@ paged_decode_kernel(const DecodeParams a) {
     }
   } else {
     for (int st = lw; st < nsteps; st += nw) {
-      StepData<T, D> b0;
+      StepData<T, C, D> b0;
       load_step(st, b0);
       compute_step(st, b0);
     }
   }
 
   // ---- merge the waves of the workgroup --------------------------------------------
-  if constexpr (kBf16) {
+  if constexpr (kBf16 || kFp8) {
     // add the lo rows [g, 2g) into the hi rows [0, g)
 #pragma unroll
     for (int sl = 0; sl < kNs; ++sl)
@@ -552,6 +695,7 @@ paged_decode_kernel(const DecodeParams a) {
       }
     }
     const size_t row = (size_t)su * a.Hq + kvh * g + h;
+    num *= a.v_scale;
     if (single) {
       const float o = (M == kNegInf) ? 0.f : num / den;
       if constexpr (kBf16)
@@ -632,19 +776,19 @@ inline bool use_paired(const DecodeParams& a, int D, int BS, int elt) {
          decode_lds_bytes(true, kPairWaves, a.S, D, BS, a.P, a.g, elt) <= kMaxLds;
 }
 
-template <typename T, int D, int BS>
+template <typename T, typename C, int D, int BS>
 hipError_t launch_decode(const DecodeParams& a, hipStream_t stream) {
   constexpr int elt = sizeof(T);
   if (use_paired(a, D, BS, elt)) {
     const size_t lds = decode_lds_bytes(true, kPairWaves, a.S, D, BS, a.P, a.g, elt);
     const long grid = (long)a.Hkv * ((a.S + 1) / 2);
-    hipLaunchKernelGGL((paged_decode_kernel<T, D, BS, kPairWaves, kPipe, true>),
+    hipLaunchKernelGGL((paged_decode_kernel<T, C, D, BS, kPairWaves, kPipe, true>),
                        dim3((unsigned)grid), dim3(kPairWaves * 64), lds, stream, a);
     return hipGetLastError();
   }
   const size_t lds = decode_lds_bytes(false, kWaves, a.S, D, BS, a.P, a.g, elt);
   const long grid = (long)a.Hkv * a.Pmax * a.S;
-  hipLaunchKernelGGL((paged_decode_kernel<T, D, BS, kWaves, kPipe, false>), dim3((unsigned)grid),
+  hipLaunchKernelGGL((paged_decode_kernel<T, C, D, BS, kWaves, kPipe, false>), dim3((unsigned)grid),
                      dim3(kWaves * 64), lds, stream, a);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || a.Pmax == 1) return err;
@@ -653,10 +797,10 @@ hipError_t launch_decode(const DecodeParams& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <typename T>
+template <typename T, typename C>
 hipError_t dispatch_decode(const DecodeParams& a, int D, int BS, hipStream_t stream) {
 #define PA_CASE(DD, BB) \
-  if (D == DD && BS == BB) return launch_decode<T, DD, BB>(a, stream);
+  if (D == DD && BS == BB) return launch_decode<T, C, DD, BB>(a, stream);
   PA_CASE(64, 8) PA_CASE(64, 16) PA_CASE(64, 32)
   PA_CASE(128, 8) PA_CASE(128, 16) PA_CASE(128, 32)
 #undef PA_CASE
@@ -756,15 +900,20 @@ extern "C" size_t pa_paged_attention_workspace_size(int num_seqs, int num_heads,
 namespace {
 
 // Checks shared by pa_paged_attention and pa_decode_step, then the launch.
+bool good_scale(float s) { return s > 0.f && s <= 3.4028234663852886e38f; }
+
+// fp8: the caches hold E4M3 codes read with k_scale / v_scale (query and out bf16).
 pa_status run_decode(void* out, const void* query, const int32_t* block_table,
                      const int32_t* context_lens, const void* k_cache, const void* v_cache,
                      const void* new_k, const void* new_v, const int64_t* new_slot,
                      int num_seqs, int num_heads, int num_kv_heads, int head_dim, int block_size,
                      int max_blocks_per_seq, int num_blocks, int max_context_len, float scale,
                      pa_dtype dtype, int partition_size, void* workspace, size_t workspace_bytes,
-                     void* stream) {
+                     void* stream, bool fp8 = false, float k_scale = 1.f, float v_scale = 1.f) {
   pa_status st = check_shapes(num_heads, num_kv_heads, head_dim, block_size, dtype);
   if (st != PA_OK) return st;
+  if (fp8 && dtype != PA_DTYPE_BF16) return PA_ERR_UNSUPPORTED;
+  if (fp8 && (!good_scale(k_scale) || !good_scale(v_scale))) return PA_ERR_INVALID_ARG;
   if (num_seqs < 0 || max_blocks_per_seq <= 0 || num_blocks <= 0 || max_context_len < 0)
     return PA_ERR_INVALID_ARG;
   if ((long)max_context_len > (long)max_blocks_per_seq * block_size) return PA_ERR_INVALID_ARG;
@@ -810,15 +959,20 @@ pa_status run_decode(void* out, const void* query, const int32_t* block_table,
   a.NB = num_blocks;
   a.P = P;
   a.Pmax = pmax;
-  a.scale_log2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
+  a.scale_log2 = static_cast<float>(static_cast<double>(scale) * (fp8 ? k_scale : 1.0) *
+                                    1.4426950408889634);
+  a.v_scale = fp8 ? v_scale : 1.f;
+  a.k_quant = fp8 ? k_scale : 1.f;
+  a.v_quant = fp8 ? v_scale : 1.f;
   char* ws = static_cast<char*>(workspace);
   a.part_ml = wl.total ? reinterpret_cast<float*>(ws + wl.ml) : nullptr;
   a.part_acc = wl.total ? reinterpret_cast<float*>(ws + wl.acc) : nullptr;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t err = dtype == PA_DTYPE_BF16
-                       ? pa::dispatch_decode<uint16_t>(a, head_dim, block_size, s)
-                       : pa::dispatch_decode<float>(a, head_dim, block_size, s);
+  hipError_t err = fp8 ? pa::dispatch_decode<uint16_t, uint8_t>(a, head_dim, block_size, s)
+                  : dtype == PA_DTYPE_BF16
+                      ? pa::dispatch_decode<uint16_t, uint16_t>(a, head_dim, block_size, s)
+                      : pa::dispatch_decode<float, float>(a, head_dim, block_size, s);
   return err == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
@@ -851,4 +1005,37 @@ extern "C" pa_status pa_decode_step(void* out, const void* query, const void* ke
                     num_seqs > 0 ? slot_mapping : nullptr, num_seqs, num_heads, num_kv_heads,
                     head_dim, block_size, max_blocks_per_seq, num_blocks, max_context_len, scale,
                     dtype, partition_size, workspace, workspace_bytes, stream);
+}
+
+extern "C" pa_status pa_paged_attention_fp8(void* out, const void* query,
+                                            const int32_t* block_table,
+                                            const int32_t* context_lens, const void* k_cache,
+                                            const void* v_cache, int num_seqs, int num_heads,
+                                            int num_kv_heads, int head_dim, int block_size,
+                                            int max_blocks_per_seq, int num_blocks,
+                                            int max_context_len, float scale, float k_scale,
+                                            float v_scale, pa_dtype dtype, int partition_size,
+                                            void* workspace, size_t workspace_bytes,
+                                            void* stream) {
+  return run_decode(out, query, block_table, context_lens, k_cache, v_cache, nullptr, nullptr,
+                    nullptr, num_seqs, num_heads, num_kv_heads, head_dim, block_size,
+                    max_blocks_per_seq, num_blocks, max_context_len, scale, dtype,
+                    partition_size, workspace, workspace_bytes, stream, true, k_scale, v_scale);
+}
+
+extern "C" pa_status pa_decode_step_fp8(void* out, const void* query, const void* key,
+                                        const void* value, const int64_t* slot_mapping,
+                                        const int32_t* block_table, const int32_t* context_lens,
+                                        void* k_cache, void* v_cache, int num_seqs,
+                                        int num_heads, int num_kv_heads, int head_dim,
+                                        int block_size, int max_blocks_per_seq, int num_blocks,
+                                        int max_context_len, float scale, float k_scale,
+                                        float v_scale, pa_dtype dtype, int partition_size,
+                                        void* workspace, size_t workspace_bytes, void* stream) {
+  if (num_seqs > 0 && (!key || !value || !slot_mapping)) return PA_ERR_INVALID_ARG;
+  return run_decode(out, query, block_table, context_lens, k_cache, v_cache, key, value,
+                    num_seqs > 0 ? slot_mapping : nullptr, num_seqs, num_heads, num_kv_heads,
+                    head_dim, block_size, max_blocks_per_seq, num_blocks, max_context_len, scale,
+                    dtype, partition_size, workspace, workspace_bytes, stream, true, k_scale,
+                    v_scale);
 }

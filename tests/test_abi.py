@@ -17,7 +17,7 @@ HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))
 def declared_functions() -> list:
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(pa_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(pa_[a-z0-9_]+)\s*\(", text)))
 
 
 @pytest.fixture(scope="module")
@@ -32,7 +32,8 @@ def test_header_declares_the_boundary():
     assert declared_functions() == sorted([
         "pa_abi_version", "pa_status_string", "pa_default_partition_size",
         "pa_paged_attention_workspace_size", "pa_paged_attention", "pa_reshape_and_cache",
-        "pa_gather_kv", "pa_decode_step", "pa_copy_blocks", "pa_paged_prefill"])
+        "pa_gather_kv", "pa_decode_step", "pa_copy_blocks", "pa_paged_prefill",
+        "pa_reshape_and_cache_fp8", "pa_paged_attention_fp8", "pa_decode_step_fp8"])
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -176,6 +177,70 @@ def test_gather_rejects_before_launch(lib):
     assert f(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 8, 128, 16, 4, 64, 65, 1, None) == 1
     assert f(FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, 2, 8, 128, 16, 4, 64, 64, 1, None) == 1
     assert f(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 8, 64, 24, 4, 64, 64, 1, None) == 2
+
+
+def test_reshape_and_cache_fp8_rejects_before_launch(lib):
+    f = lib.pa_reshape_and_cache_fp8
+    ok = [FAKE, FAKE, FAKE, FAKE, FAKE, 4, 8, 128, 16, 64, 1, 0.5, 0.25, None]
+
+    def call(over):
+        a = list(ok)
+        for k, v in over.items():
+            a[k] = v
+        return f(*a)
+
+    for bad in (0.0, -1.0, float("nan"), float("inf")):
+        assert call({11: bad}) == 1                 # k_scale
+        assert call({12: bad}) == 1                 # v_scale
+    assert call({7: 96}) == 2                       # head_dim
+    assert call({8: 12}) == 2                       # block_size
+    assert call({10: 7}) == 2                       # dtype
+    assert call({0: None}) == 1
+    assert call({3: FAKE + 8}) == 1                 # k_cache misaligned
+    assert call({2: FAKE + 4}) == 1                 # slot_mapping misaligned
+    assert call({5: -1}) == 1
+    assert call({5: 0}) == 0                        # nothing to write: no launch
+
+
+def test_paged_attention_fp8_rejects_before_launch(lib):
+    f = lib.pa_paged_attention_fp8
+    ok = [FAKE] * 6 + [4, 32, 8, 128, 16, 8, 64, 128, 0.1, 0.5, 0.25, 1, 0, None, 0, None]
+
+    def call(over):
+        a = list(ok)
+        for k, v in over.items():
+            a[k] = v
+        return f(*a)
+
+    assert call({17: 0}) == 2                       # f32 queries: not built for FP8 pools
+    for bad in (0.0, -2.0, float("nan"), float("inf")):
+        assert call({15: bad}) == 1                 # k_scale
+        assert call({16: bad}) == 1                 # v_scale
+    assert call({9: 96}) == 2
+    assert call({7: 72}) == 2                       # group of 9 > 8
+    assert call({18: 96}) == 1                      # partition not a multiple of 64
+    assert call({4: FAKE + 8}) == 1                 # k_cache misaligned
+    assert call({13: 129}) == 1                     # max_context_len past the table
+    assert call({6: 0}) == 0                        # empty batch: no launch
+
+
+def test_decode_step_fp8_rejects_before_launch(lib):
+    f = lib.pa_decode_step_fp8
+    ok = [FAKE] * 9 + [4, 32, 8, 128, 16, 8, 64, 128, 0.1, 0.5, 0.25, 1, 0, None, 0, None]
+
+    def call(over):
+        a = list(ok)
+        for k, v in over.items():
+            a[k] = v
+        return f(*a)
+
+    assert call({20: 0}) == 2                       # f32: not built for FP8 pools
+    assert call({18: 0.0}) == 1                     # k_scale
+    assert call({19: float("nan")}) == 1            # v_scale
+    assert call({2: None}) == 1                     # key missing
+    assert call({4: FAKE + 4}) == 1                 # slot_mapping misaligned
+    assert call({3: FAKE + 8}) == 1                 # value misaligned
+    assert call({9: 0}) == 0                        # empty batch: no launch
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):

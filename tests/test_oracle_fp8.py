@@ -107,6 +107,14 @@ def test_quantize_divides_in_float32():
         assert np.array_equal(q, ref), scale
 
 
+def test_quantize_keeps_the_sign_of_a_nan_element():
+    """IEEE 754 leaves the sign of a NaN quotient open: the code takes the element's sign."""
+    x = np.float32([np.nan, -np.nan, -np.inf, 448.0 * 0.3 * 2])
+    assert oracle.quantize(x, "f32", 0.3).tolist() == [0x7F, 0xFF, 0xFE, 0x7E]
+    bf = np.array([0x7FC0, 0xFFC0, 0xFF80], dtype=np.uint16)       # +NaN, -NaN, -inf
+    assert oracle.quantize(bf, "bf16", 0.3).tolist() == [0x7F, 0xFF, 0xFE]
+
+
 def _fp8_workload(seed=11):
     return make_workload(name="fp8", context_lens=[1, 17, 40, 95], num_heads=8, num_kv_heads=2,
                          head_dim=64, block_size=16, dtype="bf16", seed=seed)
