@@ -8,7 +8,7 @@ it.  Every function is pinned by a check in the test suite; none is marked
 from .paged_attention import (ELEMENT_BYTES, attention_one, chunk_elems, combine_partitions,
                               copy_blocks, decode, empty_pools, gather_kv, gather_sequence,
                               k_cache_shape, paged_attention, paged_prefill, partition_stats,
-                              reshape_and_cache, v_cache_shape)
+                              reshape_and_cache, swap_blocks, v_cache_shape)
 
 from .fp8_kv import (FP8_MAX, e4m3_decode, e4m3_encode, e4m3_values, empty_fp8_pools,
                      paged_attention_fp8, quantize, reshape_and_cache_fp8)
@@ -18,4 +18,5 @@ __all__ = ["FP8_MAX", "e4m3_decode", "e4m3_encode", "e4m3_values", "empty_fp8_po
            "ELEMENT_BYTES", "attention_one", "chunk_elems", "combine_partitions", "copy_blocks",
            "decode",
            "empty_pools", "gather_kv", "gather_sequence", "k_cache_shape",
-           "paged_attention", "paged_prefill", "partition_stats", "reshape_and_cache", "v_cache_shape"]
+           "paged_attention", "paged_prefill", "partition_stats", "reshape_and_cache", "swap_blocks",
+           "v_cache_shape"]

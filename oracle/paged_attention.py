@@ -139,6 +139,35 @@ def copy_blocks(k_cache: np.ndarray, v_cache: np.ndarray, block_mapping: np.ndar
 
 
 # ---------------------------------------------------------------------------
+# swapping: whole blocks between two pools (HBM and host memory)
+# ---------------------------------------------------------------------------
+def swap_blocks(src_k: np.ndarray, src_v: np.ndarray, dst_k: np.ndarray, dst_v: np.ndarray,
+                block_mapping: np.ndarray, inplace: bool = False):
+    """Destination pools where block d holds a copy of source block s, for every (s, d).
+
+    When GPU memory runs short the scheduler moves a request's KV out block by
+    block, not the request as a whole, and can write the blocks to CPU memory;
+    they come back when there is room ("core architecture" page, section
+    2.3.2).  Swap-out is this copy from the HBM pool into a host pool, swap-in
+    the copy back (into whatever free blocks the allocator picks).  The two
+    pools have the same layout and may hold different numbers of blocks.
+    Destinations must be distinct and inside the destination pool; sources
+    inside the source pool.
+    """
+    pairs = np.asarray(block_mapping, dtype=np.int64).reshape(-1, 2)
+    src, dst = pairs[:, 0], pairs[:, 1]
+    assert len(np.unique(dst)) == len(dst), "destinations must be distinct"
+    assert ((src >= 0) & (src < src_k.shape[0])).all(), "source block outside its pool"
+    assert ((dst >= 0) & (dst < dst_k.shape[0])).all(), "destination block outside its pool"
+    assert src_k.shape[1:] == dst_k.shape[1:] and src_v.shape[1:] == dst_v.shape[1:]
+    k_new = dst_k if inplace else dst_k.copy()
+    v_new = dst_v if inplace else dst_v.copy()
+    k_new[dst] = src_k[src]
+    v_new[dst] = src_v[src]
+    return k_new, v_new
+
+
+# ---------------------------------------------------------------------------
 # read path: reassemble through the block table
 # ---------------------------------------------------------------------------
 def gather_sequence(block_table_row: np.ndarray, context_len: int,

@@ -440,6 +440,94 @@ def test_copy_blocks_reproduces_the_copy_on_write_records():
 
 
 # ---------------------------------------------------------------------------
+# swapping blocks between the HBM pool and a host pool
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "fp8"])
+def test_swap_blocks_matches_element_loop(dtype):
+    rng = np.random.default_rng(90)
+    Hkv, D, BS = 2, 32, 8
+    shape_k = lambda nb: (nb, Hkv, D // (16 // {"f32": 4, "bf16": 2, "fp8": 1}[dtype]), BS,
+                          16 // {"f32": 4, "bf16": 2, "fp8": 1}[dtype])
+    np_t = {"f32": np.float32, "bf16": np.uint16, "fp8": np.uint8}[dtype]
+
+    def pool(nb):
+        k = rng.integers(0, 255, size=shape_k(nb)).astype(np_t)
+        v = rng.integers(0, 255, size=(nb, Hkv, D, BS)).astype(np_t)
+        return k, v
+
+    sk, sv = pool(10)
+    dk, dv = pool(6)                       # a smaller destination pool
+    sk0, sv0, dk0, dv0 = sk.copy(), sv.copy(), dk.copy(), dv.copy()
+    pairs = np.array([[9, 0], [2, 5], [2, 3], [7, 1]], dtype=np.int64)
+    k2, v2 = oracle.swap_blocks(sk, sv, dk, dv, pairs)
+    assert np.array_equal(sk, sk0) and np.array_equal(sv, sv0)          # inputs untouched
+    assert np.array_equal(dk, dk0) and np.array_equal(dv, dv0)
+    dsts = {int(d): int(s_) for s_, d in pairs}
+    for b in range(6):
+        for pool_new, pool_old, src in ((k2, dk, sk), (v2, dv, sv)):
+            flat_new, flat_old = pool_new.reshape(6, -1), pool_old.reshape(6, -1)
+            flat_src = src.reshape(10, -1)
+            for i in range(flat_new.shape[1]):
+                want = flat_src[dsts[b], i] if b in dsts else flat_old[b, i]
+                assert flat_new[b, i].tobytes() == want.tobytes()
+
+
+def test_swap_blocks_rejects_bad_pairs():
+    k, v = oracle.empty_pools(8, 1, 16, 8, "f32")
+    hk, hv = oracle.empty_pools(4, 1, 16, 8, "f32")
+    with pytest.raises(AssertionError):
+        oracle.swap_blocks(k, v, hk, hv, np.array([[1, 2], [3, 2]]))      # same destination
+    with pytest.raises(AssertionError):
+        oracle.swap_blocks(k, v, hk, hv, np.array([[1, 4]]))              # past the host pool
+    with pytest.raises(AssertionError):
+        oracle.swap_blocks(k, v, hk, hv, np.array([[8, 0]]))              # past the HBM pool
+
+
+def test_swap_out_and_back_in_keeps_every_result():
+    """Preempt a quarter of the sequences: their blocks go to a compact host pool, the HBM
+    blocks are reused (NaN-filled here), and on resumption the blocks come back into other
+    free HBM blocks with the tables rewritten.  Every sequence's attention is unchanged, bit
+    for bit, and nothing but the chosen blocks moved."""
+    w = tiny("bf16", lens=(5, 40, 17, 64, 33, 90, 8, 71), Hq=8, Hkv=2, D=32, BS=8, seed=91,
+             pool_factor=2.0)
+    kc, vc = build_pools(w)
+    before = oracle_out(w, kc, vc)
+    victims = [1, 3]
+    nblk = {s: -(-int(w.context_lens[s]) // w.block_size) for s in victims}
+    out_pairs, host = [], 0
+    for s in victims:
+        for i in range(nblk[s]):
+            out_pairs.append([int(w.block_table[s, i]), host])
+            host += 1
+    out_pairs = np.array(out_pairs, dtype=np.int64)
+    hk, hv = oracle.empty_pools(host, w.num_kv_heads, w.head_dim, w.block_size, w.dtype)
+    hk, hv = oracle.swap_blocks(kc, vc, hk, hv, out_pairs)
+    kc2, vc2 = kc.copy(), vc.copy()
+    nan = np.uint16(0x7FC0)
+    kc2[out_pairs[:, 0]] = nan                        # the freed blocks get reused
+    vc2[out_pairs[:, 0]] = nan
+    used = {int(b) for s in range(w.num_seqs) for b in
+            w.block_table[s, :-(-int(w.context_lens[s]) // w.block_size)]}
+    free = [b for b in range(w.num_blocks) if b not in used]
+    assert len(free) >= host
+    in_pairs = np.stack([np.arange(host), np.array(free[:host])], axis=1).astype(np.int64)
+    kc2, vc2 = oracle.swap_blocks(hk, hv, kc2, vc2, in_pairs)
+    table = w.block_table.copy()
+    h = 0
+    for s in victims:
+        for i in range(nblk[s]):
+            table[s, i] = free[h]
+            h += 1
+    w2 = w.__class__(**{**w.__dict__, "block_table": table})
+    after = oracle_out(w2, kc2, vc2)
+    assert np.array_equal(before, after)
+    # only the chosen blocks changed
+    changed = {int(b) for b in range(w.num_blocks)
+               if not (np.array_equal(kc2[b], kc[b]) and np.array_equal(vc2[b], vc[b]))}
+    assert changed == set(out_pairs[:, 0].tolist()) | set(free[:host])
+
+
+# ---------------------------------------------------------------------------
 # paged prefill (causal chunks over the paged context)
 # ---------------------------------------------------------------------------
 from workloads import make_prefill  # noqa: E402
