@@ -51,10 +51,12 @@ def parse_args():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--op", default="step", choices=["step", "copy_blocks", "prefill", "fp8"],
+    ap.add_argument("--op", default="step",
+                    choices=["step", "copy_blocks", "prefill", "fp8", "swap"],
                     help="step: the decode step (default); copy_blocks: the copy-on-write "
                          "copies of the parallel-sampling workload; prefill: paged prefill; "
-                         "fp8: the decode step over FP8 (E4M3) K/V pools")
+                         "fp8: the decode step over FP8 (E4M3) K/V pools; swap: swapping a "
+                         "quarter of the sequences' blocks out to pinned host memory and back")
     ap.add_argument("--prefill-case", default="prefix-cache-prefill",
                     choices=["prefix-cache-prefill", "chunked-prefill-llama3-8b"])
     ap.add_argument("--config", type=int, default=1, choices=[0, 1, 2, 3, 4])
@@ -479,6 +481,95 @@ def bench_fp8(args) -> int:
     return 0
 
 
+PCIE_PEAK_GBS = 64.0           # PCIe 5.0 x16 per direction, the MI355X host link
+
+
+def bench_swap(args) -> int:
+    """Swap-out of a quarter of the Llama-3-8B-shaped batch's sequences (all their blocks,
+    K and V) from the HBM pools to pinned host pools, and swap-in back into HBM, each one
+    pa_swap_blocks launch; a plain contiguous device-to-host / host-to-device copy of the
+    same bytes (copy engine) is timed beside it as the practical ceiling of the link."""
+    import torch
+
+    import paged_kv_cache_425_amd as pk
+    from workloads import make_config
+    dev = torch.device("cuda:0")
+    w = make_config(args.config, seed=args.seed, block_size=args.block_size, variant=args.variant)
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    kshape = pk.k_cache_shape(w.num_blocks, w.num_kv_heads, w.head_dim, w.block_size, tdt)
+    vshape = pk.v_cache_shape(w.num_blocks, w.num_kv_heads, w.head_dim, w.block_size, tdt)
+    kd = torch.randn(kshape, dtype=torch.float32, device=dev).to(tdt)
+    vd = torch.randn(vshape, dtype=torch.float32, device=dev).to(tdt)
+    rng = np.random.default_rng(7)
+    victims = np.sort(rng.choice(w.num_seqs, max(1, w.num_seqs // 4), replace=False))
+    blocks = np.concatenate([w.block_table[s, :-(-int(w.context_lens[s]) // w.block_size)]
+                             for s in victims]).astype(np.int64)
+    nh = len(blocks)
+    out_map = torch.from_numpy(np.stack([blocks, np.arange(nh)], axis=1)).to(dev)
+    in_map = torch.from_numpy(np.stack([np.arange(nh), blocks], axis=1)).to(dev)
+    hk = torch.empty((nh,) + tuple(kshape[1:]), dtype=tdt, pin_memory=True)
+    hv = torch.empty((nh,) + tuple(vshape[1:]), dtype=tdt, pin_memory=True)
+    elt = 2 if w.dtype == "bf16" else 4
+    moved = 2 * nh * w.num_kv_heads * w.head_dim * w.block_size * elt      # K and V
+    log(f"swap: {len(victims)} of {w.num_seqs} sequences, {nh} blocks, {moved / 1e6:.1f} MB "
+        "each way")
+    swap_out = pk.prepare_swap_blocks(kd, vd, hk, hv, out_map)
+    swap_in = pk.prepare_swap_blocks(hk, hv, kd, vd, in_map)
+    torch.cuda.synchronize()
+    # the same bytes as one contiguous copy each way (the copy engine's ceiling)
+    flat_d = torch.empty(moved // 2, dtype=torch.int16, device=dev)
+    flat_h = torch.empty(moved // 2, dtype=torch.int16, pin_memory=True)
+    K, W = max(1, args.steps // 10), max(1, args.warmup // 10)
+
+    def timed(fn):
+        for _ in range(W):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        e0.record()
+        for _ in range(K):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / K, e0.elapsed_time(e1) * 1e-3 / K
+
+    out_wall, out_ev = timed(swap_out)
+    in_wall, in_ev = timed(swap_in)
+    d2h_wall, d2h_ev = timed(lambda: flat_h.copy_(flat_d, non_blocking=True))
+    h2d_wall, h2d_ev = timed(lambda: flat_d.copy_(flat_h, non_blocking=True))
+    gbs = lambda t: moved / t / 1e9
+    log(f"swap-out {out_ev * 1e6:.0f} us = {gbs(out_ev):.1f} GB/s; swap-in {in_ev * 1e6:.0f} us "
+        f"= {gbs(in_ev):.1f} GB/s; contiguous copies {gbs(d2h_ev):.1f} / {gbs(h2d_ev):.1f} GB/s")
+    # one pass of the path: the blocks out and back in
+    step_s = out_ev + in_ev
+    line = {
+        "metric": "swap_blocks HBM <-> pinned host, GB/s per direction (PCIe), "
+                  "Llama-3-8B shape, 1 GPU",
+        "value": round(2 * moved / step_s / 1e9, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": K, "warmup": W, "ms_per_step": round(step_s * 1e3, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
+        "data": "synthetic (random pools; the block lists of a seeded quarter of the batch)",
+        "config": {"workload": w.name + "-swap", "sequences_swapped": int(len(victims)),
+                   "blocks": int(nh), "bytes_each_way": int(moved),
+                   "step": "pa_swap_blocks out (HBM -> pinned host) + pa_swap_blocks in",
+                   "parallelism": "none (1 GPU)"},
+        "swap_out": {"us": round(out_ev * 1e6, 1), "GB/s": round(gbs(out_ev), 2),
+                     "us_wall": round(out_wall * 1e6, 1)},
+        "swap_in": {"us": round(in_ev * 1e6, 1), "GB/s": round(gbs(in_ev), 2),
+                    "us_wall": round(in_wall * 1e6, 1)},
+        "contiguous_copy_engine": {"d2h_GB/s": round(gbs(d2h_ev), 2),
+                                   "h2d_GB/s": round(gbs(h2d_ev), 2)},
+        "roofline": {"kernel": "swap_blocks_kernel (swap-out)", "bound": "pcie",
+                     "achieved": round(gbs(out_ev), 2), "peak": PCIE_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs(out_ev) / PCIE_PEAK_GBS, 4), "traffic": None,
+                     "algorithmic_bytes_per_launch": int(moved)},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def main() -> int:
     args = parse_args()
     if args.gpus != 1:
@@ -500,6 +591,8 @@ def main() -> int:
         return bench_prefill(args)
     if args.op == "fp8":
         return bench_fp8(args)
+    if args.op == "swap":
+        return bench_swap(args)
     dev = torch.device("cuda:0")
 
     t = time.perf_counter()

@@ -69,7 +69,9 @@ typedef enum {
 
 typedef enum {
     PA_DTYPE_F32 = 0,
-    PA_DTYPE_BF16 = 1
+    PA_DTYPE_BF16 = 1,
+    PA_DTYPE_FP8_E4M3 = 2     /* FP8 pools (uint8 codes): pa_copy_blocks and pa_swap_blocks
+                                 only; the FP8 calls below name their pool type themselves */
 } pa_dtype;
 
 /* Version of this ABI (PA_ABI_VERSION of the build). */
@@ -226,6 +228,7 @@ pa_status pa_paged_prefill(void* out, const void* query, const int32_t* query_st
  *                  copies run in parallel).  A pair with a block outside
  *                  [0, num_blocks) is skipped.
  *   k_cache, v_cache  pools in the layouts above (written in place)
+ *   dtype          the pools' element type; PA_DTYPE_FP8_E4M3 for FP8 pools
  * The copy is bit-exact; blocks that are not destinations do not change.
  */
 pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_mapping,
@@ -298,6 +301,34 @@ pa_status pa_decode_step_fp8(void* out, const void* query, const void* key, cons
                              int max_context_len, float scale, float k_scale, float v_scale,
                              pa_dtype dtype, int partition_size, void* workspace,
                              size_t workspace_bytes, void* stream);
+
+/*
+ * Swapping: make block d of the destination pools a copy of block s of the
+ * source pools, for each pair of block_mapping.  When GPU memory runs short
+ * the scheduler moves a request's KV out block by block and can write it to
+ * CPU memory, and brings it back later (page "vLLM core architecture",
+ * section 2.3.2): swap-out is a call with the HBM pools as source and pools
+ * in pinned host memory as destination, swap-in the reverse (into whatever
+ * free blocks the allocator chose).  Both pairs of pools have the layout
+ * above; they may hold different numbers of blocks.
+ *
+ *   src_k, src_v   source pools, src_num_blocks blocks
+ *   dst_k, dst_v   destination pools, dst_num_blocks blocks (written in place)
+ *   block_mapping  [num_pairs][2] int64 (source block, destination block);
+ *                  destinations distinct; a pair naming a block outside its
+ *                  pool is skipped
+ *   dtype          element type of all four pools (PA_DTYPE_FP8_E4M3: codes)
+ * Each of the four pools and block_mapping must be device memory or pinned
+ * host memory mapped for the device (hipHostMalloc, a pinned torch tensor);
+ * anything else -- pageable host memory in particular -- returns
+ * PA_ERR_INVALID_ARG before any launch.  The GPU moves the data itself in
+ * one launch, through the host memory's device mapping.  The copy is
+ * bit-exact; nothing else in the destination changes.
+ */
+pa_status pa_swap_blocks(const void* src_k, const void* src_v, void* dst_k, void* dst_v,
+                         const int64_t* block_mapping, int num_pairs, int num_kv_heads,
+                         int head_dim, int block_size, int src_num_blocks, int dst_num_blocks,
+                         pa_dtype dtype, void* stream);
 
 /*
  * Diagnostic read path: reassemble every sequence's K and V through its block

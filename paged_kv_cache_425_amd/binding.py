@@ -16,6 +16,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpagedatt
 
 PA_OK = 0
 _DTYPE_CODES = {torch.float32: 0, torch.bfloat16: 1}
+_POOL_CODES = {torch.float32: 0, torch.bfloat16: 1, torch.uint8: 2}   # uint8: FP8 E4M3 codes
 _ERRORS = {1: ValueError, 2: NotImplementedError, 3: ValueError, 4: RuntimeError}
 
 _lib = None
@@ -53,6 +54,8 @@ def load_library() -> ctypes.CDLL:
     lib.pa_gather_kv.argtypes = [vp] * 7 + [i32] * 8 + [vp]
     lib.pa_reshape_and_cache_fp8.restype = i32
     lib.pa_reshape_and_cache_fp8.argtypes = [vp] * 5 + [i32] * 6 + [f32, f32, vp]
+    lib.pa_swap_blocks.restype = i32
+    lib.pa_swap_blocks.argtypes = [vp] * 5 + [i32] * 6 + [i32, vp]
     lib.pa_decode_step_fp8.restype = i32
     lib.pa_decode_step_fp8.argtypes = [vp] * 9 + [i32] * 8 + [f32] * 3 + [i32, i32, vp, sz, vp]
     lib.pa_paged_attention_fp8.restype = i32
@@ -409,8 +412,9 @@ def copy_blocks(k_cache: torch.Tensor, v_cache: torch.Tensor, block_mapping: tor
     _require(block_mapping, "block_mapping", dev, torch.int64)
     if block_mapping.dim() != 2 or block_mapping.shape[1] != 2:
         raise ValueError("block_mapping must be [n, 2] (src, dst)")
+    _pool_code(k_cache)
     st = lib.pa_copy_blocks(_ptr(k_cache), _ptr(v_cache), _ptr(block_mapping),
-                            block_mapping.shape[0], Hkv, D, BS, NB, _dtype_code(k_cache),
+                            block_mapping.shape[0], Hkv, D, BS, NB, _pool_code(k_cache),
                             _stream(dev, stream))
     _check(st, "pa_copy_blocks")
 
@@ -421,9 +425,57 @@ def prepare_copy_blocks(k_cache, v_cache, block_mapping, stream=None) -> Prepare
     copy_blocks(k_cache, v_cache, block_mapping, stream=stream)
     NB, Hkv, D, BS = _cache_dims(k_cache, v_cache)
     args = (_ptr(k_cache), _ptr(v_cache), _ptr(block_mapping), block_mapping.shape[0], Hkv, D,
-            BS, NB, _dtype_code(k_cache), _stream(k_cache.device, stream))
+            BS, NB, _pool_code(k_cache), _stream(k_cache.device, stream))
     return PreparedCall(lib.pa_copy_blocks, args, "pa_copy_blocks",
                         (k_cache, v_cache, block_mapping))
+
+
+def _pool_code(t: torch.Tensor) -> int:
+    if t.dtype not in _POOL_CODES:
+        raise TypeError(f"unsupported pool dtype {t.dtype}; use float32, bfloat16 or uint8 (FP8)")
+    return _POOL_CODES[t.dtype]
+
+
+def _gpu_reachable(t: torch.Tensor, name: str) -> None:
+    if not (t.is_cuda or t.is_pinned()):
+        raise ValueError(f"{name} must be on the GPU or in pinned host memory")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _swap_args(src_k, src_v, dst_k, dst_v, block_mapping, stream):
+    for t, name in ((src_k, "src_k"), (src_v, "src_v"), (dst_k, "dst_k"), (dst_v, "dst_v"),
+                    (block_mapping, "block_mapping")):
+        _gpu_reachable(t, name)
+    sNB, Hkv, D, BS = _cache_dims(src_k, src_v)
+    dNB, dHkv, dD, dBS = _cache_dims(dst_k, dst_v)
+    if (dHkv, dD, dBS) != (Hkv, D, BS) or dst_k.dtype != src_k.dtype:
+        raise ValueError("source and destination pools must share layout and dtype")
+    if block_mapping.dtype != torch.int64 or block_mapping.dim() != 2 or \
+            block_mapping.shape[1] != 2:
+        raise ValueError("block_mapping must be an int64 [n, 2] tensor (src, dst)")
+    dev = next((t.device for t in (src_k, dst_k, block_mapping) if t.is_cuda), None)
+    if dev is None:
+        raise ValueError("one side of a swap must be on the GPU")
+    return (_ptr(src_k), _ptr(src_v), _ptr(dst_k), _ptr(dst_v), _ptr(block_mapping),
+            block_mapping.shape[0], Hkv, D, BS, sNB, dNB, _pool_code(src_k), _stream(dev, stream))
+
+
+def swap_blocks(src_k: torch.Tensor, src_v: torch.Tensor, dst_k: torch.Tensor,
+                dst_v: torch.Tensor, block_mapping: torch.Tensor, stream=None) -> None:
+    """Copy block s of the source pools to block d of the destination pools for every (s, d)
+    row of block_mapping; one side is typically in pinned host memory (see pa_swap_blocks)."""
+    args = _swap_args(src_k, src_v, dst_k, dst_v, block_mapping, stream)
+    _check(load_library().pa_swap_blocks(*args), "pa_swap_blocks")
+
+
+def prepare_swap_blocks(src_k, src_v, dst_k, dst_v, block_mapping, stream=None) -> PreparedCall:
+    """Check the arguments of swap_blocks once and return a re-launchable call."""
+    args = _swap_args(src_k, src_v, dst_k, dst_v, block_mapping, stream)
+    call = PreparedCall(load_library().pa_swap_blocks, args, "pa_swap_blocks",
+                        (src_k, src_v, dst_k, dst_v, block_mapping))
+    call()
+    return call
 
 
 def gather_kv(block_table: torch.Tensor, context_lens: torch.Tensor, k_cache: torch.Tensor,

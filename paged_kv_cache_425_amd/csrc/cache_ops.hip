@@ -199,7 +199,9 @@ extern "C" pa_status pa_gather_kv(void* k_out, void* v_out, const int64_t* seq_o
 extern "C" pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_mapping,
                                     int num_pairs, int num_kv_heads, int head_dim, int block_size,
                                     int num_blocks, pa_dtype dtype, void* stream) {
-  pa_status st = check_cache_shapes(num_kv_heads, head_dim, block_size, num_blocks, dtype);
+  // FP8 pools copy like any other: whole 16-byte chunks
+  pa_status st = check_cache_shapes(num_kv_heads, head_dim, block_size, num_blocks,
+                                    dtype == PA_DTYPE_FP8_E4M3 ? PA_DTYPE_BF16 : dtype);
   if (st != PA_OK) return st;
   if (num_pairs < 0) return PA_ERR_INVALID_ARG;
   if (num_pairs == 0) return PA_OK;
@@ -209,7 +211,12 @@ extern "C" pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int64_t*
   const long grid = (long)num_pairs * num_kv_heads * 2;
   if (grid > 0x7FFFFFFFL) return PA_ERR_INVALID_ARG;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (dtype == PA_DTYPE_BF16) {
+  if (dtype == PA_DTYPE_FP8_E4M3) {
+    hipLaunchKernelGGL(pa::copy_blocks_kernel<uint8_t>, dim3((unsigned)grid),
+                       dim3(pa::kCopyThreads), 0, s, static_cast<uint8_t*>(k_cache),
+                       static_cast<uint8_t*>(v_cache), block_mapping, num_kv_heads, head_dim,
+                       block_size, num_blocks);
+  } else if (dtype == PA_DTYPE_BF16) {
     hipLaunchKernelGGL(pa::copy_blocks_kernel<uint16_t>, dim3((unsigned)grid),
                        dim3(pa::kCopyThreads), 0, s, static_cast<uint16_t*>(k_cache),
                        static_cast<uint16_t*>(v_cache), block_mapping, num_kv_heads, head_dim,

@@ -33,7 +33,8 @@ def test_header_declares_the_boundary():
         "pa_abi_version", "pa_status_string", "pa_default_partition_size",
         "pa_paged_attention_workspace_size", "pa_paged_attention", "pa_reshape_and_cache",
         "pa_gather_kv", "pa_decode_step", "pa_copy_blocks", "pa_paged_prefill",
-        "pa_reshape_and_cache_fp8", "pa_paged_attention_fp8", "pa_decode_step_fp8"])
+        "pa_reshape_and_cache_fp8", "pa_paged_attention_fp8", "pa_decode_step_fp8",
+        "pa_swap_blocks"])
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -241,6 +242,34 @@ def test_decode_step_fp8_rejects_before_launch(lib):
     assert call({4: FAKE + 4}) == 1                 # slot_mapping misaligned
     assert call({3: FAKE + 8}) == 1                 # value misaligned
     assert call({9: 0}) == 0                        # empty batch: no launch
+
+
+def test_swap_blocks_rejects_before_launch(lib):
+    f = lib.pa_swap_blocks
+    ok = [FAKE] * 5 + [4, 8, 128, 16, 64, 32, 1, None]
+
+    def call(over):
+        a = list(ok)
+        for k, v in over.items():
+            a[k] = v
+        return f(*a)
+
+    assert call({11: 3}) == 2                       # unknown dtype
+    assert call({7: 96}) == 2                       # head_dim
+    assert call({8: 12}) == 2                       # block_size
+    assert call({5: -1}) == 1                       # num_pairs
+    assert call({5: 0}) == 0                        # nothing to move: no launch
+    assert call({9: 0}) == 1                        # empty source pool
+    assert call({0: None}) == 1
+    assert call({2: FAKE + 8}) == 1                 # destination misaligned
+    assert call({4: FAKE + 4}) == 1                 # block_mapping misaligned
+
+
+def test_copy_blocks_accepts_fp8_pools_and_checks_them(lib):
+    f = lib.pa_copy_blocks
+    assert f(FAKE, FAKE, FAKE, 4, 8, 96, 16, 64, 2, None) == 2   # FP8 pools, bad head_dim
+    assert f(FAKE, FAKE, FAKE, 0, 8, 128, 16, 64, 2, None) == 0  # FP8 pools, nothing to copy
+    assert f(FAKE, FAKE, FAKE, 4, 8, 128, 16, 64, 3, None) == 2  # unknown dtype
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
