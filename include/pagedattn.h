@@ -204,6 +204,9 @@ pa_status pa_decode_step(void* out, const void* query, const void* key, const vo
  *   query_start_loc  [num_seqs + 1] int32, non-decreasing, query_start_loc[0] = 0,
  *                    query_start_loc[num_seqs] = num_query_tokens
  *   max_query_len    host-side upper bound of the chunk lengths (sizes the grid)
+ *   scale            softmax scale; must be positive and finite (else
+ *                    PA_ERR_INVALID_ARG): the kernel takes the row maximum on the
+ *                    raw scores and applies the scale in the exponent
  *   other arguments as in pa_paged_attention; group size g = num_heads /
  *   num_kv_heads must divide 128 (1, 2, 4, 8, 16)
  * Values outside these ranges are clamped on the device (rows that fall outside

@@ -159,31 +159,50 @@ paged_prefill_kernel(const PrefillParams a) {
   };
 
   // chunk ids: K id = q * kStep + key (q = 16-byte chunk of the row), V id = channel *
-  // (kStep / kX) + group; consecutive threads read consecutive addresses within a block
+  // (kStep / kX) + group; consecutive threads read consecutive addresses within a block.
+  // A step is kStep keys starting at a multiple of kStep.  When BS divides kStep, each
+  // chunk's block within the step and its offset inside the block are fixed per thread
+  // and a step only adds its first block; when kStep divides BS (f32, BS 32) the step
+  // also adds its own offset inside the block.  Blocks past the last one with a seen key
+  // are clamped to it (in bounds; those keys are masked, their V zeroed).
+  static_assert(kStep % BS == 0 || BS % kStep == 0, "steps and blocks must nest");
+  int k_blk[kLoadsK], v_blk[kLoadsV];                       // block offset within the step
+  int k_off[kLoadsK], v_off[kLoadsV];                       // element offset in the tile
+#pragma unroll
+  for (int i = 0; i < kLoadsK; ++i) {
+    const int cid = threadIdx.x + i * kThreads;
+    const int q = cid / kStep, kk = cid % kStep;
+    k_blk[i] = kk / BS;
+    k_off[i] = (q * BS + kk % BS) * kX;
+  }
+#pragma unroll
+  for (int i = 0; i < kLoadsV; ++i) {
+    const int cid = threadIdx.x + i * kThreads;
+    const int ch = cid / (kStep / kX), grp = cid % (kStep / kX);
+    v_blk[i] = grp * kX / BS;
+    v_off[i] = ch * BS + grp * kX % BS;
+  }
+  const int last_blk = (kmax - 1) / BS;                     // last block with a seen key
+  const size_t blk_stride = (size_t)a.Hkv * head_elems;      // elements per physical block
+  const T* kbase = kc + (size_t)kvh * head_elems;
+  const T* vbase = vc + (size_t)kvh * head_elems;
   auto fetch = [&](int st) {
-    const int base = st * kStep;
-    const int tb0 = (base / BS) / 1024 * 1024;               // table chunk of this step
+    const int b0 = st * kStep / BS;                          // first block of the step
+    const int boff = st * kStep % BS;                        // 0 unless kStep < BS
+    const int tb0 = b0 / 1024 * 1024;                        // its table window
 #pragma unroll
     for (int i = 0; i < kLoadsK; ++i) {
-      const int cid = threadIdx.x + i * kThreads;
-      const int q = cid / kStep;
-      const int key = min(base + cid % kStep, kmax - 1);      // past kmax: a seen key (masked)
-      const int phys = tbl_lds[key / BS - tb0];
-      const T* src = kc + ((size_t)phys * a.Hkv + kvh) * head_elems +
-                     ((size_t)q * BS + key % BS) * kX;
+      const int phys = tbl_lds[min(b0 + k_blk[i], last_blk) - tb0];
       const u32x4 z = {0u, 0u, 0u, 0u};
-      kreg[i] = cid < Sh::kKChunks ? load16(src) : z;
+      kreg[i] = threadIdx.x + i * kThreads < Sh::kKChunks
+                    ? load16(kbase + (size_t)phys * blk_stride + k_off[i] + boff * kX) : z;
     }
 #pragma unroll
     for (int i = 0; i < kLoadsV; ++i) {
-      const int cid = threadIdx.x + i * kThreads;
-      const int ch = cid / (kStep / kX);
-      const int grp = cid % (kStep / kX);
-      const int key = min(base + grp * kX, (kmax - 1) / kX * kX);
-      const int phys = tbl_lds[key / BS - tb0];
-      const T* src = vc + ((size_t)phys * a.Hkv + kvh) * head_elems + (size_t)ch * BS + key % BS;
+      const int phys = tbl_lds[min(b0 + v_blk[i], last_blk) - tb0];
       const u32x4 z = {0u, 0u, 0u, 0u};
-      vreg[i] = cid < Sh::kVChunks ? load16(src) : z;
+      vreg[i] = threadIdx.x + i * kThreads < Sh::kVChunks
+                    ? load16(vbase + (size_t)phys * blk_stride + v_off[i] + boff) : z;
     }
   };
   auto stage = [&](int st, int buf) {
@@ -203,17 +222,19 @@ paged_prefill_kernel(const PrefillParams a) {
       const int cid = threadIdx.x + i * kThreads;
       if (cid < Sh::kVChunks) {
         const int ch = cid / (kStep / kX), grp = cid % (kStep / kX);
-        // zero positions >= L (kmax <= L): weight 0 must not meet NaN
-        const int nv = min(max(kmax - (base + grp * kX), 0), kX);
         u32x4 v = vreg[i];
+        if (base + kStep > kmax) {                           // the step ends past kmax
+          // zero positions >= L (kmax <= L): weight 0 must not meet NaN
+          const int nv = min(max(kmax - (base + grp * kX), 0), kX);
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          uint32_t mask;
-          if (kBf16)
-            mask = (2 * w + 1 < nv) ? 0xFFFFFFFFu : ((2 * w < nv) ? 0x0000FFFFu : 0u);
-          else
-            mask = (w < nv) ? 0xFFFFFFFFu : 0u;
-          v[w] &= mask;
+          for (int w = 0; w < 4; ++w) {
+            uint32_t mask;
+            if (kBf16)
+              mask = (2 * w + 1 < nv) ? 0xFFFFFFFFu : ((2 * w < nv) ? 0x0000FFFFu : 0u);
+            else
+              mask = (w < nv) ? 0xFFFFFFFFu : 0u;
+            v[w] &= mask;
+          }
         }
         *reinterpret_cast<u32x4*>(vb + (ch * Sh::kVRow + grp) * 16) = v;
       }
@@ -293,9 +314,11 @@ paged_prefill_kernel(const PrefillParams a) {
     }
 
     // online softmax (base 2).  Masked steps: key base + kTpl*j + v counts if <= the
-    // row's position.  A row's running max moves only when a step raises it by more
-    // than kLazy (its weights then stay below 2^kLazy), so the accumulators are
-    // rescaled on few steps; the result is the same sum with another common factor.
+    // row's position.  The scale (> 0) enters in the exponent, exp2(y * s - m), and the
+    // row max is taken on the raw scores (max(y * s) = s * max(y) for s > 0).  A row's
+    // running max moves only when a step raises it by more than kLazy (its weights then
+    // stay below 2^kLazy), so the accumulators are rescaled on few steps; the result is
+    // the same sum with another common factor.
     float pw[kPrefillBlocks][kTpl];
     float alpha[kPrefillBlocks];
     bool moved = false;
@@ -306,14 +329,13 @@ paged_prefill_kernel(const PrefillParams a) {
       for (int v = 0; v < kTpl; ++v) {
         if constexpr (kMasked) {
           const bool live = base + kTpl * j + v <= pos[cb];
-          y[cb][v] = live ? y[cb][v] * a.scale_log2 : kNegInf;
-        } else {
-          y[cb][v] *= a.scale_log2;
+          y[cb][v] = live ? y[cb][v] : kNegInf;
         }
         mx = fmaxf(mx, y[cb][v]);
       }
       mx = fmaxf(mx, xor16(mx));
       mx = fmaxf(mx, xor32(mx));
+      mx *= a.scale_log2;                                    // -inf stays -inf
       const float m_old = m_run[cb];
       const float m_new = (mx > m_old + kLazy) ? mx : m_old;    // -inf + kLazy = -inf
       const float m_use = (m_new == kNegInf) ? 0.f : m_new;
@@ -321,7 +343,7 @@ paged_prefill_kernel(const PrefillParams a) {
       float psum = 0.f;
 #pragma unroll
       for (int v = 0; v < kTpl; ++v) {
-        pw[cb][v] = exp2_fast(y[cb][v] - m_use);
+        pw[cb][v] = exp2_fast(fmaf(y[cb][v], a.scale_log2, -m_use));
         psum += pw[cb][v];
       }
       l_run[cb] = l_run[cb] * alpha[cb] + psum;
@@ -338,15 +360,24 @@ paged_prefill_kernel(const PrefillParams a) {
 
     // P.V: each V fragment (A operand) is read once and used by both blocks' weights (B)
     if constexpr (kBf16) {
+      // p = hi + lo: hi is p with its low 16 bits cleared (exact), lo = bf16(p - hi), so
+      // the pair carries p to ~2^-16; two weights per packing instruction
       bf16x8 phi[kPrefillBlocks], plo[kPrefillBlocks];
 #pragma unroll
-      for (int cb = 0; cb < kPrefillBlocks; ++cb)
+      for (int cb = 0; cb < kPrefillBlocks; ++cb) {
+        u32x4 hw, lw;
 #pragma unroll
-        for (int v = 0; v < 8; ++v) {
-          const __bf16 hi = f32_to_bf16(pw[cb][v]);
-          phi[cb][v] = hi;
-          plo[cb][v] = f32_to_bf16(pw[cb][v] - bf16_to_f32(hi));
+        for (int k = 0; k < 4; ++k) {
+          const uint32_t u0 = __float_as_uint(pw[cb][2 * k]);
+          const uint32_t u1 = __float_as_uint(pw[cb][2 * k + 1]);
+          hw[k] = __builtin_amdgcn_perm(u1, u0, 0x07060302u);    // upper halves of u0, u1
+          const f32x2 r = {pw[cb][2 * k] - __uint_as_float(u0 & 0xFFFF0000u),
+                           pw[cb][2 * k + 1] - __uint_as_float(u1 & 0xFFFF0000u)};
+          lw[k] = __builtin_bit_cast(uint32_t, __builtin_convertvector(r, bf16x2));
         }
+        phi[cb] = __builtin_bit_cast(bf16x8, hw);
+        plo[cb] = __builtin_bit_cast(bf16x8, lw);
+      }
 #pragma unroll
       for (int sl = 0; sl < kNs; ++sl) {
         const bf16x8 vv = __builtin_bit_cast(
@@ -450,6 +481,7 @@ extern "C" pa_status pa_paged_prefill(void* out, const void* query, const int32_
   if (num_seqs < 0 || max_blocks_per_seq <= 0 || num_blocks <= 0 || num_query_tokens < 0 ||
       max_query_len < 0)
     return PA_ERR_INVALID_ARG;
+  if (!(scale > 0.f) || !(scale <= 3.4028234663852886e38f)) return PA_ERR_INVALID_ARG;
   if (num_seqs == 0 || num_query_tokens == 0 || max_query_len == 0) return PA_OK;
   if (!out || !query || !query_start_loc || !block_table || !context_lens || !k_cache ||
       !v_cache)

@@ -156,6 +156,8 @@ def test_prefill_rejects_before_launch(lib):
         return f(*a)
     assert call({1: None}) == 1                  # query missing
     assert call({2: FAKE + 2}) == 1              # query_start_loc misaligned
+    for bad in (0.0, -0.5, float("nan"), float("inf")):
+        assert call({16: bad}) == 1              # scale must be positive and finite
     assert call({10: 96}) == 2                   # head size
     assert call({11: 24}) == 2                   # block size
     assert call({8: 24, 9: 8}) == 2              # group of 3 does not divide 128
