@@ -30,9 +30,32 @@ __device__ __forceinline__ float exp2_fast(float x) {
   return __builtin_amdgcn_exp2f(x);
 }
 
-// Butterfly partner across the four 16-lane rows of a wave64.
-__device__ __forceinline__ float xor16(float x) { return __shfl_xor(x, 16, 64); }
-__device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); }
+// Reductions across the four 16-lane rows of a wave64 (lanes n, n + 16, n + 32, n + 48)
+// with gfx950's VALU lane swaps instead of an LDS permute.  v_permlane16_swap exchanges
+// odd rows of its first operand with even rows of its second; given x twice, one result
+// holds x and the other the partner row's x (lane l ^ 16), in an order that depends on the
+// row -- so a symmetric op of the two results is x op x[l ^ 16] in every lane.
+// v_permlane32_swap does the same across the two halves of the wave (lane l ^ 32).
+__device__ __forceinline__ float max_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x),
+                                                  false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                  false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x),
+                                                  false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                  false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 // bfloat16 <-> float32 (round to nearest even on the way down).
 __device__ __forceinline__ float bf16_to_f32(__bf16 h) { return static_cast<float>(h); }

@@ -561,8 +561,8 @@ paged_decode_kernel(const DecodeParams a) {
       y[v] = live ? y[v] * a.scale_log2 : kNegInf;
       mx = fmaxf(mx, y[v]);
     }
-    mx = fmaxf(mx, xor16(mx));
-    mx = fmaxf(mx, xor32(mx));
+    mx = max_xor16(mx);
+    mx = max_xor32(mx);
     const float m_new = fmaxf(m_run, mx);
     const float m_use = (m_new == kNegInf) ? 0.f : m_new;
     const float alpha = exp2_fast(m_run - m_use);
@@ -659,8 +659,8 @@ paged_decode_kernel(const DecodeParams a) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) acc[sl][e] += __shfl_down(acc[sl][e], g, 16);
   }
-  float lsum = l_run + xor16(l_run);
-  lsum += xor32(lsum);
+  float lsum = sum_xor16(l_run);
+  lsum = sum_xor32(lsum);
   const int wstride = merge_words(D, g);
   float* wr = red + wave * wstride;
   if (n < g) {

@@ -333,8 +333,8 @@ paged_prefill_kernel(const PrefillParams a) {
         }
         mx = fmaxf(mx, y[cb][v]);
       }
-      mx = fmaxf(mx, xor16(mx));
-      mx = fmaxf(mx, xor32(mx));
+      mx = max_xor16(mx);
+      mx = max_xor32(mx);
       mx *= a.scale_log2;                                    // -inf stays -inf
       const float m_old = m_run[cb];
       const float m_new = (mx > m_old + kLazy) ? mx : m_old;    // -inf + kLazy = -inf
@@ -419,8 +419,8 @@ paged_prefill_kernel(const PrefillParams a) {
   // ---- normalise and write the rows -----------------------------------------------------
 #pragma unroll
   for (int cb = 0; cb < kPrefillBlocks; ++cb) {
-    float lsum = l_run[cb] + xor16(l_run[cb]);
-    lsum += xor32(lsum);
+    float lsum = sum_xor16(l_run[cb]);
+    lsum = sum_xor32(lsum);
     if (pos[cb] < 0) continue;
     const float inv = (m_run[cb] == kNegInf || lsum == 0.f) ? 0.f : 1.f / lsum;
 #pragma unroll
