@@ -173,16 +173,32 @@ paged_decode_kernel(const DecodeParams a) {
       lens[t] = t < a.S ? clamped_len(a, t, BS) : -1;
     __syncthreads();
     const int rB = a.S - 1 - r;
-    for (int t = threadIdx.x; t < a.S; t += kThreads) {
+    // rank of sequence t = how many sequences are longer (ties broken by index).  The
+    // S x S comparisons are spread over every thread: thread x compares t = x % S with
+    // the nparts-th slice (x / S) of the lengths and leaves a partial count in the merge
+    // area (free until the end), and thread t then adds its partial counts.
+    int* part_rank = reinterpret_cast<int*>(red);           // [nparts][S]
+    const int nparts = max(1, kThreads / a.S);              // S <= kThreads here
+    const int nq = lens_words / 4;                          // int4 groups of lengths
+    const int per = (nq + nparts - 1) / nparts;
+    for (int x = threadIdx.x; x < nparts * a.S; x += kThreads) {
+      const int t = x % a.S, pt = x / a.S;
       const int Lt = lens[t];
       int rank = 0;
-#pragma unroll 4
-      for (int u4 = 0; u4 < lens_words / 4; ++u4) {
-        const int4 v = reinterpret_cast<const int4*>(lens)[u4];   // same address in every lane
+      const int q1 = min(nq, (pt + 1) * per);
+#pragma unroll 2
+      for (int u4 = pt * per; u4 < q1; ++u4) {
+        const int4 v = reinterpret_cast<const int4*>(lens)[u4];
         const int u = 4 * u4;
         rank += (v.x > Lt) + (v.x == Lt && u < t) + (v.y > Lt) + (v.y == Lt && u + 1 < t) +
                 (v.z > Lt) + (v.z == Lt && u + 2 < t) + (v.w > Lt) + (v.w == Lt && u + 3 < t);
       }
+      part_rank[x] = rank;
+    }
+    __syncthreads();
+    for (int t = threadIdx.x; t < a.S; t += kThreads) {
+      int rank = 0;
+      for (int pt = 0; pt < nparts; ++pt) rank += part_rank[pt * a.S + t];
       if (rank == r) ctrl[0] = t;
       if (rank == rB) ctrl[1] = t;
     }
