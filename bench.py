@@ -566,8 +566,38 @@ def bench_swap(args) -> int:
                      "algorithmic_bytes_per_launch": int(moved)},
         "cpu_baseline": None,
     }
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle) ...")
+        line["cpu_baseline"] = cpu_baseline_swap(w, blocks, min(args.cpu_budget, 5.0))
     print(json.dumps(line), flush=True)
     return 0
+
+
+def cpu_baseline_swap(w, blocks: np.ndarray, budget_s: float) -> dict:
+    """The oracle's whole-block copies of the same blocks between two host pools (out and
+    back in), repeated for about budget_s (reported baseline)."""
+    import oracle
+    kc, vc = oracle.empty_pools(w.num_blocks, w.num_kv_heads, w.head_dim, w.block_size, w.dtype,
+                                fill="zero")
+    nh = len(blocks)
+    hk, hv = oracle.empty_pools(nh, w.num_kv_heads, w.head_dim, w.block_size, w.dtype,
+                                fill="zero")
+    out_map = np.stack([blocks, np.arange(nh)], axis=1)
+    in_map = np.stack([np.arange(nh), blocks], axis=1)
+    elt = 2 if w.dtype == "bf16" else 4
+    moved = 2 * nh * w.num_kv_heads * w.head_dim * w.block_size * elt
+    rounds = 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < budget_s:
+        oracle.swap_blocks(kc, vc, hk, hv, out_map, inplace=True)
+        oracle.swap_blocks(hk, hv, kc, vc, in_map, inplace=True)
+        rounds += 1
+    dt = time.perf_counter() - t0
+    return {"value": round(2 * rounds * moved / dt / 1e9, 3), "unit": "GB/s", "cores": 1,
+            "kind": "oracle",
+            "sample": (f"NumPy oracle, the same {nh} blocks out and back in between host "
+                       f"arrays, {rounds} rounds, {2 * rounds * moved / 1e6:.0f} MB in "
+                       f"{dt:.1f} s (one thread: NumPy copies)")}
 
 
 def main() -> int:
