@@ -91,6 +91,31 @@ def algorithmic_bytes(w) -> dict:
     return {"kv": kv, "other": 2 * q + table + 4 * w.num_seqs, "total": kv + 2 * q + table + 4 * w.num_seqs}
 
 
+def unique_kv_bytes(w) -> int:
+    """K+V bytes of the distinct slots the step reads: shared blocks (a common prefix, parallel
+    samples) count once, as HBM must deliver them at least once."""
+    elt = 2 if w.dtype == "bf16" else 4
+    slots = set()
+    for s in range(w.num_seqs):
+        L = int(w.context_lens[s])
+        nb = -(-L // w.block_size)
+        blocks = w.block_table[s, :nb].astype(np.int64)
+        pos = np.arange(L)
+        slots.update((blocks[pos // w.block_size] * w.block_size + pos % w.block_size).tolist())
+    return len(slots) * 2 * w.num_kv_heads * w.head_dim * elt
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown CPU"
+
+
 def source_digest() -> str:
     with open(KERNEL_SOURCE, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()
@@ -152,9 +177,9 @@ def cpu_baseline(w, budget_s: float) -> dict:
             "sample": (f"float64 NumPy oracle, same workload: {steps} whole steps (scatter of "
                        f"{len(new)} new tokens + decode of all {w.num_seqs} sequences) plus "
                        f"{done - steps * w.num_seqs} sequences of a partial step, "
-                       f"{kv / 1e6:.1f} MB of KV in {dt:.1f} s; "
-                       f"{len(os.sched_getaffinity(0))} cores visible, BLAS pool "
-                       f"{blas_threads} threads")}
+                       f"{kv / 1e6:.1f} MB of KV in {dt:.1f} s; {cpu_model()}, "
+                       f"{len(os.sched_getaffinity(0))} of {os.cpu_count()} cores visible, "
+                       f"BLAS pool {blas_threads} threads")}
 
 
 # ---------------------------------------------------------------------------
@@ -725,6 +750,7 @@ def main() -> int:
     ms_step = wall / K * 1e3
     value = nb["kv"] / (ms_step * 1e-3) / 1e9
     launch_avg_s = ev_s / K
+    kv_unique = unique_kv_bytes(w)
     achieved = fused_bytes / launch_avg_s / 1e9
     traffic = load_traffic(w.name)
     kernels = "paged_decode_kernel" + (" + reduce_partitions_kernel" if needs_reduce else "")
@@ -738,6 +764,7 @@ def main() -> int:
         "ms_per_step": round(ms_step, 5),
         "us_per_step": round(ms_step * 1e3, 2),
         "hbm_frac": round(value / HBM_PEAK_GBS, 4),
+        "hbm_frac_unique_kv": round(kv_unique / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -749,7 +776,8 @@ def main() -> int:
                    "max_context_len": w.max_context_len,
                    "total_context_tokens": int(w.context_lens.astype(np.int64).sum()),
                    "partition_size": part_used,
-                   "kv_bytes_per_step": nb["kv"], "seed": w.info["seed"],
+                   "kv_bytes_per_step": nb["kv"], "kv_bytes_unique": kv_unique,
+                   "seed": w.info["seed"],
                    "step": "pa_decode_step: scatter of the new tokens + paged decode, one launch",
                    "pool_bytes_each": int(kc0.numel() * kc0.element_size()),
                    "pool_replicas": R, "parallelism": "none (1 GPU)"},
