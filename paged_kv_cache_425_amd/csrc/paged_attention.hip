@@ -43,6 +43,16 @@
 //   rows [0, g) carry hi, rows [g, 2g) carry lo, and the two are added at the
 //   end.  The rows are there anyway (g <= 8 < 16), so this costs no extra MFMA.
 //
+// FP8 pools (cache element C = uint8_t, E4M3 codes; queries bf16)
+//   The cache element type is a template parameter.  With 1-byte codes a 16-byte
+//   load holds 16 channels of a K row or 16 tokens of a V row, so a step is 64
+//   tokens (four 16-row K tiles) at the register cost of a 32-token bf16 step.
+//   Codes are widened to bf16 in registers (v_cvt_scalef32_pk_bf16_fp8 at scale 1,
+//   exact: every E4M3 value is a bf16 value) and go through the same bf16 MFMAs;
+//   k_scale is folded into the softmax scale on the host and v_scale multiplies
+//   the output.  The fused step quantises the new token with the write kernel's
+//   encoder (e4m3_code) before patching it in.
+//
 // Lane mapping of a 16x16 MFMA output: lane l holds rows 4*(l/16)..+3 of
 // column l%16.  Below, n = l%16 and j = l/16.
 #include <algorithm>

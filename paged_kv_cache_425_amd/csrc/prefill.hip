@@ -18,15 +18,20 @@
 //   The workgroup streams the keys 0 .. (last position of the tile) in steps of
 //   32 keys (bf16) or 16 keys (f32).  Each step's K and V tiles are loaded once
 //   into LDS (every thread one 16-byte chunk of K and of V per 256 chunks) and
-//   read by all waves; the next step's chunks are loaded into registers while the
-//   current step is computed.
+//   read by all waves.  LDS holds two tile buffers: step st is computed from one
+//   while step st + 1 is staged into the other (one barrier per step), and the
+//   global loads run two steps ahead in registers.
 //   Q.K^T per column block is [keys x D] . [D x 16 rows] on MFMA (the K tile is the
 //   A operand, the query rows the B operand), P.V is [D x keys] . [keys x 16 rows]
-//   -- the same lane mapping as the decode kernel.  For bf16 the softmax weights
-//   enter P.V as two bf16 MFMAs, p = hi + lo, accumulated into one output.
-//   Rows keep a running max and sum (online softmax); key t counts for a row at
-//   position p only if t <= p.  V rows at positions >= L are zeroed in LDS (their
-//   weight is 0, and 0 * NaN is NaN).
+//   -- the same lane mapping as the decode kernel; each K or V fragment read from
+//   LDS feeds both column blocks of the wave.  For bf16 the softmax weights enter
+//   P.V as two bf16 MFMAs, p = hi + lo, accumulated into one output.
+//   Rows keep a running max and sum (online softmax, base 2, the scale applied in
+//   the exponent); the max moves only when a step raises it by more than kLazy, so
+//   the accumulators are rescaled on few steps.  Key t counts for a row at position
+//   p only if t <= p; steps wholly below the tile's first position skip the mask.
+//   V rows at positions >= L are zeroed in LDS (their weight is 0, and 0 * NaN is
+//   NaN).
 #include <algorithm>
 #include <type_traits>
 
