@@ -23,7 +23,6 @@ launches go to), and the CPU oracle's throughput on a bounded sample of the same
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -117,8 +116,8 @@ def cpu_model() -> str:
 
 
 def source_digest() -> str:
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    from paged_kv_cache_425_amd.rocprof_summary import kernel_source_digest
+    return kernel_source_digest(KERNEL_SOURCE)
 
 
 def load_traffic(workload: str, path: str = TRAFFIC_FILE):

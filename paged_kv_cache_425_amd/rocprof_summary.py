@@ -19,8 +19,9 @@ reads for a plain device copy of known size recorded in the same run: the
 largest ``__amd_rocclr_copyBuffer`` dispatches (the copies that clone the K/V
 pools) move ``--copy-bytes`` bytes each way, so the scale factor of a counter
 is copy_bytes / (its reading x 1024).  The JSON record carries the SHA-256 of
-the kernel source the counters were taken on, so a later change to the
-kernel makes the benchmark drop the figure.
+the kernel source the counters were taken on (comments and whitespace
+removed), so a later change to the kernel's code makes the benchmark drop
+the figure.
 """
 from __future__ import annotations
 
@@ -28,12 +29,24 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sqlite3
 import statistics
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 KERNEL_SOURCE = os.path.join(HERE, "csrc", "paged_attention.hip")
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
+
+
+def kernel_source_digest(path: str = KERNEL_SOURCE) -> str:
+    """SHA-256 of a kernel source with its comments and whitespace removed: it changes
+    when the code changes, not when a comment does."""
+    with open(path) as fh:
+        text = fh.read()
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)       # block comments
+    text = re.sub(r"//[^\n]*", " ", text)                     # line comments
+    text = re.sub(r"\s+", " ", text).strip()
+    return hashlib.sha256(text.encode()).hexdigest()
 
 
 def short(name: str) -> str:
@@ -217,8 +230,7 @@ def main() -> None:
     fetch_b = statistics.median(fk) * 1024.0 * ff
     write_b = statistics.median(wk) * 1024.0 * wf
     total = fetch_b + write_b
-    with open(KERNEL_SOURCE, "rb") as fh:
-        sha = hashlib.sha256(fh.read()).hexdigest()
+    sha = kernel_source_digest()
     rec = {"workload": a.workload, "kernel": a.kernel, "bytes_per_launch": int(round(total)),
            "fetch_bytes_per_launch": int(round(fetch_b)),
            "write_bytes_per_launch": int(round(write_b)),
@@ -249,7 +261,7 @@ K/V pools, {a.copy_bytes} bytes each.  FETCH_SIZE reads {fread:.1f} KiB for them
 | algorithmic bytes per launch | {a.algorithmic_bytes:,} |
 | measured / algorithmic | {total / a.algorithmic_bytes:.4f} |
 
-Kernel source SHA-256: `{sha}`.
+Kernel source SHA-256 (comments and whitespace removed): `{sha}`.
 """
     with open(a.out, "w") as fh:
         fh.write(text)
