@@ -141,7 +141,11 @@ FUSED_CASES = [("cfg0", lambda: make_config(0), 0),
                ("tiny-bf16-bs8-P128", lambda: tiny("bf16", LENS, 16, 2, 64, 8, seed=32), 128),
                ("tiny-bf16-paired", lambda: tiny("bf16", LENS, 16, 2, 64, 32, seed=33), 0),
                ("many-seqs-unpaired", lambda: tiny("bf16", np.random.default_rng(34).integers(
-                   1, 90, size=600), 8, 2, 128, 16, seed=34), 128)]
+                   1, 90, size=600), 8, 2, 128, 16, seed=34), 128),
+               ("long-tail-P512", lambda: tiny("bf16", long_tail_lens(37), 32, 8, 128, 16,
+                                               seed=37), 512),
+               ("long-tail-f32-bs8-P64", lambda: tiny("f32", long_tail_lens(38), 32, 8, 64, 8,
+                                                      seed=38), 64)]
 
 
 def fused_inputs(w):
@@ -234,6 +238,33 @@ def test_paired_mode_odd_count_and_uneven_pairs():
     kc, vc = build_pools(w)
     say("paired mode, 7 sequences")
     check_close(to_f64(run_gpu(w, kc, vc, 768)), oracle_out(w, kc, vc), "bf16", "paired-odd")
+
+
+def long_tail_lens(seed: int) -> np.ndarray:
+    """64 sequences: 58 short, 6 long, three at exact multiples of 512."""
+    rng = np.random.default_rng(seed)
+    lens = np.concatenate([rng.integers(1, 300, size=58), rng.integers(2000, 4500, size=6)])
+    lens[3], lens[10], lens[60] = 512, 1024, 4096
+    return rng.permutation(lens)
+
+
+@pytest.mark.parametrize("dtype,D,BS", [("bf16", 128, 16), ("bf16", 64, 8), ("f32", 64, 32),
+                                        ("f32", 128, 16)])
+def test_full_batch_with_a_long_tail(dtype, D, BS):
+    """A batch whose (sequence, kv head) pairs alone fill the GPU (64 x 8), with a few
+    sequences far longer than the partition, an empty one and lengths at exact multiples of
+    the partition: partitions from 64 to 2048 tokens, merged by the log-sum-exp reduce."""
+    lens = long_tail_lens(50 + D + BS)
+    w = tiny(dtype, lens, 32, 8, D, BS, seed=51 + D + BS)
+    kc, vc = build_pools(w)
+    w.context_lens = w.context_lens.copy()
+    w.context_lens[7] = 0
+    ref = oracle_out(w, kc, vc)
+    for part in (64, 512, 1024, 2048):
+        say(f"long tail {dtype} D={D} BS={BS} P={part}")
+        out = run_gpu(w, kc, vc, part)
+        assert np.array_equal(bits(out)[7], np.zeros_like(bits(out)[7]))
+        check_close(to_f64(out), ref, dtype, f"long-tail/{dtype}/{D}/{BS}/{part}")
 
 
 def test_many_sequences_single_partition_unpaired():
