@@ -150,7 +150,7 @@ paged_decode_kernel(const DecodeParams a) {
   constexpr int kNs = Sh::kNs;
   constexpr int kThreads = NW * 64;
 
-  // LDS: [ctrl: 16 ints][new K/V: 2 units x 2 x D elements][lens: S ints, PAIRED only]
+  // LDS: [ctrl: 16 ints][new K/V: 2 units x 2 x D elements][sort keys: S ints, PAIRED only]
   //      [tables: 1 or 2 windows of P/BS][merge]
   extern __shared__ __align__(16) unsigned char smem[];
   int* ctrl = reinterpret_cast<int*>(smem);
@@ -178,30 +178,31 @@ paged_decode_kernel(const DecodeParams a) {
   const int* tblw = tbl;
   if constexpr (PAIRED) {
     const int r = id;                                       // pair index
-    // lengths, padded with -1 to a multiple of 4 (a pad never counts as longer)
+    // Sort keys: key_t = (L_t << 10) | (1023 - t), unique per sequence and ordered by
+    // length, then by index for equal lengths (L_t <= P <= 8192 here, and S <= 512, so the
+    // key fits in 24 bits; L_t = key >> 10).  Padded to a multiple of 4 with 0, below
+    // every real key.
     for (int t = threadIdx.x; t < lens_words; t += kThreads)
-      lens[t] = t < a.S ? clamped_len(a, t, BS) : -1;
+      lens[t] = t < a.S ? (clamped_len(a, t, BS) << 10) | (1023 - t) : 0;
     __syncthreads();
     const int rB = a.S - 1 - r;
-    // rank of sequence t = how many sequences are longer (ties broken by index).  The
-    // S x S comparisons are spread over every thread: thread x compares t = x % S with
-    // the nparts-th slice (x / S) of the lengths and leaves a partial count in the merge
-    // area (free until the end), and thread t then adds its partial counts.
+    // rank of sequence t = how many keys are larger: one comparison per pair.  The S x S
+    // comparisons are spread over every thread: thread x compares t = x % S with the
+    // nparts-th slice (x / S) of the keys and leaves a partial count in the merge area
+    // (free until the end), and thread t then adds its partial counts.
     int* part_rank = reinterpret_cast<int*>(red);           // [nparts][S]
     const int nparts = max(1, kThreads / a.S);              // S <= kThreads here
-    const int nq = lens_words / 4;                          // int4 groups of lengths
+    const int nq = lens_words / 4;                          // int4 groups of keys
     const int per = (nq + nparts - 1) / nparts;
     for (int x = threadIdx.x; x < nparts * a.S; x += kThreads) {
       const int t = x % a.S, pt = x / a.S;
-      const int Lt = lens[t];
+      const int Kt = lens[t];
       int rank = 0;
       const int q1 = min(nq, (pt + 1) * per);
-#pragma unroll 2
+#pragma unroll 4
       for (int u4 = pt * per; u4 < q1; ++u4) {
         const int4 v = reinterpret_cast<const int4*>(lens)[u4];
-        const int u = 4 * u4;
-        rank += (v.x > Lt) + (v.x == Lt && u < t) + (v.y > Lt) + (v.y == Lt && u + 1 < t) +
-                (v.z > Lt) + (v.z == Lt && u + 2 < t) + (v.w > Lt) + (v.w == Lt && u + 3 < t);
+        rank += (v.x > Kt) + (v.y > Kt) + (v.z > Kt) + (v.w > Kt);
       }
       part_rank[x] = rank;
     }
@@ -215,8 +216,8 @@ paged_decode_kernel(const DecodeParams a) {
     __syncthreads();
     sA = __builtin_amdgcn_readfirstlane(ctrl[0]);
     sB = r == rB ? -1 : __builtin_amdgcn_readfirstlane(ctrl[1]);
-    const int LA = lens[sA];
-    const int LB = sB >= 0 ? lens[sB] : 0;
+    const int LA = lens[sA] >> 10;
+    const int LB = sB >= 0 ? lens[sB] >> 10 : 0;
     // split the waves so that the busier unit's waves finish together
     const int stA = (LA + kStep - 1) / kStep, stB = (LB + kStep - 1) / kStep;
     if (stB > 0) {
@@ -340,7 +341,7 @@ paged_decode_kernel(const DecodeParams a) {
 
   // a new slot that is not where position L - 1 is read from: store it here
   if (new_slot >= 0 && new_slot < nslots) {
-    const int Lu = PAIRED ? lens[new_u ? sB : sA] : tok1;
+    const int Lu = PAIRED ? lens[new_u ? sB : sA] >> 10 : tok1;
     const int64_t loc =
         Lu > 0 ? slot_of(PAIRED ? tbl + new_u * win : tbl, PAIRED ? 0 : tok0, Lu - 1) : -1;
     if (new_slot != loc && kFp8) {
@@ -784,6 +785,7 @@ constexpr int kWaves = PA_DECODE_WAVES;     // waves per workgroup, partition mo
 constexpr int kPairWaves = 8;               // waves per workgroup, paired mode
 constexpr int kPipe = PA_DECODE_PIPE;
 constexpr int kMaxPairedSeqs = 512;         // the in-kernel ordering is O(S^2 / threads)
+static_assert(kMaxPairedSeqs <= 1024, "a sort key holds 10 bits of sequence index");
 constexpr size_t kMaxLds = 64 * 1024;
 
 // Dynamic LDS of one workgroup; mirrors the layout at the top of paged_decode_kernel.
@@ -889,6 +891,7 @@ int device_cu_count() {
 }
 
 constexpr int kMaxPartition = 8192;
+static_assert(kMaxPartition <= (1 << 20), "a paired-mode sort key holds the length in 21 bits");
 
 }  // namespace
 
