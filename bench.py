@@ -66,6 +66,10 @@ def parse_args():
                     help="tokens per partition (0 = library default)")
     ap.add_argument("--replicas", type=int, default=4,
                     help="copies of the K/V pools the steps rotate over")
+    ap.add_argument("--order", choices=["host", "device"], default="host",
+                    help="order of the sequences for the paired decode: sorted on the host "
+                         "from a host copy of the lengths (host_context_lens), or ranked "
+                         "inside every workgroup; the other order is timed beside it")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--warm", action="store_true",
                     help="also time K steps over one pool copy (Infinity Cache warm)")
@@ -418,33 +422,43 @@ def bench_fp8(args) -> int:
                              w.max_context_len, part, torch.bfloat16)
     ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
-    fused = [pk.prepare_decode_step_fp8(query, key_new, val_new, slot_new, table, lens, kc, vc,
-                                        w.scale, FP8_K_SCALE, FP8_V_SCALE,
-                                        max_context_len=w.max_context_len, out=out,
-                                        partition_size=part, workspace=ws) for kc, vc in pools]
+    host_lens = w.context_lens.copy()
+
+    def prep_fused(order):
+        hl = host_lens if order == "host" else None
+        return [pk.prepare_decode_step_fp8(query, key_new, val_new, slot_new, table, lens, kc,
+                                           vc, w.scale, FP8_K_SCALE, FP8_V_SCALE,
+                                           max_context_len=w.max_context_len, out=out,
+                                           partition_size=part, workspace=ws,
+                                           host_context_lens=hl) for kc, vc in pools]
+    other_order = "device" if args.order == "host" else "host"
+    fused, fused_other = prep_fused(args.order), prep_fused(other_order)
     writes = [pk.prepare_reshape_and_cache_fp8(key_new, val_new, slot_new, kc, vc, FP8_K_SCALE,
                                                FP8_V_SCALE) for kc, vc in pools]
     decodes = [pk.prepare_paged_attention_fp8(query, table, lens, kc, vc, w.scale, FP8_K_SCALE,
                                               FP8_V_SCALE, max_context_len=w.max_context_len,
-                                              out=out, partition_size=part, workspace=ws)
+                                              out=out, partition_size=part, workspace=ws,
+                                              host_context_lens=host_lens
+                                              if args.order == "host" else None)
                for kc, vc in pools]
     R, K, W = len(pools), args.steps, args.warmup
 
-    def run_fused(steps: int) -> None:
+    def run_fused(steps: int, calls=None) -> None:
+        calls = fused if calls is None else calls
         for i in range(steps):
-            fused[i % R]()
+            calls[i % R]()
 
     def run_two_calls(steps: int) -> None:
         for i in range(steps):
             writes[i % R]()
             decodes[i % R]()
 
-    def timed(fn, steps):
+    def timed(fn, steps, *a):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         e0.record()
-        fn(steps)
+        fn(steps, *a)
         e1.record()
         torch.cuda.synchronize()
         return time.perf_counter() - t0, e0.elapsed_time(e1) * 1e-3
@@ -456,6 +470,9 @@ def bench_fp8(args) -> int:
     run_two_calls(W)
     wall2, ev2 = timed(run_two_calls, K)
     log(f"FP8 two-call step: {wall2 / K * 1e6:.1f} us/step wall")
+    run_fused(W, fused_other)
+    wall3, ev3 = timed(run_fused, K, fused_other)
+    log(f"FP8 fused step, {other_order} order: {wall3 / K * 1e6:.1f} us/step wall")
 
     lens64 = w.context_lens.astype(np.int64)
     kv = int(lens64.sum()) * 2 * w.num_kv_heads * w.head_dim            # 1 byte per element
@@ -485,12 +502,16 @@ def bench_fp8(args) -> int:
                    "k_scale": FP8_K_SCALE, "v_scale": FP8_V_SCALE, "kv_bytes_per_step": kv,
                    "step": "pa_decode_step_fp8: quantised scatter of the new tokens + paged "
                            "decode, one launch",
+                   "order": args.order,
                    "pool_bytes_each": int(kc0.numel()), "pool_replicas": R,
                    "parallelism": "none (1 GPU)"},
         "launch_us_events": round(ev / K * 1e6, 2),
         "two_call_step": {"us_per_step": round(wall2 / K * 1e6, 2),
                           "us_per_step_events": round(ev2 / K * 1e6, 2),
                           "value": round(kv / (wall2 / K) / 1e9, 2)},
+        f"{other_order}_order_step": {"us_per_step": round(wall3 / K * 1e6, 2),
+                                      "launch_us_events": round(ev3 / K * 1e6, 2),
+                                      "value": round(kv / (wall3 / K) / 1e9, 2)},
         "roofline": {"kernel": "pa_decode_step_fp8: paged_decode_kernel<bf16, e4m3>",
                      "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
@@ -684,14 +705,25 @@ def main() -> int:
     ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
 
-    # the step as one launch (pa_decode_step) and as the two calls
-    fused = [pk.prepare_decode_step(query, key_new, val_new, slot_new, table, lens, kc, vc,
-                                    w.scale, max_context_len=w.max_context_len, out=out,
-                                    partition_size=part, workspace=ws) for kc, vc in pools]
+    # the step as one launch (pa_decode_step) and as the two calls.  With --order host the
+    # library sorts the scheduler's host copy of the lengths on every call (the copy a
+    # serving loop keeps), so the host work of each step is inside the timed loop.
+    host_lens = w.context_lens.copy()
+
+    def prep_fused(order):
+        hl = host_lens if order == "host" else None
+        return [pk.prepare_decode_step(query, key_new, val_new, slot_new, table, lens, kc, vc,
+                                       w.scale, max_context_len=w.max_context_len, out=out,
+                                       partition_size=part, workspace=ws, host_context_lens=hl)
+                for kc, vc in pools]
+    other_order = "device" if args.order == "host" else "host"
+    fused, fused_other = prep_fused(args.order), prep_fused(other_order)
     writes = [pk.prepare_reshape_and_cache(key_new, val_new, slot_new, kc, vc) for kc, vc in pools]
     decodes = [pk.prepare_paged_attention(query, table, lens, kc, vc, w.scale,
                                           max_context_len=w.max_context_len, out=out,
-                                          partition_size=part, workspace=ws)
+                                          partition_size=part, workspace=ws,
+                                          host_context_lens=host_lens if args.order == "host"
+                                          else None)
                for kc, vc in pools]
     nb = algorithmic_bytes(w)
     elt = 2 if w.dtype == "bf16" else 4
@@ -701,9 +733,10 @@ def main() -> int:
     part_used = part or pk.default_partition_size(w.num_seqs, w.num_kv_heads, w.max_context_len, tdt)
     needs_reduce = w.max_context_len > part_used
 
-    def run_fused(n_rep: int, steps: int) -> None:
+    def run_fused(n_rep: int, steps: int, calls=None) -> None:
+        calls = fused if calls is None else calls
         for i in range(steps):
-            fused[i % n_rep]()
+            calls[i % n_rep]()
 
     def run_two_calls(n_rep: int, steps: int) -> None:
         for i in range(steps):
@@ -735,6 +768,10 @@ def main() -> int:
     run_two_calls(R, W)
     wall2, ev2 = timed(run_two_calls, R, K)
     log(f"cold two-call step: {wall2 / K * 1e6:.1f} us/step wall")
+    # ---- the fused step with the other order of the sequences -----------------
+    run_fused(R, W, fused_other)
+    wall3, ev3 = timed(run_fused, R, K, fused_other)
+    log(f"cold fused step, {other_order} order: {wall3 / K * 1e6:.1f} us/step wall")
 
     # ---- warm (optional): one pool, repeated ----------------------------------
     warm = None
@@ -778,12 +815,17 @@ def main() -> int:
                    "kv_bytes_per_step": nb["kv"], "kv_bytes_unique": kv_unique,
                    "seed": w.info["seed"],
                    "step": "pa_decode_step: scatter of the new tokens + paged decode, one launch",
+                   "order": args.order + (" (host_context_lens sorted on the host every call)"
+                                          if args.order == "host" else " (ranked in-kernel)"),
                    "pool_bytes_each": int(kc0.numel() * kc0.element_size()),
                    "pool_replicas": R, "parallelism": "none (1 GPU)"},
         "launch_us_events": round(launch_avg_s * 1e6, 2),
         "two_call_step": {"us_per_step": round(wall2 / K * 1e6, 2),
                           "us_per_step_events": round(ev2 / K * 1e6, 2),
                           "value": round(nb["kv"] / (wall2 / K) / 1e9, 2)},
+        f"{other_order}_order_step": {"us_per_step": round(wall3 / K * 1e6, 2),
+                                      "launch_us_events": round(ev3 / K * 1e6, 2),
+                                      "value": round(nb["kv"] / (wall3 / K) / 1e9, 2)},
         "warm": warm,
         "roofline": {"kernel": f"pa_decode_step: {kernels}",
                      "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,

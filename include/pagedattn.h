@@ -17,7 +17,8 @@
  *
  * Conventions shared by every call
  * --------------------------------
- * - All array arguments are DEVICE pointers owned by the caller; the library
+ * - All array arguments are DEVICE pointers owned by the caller (the one
+ *   exception, host_context_lens of the decode calls, says so); the library
  *   allocates nothing and keeps no device state between calls.
  * - Every call is asynchronous on `stream` (a hipStream_t passed as void*;
  *   NULL means the null stream) and never synchronises the host.
@@ -57,7 +58,7 @@
 extern "C" {
 #endif
 
-#define PA_ABI_VERSION 1
+#define PA_ABI_VERSION 2
 
 typedef enum {
     PA_OK = 0,
@@ -132,6 +133,17 @@ size_t pa_paged_attention_workspace_size(int num_seqs, int num_heads, int num_kv
  *                  It holds per-partition (max, sum, partial output) rows
  *                  between the two kernels.  Two calls in flight at once must
  *                  not share a workspace.
+ *   host_context_lens  optional HOST copy of context_lens ([num_seqs] int32,
+ *                  read during the call only), or NULL.  When every sequence
+ *                  is one partition, the kernel gives each workgroup the r-th
+ *                  longest and the r-th shortest sequence; with this copy the
+ *                  library sorts the lengths on the host and passes the order
+ *                  with the launch, so that the workgroups need not rank the
+ *                  lengths themselves.  The device context_lens still decide
+ *                  every length the kernel reads; a host copy that differs
+ *                  from them changes only how the work is spread, not the
+ *                  result's accuracy.  When it matches, the output is the same
+ *                  bit for bit as with NULL.
  */
 pa_status pa_paged_attention(void* out, const void* query, const int32_t* block_table,
                              const int32_t* context_lens, const void* k_cache,
@@ -139,7 +151,8 @@ pa_status pa_paged_attention(void* out, const void* query, const int32_t* block_
                              int num_kv_heads, int head_dim, int block_size,
                              int max_blocks_per_seq, int num_blocks, int max_context_len,
                              float scale, pa_dtype dtype, int partition_size,
-                             void* workspace, size_t workspace_bytes, void* stream);
+                             void* workspace, size_t workspace_bytes, void* stream,
+                             const int32_t* host_context_lens);
 
 /*
  * Write path: store each new token's K and V into its slot.
@@ -184,7 +197,8 @@ pa_status pa_decode_step(void* out, const void* query, const void* key, const vo
                          int num_seqs, int num_heads, int num_kv_heads, int head_dim,
                          int block_size, int max_blocks_per_seq, int num_blocks,
                          int max_context_len, float scale, pa_dtype dtype, int partition_size,
-                         void* workspace, size_t workspace_bytes, void* stream);
+                         void* workspace, size_t workspace_bytes, void* stream,
+                         const int32_t* host_context_lens);
 
 /*
  * Paged prefill: causal attention of a chunk of new query tokens per sequence
@@ -286,7 +300,7 @@ pa_status pa_paged_attention_fp8(void* out, const void* query, const int32_t* bl
                                  int max_blocks_per_seq, int num_blocks, int max_context_len,
                                  float scale, float k_scale, float v_scale, pa_dtype dtype,
                                  int partition_size, void* workspace, size_t workspace_bytes,
-                                 void* stream);
+                                 void* stream, const int32_t* host_context_lens);
 
 /*
  * One decode step over FP8 pools in a single launch: quantise each sequence's
@@ -303,7 +317,8 @@ pa_status pa_decode_step_fp8(void* out, const void* query, const void* key, cons
                              int block_size, int max_blocks_per_seq, int num_blocks,
                              int max_context_len, float scale, float k_scale, float v_scale,
                              pa_dtype dtype, int partition_size, void* workspace,
-                             size_t workspace_bytes, void* stream);
+                             size_t workspace_bytes, void* stream,
+                             const int32_t* host_context_lens);
 
 /*
  * Swapping: make block d of the destination pools a copy of block s of the

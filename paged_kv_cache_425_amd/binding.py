@@ -41,11 +41,11 @@ def load_library() -> ctypes.CDLL:
     lib.pa_paged_attention_workspace_size.restype = sz
     lib.pa_paged_attention_workspace_size.argtypes = [i32] * 7
     lib.pa_paged_attention.restype = i32
-    lib.pa_paged_attention.argtypes = [vp] * 6 + [i32] * 8 + [f32, i32, i32, vp, sz, vp]
+    lib.pa_paged_attention.argtypes = [vp] * 6 + [i32] * 8 + [f32, i32, i32, vp, sz, vp, vp]
     lib.pa_reshape_and_cache.restype = i32
     lib.pa_reshape_and_cache.argtypes = [vp] * 5 + [i32] * 6 + [vp]
     lib.pa_decode_step.restype = i32
-    lib.pa_decode_step.argtypes = [vp] * 9 + [i32] * 8 + [f32, i32, i32, vp, sz, vp]
+    lib.pa_decode_step.argtypes = [vp] * 9 + [i32] * 8 + [f32, i32, i32, vp, sz, vp, vp]
     lib.pa_paged_prefill.restype = i32
     lib.pa_paged_prefill.argtypes = [vp] * 7 + [i32] * 9 + [f32, i32, vp]
     lib.pa_copy_blocks.restype = i32
@@ -57,10 +57,11 @@ def load_library() -> ctypes.CDLL:
     lib.pa_swap_blocks.restype = i32
     lib.pa_swap_blocks.argtypes = [vp] * 5 + [i32] * 6 + [i32, vp]
     lib.pa_decode_step_fp8.restype = i32
-    lib.pa_decode_step_fp8.argtypes = [vp] * 9 + [i32] * 8 + [f32] * 3 + [i32, i32, vp, sz, vp]
+    lib.pa_decode_step_fp8.argtypes = [vp] * 9 + [i32] * 8 + [f32] * 3 + [i32, i32, vp, sz, vp,
+                                                                          vp]
     lib.pa_paged_attention_fp8.restype = i32
     lib.pa_paged_attention_fp8.argtypes = [vp] * 6 + [i32] * 8 + [f32] * 3 + [i32, i32, vp, sz,
-                                                                              vp]
+                                                                              vp, vp]
     _lib = lib
     return lib
 
@@ -84,6 +85,24 @@ def _ptr(t: torch.Tensor | None) -> int | None:
 def _stream(device: torch.device, stream) -> int:
     s = torch.cuda.current_stream(device) if stream is None else stream
     return s.cuda_stream
+
+
+def _host_lens(host_context_lens, num_seqs: int):
+    """(pointer, holder) of an optional host int32 copy of context_lens [num_seqs]."""
+    if host_context_lens is None:
+        return None, None
+    if isinstance(host_context_lens, torch.Tensor):
+        if host_context_lens.is_cuda:
+            raise ValueError("host_context_lens must be in host memory")
+        arr = host_context_lens.detach().to(torch.int32).contiguous()
+        ptr = arr.data_ptr()
+    else:
+        import numpy as np
+        arr = np.ascontiguousarray(host_context_lens, dtype=np.int32)
+        ptr = arr.ctypes.data
+    if arr.shape != (num_seqs,):
+        raise ValueError(f"host_context_lens must be [{num_seqs}], got {tuple(arr.shape)}")
+    return ptr, arr
 
 
 def _require(t: torch.Tensor, name: str, device: torch.device, dtype=None) -> None:
@@ -141,8 +160,9 @@ def paged_attention(query: torch.Tensor, block_table: torch.Tensor, context_lens
                     k_cache: torch.Tensor, v_cache: torch.Tensor, scale: float, *,
                     max_context_len: int, out: torch.Tensor | None = None,
                     partition_size: int = 0, workspace: torch.Tensor | None = None,
-                    stream=None) -> torch.Tensor:
-    """Decode attention of query [S, Hq, D] over the paged caches (see pagedattn.h)."""
+                    stream=None, host_context_lens=None) -> torch.Tensor:
+    """Decode attention of query [S, Hq, D] over the paged caches (see pagedattn.h).
+    host_context_lens: optional host copy of context_lens (numpy or CPU tensor)."""
     lib = load_library()
     dev = query.device
     _require(query, "query", dev)
@@ -169,16 +189,18 @@ def paged_attention(query: torch.Tensor, block_table: torch.Tensor, context_lens
     if workspace is not None:
         _require(workspace, "workspace", dev)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    hl, _hold = _host_lens(host_context_lens, S)
     st = lib.pa_paged_attention(_ptr(out), _ptr(query), _ptr(block_table), _ptr(context_lens),
                                 _ptr(k_cache), _ptr(v_cache), S, Hq, Hkv, D, BS, MB, NB,
                                 int(max_context_len), float(scale), code, int(partition_size),
-                                _ptr(workspace), ws_bytes, _stream(dev, stream))
+                                _ptr(workspace), ws_bytes, _stream(dev, stream), hl)
     _check(st, "pa_paged_attention")
     return out
 
 
 def _decode_step_args(query, key, value, slot_mapping, block_table, context_lens, k_cache,
-                      v_cache, scale, max_context_len, out, partition_size, workspace, stream):
+                      v_cache, scale, max_context_len, out, partition_size, workspace, stream,
+                      host_context_lens=None):
     """Checked argument tuple of pa_decode_step (allocates out/workspace when None)."""
     dev = query.device
     _require(query, "query", dev)
@@ -207,12 +229,13 @@ def _decode_step_args(query, key, value, slot_mapping, block_table, context_lens
     if workspace is not None:
         _require(workspace, "workspace", dev)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    hl, hold = _host_lens(host_context_lens, S)
     args = (_ptr(out), _ptr(query), _ptr(key), _ptr(value), _ptr(slot_mapping), _ptr(block_table),
             _ptr(context_lens), _ptr(k_cache), _ptr(v_cache), S, Hq, Hkv, D, BS,
             block_table.shape[1], NB, int(max_context_len), float(scale), _dtype_code(query),
-            int(partition_size), _ptr(workspace), ws_bytes, _stream(dev, stream))
+            int(partition_size), _ptr(workspace), ws_bytes, _stream(dev, stream), hl)
     keep = (query, key, value, slot_mapping, block_table, context_lens, k_cache, v_cache, out,
-            workspace)
+            workspace, hold)
     return args, out, keep
 
 
@@ -220,13 +243,14 @@ def decode_step(query: torch.Tensor, key: torch.Tensor, value: torch.Tensor,
                 slot_mapping: torch.Tensor, block_table: torch.Tensor, context_lens: torch.Tensor,
                 k_cache: torch.Tensor, v_cache: torch.Tensor, scale: float, *,
                 max_context_len: int, out: torch.Tensor | None = None, partition_size: int = 0,
-                workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+                workspace: torch.Tensor | None = None, stream=None,
+                host_context_lens=None) -> torch.Tensor:
     """One fused step: store key/value [S, Hkv, D] at slot_mapping [S], then decode
     attention of query [S, Hq, D] (see pa_decode_step in pagedattn.h)."""
     lib = load_library()
     args, out, _ = _decode_step_args(query, key, value, slot_mapping, block_table, context_lens,
                                      k_cache, v_cache, scale, max_context_len, out,
-                                     partition_size, workspace, stream)
+                                     partition_size, workspace, stream, host_context_lens)
     _check(lib.pa_decode_step(*args), "pa_decode_step")
     return out
 
@@ -285,7 +309,8 @@ def reshape_and_cache_fp8(key: torch.Tensor, value: torch.Tensor, slot_mapping: 
 
 
 def _attention_fp8_args(query, block_table, context_lens, k_cache, v_cache, scale, k_scale,
-                        v_scale, max_context_len, out, partition_size, workspace, stream):
+                        v_scale, max_context_len, out, partition_size, workspace, stream,
+                        host_context_lens=None):
     dev = query.device
     NB, Hkv, D, BS = _fp8_cache_dims(k_cache, v_cache)
     _require(query, "query", dev)
@@ -313,7 +338,9 @@ def _attention_fp8_args(query, block_table, context_lens, k_cache, v_cache, scal
             _ptr(v_cache), S, Hq, Hkv, D, BS, block_table.shape[1], NB, int(max_context_len),
             float(scale), float(k_scale), float(v_scale), _dtype_code(query),
             int(partition_size), _ptr(workspace), ws_bytes, _stream(dev, stream))
-    keep = (query, block_table, context_lens, k_cache, v_cache, out, workspace)
+    hl, hold = _host_lens(host_context_lens, S)
+    args = args + (hl,)
+    keep = (query, block_table, context_lens, k_cache, v_cache, out, workspace, hold)
     return args, out, keep
 
 
@@ -321,18 +348,19 @@ def paged_attention_fp8(query: torch.Tensor, block_table: torch.Tensor,
                         context_lens: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                         scale: float, k_scale: float, v_scale: float, *, max_context_len: int,
                         out: torch.Tensor | None = None, partition_size: int = 0,
-                        workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+                        workspace: torch.Tensor | None = None, stream=None,
+                        host_context_lens=None) -> torch.Tensor:
     """Decode attention of bf16 query [S, Hq, D] over FP8 pools (see pagedattn.h)."""
     args, out, _ = _attention_fp8_args(query, block_table, context_lens, k_cache, v_cache, scale,
                                        k_scale, v_scale, max_context_len, out, partition_size,
-                                       workspace, stream)
+                                       workspace, stream, host_context_lens)
     _check(load_library().pa_paged_attention_fp8(*args), "pa_paged_attention_fp8")
     return out
 
 
 def _decode_step_fp8_args(query, key, value, slot_mapping, block_table, context_lens, k_cache,
                           v_cache, scale, k_scale, v_scale, max_context_len, out,
-                          partition_size, workspace, stream):
+                          partition_size, workspace, stream, host_context_lens=None):
     dev = query.device
     NB, Hkv, D, BS = _fp8_cache_dims(k_cache, v_cache)
     S = query.shape[0] if query.dim() == 3 else -1
@@ -344,7 +372,7 @@ def _decode_step_fp8_args(query, key, value, slot_mapping, block_table, context_
         raise ValueError(f"key/value must be [{S}, {Hkv}, {D}] and slot_mapping [{S}]")
     args, out, keep = _attention_fp8_args(query, block_table, context_lens, k_cache, v_cache,
                                           scale, k_scale, v_scale, max_context_len, out,
-                                          partition_size, workspace, stream)
+                                          partition_size, workspace, stream, host_context_lens)
     # pa_decode_step_fp8 takes key, value and slot_mapping after query
     args = args[:2] + (_ptr(key), _ptr(value), _ptr(slot_mapping)) + args[2:]
     return args, out, keep + (key, value, slot_mapping)
@@ -355,12 +383,14 @@ def decode_step_fp8(query: torch.Tensor, key: torch.Tensor, value: torch.Tensor,
                     context_lens: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                     scale: float, k_scale: float, v_scale: float, *, max_context_len: int,
                     out: torch.Tensor | None = None, partition_size: int = 0,
-                    workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+                    workspace: torch.Tensor | None = None, stream=None,
+                    host_context_lens=None) -> torch.Tensor:
     """One fused step over FP8 pools: quantise key/value [S, Hkv, D] (bf16) into
     slot_mapping [S], then decode attention of query [S, Hq, D] (see pa_decode_step_fp8)."""
     args, out, _ = _decode_step_fp8_args(query, key, value, slot_mapping, block_table,
                                          context_lens, k_cache, v_cache, scale, k_scale, v_scale,
-                                         max_context_len, out, partition_size, workspace, stream)
+                                         max_context_len, out, partition_size, workspace, stream,
+                                         host_context_lens)
     _check(load_library().pa_decode_step_fp8(*args), "pa_decode_step_fp8")
     return out
 
@@ -521,7 +551,7 @@ class PreparedCall:
 
 def prepare_paged_attention(query, block_table, context_lens, k_cache, v_cache, scale, *,
                             max_context_len: int, out, partition_size: int = 0,
-                            workspace=None, stream=None) -> PreparedCall:
+                            workspace=None, stream=None, host_context_lens=None) -> PreparedCall:
     """Check the arguments as paged_attention does and return a re-launchable call."""
     lib = load_library()
     dev = query.device
@@ -533,16 +563,18 @@ def prepare_paged_attention(query, block_table, context_lens, k_cache, v_cache, 
     # one checked call validates every argument (and runs once)
     paged_attention(query, block_table, context_lens, k_cache, v_cache, scale,
                     max_context_len=max_context_len, out=out, partition_size=partition_size,
-                    workspace=workspace, stream=stream)
+                    workspace=workspace, stream=stream, host_context_lens=host_context_lens)
     NB, Hkv, D, BS = _cache_dims(k_cache, v_cache)
     S, Hq, _ = query.shape
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    hl, hold = _host_lens(host_context_lens, S)
     args = (_ptr(out), _ptr(query), _ptr(block_table), _ptr(context_lens), _ptr(k_cache),
             _ptr(v_cache), S, Hq, Hkv, D, BS, block_table.shape[1], NB, int(max_context_len),
             float(scale), _dtype_code(query), int(partition_size), _ptr(workspace), ws_bytes,
-            _stream(dev, stream))
+            _stream(dev, stream), hl)
     return PreparedCall(lib.pa_paged_attention, args, "pa_paged_attention",
-                        (query, block_table, context_lens, k_cache, v_cache, out, workspace))
+                        (query, block_table, context_lens, k_cache, v_cache, out, workspace,
+                         hold))
 
 
 def prepare_reshape_and_cache(key, value, slot_mapping, k_cache, v_cache,
@@ -559,12 +591,12 @@ def prepare_reshape_and_cache(key, value, slot_mapping, k_cache, v_cache,
 
 def prepare_decode_step(query, key, value, slot_mapping, block_table, context_lens, k_cache,
                         v_cache, scale, *, max_context_len: int, out, partition_size: int = 0,
-                        workspace=None, stream=None) -> PreparedCall:
+                        workspace=None, stream=None, host_context_lens=None) -> PreparedCall:
     """Check the arguments of decode_step once and return a re-launchable call."""
     lib = load_library()
     args, out, keep = _decode_step_args(query, key, value, slot_mapping, block_table,
                                         context_lens, k_cache, v_cache, scale, max_context_len,
-                                        out, partition_size, workspace, stream)
+                                        out, partition_size, workspace, stream, host_context_lens)
     call = PreparedCall(lib.pa_decode_step, args, "pa_decode_step", keep)
     call()
     return call
@@ -584,11 +616,11 @@ def prepare_reshape_and_cache_fp8(key, value, slot_mapping, k_cache, v_cache, k_
 def prepare_paged_attention_fp8(query, block_table, context_lens, k_cache, v_cache, scale,
                                 k_scale, v_scale, *, max_context_len: int, out,
                                 partition_size: int = 0, workspace=None,
-                                stream=None) -> PreparedCall:
+                                stream=None, host_context_lens=None) -> PreparedCall:
     """Check the arguments of paged_attention_fp8 once and return a re-launchable call."""
     args, out, keep = _attention_fp8_args(query, block_table, context_lens, k_cache, v_cache,
                                           scale, k_scale, v_scale, max_context_len, out,
-                                          partition_size, workspace, stream)
+                                          partition_size, workspace, stream, host_context_lens)
     call = PreparedCall(load_library().pa_paged_attention_fp8, args, "pa_paged_attention_fp8",
                         keep)
     call()
@@ -598,12 +630,12 @@ def prepare_paged_attention_fp8(query, block_table, context_lens, k_cache, v_cac
 def prepare_decode_step_fp8(query, key, value, slot_mapping, block_table, context_lens, k_cache,
                             v_cache, scale, k_scale, v_scale, *, max_context_len: int, out,
                             partition_size: int = 0, workspace=None,
-                            stream=None) -> PreparedCall:
+                            stream=None, host_context_lens=None) -> PreparedCall:
     """Check the arguments of decode_step_fp8 once and return a re-launchable call."""
     args, out, keep = _decode_step_fp8_args(query, key, value, slot_mapping, block_table,
                                             context_lens, k_cache, v_cache, scale, k_scale,
                                             v_scale, max_context_len, out, partition_size,
-                                            workspace, stream)
+                                            workspace, stream, host_context_lens)
     call = PreparedCall(load_library().pa_decode_step_fp8, args, "pa_decode_step_fp8", keep)
     call()
     return call

@@ -56,6 +56,7 @@
 // Lane mapping of a 16x16 MFMA output: lane l holds rows 4*(l/16)..+3 of
 // column l%16.  Below, n = l%16 and j = l/16.
 #include <algorithm>
+#include <type_traits>
 
 #include "common.h"
 
@@ -91,12 +92,15 @@ struct DecodeParams {
   float k_quant, v_quant;  // FP8 fused step: the scales the new token is quantised with
 };
 
-// Context length clamped to what the launch can address.
-__device__ __forceinline__ int clamped_len(const DecodeParams& a, int s, int BS) {
-  int L = a.context_lens[s];
+// A context length clamped to what the launch can address.
+__device__ __forceinline__ int clamp_len(const DecodeParams& a, int L, int BS) {
   const long cap = min((long)a.MB * BS, (long)a.P * a.Pmax);
   L = L < 0 ? 0 : L;
   return L > cap ? (int)cap : L;
+}
+
+__device__ __forceinline__ int clamped_len(const DecodeParams& a, int s, int BS) {
+  return clamp_len(a, a.context_lens[s], BS);
 }
 
 // Per-step shape constants for a query/output type T and a cache element type C (C = T,
@@ -128,17 +132,56 @@ struct StepData {
 __host__ __device__ constexpr int merge_stride(int D) { return D + 4; }
 __host__ __device__ constexpr int merge_words(int D, int g) { return 32 + g * merge_stride(D); }
 
+// Sequences the paired mode orders (the in-kernel ordering is O(S^2 / threads)).
+constexpr int kMaxPairedSeqs = 512;
+// Longest partition (tokens); a workgroup's table windows hold at most this many tokens
+// per unit.
+constexpr int kMaxPartition = 8192;
+static_assert(kMaxPairedSeqs <= 1024, "a sort key holds 10 bits of sequence index");
+
+// Paired mode: waves of the first unit, so that the busier unit's waves finish together.
+// With a second sequence each unit keeps at least one wave (even an empty one), so that
+// a split made from the host lengths never leaves a sequence without waves.
+__host__ __device__ inline int split_waves(int nw, int stA, int stB, bool two) {
+  if (!two) return nw;
+  int nA = 1, best = 1 << 30;
+  for (int c = 1; c < nw; ++c) {
+    const int tA = (stA + c - 1) / c, tB = (stB + nw - c - 1) / (nw - c);
+    const int t = tA > tB ? tA : tB;
+    if (t < best) { best = t; nA = c; }
+  }
+  return nA;
+}
+
+// The pairs of the paired mode, made on the host from the scheduler's copy of the
+// lengths and passed with the launch.  Pair r holds the r-th longest and the r-th
+// shortest sequence (ties: lower index first):
+//   pair[r].x = sA | sB << 16 (sB = 0xFFFF: none, the middle sequence of an odd count)
+//   pair[r].y = blocks of sA | blocks of sB << 12 | waves of sA << 24, from the host
+//               lengths (the table entries to stage at once -- the device lengths
+//               decide the rest -- and the split of the waves between the two)
+// pair[r].x = 0xFFFFFFFF: no plan, the kernel ranks the lengths itself.  The flag
+// sits in the entry so that one scalar load, issued with the parameters', brings both.
+struct PairOrder {
+  uint2 pair[kMaxPairedSeqs / 2];
+};
+constexpr uint32_t kNoPlan = 0xFFFFFFFFu;
+struct NoOrder {};
+template <bool PAIRED>
+using OrderArg = typename std::conditional<PAIRED, PairOrder, NoOrder>::type;
+
 // Pair-balanced mode (PAIRED): a workgroup of NW waves takes two
 // (sequence, kv head) units -- the r-th longest and the r-th shortest
 // sequence -- and splits its waves between them in proportion to their steps,
 // so that every workgroup carries about the same number of tokens.  The order
-// of the sequences by length is computed from context_lens inside every
-// workgroup (identically), by counting for each sequence the sequences that
-// are longer (ties broken by index).  Used when each sequence is one
-// partition; otherwise a workgroup is one (kv head, sequence, partition).
+// of the sequences by length comes with the launch when the host has the
+// lengths; otherwise every workgroup computes it from context_lens
+// (identically), by counting for each sequence the sequences that are longer
+// (ties broken by index).  Used when each sequence is one partition;
+// otherwise a workgroup is one (kv head, sequence, partition).
 template <typename T, typename C, int D, int BS, int NW, int PIPE, bool PAIRED>
 __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(PA_DECODE_OCC)))
-paged_decode_kernel(const DecodeParams a) {
+paged_decode_kernel(const DecodeParams a, const OrderArg<PAIRED> ord) {
   using Sh = StepShape<T, C, D>;
   constexpr bool kBf16 = Sh::kBf16;
   constexpr bool kFp8 = Sh::kFp8;
@@ -152,6 +195,14 @@ paged_decode_kernel(const DecodeParams a) {
 
   // LDS: [ctrl: 16 ints][new K/V: 2 units x 2 x D elements][sort keys: S ints, PAIRED only]
   //      [tables: 1 or 2 windows of P/BS][merge]
+  // paired mode: this pair's plan entry, requested before anything else so that its
+  // scalar load goes out with the parameters' (the barrier keeps it first)
+  uint64_t plan_entry = 0;
+  if constexpr (PAIRED) {
+    plan_entry = reinterpret_cast<const uint64_t*>(ord.pair)[blockIdx.y];
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
   extern __shared__ __align__(16) unsigned char smem[];
   int* ctrl = reinterpret_cast<int*>(smem);
   T* newkv = reinterpret_cast<T*>(smem + 64);                // [unit][K, V][D]
@@ -168,82 +219,83 @@ paged_decode_kernel(const DecodeParams a) {
   const int n = lane & 15;
   const int j = lane >> 4;
 
-  int id = blockIdx.x;
-  const int kvh = id % a.Hkv;
-  id /= a.Hkv;
+  // paired mode: a 2-D grid (kv head, pair), so that the pair's plan entry can be
+  // read together with the parameters; otherwise kv head fastest in a 1-D grid
+  int id = PAIRED ? (int)blockIdx.y : (int)blockIdx.x;
+  const int kvh = PAIRED ? (int)blockIdx.x : id % a.Hkv;
+  if constexpr (!PAIRED) id /= a.Hkv;
 
   // ---- this wave's unit: sequence s, tokens [tok0, tok1), table window, wave slot ----
-  int s, tok0, tok1, lw, nw, p = 0, nparts = 1, uidx = 0;
+  int s, tok0 = 0, tok1 = 0, lw, nw, p = 0, nparts = 1, uidx = 0;
   int sA = 0, sB = -1, nA = NW;                             // PAIRED: the two sequences
+  int LA = 0, LB = 0;                                       // PAIRED: their lengths
+  bool planned = false;                                     // PAIRED: pairs from the host
+  bool onA = true;
   const int* tblw = tbl;
   if constexpr (PAIRED) {
     const int r = id;                                       // pair index
-    // Sort keys: key_t = (L_t << 10) | (1023 - t), unique per sequence and ordered by
-    // length, then by index for equal lengths (L_t <= P <= 8192 here, and S <= 512, so the
-    // key fits in 24 bits; L_t = key >> 10).  Padded to a multiple of 4 with 0, below
-    // every real key.
-    for (int t = threadIdx.x; t < lens_words; t += kThreads)
-      lens[t] = t < a.S ? (clamped_len(a, t, BS) << 10) | (1023 - t) : 0;
-    __syncthreads();
     const int rB = a.S - 1 - r;
-    // rank of sequence t = how many keys are larger: one comparison per pair.  The S x S
-    // comparisons are spread over every thread: thread x compares t = x % S with the
-    // nparts-th slice (x / S) of the keys and leaves a partial count in the merge area
-    // (free until the end), and thread t then adds its partial counts.
-    int* part_rank = reinterpret_cast<int*>(red);           // [nparts][S]
-    const int nparts = max(1, kThreads / a.S);              // S <= kThreads here
-    const int nq = lens_words / 4;                          // int4 groups of keys
-    const int per = (nq + nparts - 1) / nparts;
-    for (int x = threadIdx.x; x < nparts * a.S; x += kThreads) {
-      const int t = x % a.S, pt = x / a.S;
-      const int Kt = lens[t];
-      int rank = 0;
-      const int q1 = min(nq, (pt + 1) * per);
+    const uint32_t ex = static_cast<uint32_t>(plan_entry);
+    const uint32_t ey = static_cast<uint32_t>(plan_entry >> 32);
+    planned = ex != kNoPlan;
+    if (planned) {
+      // the host's pair and wave split: the wave's sequence is known before any load
+      sA = (int)(ex & 0xFFFFu);
+      sB = (ex >> 16) == 0xFFFFu ? -1 : (int)(ex >> 16);
+      nA = sB < 0 ? NW : min(max((int)(ey >> 24), 1), NW - 1);
+      // the device lengths: both loads go out now and are first used after the
+      // prologue's other loads (sA stands in for a missing second sequence)
+      LA = a.context_lens[sA];
+      LB = a.context_lens[sB >= 0 ? sB : sA];
+    } else {
+      // Sort keys: key_t = (L_t << 10) | (1023 - t), unique per sequence and ordered by
+      // length, then by index for equal lengths (L_t <= P <= 8192 here, and S <= 512, so the
+      // key fits in 24 bits; L_t = key >> 10).  Padded to a multiple of 4 with 0, below
+      // every real key.
+      for (int t = threadIdx.x; t < lens_words; t += kThreads)
+        lens[t] = t < a.S ? (clamped_len(a, t, BS) << 10) | (1023 - t) : 0;
+      __syncthreads();
+      // rank of sequence t = how many keys are larger: one comparison per pair.  The S x S
+      // comparisons are spread over every thread: thread x compares t = x % S with the
+      // nparts-th slice (x / S) of the keys and leaves a partial count in the merge area
+      // (free until the end), and thread t then adds its partial counts.
+      int* part_rank = reinterpret_cast<int*>(red);           // [nparts][S]
+      const int nparts = max(1, kThreads / a.S);              // S <= kThreads here
+      const int nq = lens_words / 4;                          // int4 groups of keys
+      const int per = (nq + nparts - 1) / nparts;
+      for (int x = threadIdx.x; x < nparts * a.S; x += kThreads) {
+        const int t = x % a.S, pt = x / a.S;
+        const int Kt = lens[t];
+        int rank = 0;
+        const int q1 = min(nq, (pt + 1) * per);
 #pragma unroll 4
-      for (int u4 = pt * per; u4 < q1; ++u4) {
-        const int4 v = reinterpret_cast<const int4*>(lens)[u4];
-        rank += (v.x > Kt) + (v.y > Kt) + (v.z > Kt) + (v.w > Kt);
+        for (int u4 = pt * per; u4 < q1; ++u4) {
+          const int4 v = reinterpret_cast<const int4*>(lens)[u4];
+          rank += (v.x > Kt) + (v.y > Kt) + (v.z > Kt) + (v.w > Kt);
+        }
+        part_rank[x] = rank;
       }
-      part_rank[x] = rank;
-    }
-    __syncthreads();
-    for (int t = threadIdx.x; t < a.S; t += kThreads) {
-      int rank = 0;
-      for (int pt = 0; pt < nparts; ++pt) rank += part_rank[pt * a.S + t];
-      if (rank == r) ctrl[0] = t;
-      if (rank == rB) ctrl[1] = t;
-    }
-    __syncthreads();
-    sA = __builtin_amdgcn_readfirstlane(ctrl[0]);
-    sB = r == rB ? -1 : __builtin_amdgcn_readfirstlane(ctrl[1]);
-    const int LA = lens[sA] >> 10;
-    const int LB = sB >= 0 ? lens[sB] >> 10 : 0;
-    // split the waves so that the busier unit's waves finish together
-    const int stA = (LA + kStep - 1) / kStep, stB = (LB + kStep - 1) / kStep;
-    if (stB > 0) {
-      int best = 1 << 30;
-      for (int c = 1; c < NW; ++c) {
-        const int t = max((stA + c - 1) / c, (stB + NW - c - 1) / (NW - c));
-        if (t < best) { best = t; nA = c; }
+      __syncthreads();
+      for (int t = threadIdx.x; t < a.S; t += kThreads) {
+        int rank = 0;
+        for (int pt = 0; pt < nparts; ++pt) rank += part_rank[pt * a.S + t];
+        if (rank == r) ctrl[0] = t;
+        if (rank == rB) ctrl[1] = t;
       }
+      __syncthreads();
+      sA = __builtin_amdgcn_readfirstlane(ctrl[0]);
+      sB = r == rB ? -1 : __builtin_amdgcn_readfirstlane(ctrl[1]);
+      LA = lens[sA] >> 10;
+      LB = sB >= 0 ? lens[sB] >> 10 : 0;
+      nA = split_waves(NW, (LA + kStep - 1) / kStep, (LB + kStep - 1) / kStep, sB >= 0);
     }
     nA = __builtin_amdgcn_readfirstlane(nA);
-    const bool onA = wave < nA;
+    onA = wave < nA;
     uidx = onA ? 0 : 1;
     s = onA ? sA : sB;
-    tok0 = 0;
-    tok1 = __builtin_amdgcn_readfirstlane(onA ? LA : LB);
     lw = onA ? wave : wave - nA;
     nw = onA ? nA : NW - nA;
     tblw = tbl + (onA ? 0 : win);
-    // both table windows (clamped ids keep every read inside the pool)
-    const int nbA = (LA + BS - 1) / BS, nbB = (LB + BS - 1) / BS;
-    for (int i = threadIdx.x; i < nbA + nbB; i += kThreads) {
-      const int us = i < nbA ? sA : sB;
-      const int li = i < nbA ? i : i - nbA;
-      const unsigned b = static_cast<unsigned>(a.block_table[(size_t)us * a.MB + li]);
-      tbl[(i < nbA ? 0 : win) + li] = static_cast<int>(min(b, static_cast<unsigned>(a.NB - 1)));
-    }
   } else {
     s = id % a.S;
     p = id / a.S;
@@ -254,18 +306,78 @@ paged_decode_kernel(const DecodeParams a) {
     tok1 = min(L, tok0 + a.P);
     lw = wave;
     nw = NW;
-    const int nblk = (tok1 - tok0 + BS - 1) / BS;
-    // Block-table window of this partition (clamped ids keep every read inside the pool).
-    for (int i = threadIdx.x; i < nblk; i += kThreads) {
-      const unsigned b = static_cast<unsigned>(a.block_table[(size_t)s * a.MB + tok0 / BS + i]);
-      tbl[i] = static_cast<int>(min(b, static_cast<unsigned>(a.NB - 1)));
-    }
   }
 
   const int g = a.g;
   const int rows = kBf16 ? 2 * g : g;
   const int head = kvh * g + (n % g);
   const bool row_live = n < rows;
+
+  // Every load of the prologue is issued before the first wait on any of them: the
+  // query operand, the new tokens and the block-table windows land in one round trip.
+  //
+  // Query operand: lane (n, j) holds head-row n's channels of the chunks it multiplies.
+  // FP8: K chunk j + 4c' (16 channels) feeds MFMAs 2c' and 2c' + 1 (8 channels each).
+  const T* qrow = static_cast<const T*>(a.q) + ((size_t)s * a.Hq + head) * D;
+  u32x4 qop[kNq];
+#pragma unroll
+  for (int c = 0; c < kNq; ++c) {
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    const int off = kFp8 ? 16 * (j + 4 * (c >> 1)) + 8 * (c & 1) : kX * (4 * c + j);
+    qop[c] = row_live ? load16(qrow + off) : z;
+  }
+
+  // Block-table windows: entry i of `count` is column col(i) of row row(i), staged at
+  // LDS word dst(i); ids are clamped so that every read stays inside the pool.  The
+  // loads go to registers first (lanes past the end re-read the last entry, so no load
+  // sits in a divergent branch) and are written to LDS once the new tokens' loads are
+  // out as well.  kPer entries per thread cover two windows of the longest partition.
+  constexpr int kPer = ((PAIRED ? 2 : 1) * (kMaxPartition / BS) + kThreads - 1) / kThreads;
+  auto stage_load = [&](int count, unsigned (&b)[kPer], auto&& where) {
+    const int iters = min(kPer, (count + kThreads - 1) / kThreads);       // uniform
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      if (k < iters) {
+        const int i = min(k * kThreads + (int)threadIdx.x, count - 1);
+        int row = 0, col = 0, dst = 0;
+        where(i, row, col, dst);
+        b[k] = static_cast<unsigned>(a.block_table[(size_t)row * a.MB + col]);
+      }
+    }
+  };
+  auto stage_store = [&](int count, const unsigned (&b)[kPer], auto&& where) {
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const int i = k * kThreads + (int)threadIdx.x;
+      if (i < count) {
+        int row = 0, col = 0, dst = 0;
+        where(i, row, col, dst);
+        tbl[dst] = static_cast<int>(min(b[k], static_cast<unsigned>(a.NB - 1)));
+      }
+    }
+  };
+  unsigned tb[kPer];
+  int cA = 0, cB = 0, nblk = 0;
+  auto where_pair = [&](int i, int& row, int& col, int& dst) {
+    row = i < cA ? sA : sB;
+    col = i < cA ? i : i - cA;
+    dst = (i < cA ? 0 : win) + col;
+  };
+  auto where_part = [&](int i, int& row, int& col, int& dst) {
+    row = s;
+    col = tok0 / BS + i;
+    dst = i;
+  };
+  if constexpr (PAIRED) {
+    // the host's block counts for a planned launch, else the lengths ranked above
+    const uint32_t ey = static_cast<uint32_t>(plan_entry >> 32);
+    cA = min(planned ? (int)(ey & 0xFFFu) : (LA + BS - 1) / BS, win);
+    cB = sB < 0 ? 0 : min(planned ? (int)((ey >> 12) & 0xFFFu) : (LB + BS - 1) / BS, win);
+    if (cA + cB > 0) stage_load(cA + cB, tb, where_pair);
+  } else {
+    nblk = (tok1 - tok0 + BS - 1) / BS;
+    if (nblk > 0) stage_load(nblk, tb, where_part);
+  }
 
   // Fused step: this workgroup's units' new tokens (kv head kvh).  Only the workgroup
   // that reads a sequence's last position L - 1 handles its new token (the last
@@ -287,11 +399,40 @@ paged_decode_kernel(const DecodeParams a) {
   int new_u = 0;
   const bool new_is_v = (threadIdx.x % (2 * kCh)) >= kCh;
   const int new_cc = threadIdx.x % kCh;
-  if ((int)threadIdx.x < nun_new * 2 * kCh) {
+  const bool has_new = (int)threadIdx.x < nun_new * 2 * kCh;
+  if (has_new) {
     new_u = threadIdx.x / (2 * kCh);
     const int su = PAIRED ? (new_u ? sB : sA) : s;
     const size_t src = ((size_t)su * a.Hkv + kvh) * D + (size_t)new_cc * kSx;
     new_val = load16(static_cast<const T*>(new_is_v ? a.new_v : a.new_k) + src);
+    new_slot = a.new_slot[su];
+  }
+
+  if constexpr (PAIRED) {
+    stage_store(cA + cB, tb, where_pair);
+    if (planned) {
+      LA = clamp_len(a, LA, BS);
+      LB = sB >= 0 ? clamp_len(a, LB, BS) : 0;
+      // device lengths past the host's: stage the missing entries as well
+      const int nbA = (LA + BS - 1) / BS, nbB = (LB + BS - 1) / BS;
+      if (nbA > cA || nbB > cB) {
+        const int xA = max(nbA - cA, 0), xB = max(nbB - cB, 0);
+        auto where_more = [&](int i, int& row, int& col, int& dst) {
+          row = i < xA ? sA : sB;
+          col = i < xA ? cA + i : cB + i - xA;
+          dst = (i < xA ? 0 : win) + col;
+        };
+        unsigned more[kPer];
+        stage_load(xA + xB, more, where_more);
+        stage_store(xA + xB, more, where_more);
+      }
+    }
+    tok1 = __builtin_amdgcn_readfirstlane(onA ? LA : LB);
+  } else {
+    stage_store(nblk, tb, where_part);
+  }
+
+  if (has_new) {
     if constexpr (kFp8) {
       // 8 bf16 elements -> 8 codes (words 0 and 1 of new_val); a NaN keeps its sign
       const float sc = new_is_v ? a.v_quant : a.k_quant;
@@ -310,18 +451,6 @@ paged_decode_kernel(const DecodeParams a) {
     } else {
       store16(newkv + (2 * new_u + (new_is_v ? 1 : 0)) * D + new_cc * kX, new_val);
     }
-    new_slot = a.new_slot[su];
-  }
-
-  // Query operand: lane (n, j) holds head-row n's channels of the chunks it multiplies.
-  // FP8: K chunk j + 4c' (16 channels) feeds MFMAs 2c' and 2c' + 1 (8 channels each).
-  const T* qrow = static_cast<const T*>(a.q) + ((size_t)s * a.Hq + head) * D;
-  u32x4 qop[kNq];
-#pragma unroll
-  for (int c = 0; c < kNq; ++c) {
-    const u32x4 z = {0u, 0u, 0u, 0u};
-    const int off = kFp8 ? 16 * (j + 4 * (c >> 1)) + 8 * (c & 1) : kX * (4 * c + j);
-    qop[c] = row_live && tok1 > tok0 ? load16(qrow + off) : z;
   }
   __syncthreads();
 
@@ -341,7 +470,7 @@ paged_decode_kernel(const DecodeParams a) {
 
   // a new slot that is not where position L - 1 is read from: store it here
   if (new_slot >= 0 && new_slot < nslots) {
-    const int Lu = PAIRED ? lens[new_u ? sB : sA] >> 10 : tok1;
+    const int Lu = PAIRED ? (new_u ? LB : LA) : tok1;
     const int64_t loc =
         Lu > 0 ? slot_of(PAIRED ? tbl + new_u * win : tbl, PAIRED ? 0 : tok0, Lu - 1) : -1;
     if (new_slot != loc && kFp8) {
@@ -784,8 +913,6 @@ reduce_partitions_kernel(const DecodeParams a) {
 constexpr int kWaves = PA_DECODE_WAVES;     // waves per workgroup, partition mode
 constexpr int kPairWaves = 8;               // waves per workgroup, paired mode
 constexpr int kPipe = PA_DECODE_PIPE;
-constexpr int kMaxPairedSeqs = 512;         // the in-kernel ordering is O(S^2 / threads)
-static_assert(kMaxPairedSeqs <= 1024, "a sort key holds 10 bits of sequence index");
 constexpr size_t kMaxLds = 64 * 1024;
 
 // Dynamic LDS of one workgroup; mirrors the layout at the top of paged_decode_kernel.
@@ -804,20 +931,49 @@ inline bool use_paired(const DecodeParams& a, int D, int BS, int elt) {
          decode_lds_bytes(true, kPairWaves, a.S, D, BS, a.P, a.g, elt) <= kMaxLds;
 }
 
+// The paired mode's order of the sequences from a host copy of the lengths: the same
+// keys the kernel ranks (clamped length, then lower index first), sorted on the host.
+inline void order_on_host(const DecodeParams& a, int BS, int step, const int32_t* host_lens,
+                          PairOrder& ord) {
+  const long cap = std::min((long)a.MB * BS, (long)a.P * a.Pmax);
+  uint32_t key[kMaxPairedSeqs];
+  for (int t = 0; t < a.S; ++t) {
+    const long L = std::min(std::max(0L, (long)host_lens[t]), cap);
+    key[t] = (static_cast<uint32_t>(L) << 10) | static_cast<uint32_t>(1023 - t);
+  }
+  std::sort(key, key + a.S, [](uint32_t x, uint32_t y) { return x > y; });
+  const int npairs = (a.S + 1) / 2;
+  for (int r = 0; r < npairs; ++r) {
+    const uint32_t kA = key[r], kB = key[a.S - 1 - r];
+    const uint32_t sA = 1023u - (kA & 1023u);
+    const uint32_t sB = r == a.S - 1 - r ? 0xFFFFu : 1023u - (kB & 1023u);
+    const int LA = (int)(kA >> 10), LB = sB == 0xFFFFu ? 0 : (int)(kB >> 10);
+    const uint32_t bA = (LA + BS - 1) / BS, bB = (LB + BS - 1) / BS;
+    const uint32_t nA = split_waves(kPairWaves, (LA + step - 1) / step, (LB + step - 1) / step,
+                                    sB != 0xFFFFu);
+    ord.pair[r] = make_uint2(sA | sB << 16, bA | bB << 12 | nA << 24);
+  }
+}
+
 template <typename T, typename C, int D, int BS>
-hipError_t launch_decode(const DecodeParams& a, hipStream_t stream) {
+hipError_t launch_decode(const DecodeParams& a, const int32_t* host_lens, hipStream_t stream) {
   constexpr int elt = sizeof(T);
   if (use_paired(a, D, BS, elt)) {
     const size_t lds = decode_lds_bytes(true, kPairWaves, a.S, D, BS, a.P, a.g, elt);
-    const long grid = (long)a.Hkv * ((a.S + 1) / 2);
+    PairOrder ord;
+    if (host_lens)
+      order_on_host(a, BS, StepShape<T, C, D>::kStep, host_lens, ord);
+    else
+      for (int r = 0; r < (a.S + 1) / 2; ++r) ord.pair[r] = make_uint2(kNoPlan, 0u);
     hipLaunchKernelGGL((paged_decode_kernel<T, C, D, BS, kPairWaves, kPipe, true>),
-                       dim3((unsigned)grid), dim3(kPairWaves * 64), lds, stream, a);
+                       dim3((unsigned)a.Hkv, (unsigned)((a.S + 1) / 2)), dim3(kPairWaves * 64),
+                       lds, stream, a, ord);
     return hipGetLastError();
   }
   const size_t lds = decode_lds_bytes(false, kWaves, a.S, D, BS, a.P, a.g, elt);
   const long grid = (long)a.Hkv * a.Pmax * a.S;
   hipLaunchKernelGGL((paged_decode_kernel<T, C, D, BS, kWaves, kPipe, false>), dim3((unsigned)grid),
-                     dim3(kWaves * 64), lds, stream, a);
+                     dim3(kWaves * 64), lds, stream, a, NoOrder{});
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || a.Pmax == 1) return err;
   hipLaunchKernelGGL((reduce_partitions_kernel<T, D, BS>), dim3((unsigned)((long)a.S * a.Hq)),
@@ -826,9 +982,10 @@ hipError_t launch_decode(const DecodeParams& a, hipStream_t stream) {
 }
 
 template <typename T, typename C>
-hipError_t dispatch_decode(const DecodeParams& a, int D, int BS, hipStream_t stream) {
+hipError_t dispatch_decode(const DecodeParams& a, int D, int BS, const int32_t* host_lens,
+                           hipStream_t stream) {
 #define PA_CASE(DD, BB) \
-  if (D == DD && BS == BB) return launch_decode<T, C, DD, BB>(a, stream);
+  if (D == DD && BS == BB) return launch_decode<T, C, DD, BB>(a, host_lens, stream);
   PA_CASE(64, 8) PA_CASE(64, 16) PA_CASE(64, 32)
   PA_CASE(128, 8) PA_CASE(128, 16) PA_CASE(128, 32)
 #undef PA_CASE
@@ -890,7 +1047,7 @@ int device_cu_count() {
   return cache[dev];
 }
 
-constexpr int kMaxPartition = 8192;
+using pa::kMaxPartition;
 static_assert(kMaxPartition <= (1 << 20), "a paired-mode sort key holds the length in 21 bits");
 
 }  // namespace
@@ -938,7 +1095,8 @@ pa_status run_decode(void* out, const void* query, const int32_t* block_table,
                      int num_seqs, int num_heads, int num_kv_heads, int head_dim, int block_size,
                      int max_blocks_per_seq, int num_blocks, int max_context_len, float scale,
                      pa_dtype dtype, int partition_size, void* workspace, size_t workspace_bytes,
-                     void* stream, bool fp8 = false, float k_scale = 1.f, float v_scale = 1.f) {
+                     void* stream, const int32_t* host_lens, bool fp8 = false,
+                     float k_scale = 1.f, float v_scale = 1.f) {
   pa_status st = check_shapes(num_heads, num_kv_heads, head_dim, block_size, dtype);
   if (st != PA_OK) return st;
   if (fp8 && dtype != PA_DTYPE_BF16) return PA_ERR_UNSUPPORTED;
@@ -998,10 +1156,11 @@ pa_status run_decode(void* out, const void* query, const int32_t* block_table,
   a.part_acc = wl.total ? reinterpret_cast<float*>(ws + wl.acc) : nullptr;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t err = fp8 ? pa::dispatch_decode<uint16_t, uint8_t>(a, head_dim, block_size, s)
-                  : dtype == PA_DTYPE_BF16
-                      ? pa::dispatch_decode<uint16_t, uint16_t>(a, head_dim, block_size, s)
-                      : pa::dispatch_decode<float, float>(a, head_dim, block_size, s);
+  hipError_t err =
+      fp8 ? pa::dispatch_decode<uint16_t, uint8_t>(a, head_dim, block_size, host_lens, s)
+      : dtype == PA_DTYPE_BF16
+          ? pa::dispatch_decode<uint16_t, uint16_t>(a, head_dim, block_size, host_lens, s)
+          : pa::dispatch_decode<float, float>(a, head_dim, block_size, host_lens, s);
   return err == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
@@ -1014,11 +1173,12 @@ extern "C" pa_status pa_paged_attention(void* out, const void* query, const int3
                                         int max_blocks_per_seq, int num_blocks,
                                         int max_context_len, float scale, pa_dtype dtype,
                                         int partition_size, void* workspace,
-                                        size_t workspace_bytes, void* stream) {
+                                        size_t workspace_bytes, void* stream,
+                                        const int32_t* host_context_lens) {
   return run_decode(out, query, block_table, context_lens, k_cache, v_cache, nullptr, nullptr,
                     nullptr, num_seqs, num_heads, num_kv_heads, head_dim, block_size,
                     max_blocks_per_seq, num_blocks, max_context_len, scale, dtype,
-                    partition_size, workspace, workspace_bytes, stream);
+                    partition_size, workspace, workspace_bytes, stream, host_context_lens);
 }
 
 extern "C" pa_status pa_decode_step(void* out, const void* query, const void* key,
@@ -1028,12 +1188,13 @@ extern "C" pa_status pa_decode_step(void* out, const void* query, const void* ke
                                     int num_kv_heads, int head_dim, int block_size,
                                     int max_blocks_per_seq, int num_blocks, int max_context_len,
                                     float scale, pa_dtype dtype, int partition_size,
-                                    void* workspace, size_t workspace_bytes, void* stream) {
+                                    void* workspace, size_t workspace_bytes, void* stream,
+                                    const int32_t* host_context_lens) {
   if (num_seqs > 0 && (!key || !value || !slot_mapping)) return PA_ERR_INVALID_ARG;
   return run_decode(out, query, block_table, context_lens, k_cache, v_cache, key, value,
                     num_seqs > 0 ? slot_mapping : nullptr, num_seqs, num_heads, num_kv_heads,
                     head_dim, block_size, max_blocks_per_seq, num_blocks, max_context_len, scale,
-                    dtype, partition_size, workspace, workspace_bytes, stream);
+                    dtype, partition_size, workspace, workspace_bytes, stream, host_context_lens);
 }
 
 extern "C" pa_status pa_paged_attention_fp8(void* out, const void* query,
@@ -1045,11 +1206,12 @@ extern "C" pa_status pa_paged_attention_fp8(void* out, const void* query,
                                             int max_context_len, float scale, float k_scale,
                                             float v_scale, pa_dtype dtype, int partition_size,
                                             void* workspace, size_t workspace_bytes,
-                                            void* stream) {
+                                            void* stream, const int32_t* host_context_lens) {
   return run_decode(out, query, block_table, context_lens, k_cache, v_cache, nullptr, nullptr,
                     nullptr, num_seqs, num_heads, num_kv_heads, head_dim, block_size,
                     max_blocks_per_seq, num_blocks, max_context_len, scale, dtype,
-                    partition_size, workspace, workspace_bytes, stream, true, k_scale, v_scale);
+                    partition_size, workspace, workspace_bytes, stream, host_context_lens, true,
+                    k_scale, v_scale);
 }
 
 extern "C" pa_status pa_decode_step_fp8(void* out, const void* query, const void* key,
@@ -1060,11 +1222,12 @@ extern "C" pa_status pa_decode_step_fp8(void* out, const void* query, const void
                                         int block_size, int max_blocks_per_seq, int num_blocks,
                                         int max_context_len, float scale, float k_scale,
                                         float v_scale, pa_dtype dtype, int partition_size,
-                                        void* workspace, size_t workspace_bytes, void* stream) {
+                                        void* workspace, size_t workspace_bytes, void* stream,
+                                        const int32_t* host_context_lens) {
   if (num_seqs > 0 && (!key || !value || !slot_mapping)) return PA_ERR_INVALID_ARG;
   return run_decode(out, query, block_table, context_lens, k_cache, v_cache, key, value,
                     num_seqs > 0 ? slot_mapping : nullptr, num_seqs, num_heads, num_kv_heads,
                     head_dim, block_size, max_blocks_per_seq, num_blocks, max_context_len, scale,
-                    dtype, partition_size, workspace, workspace_bytes, stream, true, k_scale,
-                    v_scale);
+                    dtype, partition_size, workspace, workspace_bytes, stream, host_context_lens,
+                    true, k_scale, v_scale);
 }

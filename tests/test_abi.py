@@ -43,7 +43,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.pa_abi_version() == 1
+    assert lib.pa_abi_version() == 2
     for code in range(5):
         assert lib.pa_status_string(code).decode().startswith("PA_")
     assert b"unknown" in lib.pa_status_string(99)
@@ -85,13 +85,13 @@ FAKE = 0x1000          # a 16-byte aligned, never dereferenced address
 def call_attention(lib, **over):
     args = dict(out=FAKE, q=FAKE, bt=FAKE, cl=FAKE, kc=FAKE, vc=FAKE, S=4, Hq=32, Hkv=8, D=128,
                 BS=16, MB=8, NB=64, maxlen=128, scale=0.1, dtype=1, part=0, ws=None, wsb=0,
-                stream=None)
+                stream=None, host_lens=None)
     args.update(over)
     return lib.pa_paged_attention(args["out"], args["q"], args["bt"], args["cl"], args["kc"],
                                   args["vc"], args["S"], args["Hq"], args["Hkv"], args["D"],
                                   args["BS"], args["MB"], args["NB"], args["maxlen"],
                                   args["scale"], args["dtype"], args["part"], args["ws"],
-                                  args["wsb"], args["stream"])
+                                  args["wsb"], args["stream"], args["host_lens"])
 
 
 @pytest.mark.parametrize("over,code", [
@@ -119,7 +119,7 @@ def test_f32_allows_larger_groups(lib):
 
 def test_decode_step_rejects_before_launch(lib):
     f = lib.pa_decode_step
-    base = [FAKE] * 9 + [4, 32, 8, 128, 16, 8, 64, 128, 0.1, 1, 0, None, 0, None]
+    base = [FAKE] * 9 + [4, 32, 8, 128, 16, 8, 64, 128, 0.1, 1, 0, None, 0, None, None]
 
     def call(over):
         a = list(base)
@@ -207,7 +207,7 @@ def test_reshape_and_cache_fp8_rejects_before_launch(lib):
 
 def test_paged_attention_fp8_rejects_before_launch(lib):
     f = lib.pa_paged_attention_fp8
-    ok = [FAKE] * 6 + [4, 32, 8, 128, 16, 8, 64, 128, 0.1, 0.5, 0.25, 1, 0, None, 0, None]
+    ok = [FAKE] * 6 + [4, 32, 8, 128, 16, 8, 64, 128, 0.1, 0.5, 0.25, 1, 0, None, 0, None, None]
 
     def call(over):
         a = list(ok)
@@ -229,7 +229,7 @@ def test_paged_attention_fp8_rejects_before_launch(lib):
 
 def test_decode_step_fp8_rejects_before_launch(lib):
     f = lib.pa_decode_step_fp8
-    ok = [FAKE] * 9 + [4, 32, 8, 128, 16, 8, 64, 128, 0.1, 0.5, 0.25, 1, 0, None, 0, None]
+    ok = [FAKE] * 9 + [4, 32, 8, 128, 16, 8, 64, 128, 0.1, 0.5, 0.25, 1, 0, None, 0, None, None]
 
     def call(over):
         a = list(ok)
