@@ -87,6 +87,7 @@ struct DecodeParams {
   const void* new_v;
   const int64_t* new_slot;
   int S, Hq, Hkv, g, MB, NB, P, Pmax;
+  int wave_parts;          // partition mode: 1 = each wave owns one partition of NW in a row
   float scale_log2;        // scale * log2(e) (* k_scale for FP8 K): base-2 logits
   float v_scale;           // output multiplier: 1, or the FP8 V scale
   float k_quant, v_quant;  // FP8 fused step: the scales the new token is quantised with
@@ -210,7 +211,7 @@ paged_decode_kernel(const DecodeParams a, const OrderArg<PAIRED> ord) {
   const int lens_words = PAIRED ? (a.S + 3) / 4 * 4 : 0;
   int* lens = reinterpret_cast<int*>(smem + 64 + 4 * D * sizeof(T));
   int* tbl = lens + lens_words;
-  const int tbl_words = ((PAIRED ? 2 : 1) * win + 3) / 4 * 4;
+  const int tbl_words = ((PAIRED ? 2 : (a.wave_parts ? NW : 1)) * win + 3) / 4 * 4;
   float* red = reinterpret_cast<float*>(tbl + tbl_words);
 
   const int lane = threadIdx.x & 63;
@@ -227,6 +228,7 @@ paged_decode_kernel(const DecodeParams a, const OrderArg<PAIRED> ord) {
 
   // ---- this wave's unit: sequence s, tokens [tok0, tok1), table window, wave slot ----
   int s, tok0 = 0, tok1 = 0, lw, nw, p = 0, nparts = 1, uidx = 0;
+  int p0 = 0, seqL = 0;      // partition mode: the workgroup's first partition, the length
   int sA = 0, sB = -1, nA = NW;                             // PAIRED: the two sequences
   int LA = 0, LB = 0;                                       // PAIRED: their lengths
   bool planned = false;                                     // PAIRED: pairs from the host
@@ -296,6 +298,21 @@ paged_decode_kernel(const DecodeParams a, const OrderArg<PAIRED> ord) {
     lw = onA ? wave : wave - nA;
     nw = onA ? nA : NW - nA;
     tblw = tbl + (onA ? 0 : win);
+  } else if (a.wave_parts) {
+    // NW consecutive partitions, one per wave: the workgroup stages one table window
+    // for all of them and each wave streams its partition alone and writes its own
+    // partial result (no merge across waves)
+    s = id % a.S;
+    p0 = (id / a.S) * NW;
+    seqL = clamped_len(a, s, BS);
+    nparts = max(1, (seqL + a.P - 1) / a.P);
+    if (p0 >= nparts) return;
+    p = p0 + wave;
+    tok0 = min(p * a.P, seqL);
+    tok1 = min(seqL, tok0 + a.P);
+    lw = 0;
+    nw = 1;
+    tblw = tbl + (tok0 - p0 * a.P) / BS;
   } else {
     s = id % a.S;
     p = id / a.S;
@@ -306,6 +323,8 @@ paged_decode_kernel(const DecodeParams a, const OrderArg<PAIRED> ord) {
     tok1 = min(L, tok0 + a.P);
     lw = wave;
     nw = NW;
+    p0 = p;
+    seqL = L;
   }
 
   const int g = a.g;
@@ -365,7 +384,7 @@ paged_decode_kernel(const DecodeParams a, const OrderArg<PAIRED> ord) {
   };
   auto where_part = [&](int i, int& row, int& col, int& dst) {
     row = s;
-    col = tok0 / BS + i;
+    col = p0 * win + i;
     dst = i;
   };
   if constexpr (PAIRED) {
@@ -375,7 +394,9 @@ paged_decode_kernel(const DecodeParams a, const OrderArg<PAIRED> ord) {
     cB = sB < 0 ? 0 : min(planned ? (int)((ey >> 12) & 0xFFFu) : (LB + BS - 1) / BS, win);
     if (cA + cB > 0) stage_load(cA + cB, tb, where_pair);
   } else {
-    nblk = (tok1 - tok0 + BS - 1) / BS;
+    // the window of the workgroup's partitions (one, or NW with one per wave)
+    const int wend = min(seqL, (p0 + (a.wave_parts ? NW : 1)) * a.P);
+    nblk = (wend - p0 * a.P + BS - 1) / BS;
     if (nblk > 0) stage_load(nblk, tb, where_part);
   }
 
@@ -392,7 +413,7 @@ paged_decode_kernel(const DecodeParams a, const OrderArg<PAIRED> ord) {
   constexpr int kSx = ElemTraits<T>::kX;                    // new-token elements per 16 bytes
   constexpr int kCh = D / kSx;                              // 16-byte new-token chunks per head
   const bool fused = a.new_slot != nullptr;
-  const bool last_part = p == nparts - 1;
+  const bool last_part = nparts - 1 < p0 + (a.wave_parts ? NW : 1);    // holds the last
   const int nun_new = !fused ? 0 : (PAIRED ? (sB >= 0 ? 2 : 1) : (last_part ? 1 : 0));
   u32x4 new_val = {0u, 0u, 0u, 0u};
   int64_t new_slot = -1;
@@ -462,7 +483,7 @@ paged_decode_kernel(const DecodeParams a, const OrderArg<PAIRED> ord) {
 
   // position this wave takes from LDS and writes back (-1: none)
   int lm1 = -1;
-  if (fused && uidx < nun_new && tok1 > tok0) {
+  if (fused && uidx < nun_new && tok1 > tok0 && (PAIRED || p == nparts - 1)) {
     const int64_t sl = a.new_slot[s];
     if (sl >= 0 && sl < nslots && sl == slot_of(tblw, tok0, tok1 - 1)) lm1 = tok1 - 1;
   }
@@ -470,9 +491,9 @@ paged_decode_kernel(const DecodeParams a, const OrderArg<PAIRED> ord) {
 
   // a new slot that is not where position L - 1 is read from: store it here
   if (new_slot >= 0 && new_slot < nslots) {
-    const int Lu = PAIRED ? (new_u ? LB : LA) : tok1;
+    const int Lu = PAIRED ? (new_u ? LB : LA) : seqL;
     const int64_t loc =
-        Lu > 0 ? slot_of(PAIRED ? tbl + new_u * win : tbl, PAIRED ? 0 : tok0, Lu - 1) : -1;
+        Lu > 0 ? slot_of(PAIRED ? tbl + new_u * win : tbl, PAIRED ? 0 : p0 * a.P, Lu - 1) : -1;
     if (new_slot != loc && kFp8) {
       uint8_t* kcw = static_cast<uint8_t*>(const_cast<void*>(a.k_cache));
       uint8_t* vcw = static_cast<uint8_t*>(const_cast<void*>(a.v_cache));
@@ -817,6 +838,41 @@ paged_decode_kernel(const DecodeParams a, const OrderArg<PAIRED> ord) {
   }
   float lsum = sum_xor16(l_run);
   lsum = sum_xor32(lsum);
+  if (!PAIRED && a.wave_parts) {
+    // one partition per wave: lane (n, j) holds row n's channels 16 sl + 4 j .. + 3;
+    // the wave writes its partition's result itself (the output when the sequence has
+    // one partition, else its (max, sum, partial output) for the merge)
+    if (p < nparts && n < g) {
+      const size_t row = (size_t)s * a.Hq + kvh * g + n;
+      if (nparts == 1) {
+#pragma unroll
+        for (int sl = 0; sl < kNs; ++sl)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float o = m_run == kNegInf ? 0.f : (acc[sl][e] * a.v_scale) / lsum;
+            const size_t at = row * D + 16 * sl + 4 * j + e;
+            if constexpr (kBf16)
+              static_cast<uint16_t*>(a.out)[at] = bf16_bits(o);
+            else
+              static_cast<float*>(a.out)[at] = o;
+          }
+      } else {
+        float* dst = a.part_acc + (row * a.Pmax + p) * D + 4 * j;
+#pragma unroll
+        for (int sl = 0; sl < kNs; ++sl) {
+          f32x4 v = acc[sl];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] *= a.v_scale;
+          *reinterpret_cast<f32x4*>(dst + 16 * sl) = v;
+        }
+        if (j == 0) {
+          a.part_ml[(row * a.Pmax + p) * 2 + 0] = m_run;
+          a.part_ml[(row * a.Pmax + p) * 2 + 1] = lsum;
+        }
+      }
+    }
+    return;
+  }
   const int wstride = merge_words(D, g);
   float* wr = red + wave * wstride;
   if (n < g) {
@@ -917,9 +973,10 @@ constexpr size_t kMaxLds = 64 * 1024;
 
 // Dynamic LDS of one workgroup; mirrors the layout at the top of paged_decode_kernel.
 inline size_t decode_lds_bytes(bool paired, int nw, int S, int D, int BS, int P, int g,
-                               int elt) {
+                               int elt, bool wave_parts = false) {
   const size_t lens_words = paired ? (size_t)(S + 3) / 4 * 4 : 0;
-  const size_t tbl_words = ((size_t)(paired ? 2 : 1) * (P / BS) + 3) / 4 * 4;
+  const size_t tbl_words =
+      ((size_t)(paired ? 2 : (wave_parts ? nw : 1)) * (P / BS) + 3) / 4 * 4;
   return 64 + 4 * (size_t)D * elt +
          4 * (lens_words + tbl_words + (size_t)nw * merge_words(D, g));
 }
@@ -970,8 +1027,9 @@ hipError_t launch_decode(const DecodeParams& a, const int32_t* host_lens, hipStr
                        lds, stream, a, ord);
     return hipGetLastError();
   }
-  const size_t lds = decode_lds_bytes(false, kWaves, a.S, D, BS, a.P, a.g, elt);
-  const long grid = (long)a.Hkv * a.Pmax * a.S;
+  const size_t lds = decode_lds_bytes(false, kWaves, a.S, D, BS, a.P, a.g, elt, a.wave_parts);
+  const long groups = a.wave_parts ? (a.Pmax + kWaves - 1) / kWaves : a.Pmax;
+  const long grid = (long)a.Hkv * groups * a.S;
   hipLaunchKernelGGL((paged_decode_kernel<T, C, D, BS, kWaves, kPipe, false>), dim3((unsigned)grid),
                      dim3(kWaves * 64), lds, stream, a, NoOrder{});
   hipError_t err = hipGetLastError();
@@ -1146,6 +1204,14 @@ pa_status run_decode(void* out, const void* query, const int32_t* block_table,
   a.NB = num_blocks;
   a.P = P;
   a.Pmax = pmax;
+  // Short partitions: each wave of a workgroup owns one of kWaves consecutive
+  // partitions, so one prologue serves them all and no cross-wave merge is needed --
+  // when the workgroups still give every compute unit two.
+  {
+    const long groups = (pmax + pa::kWaves - 1) / pa::kWaves;
+    a.wave_parts = pmax >= 2 && (long)P * pa::kWaves <= pa::kMaxPartition &&
+                   (long)num_kv_heads * num_seqs * groups >= 2L * device_cu_count();
+  }
   a.scale_log2 = static_cast<float>(static_cast<double>(scale) * (fp8 ? k_scale : 1.0) *
                                     1.4426950408889634);
   a.v_scale = fp8 ? v_scale : 1.f;
