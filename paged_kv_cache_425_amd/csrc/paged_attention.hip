@@ -926,7 +926,10 @@ paged_decode_kernel(const DecodeParams a, const OrderArg<PAIRED> ord) {
 
 // Log-sum-exp merge of the partitions of one (sequence, query head):
 //   M = max_p m_p,  out = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p.
-// One wave per row; lane i handles channels i, i + 64, ...
+// One wave per row.  The lanes read the partitions' (m, l) pairs side by side for M
+// and the denominator; for the numerator lane i handles channels i, i + 64, ..., and
+// the partitions are taken 8 at a time so that their loads are in flight together
+// (each partition's weight is a wave-uniform value).
 template <typename T, int D, int BS>
 __global__ void __launch_bounds__(64)
 reduce_partitions_kernel(const DecodeParams a) {
@@ -938,8 +941,9 @@ reduce_partitions_kernel(const DecodeParams a) {
   const size_t row = (size_t)s * a.Hq + h;
   const float* ml = a.part_ml + row * a.Pmax * 2;
   const float* acc = a.part_acc + row * a.Pmax * D;
+  const int lane = threadIdx.x;
   float M = kNegInf;
-  for (int q = threadIdx.x; q < nparts; q += 64) M = fmaxf(M, ml[2 * q]);
+  for (int q = lane; q < nparts; q += 64) M = fmaxf(M, ml[2 * q]);
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
   constexpr int kPer = D / 64;
@@ -948,17 +952,29 @@ reduce_partitions_kernel(const DecodeParams a) {
   for (int i = 0; i < kPer; ++i) num[i] = 0.f;
   float den = 0.f;
   if (M != kNegInf) {
-    for (int q = 0; q < nparts; ++q) {
-      const float f = exp2_fast(ml[2 * q] - M);
-      den += f * ml[2 * q + 1];
+    for (int q = lane; q < nparts; q += 64) den += exp2_fast(ml[2 * q] - M) * ml[2 * q + 1];
 #pragma unroll
-      for (int i = 0; i < kPer; ++i) num[i] += f * acc[(size_t)q * D + threadIdx.x + 64 * i];
+    for (int o = 32; o >= 1; o >>= 1) den += __shfl_xor(den, o, 64);
+    constexpr int kU = 8;
+    for (int q0 = 0; q0 < nparts; q0 += kU) {
+      float f[kU], v[kU][kPer];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int q = min(q0 + u, nparts - 1);               // past the end: re-read, weight 0
+        f[u] = q0 + u < nparts ? exp2_fast(ml[2 * q] - M) : 0.f;
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) v[u][i] = acc[(size_t)q * D + lane + 64 * i];
+      }
+#pragma unroll
+      for (int u = 0; u < kU; ++u)
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) num[i] += f[u] * v[u][i];
     }
   }
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
     const float o = (M == kNegInf || den == 0.f) ? 0.f : num[i] / den;
-    const size_t idx = row * D + threadIdx.x + 64 * i;
+    const size_t idx = row * D + lane + 64 * i;
     if constexpr (ElemTraits<T>::kBf16)
       static_cast<uint16_t*>(a.out)[idx] = bf16_bits(o);
     else
