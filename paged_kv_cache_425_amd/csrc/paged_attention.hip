@@ -928,7 +928,7 @@ paged_decode_kernel(const DecodeParams a, const OrderArg<PAIRED> ord) {
 //   M = max_p m_p,  out = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p.
 // One wave per row.  The lanes read the partitions' (m, l) pairs side by side for M
 // and the denominator; for the numerator lane i handles channels i, i + 64, ..., and
-// the partitions are taken 8 at a time so that their loads are in flight together
+// the partitions are taken 16 at a time so that their loads are in flight together
 // (each partition's weight is a wave-uniform value).
 template <typename T, int D, int BS>
 __global__ void __launch_bounds__(64)
@@ -955,7 +955,7 @@ reduce_partitions_kernel(const DecodeParams a) {
     for (int q = lane; q < nparts; q += 64) den += exp2_fast(ml[2 * q] - M) * ml[2 * q + 1];
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) den += __shfl_xor(den, o, 64);
-    constexpr int kU = 8;
+    constexpr int kU = 16;
     for (int q0 = 0; q0 < nparts; q0 += kU) {
       float f[kU], v[kU][kPer];
 #pragma unroll
