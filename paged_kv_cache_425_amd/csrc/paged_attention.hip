@@ -21,6 +21,12 @@
 //     so the compiler's wait counts never fall back to "wait for everything").
 //   One step is 32 tokens (bf16) or 16 tokens (f32) of one KV head, shared by
 //     the whole query-head group (GQA): each K/V byte is fetched once per group.
+//   When partitions are short and plentiful, a workgroup instead takes NW
+//     consecutive partitions of one sequence, one per wave: one table window and
+//     prologue serve them all, and each wave writes its own partition's result.
+//   When every sequence is one partition, a workgroup takes two (sequence, kv
+//     head) units, the r-th longest and the r-th shortest sequence (the paired
+//     mode below); the order comes from the host when it has the lengths.
 //   Sequences that fit in one partition write their output directly.  Longer
 //     ones write (max, sum, unnormalised output) per partition to the
 //     workspace and a second kernel merges the partitions with a log-sum-exp
