@@ -297,33 +297,34 @@ def test_fused_fp8_step_matches_two_calls_and_oracle(D, BS, g, part):
 
 
 @pytest.mark.parametrize("part", [64, 512])
-def test_fp8_full_batch_with_a_long_tail(part):
+@pytest.mark.parametrize("BS,D", [(16, 128), (8, 64), (32, 128)])
+def test_fp8_full_batch_with_a_long_tail(part, BS, D):
     """A batch of 64 sequences x 8 kv heads (fills the GPU) with six long ones, in
-    partitions of P tokens: plain decode and the fused step both agree with the oracle, and
-    the step's pools are bit-exact."""
+    partitions of P tokens (here one partition per wave): plain decode and the fused step
+    both agree with the oracle, and the step's pools are bit-exact."""
     rng = np.random.default_rng(540 + part)
     lens = rng.permutation(np.concatenate([rng.integers(1, 300, size=58),
                                            rng.integers(2000, 4500, size=6)]))
-    w = tiny("bf16", lens, 32, 8, 128, 16, seed=541 + part)
+    w = tiny("bf16", lens, 32, 8, D, BS, seed=541 + part + BS + D)
     new, slots = _new_tokens(w)
     hist = np.setdiff1d(np.arange(len(w.rec_slot)), new)
-    hk, hv = oracle.empty_fp8_pools(w.num_blocks, w.num_kv_heads, 128, 16)
+    hk, hv = oracle.empty_fp8_pools(w.num_blocks, w.num_kv_heads, D, BS)
     oracle.reshape_and_cache_fp8(w.rec_key[hist], w.rec_value[hist], w.rec_slot[hist], hk, hv,
                                  "bf16", K_SCALE, V_SCALE, inplace=True)
     ref_k, ref_v = oracle.reshape_and_cache_fp8(w.rec_key[new], w.rec_value[new], slots, hk, hv,
                                                 "bf16", K_SCALE, V_SCALE)
     ref = oracle.paged_attention_fp8(w.query, w.block_table, w.context_lens, ref_k, ref_v,
                                      w.scale, K_SCALE, V_SCALE, "bf16")
-    say(f"fp8 long tail P={part}")
+    say(f"fp8 long tail P={part} BS={BS} D={D}")
     got = run_attention(w, ref_k, ref_v, partition_size=part)
-    check_close(to_f64(got), ref, "bf16", f"fp8-long-tail/{part}")
+    check_close(to_f64(got), ref, "bf16", f"fp8-long-tail/{part}/{BS}/{D}")
     key, val = to_dev(w.rec_key[new], "bf16", DEV), to_dev(w.rec_value[new], "bf16", DEV)
     kc, vc = u8(hk), u8(hv)
     out = _fused_fp8(w, key, val, torch.from_numpy(slots).to(DEV), kc, vc, part)
     torch.cuda.synchronize()
     assert np.array_equal(kc.cpu().numpy(), ref_k)
     assert np.array_equal(vc.cpu().numpy(), ref_v)
-    check_close(to_f64(out), ref, "bf16", f"fused-fp8-long-tail/{part}")
+    check_close(to_f64(out), ref, "bf16", f"fused-fp8-long-tail/{part}/{BS}/{D}")
 
 
 def test_fused_fp8_step_negative_and_unread_slots():
