@@ -34,14 +34,15 @@
  * - query/out/key/value/k_cache/v_cache must be 16-byte aligned; tables
  *   4-byte aligned; slot_mapping and seq_offsets 8-byte aligned.
  *
- * Cache layout (one K pool and one V pool, X = 16 / element bytes, so X = 8
- * for bf16 and X = 4 for f32):
- *   k_cache: [num_blocks][num_kv_heads][D / X][BS][X]
- *   v_cache: [num_blocks][num_kv_heads][D][BS]
+ * Cache layout (one K pool and one V pool):
+ *   k_cache: [num_blocks][num_kv_heads][BS][D]   (token-major: a token's K row of
+ *            one kv head is D contiguous elements)
+ *   v_cache: [num_blocks][num_kv_heads][D][BS]   (channel-major: one channel's BS
+ *            tokens are contiguous)
  * Token t of a sequence with block-table row `bt` lives in physical block
- * b = bt[t / BS] at offset o = t % BS; its K channel d is
- * k_cache[b][h][d / X][o][d % X] and its V channel d is v_cache[b][h][d][o].
- * A slot is b * BS + o.
+ * b = bt[t / BS] at offset o = t % BS; its K channel d is k_cache[b][h][o][d] and
+ * its V channel d is v_cache[b][h][d][o].  One (block, kv head) tile of either
+ * pool is BS * D contiguous elements.  A slot is b * BS + o.
  *
  * Device-side preconditions (not checked by the library; violating them gives
  * wrong results but no access outside the buffers passed in):
@@ -267,8 +268,8 @@ pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_mapp
  * E4M3(code) * k_scale; likewise V with v_scale.  k_scale and v_scale must be
  * finite and > 0 (else PA_ERR_INVALID_ARG).
  *
- * Layout: the pools above with 1-byte elements, so X = 16:
- *   k_cache: [num_blocks][num_kv_heads][D / 16][BS][16] uint8
+ * Layout: the pools above with 1-byte elements:
+ *   k_cache: [num_blocks][num_kv_heads][BS][D] uint8
  *   v_cache: [num_blocks][num_kv_heads][D][BS] uint8
  */
 

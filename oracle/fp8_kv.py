@@ -29,7 +29,7 @@ plainest reading of an FP8 K/V cache:
 * Attention over an FP8 cache is attention over the dequantised K and V.
 
 Cache layout: the boundary's layout with 1-byte elements, so X = 16:
-k_cache uint8 [num_blocks, Hkv, D // 16, block_size, 16], v_cache uint8
+k_cache uint8 [num_blocks, Hkv, block_size, D], v_cache uint8
 [num_blocks, Hkv, D, block_size].
 
 Pins (in the test suite): the code values the OCP specification lists
@@ -45,7 +45,6 @@ import numpy as np
 from .paged_attention import attention_one, decode, gather_sequence, reshape_and_cache
 
 FP8_MAX = 448.0
-CHUNK = 16                       # elements per 16-byte chunk of a K row
 
 
 def e4m3_values() -> np.ndarray:
@@ -104,10 +103,18 @@ def quantize(x: np.ndarray, dtype: str, scale: float) -> np.ndarray:
     return codes
 
 
+def quantize_bf16(x_bits: np.ndarray, scale: float) -> np.ndarray:
+    """quantize() of bfloat16 elements, looked up in a table of quantize() over all 65536
+    bit patterns: the code of an element depends only on its bits and the scale, so the
+    result is the same array of codes (a pin in the test suite compares the two)."""
+    table = quantize(np.arange(1 << 16, dtype=np.uint32).astype(np.uint16), "bf16", scale)
+    return table[np.asarray(x_bits, dtype=np.uint16)]
+
+
 def empty_fp8_pools(num_blocks: int, num_kv_heads: int, head_dim: int, block_size: int,
                     fill: int = 0x7F):
     """FP8 pools filled with one code (NaN by default, so stray reads show)."""
-    ks = (num_blocks, num_kv_heads, head_dim // CHUNK, block_size, CHUNK)
+    ks = (num_blocks, num_kv_heads, block_size, head_dim)
     vs = (num_blocks, num_kv_heads, head_dim, block_size)
     return np.full(ks, fill, dtype=np.uint8), np.full(vs, fill, dtype=np.uint8)
 

@@ -31,11 +31,11 @@ What is computed, and where the pages define it
 
 Cache layout (the library's boundary format; the pages show only that a
 physical block yields its k and v):
-* k_cache: [num_blocks, Hkv, D // X, block_size, X] with X = 16 bytes / element
-  size (X = 8 for bfloat16, 4 for float32);
-* v_cache: [num_blocks, Hkv, D, block_size].
+* k_cache: [num_blocks, Hkv, block_size, D] (token-major: one token's K row of
+  one kv head is contiguous);
+* v_cache: [num_blocks, Hkv, D, block_size] (channel-major).
 Element (token t, kv head h, channel d) of sequence s lives at
-``k_cache[b, h, d // X, t % BS, d % X]`` and ``v_cache[b, h, d, t % BS]`` with
+``k_cache[b, h, t % BS, d]`` and ``v_cache[b, h, d, t % BS]`` with
 ``b = block_table[s, t // BS]``.
 
 Precision: inputs are float32 arrays or bfloat16 bit patterns (uint16);
@@ -75,14 +75,13 @@ def decode(x: np.ndarray, dtype: str) -> np.ndarray:
 
 
 def chunk_elems(dtype: str) -> int:
-    """X: elements in one 16-byte chunk of a K row."""
+    """Elements in one 16-byte chunk."""
     return 16 // ELEMENT_BYTES[dtype]
 
 
 def k_cache_shape(num_blocks: int, num_kv_heads: int, head_dim: int, block_size: int,
                   dtype: str) -> tuple:
-    X = chunk_elems(dtype)
-    return (num_blocks, num_kv_heads, head_dim // X, block_size, X)
+    return (num_blocks, num_kv_heads, block_size, head_dim)
 
 
 def v_cache_shape(num_blocks: int, num_kv_heads: int, head_dim: int, block_size: int,
@@ -102,13 +101,13 @@ def reshape_and_cache(key: np.ndarray, value: np.ndarray, slot_mapping: np.ndarr
     """
     k_new = k_cache if inplace else k_cache.copy()
     v_new = v_cache if inplace else v_cache.copy()
-    NB, Hkv, DX, BS, X = k_cache.shape
+    NB, Hkv, BS, D = k_cache.shape
     slots = np.asarray(slot_mapping, dtype=np.int64)
     live = np.nonzero(slots >= 0)[0]
     assert len(np.unique(slots[live])) == len(live), "slots of one call must be distinct"
     assert (slots[live] < NB * BS).all(), "slot outside the pool"
     blk, off = slots[live] // BS, slots[live] % BS
-    k_new[blk, :, :, off, :] = key[live].reshape(len(live), Hkv, DX, X)
+    k_new[blk, :, off, :] = key[live]
     v_new[blk, :, :, off] = value[live]
     return k_new, v_new
 
@@ -173,12 +172,12 @@ def swap_blocks(src_k: np.ndarray, src_v: np.ndarray, dst_k: np.ndarray, dst_v: 
 def gather_sequence(block_table_row: np.ndarray, context_len: int,
                     k_cache: np.ndarray, v_cache: np.ndarray):
     """Contiguous K and V ([L, Hkv, D], pool dtype, bit-exact) of one sequence."""
-    NB, Hkv, DX, BS, X = k_cache.shape
+    NB, Hkv, BS, D = k_cache.shape
     L = int(context_len)
     n = -(-L // BS)
     blocks = np.asarray(block_table_row[:n], dtype=np.int64)
-    k = k_cache[blocks].transpose(0, 3, 1, 2, 4).reshape(n * BS, Hkv, DX * X)[:L]
-    v = v_cache[blocks].transpose(0, 3, 1, 2).reshape(n * BS, Hkv, DX * X)[:L]
+    k = k_cache[blocks].transpose(0, 2, 1, 3).reshape(n * BS, Hkv, D)[:L]
+    v = v_cache[blocks].transpose(0, 3, 1, 2).reshape(n * BS, Hkv, D)[:L]
     return k, v
 
 
@@ -253,14 +252,20 @@ def paged_prefill(query: np.ndarray, query_start_loc: np.ndarray, block_table: n
         L = int(context_lens[s])
         n = r1 - r0
         assert 0 <= n <= L, "a chunk cannot be longer than its context"
+        if n == 0:
+            continue
         k, v = gather_sequence(block_table[s], L, k_cache, v_cache)
         kf, vf, qf = decode(k, dtype), decode(v, dtype), decode(query[r0:r1], dtype)
-        for i in range(n):
-            p = L - n + i
-            for kvh in range(Hkv):
-                heads = slice(kvh * g, (kvh + 1) * g)
-                out[r0 + i, heads] = attention_one(qf[i, heads], kf[:p + 1, kvh],
-                                                   vf[:p + 1, kvh], scale)
+        # query row (i, head) sits at position p_i = L - n + i and sees the keys t <= p_i
+        pos = np.repeat(L - n + np.arange(n), g)                               # [n * g]
+        seen = np.arange(L)[None, :] <= pos[:, None]                            # [n * g, L]
+        for kvh in range(Hkv):
+            heads = slice(kvh * g, (kvh + 1) * g)
+            q = qf[:, heads].reshape(n * g, D)
+            z = np.where(seen, scale * (q @ kf[:, kvh].T), -np.inf)             # logits
+            w = np.exp(z - z.max(axis=1, keepdims=True))                        # 0 where unseen
+            o = (w @ vf[:, kvh]) / w.sum(axis=1)[:, None]
+            out[r0:r1, heads] = o.reshape(n, g, D)
     return out
 
 

@@ -87,6 +87,17 @@ def _stream(device: torch.device, stream) -> int:
     return s.cuda_stream
 
 
+def _record(stream, made) -> None:
+    """Tensors this module allocated (on torch's current stream) that a kernel on the
+    caller's `stream` still uses after the call returns: the caching allocator must not
+    hand their memory to another tensor before that stream's work is done."""
+    if stream is None:
+        return
+    for t in made:
+        if t is not None:
+            t.record_stream(stream)
+
+
 def _host_lens(host_context_lens, num_seqs: int):
     """(pointer, holder) of an optional host int32 copy of context_lens [num_seqs]."""
     if host_context_lens is None:
@@ -115,26 +126,24 @@ def _require(t: torch.Tensor, name: str, device: torch.device, dtype=None) -> No
 
 
 def chunk_elems(dtype: torch.dtype) -> int:
-    """Elements of one 16-byte K chunk (8 for bfloat16, 4 for float32)."""
+    """Elements of one 16-byte chunk (8 for bfloat16, 4 for float32, 16 for FP8 codes)."""
     return 16 // torch.empty((), dtype=dtype).element_size()
 
 
-def k_cache_shape(num_blocks, num_kv_heads, head_dim, block_size, dtype) -> tuple:
-    X = chunk_elems(dtype)
-    return (num_blocks, num_kv_heads, head_dim // X, block_size, X)
+def k_cache_shape(num_blocks, num_kv_heads, head_dim, block_size, dtype=None) -> tuple:
+    """K pool shape: token-major [NB, Hkv, BS, D]."""
+    return (num_blocks, num_kv_heads, block_size, head_dim)
 
 
-def v_cache_shape(num_blocks, num_kv_heads, head_dim, block_size, dtype) -> tuple:
+def v_cache_shape(num_blocks, num_kv_heads, head_dim, block_size, dtype=None) -> tuple:
+    """V pool shape: channel-major [NB, Hkv, D, BS]."""
     return (num_blocks, num_kv_heads, head_dim, block_size)
 
 
 def _cache_dims(k_cache: torch.Tensor, v_cache: torch.Tensor):
-    if k_cache.dim() != 5 or v_cache.dim() != 4:
-        raise ValueError("k_cache must be [NB, Hkv, D/X, BS, X] and v_cache [NB, Hkv, D, BS]")
-    NB, Hkv, DX, BS, X = k_cache.shape
-    D = DX * X
-    if X != chunk_elems(k_cache.dtype):
-        raise ValueError(f"k_cache last dim must be {chunk_elems(k_cache.dtype)} for {k_cache.dtype}")
+    if k_cache.dim() != 4 or v_cache.dim() != 4:
+        raise ValueError("k_cache must be [NB, Hkv, BS, D] and v_cache [NB, Hkv, D, BS]")
+    NB, Hkv, BS, D = k_cache.shape
     if tuple(v_cache.shape) != (NB, Hkv, D, BS) or v_cache.dtype != k_cache.dtype:
         raise ValueError(f"v_cache must be {(NB, Hkv, D, BS)} of {k_cache.dtype}, got "
                          f"{tuple(v_cache.shape)} of {v_cache.dtype}")
@@ -177,8 +186,10 @@ def paged_attention(query: torch.Tensor, block_table: torch.Tensor, context_lens
     if block_table.dim() != 2 or block_table.shape[0] != S or tuple(context_lens.shape) != (S,):
         raise ValueError("block_table must be [S, MB] and context_lens [S]")
     MB = block_table.shape[1]
+    made = []
     if out is None:
         out = torch.empty_like(query)
+        made.append(out)
     _require(out, "out", dev, query.dtype)
     if tuple(out.shape) != tuple(query.shape):
         raise ValueError("out must have the shape of query")
@@ -186,6 +197,7 @@ def paged_attention(query: torch.Tensor, block_table: torch.Tensor, context_lens
     need = workspace_size(S, Hq, Hkv, D, max_context_len, partition_size, query.dtype)
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+        made.append(workspace)
     if workspace is not None:
         _require(workspace, "workspace", dev)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
@@ -195,6 +207,7 @@ def paged_attention(query: torch.Tensor, block_table: torch.Tensor, context_lens
                                 int(max_context_len), float(scale), code, int(partition_size),
                                 _ptr(workspace), ws_bytes, _stream(dev, stream), hl)
     _check(st, "pa_paged_attention")
+    _record(stream, made)
     return out
 
 
@@ -218,14 +231,17 @@ def _decode_step_args(query, key, value, slot_mapping, block_table, context_lens
         raise ValueError(f"key/value must be [{S}, {Hkv}, {D}] and slot_mapping [{S}]")
     if block_table.dim() != 2 or block_table.shape[0] != S or tuple(context_lens.shape) != (S,):
         raise ValueError("block_table must be [S, MB] and context_lens [S]")
+    made = []
     if out is None:
         out = torch.empty_like(query)
+        made.append(out)
     _require(out, "out", dev, query.dtype)
     if tuple(out.shape) != tuple(query.shape):
         raise ValueError("out must have the shape of query")
     need = workspace_size(S, Hq, Hkv, D, max_context_len, partition_size, query.dtype)
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+        made.append(workspace)
     if workspace is not None:
         _require(workspace, "workspace", dev)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
@@ -236,7 +252,7 @@ def _decode_step_args(query, key, value, slot_mapping, block_table, context_lens
             int(partition_size), _ptr(workspace), ws_bytes, _stream(dev, stream), hl)
     keep = (query, key, value, slot_mapping, block_table, context_lens, k_cache, v_cache, out,
             workspace, hold)
-    return args, out, keep
+    return args, out, keep, made
 
 
 def decode_step(query: torch.Tensor, key: torch.Tensor, value: torch.Tensor,
@@ -248,10 +264,12 @@ def decode_step(query: torch.Tensor, key: torch.Tensor, value: torch.Tensor,
     """One fused step: store key/value [S, Hkv, D] at slot_mapping [S], then decode
     attention of query [S, Hq, D] (see pa_decode_step in pagedattn.h)."""
     lib = load_library()
-    args, out, _ = _decode_step_args(query, key, value, slot_mapping, block_table, context_lens,
-                                     k_cache, v_cache, scale, max_context_len, out,
-                                     partition_size, workspace, stream, host_context_lens)
+    args, out, _, made = _decode_step_args(query, key, value, slot_mapping, block_table,
+                                           context_lens, k_cache, v_cache, scale,
+                                           max_context_len, out, partition_size, workspace,
+                                           stream, host_context_lens)
     _check(lib.pa_decode_step(*args), "pa_decode_step")
+    _record(stream, made)
     return out
 
 
@@ -323,14 +341,17 @@ def _attention_fp8_args(query, block_table, context_lens, k_cache, v_cache, scal
     S, Hq, _ = query.shape
     if block_table.dim() != 2 or block_table.shape[0] != S or tuple(context_lens.shape) != (S,):
         raise ValueError("block_table must be [S, MB] and context_lens [S]")
+    made = []
     if out is None:
         out = torch.empty_like(query)
+        made.append(out)
     _require(out, "out", dev, query.dtype)
     if tuple(out.shape) != tuple(query.shape):
         raise ValueError("out must have the shape of query")
     need = workspace_size(S, Hq, Hkv, D, max_context_len, partition_size, torch.bfloat16)
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+        made.append(workspace)
     if workspace is not None:
         _require(workspace, "workspace", dev)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
@@ -341,7 +362,7 @@ def _attention_fp8_args(query, block_table, context_lens, k_cache, v_cache, scal
     hl, hold = _host_lens(host_context_lens, S)
     args = args + (hl,)
     keep = (query, block_table, context_lens, k_cache, v_cache, out, workspace, hold)
-    return args, out, keep
+    return args, out, keep, made
 
 
 def paged_attention_fp8(query: torch.Tensor, block_table: torch.Tensor,
@@ -351,10 +372,12 @@ def paged_attention_fp8(query: torch.Tensor, block_table: torch.Tensor,
                         workspace: torch.Tensor | None = None, stream=None,
                         host_context_lens=None) -> torch.Tensor:
     """Decode attention of bf16 query [S, Hq, D] over FP8 pools (see pagedattn.h)."""
-    args, out, _ = _attention_fp8_args(query, block_table, context_lens, k_cache, v_cache, scale,
-                                       k_scale, v_scale, max_context_len, out, partition_size,
-                                       workspace, stream, host_context_lens)
+    args, out, _, made = _attention_fp8_args(query, block_table, context_lens, k_cache, v_cache,
+                                             scale, k_scale, v_scale, max_context_len, out,
+                                             partition_size, workspace, stream,
+                                             host_context_lens)
     _check(load_library().pa_paged_attention_fp8(*args), "pa_paged_attention_fp8")
+    _record(stream, made)
     return out
 
 
@@ -370,12 +393,13 @@ def _decode_step_fp8_args(query, key, value, slot_mapping, block_table, context_
     if tuple(key.shape) != (S, Hkv, D) or tuple(value.shape) != (S, Hkv, D) or \
             tuple(slot_mapping.shape) != (S,):
         raise ValueError(f"key/value must be [{S}, {Hkv}, {D}] and slot_mapping [{S}]")
-    args, out, keep = _attention_fp8_args(query, block_table, context_lens, k_cache, v_cache,
-                                          scale, k_scale, v_scale, max_context_len, out,
-                                          partition_size, workspace, stream, host_context_lens)
+    args, out, keep, made = _attention_fp8_args(query, block_table, context_lens, k_cache,
+                                                v_cache, scale, k_scale, v_scale,
+                                                max_context_len, out, partition_size, workspace,
+                                                stream, host_context_lens)
     # pa_decode_step_fp8 takes key, value and slot_mapping after query
     args = args[:2] + (_ptr(key), _ptr(value), _ptr(slot_mapping)) + args[2:]
-    return args, out, keep + (key, value, slot_mapping)
+    return args, out, keep + (key, value, slot_mapping), made
 
 
 def decode_step_fp8(query: torch.Tensor, key: torch.Tensor, value: torch.Tensor,
@@ -387,11 +411,12 @@ def decode_step_fp8(query: torch.Tensor, key: torch.Tensor, value: torch.Tensor,
                     host_context_lens=None) -> torch.Tensor:
     """One fused step over FP8 pools: quantise key/value [S, Hkv, D] (bf16) into
     slot_mapping [S], then decode attention of query [S, Hq, D] (see pa_decode_step_fp8)."""
-    args, out, _ = _decode_step_fp8_args(query, key, value, slot_mapping, block_table,
-                                         context_lens, k_cache, v_cache, scale, k_scale, v_scale,
-                                         max_context_len, out, partition_size, workspace, stream,
-                                         host_context_lens)
+    args, out, _, made = _decode_step_fp8_args(query, key, value, slot_mapping, block_table,
+                                               context_lens, k_cache, v_cache, scale, k_scale,
+                                               v_scale, max_context_len, out, partition_size,
+                                               workspace, stream, host_context_lens)
     _check(load_library().pa_decode_step_fp8(*args), "pa_decode_step_fp8")
+    _record(stream, made)
     return out
 
 
@@ -417,8 +442,10 @@ def paged_prefill(query: torch.Tensor, query_start_loc: torch.Tensor, block_tabl
     if tuple(query_start_loc.shape) != (S + 1,) or block_table.dim() != 2 or \
             block_table.shape[0] != S:
         raise ValueError("query_start_loc must be [S + 1] and block_table [S, MB]")
+    made = []
     if out is None:
         out = torch.empty_like(query)
+        made.append(out)
     _require(out, "out", dev, query.dtype)
     if tuple(out.shape) != tuple(query.shape):
         raise ValueError("out must have the shape of query")
@@ -427,6 +454,7 @@ def paged_prefill(query: torch.Tensor, query_start_loc: torch.Tensor, block_tabl
                               BS, block_table.shape[1], NB, T, int(max_query_len), float(scale),
                               _dtype_code(query), _stream(dev, stream))
     _check(st, "pa_paged_prefill")
+    _record(stream, made)
     return out
 
 
@@ -527,6 +555,7 @@ def gather_kv(block_table: torch.Tensor, context_lens: torch.Tensor, k_cache: to
                           _ptr(context_lens), _ptr(k_cache), _ptr(v_cache), S, Hkv, D, BS, MB,
                           NB, int(max_context_len), _dtype_code(k_cache), _stream(dev, stream))
     _check(st, "pa_gather_kv")
+    _record(stream, (k_out, v_out))
     return k_out, v_out
 
 
@@ -556,8 +585,8 @@ def prepare_paged_attention(query, block_table, context_lens, k_cache, v_cache, 
     lib = load_library()
     dev = query.device
     need = workspace_size(query.shape[0], query.shape[1], k_cache.shape[1],
-                          k_cache.shape[2] * k_cache.shape[4], max_context_len, partition_size,
-                          query.dtype) if k_cache.dim() == 5 and query.dim() == 3 else 0
+                          k_cache.shape[3], max_context_len, partition_size,
+                          query.dtype) if k_cache.dim() == 4 and query.dim() == 3 else 0
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     # one checked call validates every argument (and runs once)
@@ -594,9 +623,10 @@ def prepare_decode_step(query, key, value, slot_mapping, block_table, context_le
                         workspace=None, stream=None, host_context_lens=None) -> PreparedCall:
     """Check the arguments of decode_step once and return a re-launchable call."""
     lib = load_library()
-    args, out, keep = _decode_step_args(query, key, value, slot_mapping, block_table,
-                                        context_lens, k_cache, v_cache, scale, max_context_len,
-                                        out, partition_size, workspace, stream, host_context_lens)
+    args, out, keep, _ = _decode_step_args(query, key, value, slot_mapping, block_table,
+                                           context_lens, k_cache, v_cache, scale,
+                                           max_context_len, out, partition_size, workspace,
+                                           stream, host_context_lens)
     call = PreparedCall(lib.pa_decode_step, args, "pa_decode_step", keep)
     call()
     return call
@@ -618,9 +648,10 @@ def prepare_paged_attention_fp8(query, block_table, context_lens, k_cache, v_cac
                                 partition_size: int = 0, workspace=None,
                                 stream=None, host_context_lens=None) -> PreparedCall:
     """Check the arguments of paged_attention_fp8 once and return a re-launchable call."""
-    args, out, keep = _attention_fp8_args(query, block_table, context_lens, k_cache, v_cache,
-                                          scale, k_scale, v_scale, max_context_len, out,
-                                          partition_size, workspace, stream, host_context_lens)
+    args, out, keep, _ = _attention_fp8_args(query, block_table, context_lens, k_cache,
+                                             v_cache, scale, k_scale, v_scale, max_context_len,
+                                             out, partition_size, workspace, stream,
+                                             host_context_lens)
     call = PreparedCall(load_library().pa_paged_attention_fp8, args, "pa_paged_attention_fp8",
                         keep)
     call()
@@ -632,10 +663,10 @@ def prepare_decode_step_fp8(query, key, value, slot_mapping, block_table, contex
                             partition_size: int = 0, workspace=None,
                             stream=None, host_context_lens=None) -> PreparedCall:
     """Check the arguments of decode_step_fp8 once and return a re-launchable call."""
-    args, out, keep = _decode_step_fp8_args(query, key, value, slot_mapping, block_table,
-                                            context_lens, k_cache, v_cache, scale, k_scale,
-                                            v_scale, max_context_len, out, partition_size,
-                                            workspace, stream, host_context_lens)
+    args, out, keep, _ = _decode_step_fp8_args(query, key, value, slot_mapping, block_table,
+                                               context_lens, k_cache, v_cache, scale, k_scale,
+                                               v_scale, max_context_len, out, partition_size,
+                                               workspace, stream, host_context_lens)
     call = PreparedCall(load_library().pa_decode_step_fp8, args, "pa_decode_step_fp8", keep)
     call()
     return call

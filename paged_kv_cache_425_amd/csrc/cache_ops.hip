@@ -6,9 +6,9 @@
 // gather_kv: the inverse, reassembling each sequence through its block table
 // (page "vLLM core architecture", section 2.2.2) as plain copies.
 //
-// Both are bit-exact copies; K moves in 16-byte chunks (one K chunk is
-// contiguous in both layouts), V element by element (its cache rows run
-// along tokens).
+// Both are bit-exact copies; K moves in 16-byte chunks (a token's K row is
+// contiguous in the token-major K pool), V element by element (its cache rows
+// run along tokens).
 #include "common.h"
 
 namespace pa {
@@ -41,7 +41,7 @@ reshape_and_cache_kernel(const T* __restrict__ key, const T* __restrict__ value,
     const int h = cc / chunks;
     const int dc = cc % chunks;
     if (!is_v) {
-      store16(k_cache + (((size_t)blk * Hkv + h) * chunks + dc) * BS * X + (size_t)off * X, val);
+      store16(k_cache + (((size_t)blk * Hkv + h) * BS + off) * D + (size_t)dc * X, val);
     } else {
       T* dst = v_cache + (((size_t)blk * Hkv + h) * D + (size_t)dc * X) * BS + off;
       const T* e = reinterpret_cast<const T*>(&val);
@@ -76,7 +76,7 @@ gather_kv_kernel(T* __restrict__ k_out, T* __restrict__ v_out,
     const int r = c % (Hkv * chunks);
     const int h = r / chunks;
     const int dc = r % chunks;
-    const T* src = k_cache + ((phys * Hkv + h) * chunks + dc) * BS * X + (size_t)o * X;
+    const T* src = k_cache + ((phys * Hkv + h) * BS + o) * D + (size_t)dc * X;
     store16(k_out + ((row0 + o) * Hkv + h) * D + dc * X, load16(src));
   }
   for (int e = threadIdx.x; e < nt * Hkv * D; e += kCopyThreads) {

@@ -37,15 +37,14 @@ __device__ __forceinline__ void load8_elems(const T* p, float (&x)[8]) {
 }
 
 // One workgroup per token.  Thread c quantises 8 consecutive channels of the token's K
-// (c < Hkv*D/8) or V (the rest): K codes are one 8-byte store (half a 16-byte chunk of
-// the cache row), V codes are 8 byte stores along the cache's token axis.
+// (c < Hkv*D/8) or V (the rest): K codes are one 8-byte store into the token's K row,
+// V codes are 8 byte stores along the cache's token axis.
 template <typename T>
 __global__ void __launch_bounds__(kFp8Threads)
 reshape_and_cache_fp8_kernel(const T* __restrict__ key, const T* __restrict__ value,
                              const int64_t* __restrict__ slot_mapping,
                              uint8_t* __restrict__ k_cache, uint8_t* __restrict__ v_cache,
                              int Hkv, int D, int BS, int NB, float k_scale, float v_scale) {
-  constexpr int X = 16;
   const int i = blockIdx.x;
   const int groups = D / 8;                 // 8-channel groups per head
   const int ngroup = Hkv * groups;          // per token, for K and for V
@@ -71,8 +70,7 @@ reshape_and_cache_fp8_kernel(const T* __restrict__ key, const T* __restrict__ va
     const int h = cc / groups;
     const int d0 = (cc % groups) * 8;         // first channel of the group
     if (!is_v) {
-      uint8_t* dst = k_cache + ((((size_t)blk * Hkv + h) * (D / X) + d0 / X) * BS + off) * X +
-                     d0 % X;
+      uint8_t* dst = k_cache + (((size_t)blk * Hkv + h) * BS + off) * D + d0;
       *reinterpret_cast<uint2*>(dst) = make_uint2(codes[0], codes[1]);
     } else {
       uint8_t* dst = v_cache + (((size_t)blk * Hkv + h) * D + (size_t)d0) * BS + off;

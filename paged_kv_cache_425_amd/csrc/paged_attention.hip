@@ -62,6 +62,7 @@
 // Lane mapping of a 16x16 MFMA output: lane l holds rows 4*(l/16)..+3 of
 // column l%16.  Below, n = l%16 and j = l/16.
 #include <algorithm>
+#include <atomic>
 #include <type_traits>
 
 #include "common.h"
@@ -507,8 +508,7 @@ paged_decode_kernel(const DecodeParams a, const OrderArg<PAIRED> ord) {
       const int off = (int)(new_slot % BS);
       const int d0 = new_cc * 8;                           // first channel of the 8 codes
       if (!new_is_v) {
-        uint8_t* dst = kcw + (((blk * a.Hkv + kvh) * (D / 16) + d0 / 16) * BS + off) * 16 +
-                       d0 % 16;
+        uint8_t* dst = kcw + ((blk * a.Hkv + kvh) * BS + off) * D + d0;
         *reinterpret_cast<uint2*>(dst) = make_uint2(new_val[0], new_val[1]);
       } else {
         uint8_t* dst = vcw + ((blk * a.Hkv + kvh) * D + (size_t)d0) * BS + off;
@@ -522,7 +522,7 @@ paged_decode_kernel(const DecodeParams a, const OrderArg<PAIRED> ord) {
       const size_t blk = (size_t)(new_slot / BS);
       const int off = (int)(new_slot % BS);
       if (!new_is_v) {
-        store16(kcw + ((blk * a.Hkv + kvh) * kCh + new_cc) * BS * kX + (size_t)off * kX, new_val);
+        store16(kcw + ((blk * a.Hkv + kvh) * BS + off) * D + (size_t)new_cc * kSx, new_val);
       } else {
         T* dst = vcw + ((blk * a.Hkv + kvh) * D + (size_t)new_cc * kX) * BS + off;
         const T* e = reinterpret_cast<const T*>(&new_val);
@@ -548,10 +548,11 @@ paged_decode_kernel(const DecodeParams a, const OrderArg<PAIRED> ord) {
       const int tok =
           min(Sh::kTiles == 1 ? base + n : base + kTpl * (n >> 2) + 4 * t + (n & 3), tok1 - 1);
       const int phys = tblw[(tok - tok0) / BS];
-      const C* kp = kc + ((size_t)phys * a.Hkv + kvh) * head_elems + (size_t)j * BS * kX +
-                    (size_t)(tok % BS) * kX;
+      // token-major K: the row of token `tok` is D contiguous elements; lane j takes its
+      // 16-byte chunks j, j + 4, ...
+      const C* kp = kc + (((size_t)phys * a.Hkv + kvh) * BS + tok % BS) * D + (size_t)j * kX;
 #pragma unroll
-      for (int c = 0; c < kNc; ++c) b.k[t][c] = load16(kp + (size_t)4 * c * BS * kX);
+      for (int c = 0; c < kNc; ++c) b.k[t][c] = load16(kp + 4 * c * kX);
     }
     // V operand of slice sl: channel 16*sl + n, tokens base + kTpl*j .. + kTpl - 1.  A group
     // wholly past the end reads the group of the last live token (in bounds; it is zeroed
@@ -598,12 +599,11 @@ paged_decode_kernel(const DecodeParams a, const OrderArg<PAIRED> ord) {
           const int tok = base + kTpl * (n >> 2) + 4 * t + (n & 3);
           if (tok == lm1) {
             const int phys = tblw[(tok - tok0) / BS];
-            uint8_t* kp = kcw + ((size_t)phys * a.Hkv + kvh) * head_elems +
-                          (size_t)j * BS * kX + (size_t)(tok % BS) * kX;
+            uint8_t* kp = kcw + (((size_t)phys * a.Hkv + kvh) * BS + tok % BS) * D + j * kX;
 #pragma unroll
             for (int c = 0; c < kNc; ++c) {
               b.k[t][c] = *reinterpret_cast<const u32x4*>(nk + 16 * (j + 4 * c));
-              store16(kp + (size_t)4 * c * BS * kX, b.k[t][c]);
+              store16(kp + 4 * c * kX, b.k[t][c]);
             }
           }
         }
@@ -641,12 +641,11 @@ paged_decode_kernel(const DecodeParams a, const OrderArg<PAIRED> ord) {
         const int tok = kBf16 ? base + 8 * (n >> 2) + 4 * t + (n & 3) : base + n;
         if (tok == lm1) {
           const int phys = tblw[(tok - tok0) / BS];
-          T* kp = kcw + ((size_t)phys * a.Hkv + kvh) * head_elems + (size_t)j * BS * kX +
-                  (size_t)(tok % BS) * kX;
+          T* kp = kcw + (((size_t)phys * a.Hkv + kvh) * BS + tok % BS) * D + j * kX;
 #pragma unroll
           for (int c = 0; c < kNc; ++c) {
             b.k[t][c] = *reinterpret_cast<const u32x4*>(nk + kX * (4 * c + j));
-            store16(kp + (size_t)4 * c * BS * kX, b.k[t][c]);
+            store16(kp + 4 * c * kX, b.k[t][c]);
           }
         }
       }
@@ -1112,19 +1111,20 @@ WorkspaceLayout workspace_layout(int S, int Hq, int D, int pmax) {
   return w;
 }
 
-// Compute units of the current device (queried once per device).
+// Compute units of the current device (queried once per device; concurrent first calls
+// may both query, and store the same value).
 int device_cu_count() {
-  static int cache[64] = {0};
+  static std::atomic<int> cache[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cache[dev] == 0) {
-    int n = 0;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         n <= 0)
       n = 256;
-    cache[dev] = n;
+    cache[dev].store(n, std::memory_order_relaxed);
   }
-  return cache[dev];
+  return n;
 }
 
 using pa::kMaxPartition;

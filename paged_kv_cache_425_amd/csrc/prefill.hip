@@ -163,8 +163,9 @@ paged_prefill_kernel(const PrefillParams a) {
     return kBf16 ? ((key >> 2) & 1) * 16 + (key & 3) + 4 * ((key >> 3) & 3) : key;
   };
 
-  // chunk ids: K id = q * kStep + key (q = 16-byte chunk of the row), V id = channel *
-  // (kStep / kX) + group; consecutive threads read consecutive addresses within a block.
+  // chunk ids: K id = key * (D / kX) + q (q = 16-byte chunk of the key's row in the
+  // token-major K pool), V id = channel * (kStep / kX) + group; consecutive threads read
+  // consecutive addresses within a block.
   // A step is kStep keys starting at a multiple of kStep.  When BS divides kStep, each
   // chunk's block within the step and its offset inside the block are fixed per thread
   // and a step only adds its first block; when kStep divides BS (f32, BS 32) the step
@@ -176,9 +177,9 @@ paged_prefill_kernel(const PrefillParams a) {
 #pragma unroll
   for (int i = 0; i < kLoadsK; ++i) {
     const int cid = threadIdx.x + i * kThreads;
-    const int q = cid / kStep, kk = cid % kStep;
+    const int q = cid % (D / kX), kk = cid / (D / kX);
     k_blk[i] = kk / BS;
-    k_off[i] = (q * BS + kk % BS) * kX;
+    k_off[i] = (kk % BS) * D + q * kX;
   }
 #pragma unroll
   for (int i = 0; i < kLoadsV; ++i) {
@@ -200,7 +201,7 @@ paged_prefill_kernel(const PrefillParams a) {
       const int phys = tbl_lds[min(b0 + k_blk[i], last_blk) - tb0];
       const u32x4 z = {0u, 0u, 0u, 0u};
       kreg[i] = threadIdx.x + i * kThreads < Sh::kKChunks
-                    ? load16(kbase + (size_t)phys * blk_stride + k_off[i] + boff * kX) : z;
+                    ? load16(kbase + (size_t)phys * blk_stride + k_off[i] + boff * D) : z;
     }
 #pragma unroll
     for (int i = 0; i < kLoadsV; ++i) {
@@ -218,7 +219,7 @@ paged_prefill_kernel(const PrefillParams a) {
     for (int i = 0; i < kLoadsK; ++i) {
       const int cid = threadIdx.x + i * kThreads;
       if (cid < Sh::kKChunks) {
-        const int q = cid / kStep, key = cid % kStep;
+        const int q = cid % (D / kX), key = cid / (D / kX);
         *reinterpret_cast<u32x4*>(kb + (krow(key) * Sh::kKRow + q) * 16) = kreg[i];
       }
     }

@@ -35,10 +35,18 @@ def upload_inputs(w, dev) -> dict:
     }
 
 
+# bf16 outputs: the absolute bound holds where bf16 can meet it.  From |x| = 4 up, half a
+# bf16 ulp is 2^-6 = 0.0156 > 1e-2, so even the exact result rounded to bf16 (the output
+# format) can miss 1e-2 there; the relative bound governs those elements.
+BF16_ABS_LIMIT = 4.0
+
+
 def check_close(got: np.ndarray, ref: np.ndarray, dtype: str, what: str = "") -> dict:
-    """The parity bar: f32 max |err| <= 1e-5; bf16 max |err| <= 1e-2 and
-    |err| / |ref| <= 2e-2 wherever |ref| >= 1e-2 (below that floor the bf16
-    relative error is meaningless and the absolute bound governs)."""
+    """The parity bar: f32 max |err| <= 1e-5; bf16 max |err| <= 1e-2 wherever |ref| < 4,
+    and |err| / |ref| <= 2e-2 wherever |ref| >= 1e-2.  Below 1e-2 the relative error of
+    N(0,1) data near zero crossings is meaningless and the absolute bound governs; from 4
+    up the output format's own rounding (half an ulp, 0.0156 at 4) exceeds 1e-2 and the
+    relative bound governs."""
     assert got.shape == ref.shape, (got.shape, ref.shape)
     assert np.isfinite(got).all(), f"{what}: non-finite output"
     err = np.abs(got - ref)
@@ -46,9 +54,13 @@ def check_close(got: np.ndarray, ref: np.ndarray, dtype: str, what: str = "") ->
     if dtype == "f32":
         assert stats["max_abs"] <= 1e-5, f"{what}: max abs err {stats['max_abs']:.3e} > 1e-5"
     else:
-        big = np.abs(ref) >= 1e-2
-        rel = err[big] / np.abs(ref[big])
+        mag = np.abs(ref)
+        big = mag >= 1e-2
+        rel = err[big] / mag[big]
         stats["max_rel"] = float(rel.max()) if rel.size else 0.0
-        assert stats["max_abs"] <= 1e-2, f"{what}: max abs err {stats['max_abs']:.3e} > 1e-2"
+        small = err[mag < BF16_ABS_LIMIT]
+        stats["max_abs_below_4"] = float(small.max()) if small.size else 0.0
+        assert stats["max_abs_below_4"] <= 1e-2, \
+            f"{what}: max abs err {stats['max_abs_below_4']:.3e} > 1e-2 (|ref| < 4)"
         assert stats["max_rel"] <= 2e-2, f"{what}: max rel err {stats['max_rel']:.3e} > 2e-2"
     return stats

@@ -1,8 +1,9 @@
 """GPU parity: the HIP library (called through its C ABI) against the CPU oracle.
 
 * reshape_and_cache and the block gather: bit-exact;
-* paged attention: f32 max |err| <= 1e-5; bf16 max |err| <= 1e-2 and relative
-  error <= 2e-2 where |ref| >= 1e-2;
+* paged attention: f32 max |err| <= 1e-5; bf16 max |err| <= 1e-2 where |ref| < 4
+  (from 4 up half a bf16 ulp of the output exceeds 1e-2) and relative error <= 2e-2
+  where |ref| >= 1e-2;
 * the invariances the pages state hold bit for bit on the GPU (physical block
   permutation, shared blocks vs private copies, block size), and the result
   is deterministic.
@@ -20,7 +21,7 @@ import torch
 import oracle
 import paged_kv_cache_425_amd as pk
 from tests.gpu_util import bits, check_close, to_dev, to_f64, upload_inputs
-from tests.helpers import build_pools, oracle_out
+from tests.helpers import build_pools, oracle_out, prefill_reference
 from workloads import make_config, make_workload
 
 pytestmark = pytest.mark.gpu
@@ -521,8 +522,8 @@ def test_prefill_rising_scores_move_the_running_max():
 
 
 @pytest.mark.parametrize("name", ["prefix-cache-prefill", "chunked-prefill-llama3-8b"])
-def test_prefill_named_cases_on_sampled_sequences(name):
-    """Full-size batches; the oracle checks every row of a sample of sequences."""
+def test_prefill_named_cases_every_row(name):
+    """Full-size batches; the oracle checks every row of every sequence."""
     w, pb = make_prefill_config(name)
     hist = pb.history_records(w)
     kc_np, vc_np = oracle.empty_pools(w.num_blocks, w.num_kv_heads, w.head_dim, w.block_size,
@@ -543,11 +544,122 @@ def test_prefill_named_cases_on_sampled_sequences(name):
     torch.cuda.synchronize()
     oracle.reshape_and_cache(w.rec_key[rec], w.rec_value[rec], w.rec_slot[rec], kc_np, vc_np,
                              inplace=True)
-    sample = sorted(set(np.random.default_rng(76).choice(w.num_seqs, 6, replace=False).tolist()
-                        + [int(np.argmax(np.diff(pb.query_start_loc)))]))
-    ref = oracle.paged_prefill(pb.query, pb.query_start_loc, w.block_table, w.context_lens,
-                               kc_np, vc_np, w.scale, w.dtype, seqs=sample)
-    rows = np.concatenate([np.arange(pb.query_start_loc[s], pb.query_start_loc[s + 1])
-                           for s in sample])
-    stats = check_close(to_f64(out)[rows], ref[rows], w.dtype, name)
+    assert np.array_equal(bits(kc), kc_np.view(bits(kc).dtype))
+    assert np.array_equal(bits(vc), vc_np.view(bits(vc).dtype))
+    got = to_f64(out)
+    del kc, vc, out
+    ref = prefill_reference(w, pb, kc_np, vc_np)
+    stats = check_close(got, ref, w.dtype, name)
     say(f"  {name}: {stats}")
+
+
+# ---------------------------------------------------------------------------
+# every group size the host check admits (g <= 8 for bf16, <= 16 for f32)
+# ---------------------------------------------------------------------------
+GROUP_CASES = ([("bf16", g) for g in (2, 3, 5, 6, 7)] +
+               [("f32", g) for g in (2, 3, 5, 6, 7, 9, 11, 12, 13, 15, 16)])
+
+
+@pytest.mark.parametrize("D,BS", [(128, 16), (64, 8), (128, 32)])
+@pytest.mark.parametrize("dtype,g", GROUP_CASES, ids=[f"{d}-g{g}" for d, g in GROUP_CASES])
+def test_every_accepted_group_size(dtype, g, D, BS):
+    """The group sizes beyond 1, 4 and 8 run the same lane code with other row counts:
+    the hi/lo rows [g, 2g) of the bf16 MFMA, the head of each row (n % g), the fold of
+    the lo rows (a shuffle by g) and the merge's g rows.  Decode in the paired mode, with
+    the merge kernel and one partition per wave, and the fused step (caches bit-exact,
+    output equal to the two calls)."""
+    Hkv = 2
+    w = tiny(dtype, LENS, g * Hkv, Hkv, D, BS, seed=900 + 16 * g + D + BS,
+             scale=0.6 / np.sqrt(D) * 4)
+    kc, vc = build_pools(w)
+    ref = oracle_out(w, kc, vc)
+    for part in (0, 64, 768):
+        say(f"group {dtype} g={g} D={D} BS={BS} P={part}")
+        check_close(to_f64(run_gpu(w, kc, vc, part)), ref, dtype, f"g{g}/{dtype}/{D}/{BS}/{part}")
+    new, slots = fused_inputs(w)
+    hist_k, hist_v = build_pools(w, include_new=False)
+    ref_k, ref_v = oracle.reshape_and_cache(w.rec_key[new], w.rec_value[new], slots, hist_k, hist_v)
+    inp = upload_inputs(w, DEV)
+    key, val = to_dev(w.rec_key[new], w.dtype, DEV), to_dev(w.rec_value[new], w.dtype, DEV)
+    slot_t = torch.from_numpy(slots).to(DEV)
+    for part in (0, 64):
+        say(f"group fused step {dtype} g={g} D={D} BS={BS} P={part}")
+        kd, vd = to_dev(hist_k, w.dtype, DEV), to_dev(hist_v, w.dtype, DEV)
+        out = pk.decode_step(inp["query"], key, val, slot_t, inp["block_table"],
+                             inp["context_lens"], kd, vd, w.scale,
+                             max_context_len=w.max_context_len, partition_size=part)
+        kd2, vd2 = to_dev(hist_k, w.dtype, DEV), to_dev(hist_v, w.dtype, DEV)
+        pk.reshape_and_cache(key, val, slot_t, kd2, vd2)
+        out2 = pk.paged_attention(inp["query"], inp["block_table"], inp["context_lens"], kd2,
+                                  vd2, w.scale, max_context_len=w.max_context_len,
+                                  partition_size=part)
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(kd), ref_k.view(bits(kd).dtype))
+        assert np.array_equal(bits(vd), ref_v.view(bits(vd).dtype))
+        assert np.array_equal(bits(out), bits(out2))
+        check_close(to_f64(out), ref, dtype, f"fused g{g}/{dtype}/{D}/{BS}/{part}")
+
+
+def test_group_sizes_past_the_limit_are_refused():
+    """g = 9 in bf16 and g = 17 in f32 are not built: refused before any launch."""
+    for dtype, g in (("bf16", 9), ("f32", 17)):
+        w = tiny(dtype, (5, 9), g, 1, 64, 16, seed=950)
+        kc, vc = build_pools(w)
+        with pytest.raises(NotImplementedError):
+            run_gpu(w, kc, vc)
+
+
+def test_prefill_group_sizes_two_and_sixteen():
+    """The prefill's other admitted group sizes (its tile of 128 rows takes g in
+    {1, 2, 4, 8, 16}); g = 3 is refused."""
+    for dtype, g, D, BS in (("bf16", 2, 128, 16), ("bf16", 16, 64, 8), ("f32", 2, 64, 32),
+                            ("f32", 16, 128, 16), ("bf16", 2, 64, 32), ("bf16", 16, 128, 32)):
+        Hkv = 2
+        w = tiny(dtype, PREFILL_LENS, g * Hkv, Hkv, D, BS, seed=960 + g + D + BS,
+                 scale=0.6 / np.sqrt(D) * 4)
+        chunks = [1, 5, 17, 33, 64, 40, 200, 129]
+        pb = make_prefill(w, chunks, 960 + g)
+        kc, vc = build_pools(w)
+        say(f"prefill group {dtype} g={g} D={D} BS={BS}")
+        got = run_prefill(w, pb, kc, vc)
+        ref = oracle.paged_prefill(pb.query, pb.query_start_loc, w.block_table, w.context_lens,
+                                   kc, vc, w.scale, dtype)
+        check_close(to_f64(got), ref, dtype, f"prefill g{g}/{dtype}/{D}/{BS}")
+    w = tiny("bf16", (5, 9), 6, 2, 64, 16, seed=969)
+    pb = make_prefill(w, [5, 9], 969)
+    kc, vc = build_pools(w)
+    with pytest.raises(NotImplementedError):
+        run_prefill(w, pb, kc, vc)
+
+
+# ---------------------------------------------------------------------------
+# a caller's side stream: memory the binding allocates is not reused too early
+# ---------------------------------------------------------------------------
+def test_side_stream_with_binding_allocated_workspace_and_output():
+    """The binding allocates out and the partition workspace on torch's current stream
+    while the kernels run on the caller's stream.  Right after the call the test
+    allocates and fills other tensors on the current stream: had the binding not marked
+    its tensors as used on the side stream, the caching allocator could hand their memory
+    to those tensors while the decode still writes and reads it."""
+    w = tiny("bf16", long_tail_lens(71), 32, 8, 128, 16, seed=71)
+    kc_np, vc_np = build_pools(w)
+    ref = oracle_out(w, kc_np, vc_np)
+    inp = upload_inputs(w, DEV)
+    kc, vc = to_dev(kc_np, w.dtype, DEV), to_dev(vc_np, w.dtype, DEV)
+    side = torch.cuda.Stream(DEV)
+    side.wait_stream(torch.cuda.current_stream(DEV))
+    say("side stream: decode with binding-allocated out and workspace")
+    outs = []
+    for rep in range(3):
+        out = pk.paged_attention(inp["query"], inp["block_table"], inp["context_lens"], kc, vc,
+                                 w.scale, max_context_len=w.max_context_len, partition_size=64,
+                                 stream=side)
+        outs.append(out)
+        # freed workspace and other allocations on the current stream, filled at once
+        junk = [torch.full((1 << 20,), float("nan"), dtype=torch.float32, device=DEV)
+                for _ in range(16)]
+        del junk
+    side.synchronize()
+    torch.cuda.synchronize()
+    for out in outs:
+        check_close(to_f64(out), ref, "bf16", "side-stream")

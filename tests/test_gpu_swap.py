@@ -35,8 +35,7 @@ def say(msg: str) -> None:
 
 
 def shapes(nb, Hkv, D, BS, dtype):
-    X = 16 // np.dtype(NP[dtype]).itemsize
-    return (nb, Hkv, D // X, BS, X), (nb, Hkv, D, BS)
+    return (nb, Hkv, BS, D), (nb, Hkv, D, BS)
 
 
 def random_pools(rng, nb, Hkv, D, BS, dtype):
@@ -181,8 +180,8 @@ def test_preempt_and_resume_keeps_the_decode_result(dtype):
 
 def test_pageable_host_memory_is_refused_before_launch():
     lib = pk.load_library()
-    pageable = np.zeros((4, 2, 8, 16, 8), dtype=np.uint16)      # not pinned, not mapped
-    dk = torch.zeros((4, 2, 8, 16, 8), dtype=torch.bfloat16, device=DEV)
+    pageable = np.zeros((4, 2, 16, 64), dtype=np.uint16)      # not pinned, not mapped
+    dk = torch.zeros((4, 2, 16, 64), dtype=torch.bfloat16, device=DEV)
     dv = torch.zeros((4, 2, 64, 16), dtype=torch.bfloat16, device=DEV)
     mapping = torch.tensor([[0, 1]], dtype=torch.int64, device=DEV)
     say("swap with pageable host memory: refused")
@@ -191,10 +190,10 @@ def test_pageable_host_memory_is_refused_before_launch():
                             4, 1, None)
     assert st == 1
     with pytest.raises(ValueError):
-        pk.swap_blocks(torch.zeros((4, 2, 8, 16, 8), dtype=torch.bfloat16), dv.new_zeros(
+        pk.swap_blocks(torch.zeros((4, 2, 16, 64), dtype=torch.bfloat16), dv.new_zeros(
             (4, 2, 64, 16)).cpu(), dk, dv, mapping)
     # the refused call leaves no error behind: the next call goes through
-    hk = torch.zeros((4, 2, 8, 16, 8), dtype=torch.bfloat16, pin_memory=True)
+    hk = torch.zeros((4, 2, 16, 64), dtype=torch.bfloat16, pin_memory=True)
     hv = torch.zeros((4, 2, 64, 16), dtype=torch.bfloat16, pin_memory=True)
     dk.fill_(1.5)
     pk.swap_blocks(dk, dv, hk, hv, mapping)

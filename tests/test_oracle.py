@@ -125,7 +125,7 @@ def test_golden_append_then_attention():
     changed_k = ~((kc2 == kc) | (np.isnan(kc2) & np.isnan(kc)))
     changed_v = ~((vc2 == vc) | (np.isnan(vc2) & np.isnan(vc)))
     # slot 1 = physical block 0, offset 1: only those elements changed
-    assert changed_k.sum() == 8 and changed_k[0, :, :, 1, :].all()
+    assert changed_k.sum() == 8 and changed_k[0, :, 1, :].all()
     assert changed_v.sum() == 8 and changed_v[0, :, :, 1].all()
     out = oracle.paged_attention(arr(g["query"]), np.array(g["block_table"]),
                                  np.array(a["context_lens_after"]), kc2, vc2, g["scale"], "f32")
@@ -143,7 +143,6 @@ def test_golden_append_then_attention():
 def test_gather_matches_flat_index_loop_and_never_paged_records(dtype, BS, D):
     w = tiny(dtype=dtype, BS=BS, D=D, lens=(1, 9, 33))
     kc, vc = build_pools(w)
-    X = 16 // oracle.ELEMENT_BYTES[dtype]
     kflat, vflat = kc.reshape(-1), vc.reshape(-1)
     Hkv = w.num_kv_heads
     for s in range(w.num_seqs):
@@ -157,7 +156,7 @@ def test_gather_matches_flat_index_loop_and_never_paged_records(dtype, BS, D):
             o = t % BS
             for h in range(Hkv):
                 for d in range(D):
-                    ko = (((b * Hkv + h) * (D // X) + d // X) * BS + o) * X + d % X
+                    ko = ((b * Hkv + h) * BS + o) * D + d
                     vo = ((b * Hkv + h) * D + d) * BS + o
                     assert k[t, h, d] == kflat[ko]
                     assert v[t, h, d] == vflat[vo]
@@ -174,9 +173,9 @@ def test_scatter_touches_only_its_slots_and_skips_negative():
     for i, slot in enumerate(slots):
         blk, off = divmod(int(w.rec_slot[new][i]), BS)
         if slot < 0:
-            assert np.array_equal(kc2[blk, :, :, off, :], kc[blk, :, :, off, :])
+            assert np.array_equal(kc2[blk, :, off, :], kc[blk, :, off, :])
             continue
-        kc2[blk, :, :, off, :] = kc[blk, :, :, off, :]
+        kc2[blk, :, off, :] = kc[blk, :, off, :]
         vc2[blk, :, :, off] = vc[blk, :, :, off]
     assert np.array_equal(kc2, kc) and np.array_equal(vc2, vc)  # nothing else changed
 
@@ -446,8 +445,7 @@ def test_copy_blocks_reproduces_the_copy_on_write_records():
 def test_swap_blocks_matches_element_loop(dtype):
     rng = np.random.default_rng(90)
     Hkv, D, BS = 2, 32, 8
-    shape_k = lambda nb: (nb, Hkv, D // (16 // {"f32": 4, "bf16": 2, "fp8": 1}[dtype]), BS,
-                          16 // {"f32": 4, "bf16": 2, "fp8": 1}[dtype])
+    shape_k = lambda nb: (nb, Hkv, BS, D)
     np_t = {"f32": np.float32, "bf16": np.uint16, "fp8": np.uint8}[dtype]
 
     def pool(nb):
@@ -540,7 +538,9 @@ def test_prefill_of_one_token_is_the_decode():
     a = oracle.paged_prefill(pb.query, pb.query_start_loc, w.block_table, w.context_lens, kc, vc,
                              w.scale, w.dtype)
     b = oracle.paged_attention(pb.query, w.block_table, w.context_lens, kc, vc, w.scale, w.dtype)
-    assert np.array_equal(a, b)
+    # the two take their products in other orders (a masked matrix product against one
+    # query row at a time), so they agree to float64 rounding, not bit for bit
+    np.testing.assert_allclose(a, b, rtol=0, atol=1e-13)
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
@@ -571,7 +571,7 @@ def test_prefill_matches_causal_bruteforce(dtype):
                 np.testing.assert_allclose(got[r0 + i, h], ref, rtol=1e-12, atol=1e-13)
 
 
-def test_prefill_chunk_split_in_two_calls_is_identical():
+def test_prefill_chunk_split_in_two_calls_agrees():
     """A chunk of n tokens equals its first half (context shortened to end there) followed
     by its second half: each token only sees positions up to its own."""
     w = tiny("bf16", lens=(40, 64, 25), Hq=8, Hkv=2, D=32, BS=16, seed=62)
@@ -591,7 +591,9 @@ def test_prefill_chunk_split_in_two_calls_is_identical():
                                   kc, vc, w.scale, w.dtype)
     part_b = oracle.paged_prefill(pb.query[rows_b], qb, w.block_table, w.context_lens, kc, vc,
                                   w.scale, w.dtype)
-    assert np.array_equal(whole[rows_a], part_a) and np.array_equal(whole[rows_b], part_b)
+    # the calls sum over key ranges of other lengths, so they agree to float64 rounding
+    np.testing.assert_allclose(whole[rows_a], part_a, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(whole[rows_b], part_b, rtol=0, atol=1e-13)
 
 
 def test_prefill_is_block_permutation_invariant():

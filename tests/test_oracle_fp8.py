@@ -134,11 +134,8 @@ def test_fp8_attention_equals_bf16_attention_on_the_decoded_values():
     kc, vc = _fp8_pools(w, 1.0, 1.0)
     from workloads.configs import f32_to_bf16_bits
     vb = f32_to_bf16_bits(oracle.e4m3_decode(vc).astype(np.float32))
-    # regroup K into the bf16 layout: 16-byte chunks of 8 elements
-    kd = oracle.e4m3_decode(kc)                                   # [NB, H, D/16, BS, 16]
-    kd = kd.transpose(0, 1, 3, 2, 4).reshape(kc.shape[0], kc.shape[1], kc.shape[3], -1)
-    kb = f32_to_bf16_bits(kd.astype(np.float32))                 # [NB, H, BS, D]
-    kb = kb.reshape(kc.shape[0], kc.shape[1], kc.shape[3], -1, 8).transpose(0, 1, 3, 2, 4)
+    # both pools have the token-major K layout [NB, H, BS, D]
+    kb = f32_to_bf16_bits(oracle.e4m3_decode(kc).astype(np.float32))
     got = oracle.paged_attention_fp8(w.query, w.block_table, w.context_lens, kc, vc, w.scale,
                                      1.0, 1.0, "bf16")
     ref = oracle.paged_attention(w.query, w.block_table, w.context_lens,
@@ -199,3 +196,13 @@ def test_nan_codes_poison_only_their_reader(bad):
     assert np.isnan(out[s, :g, 5]).all()
     assert not np.isnan(out[s, g:]).any()
     assert not np.isnan(out[:s]).any()
+
+
+@pytest.mark.parametrize("scale", [0.0135, 1.0, 3.7e-3, 250.0])
+def test_quantize_bf16_table_equals_quantize(scale):
+    """The table form gives the codes quantize() gives, element for element: random bf16
+    patterns of every magnitude, both NaNs, both infinities, zeros and subnormals."""
+    rng = np.random.default_rng(77)
+    x = rng.integers(0, 1 << 16, size=300_000).astype(np.uint16)
+    x[:8] = [0x0000, 0x8000, 0x7F80, 0xFF80, 0x7FC0, 0xFFC0, 0x0001, 0x8001]
+    assert np.array_equal(oracle.quantize_bf16(x, scale), oracle.quantize(x, "bf16", scale))
