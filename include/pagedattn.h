@@ -202,6 +202,35 @@ pa_status pa_decode_step(void* out, const void* query, const void* key, const vo
                          const int32_t* host_context_lens);
 
 /*
+ * pa_decode_step for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * It takes no workspace: when the call needs one (sequences split into
+ * partitions) it uses a fixed scratch array inside the library,
+ * PA_NOALLOC_SCRATCH_BYTES on each GPU, held from the first call on that GPU
+ * until the process ends.  The call itself allocates nothing.
+ *   - Arguments, result, caches and preconditions as pa_decode_step (same
+ *     kernels; out and the caches are the same bit for bit).
+ *   - A call needing more than PA_NOALLOC_SCRATCH_BYTES
+ *     (pa_paged_attention_workspace_size) returns PA_ERR_WORKSPACE and
+ *     launches nothing; pass a larger partition_size or use pa_decode_step.
+ *   - Every call on one GPU shares that GPU's scratch, and the array keeps
+ *     what the last call left (nothing in it needs to start at zero: each
+ *     call writes every partial result it reads).  Calls that overlap on one
+ *     GPU (other streams, other host threads) race on it and give wrong
+ *     results: order them, e.g. on one stream.
+ *   - PA_ERR_HIP if the scratch array's address cannot be obtained.
+ */
+#define PA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+pa_status pa_decode_step_noalloc(void* out, const void* query, const void* key,
+                                 const void* value, const int64_t* slot_mapping,
+                                 const int32_t* block_table, const int32_t* context_lens,
+                                 void* k_cache, void* v_cache, int num_seqs, int num_heads,
+                                 int num_kv_heads, int head_dim, int block_size,
+                                 int max_blocks_per_seq, int num_blocks, int max_context_len,
+                                 float scale, pa_dtype dtype, int partition_size, void* stream,
+                                 const int32_t* host_context_lens);
+
+/*
  * Paged prefill: causal attention of a chunk of new query tokens per sequence
  * over the sequence's paged K/V (the chunk's own K/V already stored, e.g. by
  * pa_reshape_and_cache).  A request's earlier context -- a system prompt kept

@@ -59,6 +59,8 @@ def load_library() -> ctypes.CDLL:
     lib.pa_decode_step_fp8.restype = i32
     lib.pa_decode_step_fp8.argtypes = [vp] * 9 + [i32] * 8 + [f32] * 3 + [i32, i32, vp, sz, vp,
                                                                           vp]
+    lib.pa_decode_step_noalloc.restype = i32
+    lib.pa_decode_step_noalloc.argtypes = [vp] * 9 + [i32] * 8 + [f32, i32, i32, vp, vp]
     lib.pa_paged_attention_fp8.restype = i32
     lib.pa_paged_attention_fp8.argtypes = [vp] * 6 + [i32] * 8 + [f32] * 3 + [i32, i32, vp, sz,
                                                                               vp, vp]
@@ -213,7 +215,7 @@ def paged_attention(query: torch.Tensor, block_table: torch.Tensor, context_lens
 
 def _decode_step_args(query, key, value, slot_mapping, block_table, context_lens, k_cache,
                       v_cache, scale, max_context_len, out, partition_size, workspace, stream,
-                      host_context_lens=None):
+                      host_context_lens=None, need_workspace=True):
     """Checked argument tuple of pa_decode_step (allocates out/workspace when None)."""
     dev = query.device
     _require(query, "query", dev)
@@ -238,7 +240,8 @@ def _decode_step_args(query, key, value, slot_mapping, block_table, context_lens
     _require(out, "out", dev, query.dtype)
     if tuple(out.shape) != tuple(query.shape):
         raise ValueError("out must have the shape of query")
-    need = workspace_size(S, Hq, Hkv, D, max_context_len, partition_size, query.dtype)
+    need = workspace_size(S, Hq, Hkv, D, max_context_len, partition_size, query.dtype) \
+        if need_workspace else 0
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
         made.append(workspace)
@@ -270,6 +273,28 @@ def decode_step(query: torch.Tensor, key: torch.Tensor, value: torch.Tensor,
                                            stream, host_context_lens)
     _check(lib.pa_decode_step(*args), "pa_decode_step")
     _record(stream, made)
+    return out
+
+
+def decode_step_noalloc(query: torch.Tensor, key: torch.Tensor, value: torch.Tensor,
+                        slot_mapping: torch.Tensor, block_table: torch.Tensor,
+                        context_lens: torch.Tensor, k_cache: torch.Tensor,
+                        v_cache: torch.Tensor, scale: float, *, max_context_len: int,
+                        out: torch.Tensor, partition_size: int = 0, stream=None,
+                        host_context_lens=None) -> torch.Tensor:
+    """decode_step without a workspace and without allocating: the library's fixed
+    per-GPU scratch holds the partitions' partial results (pa_decode_step_noalloc).
+    `out` must be given; calls that overlap on one GPU race on the scratch."""
+    if out is None:
+        raise ValueError("decode_step_noalloc allocates nothing: pass out")
+    lib = load_library()
+    args, out, _, made = _decode_step_args(query, key, value, slot_mapping, block_table,
+                                           context_lens, k_cache, v_cache, scale,
+                                           max_context_len, out, partition_size, None, stream,
+                                           host_context_lens, need_workspace=False)
+    assert not made
+    # pa_decode_step_noalloc takes pa_decode_step's arguments minus workspace and its size
+    _check(lib.pa_decode_step_noalloc(*(args[:20] + args[22:])), "pa_decode_step_noalloc")
     return out
 
 

@@ -1285,6 +1285,65 @@ extern "C" pa_status pa_decode_step(void* out, const void* query, const void* ke
                     dtype, partition_size, workspace, workspace_bytes, stream, host_context_lens);
 }
 
+// ---------------------------------------------------------------------------
+// the decode step without a caller's workspace
+// ---------------------------------------------------------------------------
+// Partition workspace of pa_decode_step_noalloc: one array per GPU, in the library's
+// code object.  In host code `scratch` names a host-side stand-in, never the device
+// memory: kernels and copies get its device address from scratch_address().
+static __device__ __align__(256) unsigned char scratch[PA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+// Device address of `scratch` on the current GPU, looked up once per GPU (with that GPU
+// current) and kept; concurrent first calls look it up twice and keep the same address.
+// nullptr when the lookup fails.
+void* scratch_address() {
+  static std::atomic<void*> addr[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  void* p = addr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+      return nullptr;
+    addr[dev].store(p, std::memory_order_release);
+  }
+  return p;
+}
+
+}  // namespace
+
+extern "C" pa_status pa_decode_step_noalloc(void* out, const void* query, const void* key,
+                                            const void* value, const int64_t* slot_mapping,
+                                            const int32_t* block_table,
+                                            const int32_t* context_lens, void* k_cache,
+                                            void* v_cache, int num_seqs, int num_heads,
+                                            int num_kv_heads, int head_dim, int block_size,
+                                            int max_blocks_per_seq, int num_blocks,
+                                            int max_context_len, float scale, pa_dtype dtype,
+                                            int partition_size, void* stream,
+                                            const int32_t* host_context_lens) {
+  if (num_seqs > 0 && (!key || !value || !slot_mapping)) return PA_ERR_INVALID_ARG;
+  // the workspace this call needs (0 when no sequence is split, or for arguments that the
+  // checks in run_decode reject)
+  const size_t need = num_seqs > 0
+                          ? pa_paged_attention_workspace_size(num_seqs, num_heads, num_kv_heads,
+                                                              head_dim, max_context_len,
+                                                              partition_size, dtype)
+                          : 0;
+  if (need > PA_NOALLOC_SCRATCH_BYTES) return PA_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if (need > 0) {
+    ws = scratch_address();
+    if (ws == nullptr) return PA_ERR_HIP;
+  }
+  return run_decode(out, query, block_table, context_lens, k_cache, v_cache, key, value,
+                    num_seqs > 0 ? slot_mapping : nullptr, num_seqs, num_heads, num_kv_heads,
+                    head_dim, block_size, max_blocks_per_seq, num_blocks, max_context_len, scale,
+                    dtype, partition_size, ws, need > 0 ? PA_NOALLOC_SCRATCH_BYTES : 0, stream,
+                    host_context_lens);
+}
+
 extern "C" pa_status pa_paged_attention_fp8(void* out, const void* query,
                                             const int32_t* block_table,
                                             const int32_t* context_lens, const void* k_cache,

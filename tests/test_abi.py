@@ -34,7 +34,7 @@ def test_header_declares_the_boundary():
         "pa_paged_attention_workspace_size", "pa_paged_attention", "pa_reshape_and_cache",
         "pa_gather_kv", "pa_decode_step", "pa_copy_blocks", "pa_paged_prefill",
         "pa_reshape_and_cache_fp8", "pa_paged_attention_fp8", "pa_decode_step_fp8",
-        "pa_swap_blocks"])
+        "pa_swap_blocks", "pa_decode_step_noalloc"])
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -133,6 +133,28 @@ def test_decode_step_rejects_before_launch(lib):
     assert call({16: 129}) == 1                 # max_context_len past the table
     assert call({9: 0, 2: None, 3: None, 4: None}) == 0   # empty batch
     assert call({16: 128, 19: 64}) == 3         # two partitions, no workspace
+
+
+def test_decode_step_noalloc_rejects_before_launch(lib):
+    """The allocation-free step takes the arguments of pa_decode_step minus the workspace;
+    a call whose partitions need more than the fixed scratch is refused."""
+    f = lib.pa_decode_step_noalloc
+    base = [FAKE] * 9 + [4, 32, 8, 128, 16, 8, 64, 128, 0.1, 1, 0, None, None]
+
+    def call(over):
+        a = list(base)
+        for k, v in over.items():
+            a[k] = v
+        return f(*a)
+    assert call({2: None}) == 1                 # key missing
+    assert call({12: 96}) == 2                  # head size
+    assert call({16: 129}) == 1                 # max_context_len past the table
+    assert call({9: 0, 2: None, 3: None, 4: None}) == 0   # empty batch
+    # 4096 sequences x 64 heads in 64-token partitions of 32768 tokens: 4.4 GB of partials
+    big = {9: 4096, 10: 64, 14: 2048, 16: 32768, 19: 64}
+    need = lib.pa_paged_attention_workspace_size(4096, 64, 8, 128, 32768, 64, 1)
+    assert need > 64 << 20
+    assert call(big) == 3
 
 
 def test_reshape_and_cache_rejects_before_launch(lib):
