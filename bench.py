@@ -51,11 +51,14 @@ def parse_args():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--op", default="step",
-                    choices=["step", "copy_blocks", "prefill", "fp8", "swap"],
+                    choices=["step", "copy_blocks", "prefill", "fp8", "swap", "ceiling"],
                     help="step: the decode step (default); copy_blocks: the copy-on-write "
                          "copies of the parallel-sampling workload; prefill: paged prefill; "
                          "fp8: the decode step over FP8 (E4M3) K/V pools; swap: swapping a "
-                         "quarter of the sequences' blocks out to pinned host memory and back")
+                         "quarter of the sequences' blocks out to pinned host memory and back; "
+                         "ceiling: the read-bandwidth probe over the workload's KV bytes, "
+                         "streaming and as a gather of scattered 4 KB tiles, every launch "
+                         "shape of the sweep")
     ap.add_argument("--prefill-case", default="prefix-cache-prefill",
                     choices=["prefix-cache-prefill", "chunked-prefill-llama3-8b"])
     ap.add_argument("--config", type=int, default=1, choices=[0, 1, 2, 3, 4])
@@ -71,6 +74,8 @@ def parse_args():
                          "from a host copy of the lengths (host_context_lens), or ranked "
                          "inside every workgroup; the other order is timed beside it")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ceiling", action="store_true",
+                    help="skip the read-probe sweep beside the step (e.g. under a profiler)")
     ap.add_argument("--warm", action="store_true",
                     help="also time K steps over one pool copy (Infinity Cache warm)")
     ap.add_argument("--cpu-budget", type=float, default=10.0,
@@ -106,6 +111,100 @@ def unique_kv_bytes(w) -> int:
         pos = np.arange(L)
         slots.update((blocks[pos // w.block_size] * w.block_size + pos % w.block_size).tolist())
     return len(slots) * 2 * w.num_kv_heads * w.head_dim * elt
+
+
+# ---------------------------------------------------------------------------
+# the read ceiling: pa_read_probe over the same number of bytes as the step's KV
+# ---------------------------------------------------------------------------
+CEILING_SHAPES = [(wg, u) for wg in (256, 512, 1024, 2048) for u in (4, 8, 16)]
+
+
+def measure_ceiling(kv_bytes: int, steps: int, warmup: int, replicas: int = 4,
+                    piece_bytes: int = 4096, shapes=CEILING_SHAPES, seed: int = 0) -> dict:
+    """Best rate of the read probe over kv_bytes (rounded down to whole pieces), rotating
+    over `replicas` windows of a buffer so that the Infinity Cache cannot serve repeats,
+    as a streaming read (pieces in order) and as a gather of randomly placed pieces (the
+    paged pattern), for every launch shape in `shapes`.  Rates in GB/s from HIP events."""
+    import torch
+
+    import paged_kv_cache_425_amd as pk
+    dev = torch.device("cuda:0")
+    n = max(1, kv_bytes // piece_bytes)
+    window = n * piece_bytes
+    buf = torch.empty(replicas * window, dtype=torch.uint8, device=dev)
+    buf.random_(0, 256)
+    rng = np.random.default_rng(seed)
+    offs = {"stream": [], "gather": []}
+    for r in range(replicas):
+        base = r * window
+        offs["stream"].append(torch.from_numpy(base + np.arange(n, dtype=np.int64) * piece_bytes)
+                              .to(dev))
+        offs["gather"].append(torch.from_numpy(base + rng.permutation(n).astype(np.int64) *
+                                               piece_bytes).to(dev))
+    for lst in offs.values():                        # every piece inside the buffer
+        assert all(int(o.max()) + piece_bytes <= buf.numel() for o in lst)
+    sink = torch.empty(max(wg for wg, _ in shapes) * 256, dtype=torch.int32, device=dev)
+    table = []
+    best = {}
+    for pattern in ("stream", "gather"):
+        for wg, u in shapes:
+            def run(k):
+                for i in range(k):
+                    pk.read_probe(buf, offs[pattern][i % replicas], piece_bytes, wg, u, sink)
+            run(warmup)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record()
+            run(steps)
+            e1.record()
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / steps
+            gbs = window / (us * 1e-6) / 1e9
+            table.append({"pattern": pattern, "workgroups": wg, "in_flight": u,
+                          "us": round(us, 2), "GB/s": round(gbs, 1)})
+            if gbs > best.get(pattern, {}).get("GB/s", 0):
+                best[pattern] = {"GB/s": round(gbs, 1), "us": round(us, 2), "workgroups": wg,
+                                 "in_flight": u}
+    del buf
+    return {"bytes": window, "piece_bytes": piece_bytes, "replicas": replicas,
+            "stream": best["stream"], "gather": best["gather"], "sweep": table}
+
+
+def bench_ceiling(args) -> int:
+    """The read probe's sweep over the workload's KV bytes (one JSON line)."""
+    from workloads import make_config
+    w = make_config(args.config, seed=args.seed, block_size=args.block_size, variant=args.variant)
+    kv = algorithmic_bytes(w)["kv"]
+    log(f"read ceiling over {kv / 1e6:.1f} MB ({w.name})")
+    c = measure_ceiling(kv, args.steps, args.warmup, replicas=max(1, args.replicas))
+    line = {"metric": "read-probe GB/s over the decode step's KV bytes", "value": c["gather"]["GB/s"],
+            "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "higher_is_better": True, "dtype": "u8", "data": "synthetic (random bytes)",
+            "config": {"workload": w.name, "bytes_per_launch": c["bytes"],
+                       "piece_bytes": c["piece_bytes"], "replicas": c["replicas"]},
+            "stream": c["stream"], "gather": c["gather"],
+            "hbm_frac_stream": round(c["stream"]["GB/s"] / HBM_PEAK_GBS, 4),
+            "hbm_frac_gather": round(c["gather"]["GB/s"] / HBM_PEAK_GBS, 4),
+            "sweep": c["sweep"]}
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+def pool_utilisation(w) -> dict:
+    """Share of the KV memory holding live tokens: paged (the blocks the batch holds; only
+    the tail of each sequence's last block is empty) and, for contrast, one contiguous
+    region per sequence sized for the batch's longest context."""
+    lens = w.context_lens.astype(np.int64)
+    used = set()
+    for s in range(w.num_seqs):
+        used.update(w.block_table[s, :-(-int(lens[s]) // w.block_size)].tolist())
+    stored = unique_kv_bytes(w) // (2 * w.num_kv_heads * w.head_dim *
+                                    (2 if w.dtype == "bf16" else 4))
+    return {"paged": round(stored / (len(used) * w.block_size), 4),
+            "contiguous_at_max_len": round(int(lens.sum()) / (w.num_seqs * int(lens.max())), 4),
+            "blocks_held": len(used), "tokens_stored": int(stored),
+            "pages_claim": ("20-30% before paging, above 95% with it, on A100 ('architecture & "
+                            "core features' section 3.1; 'core inference engine' section 2.2)")}
 
 
 def cpu_model() -> str:
@@ -668,6 +767,8 @@ def main() -> int:
         return bench_fp8(args)
     if args.op == "swap":
         return bench_swap(args)
+    if args.op == "ceiling":
+        return bench_ceiling(args)
     dev = torch.device("cuda:0")
 
     t = time.perf_counter()
@@ -726,6 +827,7 @@ def main() -> int:
                                           else None)
                for kc, vc in pools]
     nb = algorithmic_bytes(w)
+    kv_unique = unique_kv_bytes(w)
     elt = 2 if w.dtype == "bf16" else 4
     new_bytes = 2 * w.num_seqs * w.num_kv_heads * w.head_dim * elt     # new K and V
     fused_bytes = nb["total"] + 2 * new_bytes + 8 * w.num_seqs          # read, written, slots
@@ -780,15 +882,23 @@ def main() -> int:
         wall_w, ev_w = timed(run_fused, 1, K)
         log(f"warm fused step: {wall_w / K * 1e6:.1f} us/step wall")
         warm = {"us_per_step": round(wall_w / K * 1e6, 2),
-                "value": round(nb["kv"] / (wall_w / K) / 1e9, 2),
+                "value": round(kv_unique / (wall_w / K) / 1e9, 2),
                 "launch_us_events": round(ev_w / K * 1e6, 2)}
 
     ms_step = wall / K * 1e3
-    value = nb["kv"] / (ms_step * 1e-3) / 1e9
     launch_avg_s = ev_s / K
-    kv_unique = unique_kv_bytes(w)
-    achieved = fused_bytes / launch_avg_s / 1e9
+    # HBM must deliver each distinct slot at least once: with shared blocks (a common prefix,
+    # parallel samples) the unique bytes are the HBM figure and the logical bytes (every
+    # sequence's own view) an effective rate served partly from the caches
+    value = kv_unique / (ms_step * 1e-3) / 1e9
+    value_logical = nb["kv"] / (ms_step * 1e-3) / 1e9
+    fused_unique = fused_bytes - nb["kv"] + kv_unique
+    achieved = fused_unique / launch_avg_s / 1e9
     traffic = load_traffic(w.name)
+    ceil = None
+    if not args.no_ceiling:
+        log("read ceiling (probe sweep) ...")
+        ceil = measure_ceiling(nb["kv"], max(20, min(K, 100)), 5, replicas=R)
     kernels = "paged_decode_kernel" + (" + reduce_partitions_kernel" if needs_reduce else "")
     line = {
         "metric": METRIC,
@@ -800,7 +910,8 @@ def main() -> int:
         "ms_per_step": round(ms_step, 5),
         "us_per_step": round(ms_step * 1e3, 2),
         "hbm_frac": round(value / HBM_PEAK_GBS, 4),
-        "hbm_frac_unique_kv": round(kv_unique / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "effective_logical_kv": {"value": round(value_logical, 2), "unit": "GB/s",
+                                 "kv_bytes": nb["kv"]},
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -822,16 +933,24 @@ def main() -> int:
         "launch_us_events": round(launch_avg_s * 1e6, 2),
         "two_call_step": {"us_per_step": round(wall2 / K * 1e6, 2),
                           "us_per_step_events": round(ev2 / K * 1e6, 2),
-                          "value": round(nb["kv"] / (wall2 / K) / 1e9, 2)},
+                          "value": round(kv_unique / (wall2 / K) / 1e9, 2)},
         f"{other_order}_order_step": {"us_per_step": round(wall3 / K * 1e6, 2),
                                       "launch_us_events": round(ev3 / K * 1e6, 2),
-                                      "value": round(nb["kv"] / (wall3 / K) / 1e9, 2)},
+                                      "value": round(kv_unique / (wall3 / K) / 1e9, 2)},
         "warm": warm,
         "roofline": {"kernel": f"pa_decode_step: {kernels}",
                      "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic,
-                     "algorithmic_bytes_per_launch": fused_bytes},
+                     "algorithmic_bytes_per_launch": fused_unique},
+        "ceiling": None if ceil is None else {
+            "stream_GBs": ceil["stream"]["GB/s"], "gather_4k_GBs": ceil["gather"]["GB/s"],
+            "probe": "pa_read_probe over the step's KV bytes, best of "
+                     f"{len(CEILING_SHAPES)} launch shapes, {R} rotating windows",
+            "stream_shape": ceil["stream"], "gather_shape": ceil["gather"],
+            "frac_of_stream": round(achieved / ceil["stream"]["GB/s"], 4),
+            "frac_of_gather": round(achieved / ceil["gather"]["GB/s"], 4)},
+        "pool_utilisation": pool_utilisation(w),
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

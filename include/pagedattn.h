@@ -393,6 +393,31 @@ pa_status pa_gather_kv(void* k_out, void* v_out, const int64_t* seq_offsets,
                        int num_kv_heads, int head_dim, int block_size, int max_blocks_per_seq,
                        int num_blocks, int max_context_len, pa_dtype dtype, void* stream);
 
+/*
+ * Diagnostic read-bandwidth probe (not a step of the decode path).  A paged decode
+ * streams K and V as whole (block, kv head) tiles scattered through the pool; this
+ * call reads such pieces and keeps only a checksum, so its rate is the ceiling the
+ * decode's loads can reach on the device (in order: a streaming read; shuffled:
+ * the paged gather).
+ *
+ *   buf            device buffer read from
+ *   piece_offsets  [num_pieces] int64, device: byte offset of piece i in buf
+ *                  (16-byte aligned); every piece [off, off + piece_bytes) must
+ *                  lie inside buf (not checked: the library does not know its size)
+ *   piece_bytes    bytes per piece, a multiple of 4096
+ *   workgroups     workgroups of 256 threads; workgroup b reads pieces
+ *                  [in_flight * b, in_flight * (b + 1)), then the same group
+ *                  workgroups * in_flight pieces further on, and so on
+ *   in_flight      4, 8 or 16: pieces whose 16-byte loads each thread issues
+ *                  before using any of them
+ *   sink           [workgroups * 256] uint32, device: written with checksums
+ * Returns PA_ERR_INVALID_ARG / PA_ERR_UNSUPPORTED for bad arguments (nothing
+ * launched).
+ */
+pa_status pa_read_probe(const void* buf, const int64_t* piece_offsets, int num_pieces,
+                        int piece_bytes, int workgroups, int in_flight, uint32_t* sink,
+                        void* stream);
+
 #ifdef __cplusplus
 }
 #endif

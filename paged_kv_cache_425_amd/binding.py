@@ -59,6 +59,8 @@ def load_library() -> ctypes.CDLL:
     lib.pa_decode_step_fp8.restype = i32
     lib.pa_decode_step_fp8.argtypes = [vp] * 9 + [i32] * 8 + [f32] * 3 + [i32, i32, vp, sz, vp,
                                                                           vp]
+    lib.pa_read_probe.restype = i32
+    lib.pa_read_probe.argtypes = [vp, vp, i32, i32, i32, i32, vp, vp]
     lib.pa_decode_step_noalloc.restype = i32
     lib.pa_decode_step_noalloc.argtypes = [vp] * 9 + [i32] * 8 + [f32, i32, i32, vp, vp]
     lib.pa_paged_attention_fp8.restype = i32
@@ -582,6 +584,25 @@ def gather_kv(block_table: torch.Tensor, context_lens: torch.Tensor, k_cache: to
     _check(st, "pa_gather_kv")
     _record(stream, (k_out, v_out))
     return k_out, v_out
+
+
+def read_probe(buf: torch.Tensor, piece_offsets: torch.Tensor, piece_bytes: int,
+               workgroups: int, in_flight: int, sink: torch.Tensor, stream=None) -> None:
+    """Read-bandwidth probe (pa_read_probe): read the pieces of `buf` at `piece_offsets`
+    (int64 byte offsets) and leave checksums in `sink` (int32, workgroups * 256)."""
+    dev = buf.device
+    _require(buf, "buf", dev)
+    _require(piece_offsets, "piece_offsets", dev, torch.int64)
+    _require(sink, "sink", dev, torch.int32)
+    if sink.numel() < workgroups * 256:
+        raise ValueError(f"sink must hold {workgroups * 256} entries")
+    n = piece_offsets.numel()
+    size = buf.numel() * buf.element_size()
+    if n and piece_bytes > size:
+        raise ValueError("pieces larger than the buffer")
+    _check(load_library().pa_read_probe(_ptr(buf), _ptr(piece_offsets), n, int(piece_bytes),
+                                        int(workgroups), int(in_flight), _ptr(sink),
+                                        _stream(dev, stream)), "pa_read_probe")
 
 
 # ---------------------------------------------------------------------------

@@ -15,7 +15,8 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libpagedattn.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
-SOURCES = ["paged_attention.hip", "cache_ops.hip", "prefill.hip", "fp8_cache.hip", "swap.hip"]
+SOURCES = ["paged_attention.hip", "cache_ops.hip", "prefill.hip", "fp8_cache.hip", "swap.hip",
+           "probe.hip"]
 ARCH = "gfx950"
 
 

@@ -1,0 +1,66 @@
+// Read-bandwidth probe for gfx950: how fast the memory system delivers the paged
+// decode's access pattern when nothing else is done with the bytes.
+//
+// A paged decode streams each sequence's K and V as whole (block, kv head) tiles
+// scattered through the pool -- 4 KB each at block size 16, bf16, head size 128.
+// This kernel reads such pieces (at offsets the caller lists: in order, for a
+// streaming read, or shuffled, for the paged gather) and keeps only a checksum, so
+// its rate is the ceiling the decode's loads can reach on this part.  It is a
+// diagnostic next to the decode path, not a step of it.
+#include "common.h"
+
+namespace pa {
+
+constexpr int kProbeThreads = 256;
+
+// Workgroup b takes pieces [U*b, U*b + U), then [U*(b + grid), ...), and so on.  For a
+// group of U pieces each thread loads its 16-byte chunk of every piece before it uses
+// any of them, so U loads per thread are in flight.  Pieces past the end are skipped.
+template <int U>
+__global__ void __launch_bounds__(kProbeThreads)
+read_probe_kernel(const unsigned char* __restrict__ buf, const int64_t* __restrict__ offs,
+                  int npieces, int piece_bytes, uint32_t* __restrict__ sink) {
+  u32x4 acc = {0u, 0u, 0u, 0u};
+  const int chunks = piece_bytes / 16;
+  for (long p0 = (long)blockIdx.x * U; p0 < npieces; p0 += (long)gridDim.x * U) {
+    const int live = (int)min((long)U, npieces - p0);
+    for (int c = threadIdx.x; c < chunks; c += kProbeThreads) {
+      u32x4 v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const long p = p0 + (u < live ? u : 0);
+        v[u] = load16(buf + offs[p] + (size_t)c * 16);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) acc ^= v[u];
+    }
+  }
+  sink[(size_t)blockIdx.x * kProbeThreads + threadIdx.x] = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
+}
+
+}  // namespace pa
+
+extern "C" pa_status pa_read_probe(const void* buf, const int64_t* piece_offsets, int num_pieces,
+                                   int piece_bytes, int workgroups, int in_flight,
+                                   uint32_t* sink, void* stream) {
+  if (num_pieces < 0 || workgroups <= 0 || piece_bytes <= 0 || piece_bytes % 4096)
+    return PA_ERR_INVALID_ARG;
+  if (in_flight != 4 && in_flight != 8 && in_flight != 16) return PA_ERR_UNSUPPORTED;
+  if (num_pieces == 0) return PA_OK;
+  if (!buf || !piece_offsets || !sink) return PA_ERR_INVALID_ARG;
+  if (reinterpret_cast<uintptr_t>(buf) % 16 || reinterpret_cast<uintptr_t>(piece_offsets) % 8 ||
+      reinterpret_cast<uintptr_t>(sink) % 4)
+    return PA_ERR_INVALID_ARG;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const unsigned char* b = static_cast<const unsigned char*>(buf);
+  if (in_flight == 4)
+    hipLaunchKernelGGL(pa::read_probe_kernel<4>, dim3(workgroups), dim3(pa::kProbeThreads), 0, s,
+                       b, piece_offsets, num_pieces, piece_bytes, sink);
+  else if (in_flight == 8)
+    hipLaunchKernelGGL(pa::read_probe_kernel<8>, dim3(workgroups), dim3(pa::kProbeThreads), 0, s,
+                       b, piece_offsets, num_pieces, piece_bytes, sink);
+  else
+    hipLaunchKernelGGL(pa::read_probe_kernel<16>, dim3(workgroups), dim3(pa::kProbeThreads), 0,
+                       s, b, piece_offsets, num_pieces, piece_bytes, sink);
+  return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
+}

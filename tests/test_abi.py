@@ -34,7 +34,7 @@ def test_header_declares_the_boundary():
         "pa_paged_attention_workspace_size", "pa_paged_attention", "pa_reshape_and_cache",
         "pa_gather_kv", "pa_decode_step", "pa_copy_blocks", "pa_paged_prefill",
         "pa_reshape_and_cache_fp8", "pa_paged_attention_fp8", "pa_decode_step_fp8",
-        "pa_swap_blocks", "pa_decode_step_noalloc"])
+        "pa_swap_blocks", "pa_decode_step_noalloc", "pa_read_probe"])
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -155,6 +155,22 @@ def test_decode_step_noalloc_rejects_before_launch(lib):
     need = lib.pa_paged_attention_workspace_size(4096, 64, 8, 128, 32768, 64, 1)
     assert need > 64 << 20
     assert call(big) == 3
+
+
+def test_read_probe_rejects_before_launch(lib):
+    f = lib.pa_read_probe
+    base = [FAKE, FAKE, 16, 4096, 64, 8, FAKE, None]
+
+    def call(over):
+        a = list(base)
+        for k, v in over.items():
+            a[k] = v
+        return f(*a)
+    assert call({3: 4000}) == 1                 # piece not a multiple of 4 KB
+    assert call({5: 6}) == 2                    # in-flight count not built
+    assert call({4: 0}) == 1                    # no workgroups
+    assert call({0: FAKE + 4}) == 1             # buffer misaligned
+    assert call({2: 0}) == 0                    # nothing to read
 
 
 def test_reshape_and_cache_rejects_before_launch(lib):
