@@ -36,8 +36,7 @@ if ROOT not in sys.path:
 
 METRIC = "paged-attn decode KV GB/s (% of HBM peak) + µs/step, Llama-3-8B shape, 1 GPU"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, AMD's published peak
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_step_traffic.json")
-FP8_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_fp8_traffic.json")
+PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCE = os.path.join(ROOT, "paged_kv_cache_425_amd", "csrc", "paged_attention.hip")
 
 
@@ -223,8 +222,10 @@ def source_digest() -> str:
     return kernel_source_digest(KERNEL_SOURCE)
 
 
-def load_traffic(workload: str, path: str = TRAFFIC_FILE):
-    """Measured HBM bytes per decode launch, if the counters were taken on the current kernel."""
+def load_traffic(workload: str):
+    """Measured HBM bytes per decode launch (profiles/traffic_<workload>.json, from the
+    calibrated FETCH_SIZE / WRITE_SIZE counters), if they were taken on the current kernel."""
+    path = os.path.join(PROFILES, f"traffic_{workload}.json")
     try:
         with open(path) as f:
             rec = json.load(f)
@@ -614,7 +615,7 @@ def bench_fp8(args) -> int:
         "roofline": {"kernel": "pa_decode_step_fp8: paged_decode_kernel<bf16, e4m3>",
                      "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": load_traffic(w.name + "-fp8", FP8_TRAFFIC_FILE),
+                     "traffic": load_traffic(w.name + "-fp8"),
                      "algorithmic_bytes_per_launch": fused_bytes},
         "cpu_baseline": None,
     }
@@ -894,7 +895,8 @@ def main() -> int:
     value_logical = nb["kv"] / (ms_step * 1e-3) / 1e9
     fused_unique = fused_bytes - nb["kv"] + kv_unique
     achieved = fused_unique / launch_avg_s / 1e9
-    traffic = load_traffic(w.name)
+    traffic = load_traffic(w.name + ("" if part == (w.partition_size or 0) else
+                                     "-default-partition" if part == 0 else f"-P{part}"))
     ceil = None
     if not args.no_ceiling:
         log("read ceiling (probe sweep) ...")
