@@ -73,6 +73,9 @@ def parse_args():
                          "from a host copy of the lengths (host_context_lens), or ranked "
                          "inside every workgroup; the other order is timed beside it")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--plain-step", action="store_true",
+                    help="with a shared prefix: time only pa_decode_step (the headline is "
+                         "otherwise pa_decode_step_shared_prefix)")
     ap.add_argument("--no-ceiling", action="store_true",
                     help="skip the read-probe sweep beside the step (e.g. under a profiler)")
     ap.add_argument("--warm", action="store_true",
@@ -886,6 +889,33 @@ def main() -> int:
                 "value": round(kv_unique / (wall_w / K) / 1e9, 2),
                 "launch_us_events": round(ev_w / K * 1e6, 2)}
 
+    # ---- a prefix shared by every sequence: the step that computes it once per group ----
+    pfx_len = int(w.info.get("shared_prefix_len", 0))
+    plain = None
+    step_name = "pa_decode_step: scatter of the new tokens + paged decode, one launch"
+    if pfx_len and not args.plain_step:
+        pfx_blocks = pfx_len // w.block_size
+        need_p = pk.shared_prefix_workspace_size(w.num_seqs, w.num_heads, w.num_kv_heads,
+                                                 w.head_dim, w.max_context_len, pfx_blocks,
+                                                 w.block_size, part, tdt)
+        ws_p = torch.empty(need_p, dtype=torch.uint8, device=dev)
+        hl = host_lens if args.order == "host" else None
+        shared = [pk.prepare_decode_step_shared_prefix(
+            query, key_new, val_new, slot_new, table, lens, kc, vc, w.scale,
+            prefix_blocks=pfx_blocks, max_context_len=w.max_context_len, out=out,
+            workspace=ws_p, partition_size=part, host_context_lens=hl) for kc, vc in pools]
+        run_fused(R, W, shared)
+        wall_p, ev_p = timed(run_fused, R, K, shared)
+        log(f"cold shared-prefix step: {wall_p / K * 1e6:.1f} us/step wall, "
+            f"{ev_p / K * 1e6:.1f} us/launch pair (events)")
+        plain = {"step": "pa_decode_step", "us_per_step": round(wall / K * 1e6, 2),
+                 "launch_us_events": round(ev_s / K * 1e6, 2),
+                 "value": round(kv_unique / (wall / K) / 1e9, 2)}
+        wall, ev_s = wall_p, ev_p
+        step_name = (f"pa_decode_step_shared_prefix ({pfx_blocks} shared blocks): the prefix "
+                     "pass once per group of sequences, then the scatter of the new tokens + "
+                     "paged decode of the private suffixes with the log-sum-exp merge")
+
     ms_step = wall / K * 1e3
     launch_avg_s = ev_s / K
     # HBM must deliver each distinct slot at least once: with shared blocks (a common prefix,
@@ -896,7 +926,8 @@ def main() -> int:
     fused_unique = fused_bytes - nb["kv"] + kv_unique
     achieved = fused_unique / launch_avg_s / 1e9
     traffic = load_traffic(w.name + ("" if part == (w.partition_size or 0) else
-                                     "-default-partition" if part == 0 else f"-P{part}"))
+                                     "-default-partition" if part == 0 else f"-P{part}") +
+                           ("-shared-prefix" if plain else ""))
     ceil = None
     if not args.no_ceiling:
         log("read ceiling (probe sweep) ...")
@@ -927,7 +958,7 @@ def main() -> int:
                    "partition_size": part_used,
                    "kv_bytes_per_step": nb["kv"], "kv_bytes_unique": kv_unique,
                    "seed": w.info["seed"],
-                   "step": "pa_decode_step: scatter of the new tokens + paged decode, one launch",
+                   "step": step_name,
                    "order": args.order + (" (host_context_lens sorted on the host every call)"
                                           if args.order == "host" else " (ranked in-kernel)"),
                    "pool_bytes_each": int(kc0.numel() * kc0.element_size()),
@@ -940,7 +971,9 @@ def main() -> int:
                                       "launch_us_events": round(ev3 / K * 1e6, 2),
                                       "value": round(kv_unique / (wall3 / K) / 1e9, 2)},
         "warm": warm,
-        "roofline": {"kernel": f"pa_decode_step: {kernels}",
+        "plain_step": plain,
+        "roofline": {"kernel": (f"pa_decode_step_shared_prefix: prefix pass + {kernels}"
+                                if plain else f"pa_decode_step: {kernels}"),
                      "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic,

@@ -202,6 +202,48 @@ pa_status pa_decode_step(void* out, const void* query, const void* key, const vo
                          const int32_t* host_context_lens);
 
 /*
+ * The decode step when every sequence of the call starts with the same shared prefix:
+ * the first prefix_blocks entries of every block-table row name the same physical
+ * blocks (one system prompt stored once and shared by reference: page "vLLM core
+ * inference engine", section 2.2; prefix caching, page "vLLM core features", section
+ * 4.6).  The result (out and both caches) is that of pa_decode_step; the attention over
+ * the shared positions [0, P), P = prefix_blocks * block_size, is computed once per
+ * group of sequences (their query heads side by side in one matrix product), so each
+ * prefix block is read once per group rather than once per sequence.  The private
+ * positions [P, L) go through the paged decode, and the two parts of each row are
+ * combined with a log-sum-exp merge.
+ *
+ *   prefix_blocks  shared leading blocks (0: exactly pa_decode_step); P <= 8192
+ *                  tokens (else PA_ERR_UNSUPPORTED) and prefix_blocks <
+ *                  max_blocks_per_seq
+ *   slot_mapping   as in pa_decode_step, or NULL for decode attention alone (no token
+ *                  appended; key and value are then ignored)
+ *   workspace      pa_shared_prefix_workspace_size(...) bytes, 16-byte aligned; it
+ *                  holds each row's prefix result and the suffix partitions
+ *   dtype          PA_DTYPE_BF16 or PA_DTYPE_F32
+ *   other arguments as in pa_decode_step; partition_size applies to the private
+ *   suffixes (0: pa_default_partition_size of their longest length)
+ * Preconditions (device side): every context_lens[s] >= P, and > P when a token is
+ * appended for s (a new token goes to a private block).  With host_context_lens, a
+ * length below P is rejected (PA_ERR_INVALID_ARG) before any launch.
+ */
+pa_status pa_decode_step_shared_prefix(void* out, const void* query, const void* key,
+                                       const void* value, const int64_t* slot_mapping,
+                                       const int32_t* block_table, const int32_t* context_lens,
+                                       void* k_cache, void* v_cache, int num_seqs,
+                                       int num_heads, int num_kv_heads, int head_dim,
+                                       int block_size, int max_blocks_per_seq, int num_blocks,
+                                       int max_context_len, int prefix_blocks, float scale,
+                                       pa_dtype dtype, int partition_size, void* workspace,
+                                       size_t workspace_bytes, void* stream,
+                                       const int32_t* host_context_lens);
+
+/* Workspace bytes of pa_decode_step_shared_prefix (0 for arguments it would reject). */
+size_t pa_shared_prefix_workspace_size(int num_seqs, int num_heads, int num_kv_heads,
+                                       int head_dim, int max_context_len, int prefix_blocks,
+                                       int block_size, int partition_size, pa_dtype dtype);
+
+/*
  * pa_decode_step for callers that cannot allocate device memory: code under
  * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
  * It takes no workspace: when the call needs one (sequences split into

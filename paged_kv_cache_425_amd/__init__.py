@@ -4,7 +4,8 @@ The work runs in hand-written HIP kernels behind a C ABI (include/pagedattn.h);
 this package only marshals torch tensors to it.
 """
 from .binding import (LIB_PATH, PreparedCall, chunk_elems, copy_blocks, decode_step,
-                      decode_step_noalloc, read_probe,
+                      decode_step_noalloc, decode_step_shared_prefix, read_probe,
+                      shared_prefix_workspace_size, prepare_decode_step_shared_prefix,
                       decode_step_fp8, default_partition_size, gather_kv, k_cache_shape,
                       load_library, prepare_decode_step_fp8, paged_attention,
                       prepare_swap_blocks, swap_blocks, paged_attention_fp8, paged_prefill, prepare_copy_blocks,
@@ -13,7 +14,8 @@ from .binding import (LIB_PATH, PreparedCall, chunk_elems, copy_blocks, decode_s
                       reshape_and_cache_fp8, v_cache_shape, workspace_size)
 
 __all__ = ["LIB_PATH", "PreparedCall", "chunk_elems", "copy_blocks", "decode_step",
-           "decode_step_noalloc", "read_probe",
+           "decode_step_noalloc", "decode_step_shared_prefix", "read_probe",
+           "shared_prefix_workspace_size", "prepare_decode_step_shared_prefix",
            "decode_step_fp8", "prepare_decode_step_fp8", "prepare_swap_blocks", "swap_blocks",
            "default_partition_size", "gather_kv", "k_cache_shape", "load_library",
            "paged_attention", "paged_attention_fp8", "paged_prefill", "prepare_copy_blocks",

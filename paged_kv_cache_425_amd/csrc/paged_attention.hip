@@ -94,10 +94,23 @@ struct DecodeParams {
   const void* new_v;
   const int64_t* new_slot;
   int S, Hq, Hkv, g, MB, NB, P, Pmax;
+  int tbl_stride;          // entries per block-table row (MB, or more past a skipped prefix)
   int wave_parts;          // partition mode: 1 = each wave owns one partition of NW in a row
   float scale_log2;        // scale * log2(e) (* k_scale for FP8 K): base-2 logits
   float v_scale;           // output multiplier: 1, or the FP8 V scale
   float k_quant, v_quant;  // FP8 fused step: the scales the new token is quantised with
+  // Shared prefix (pa_decode_step_shared_prefix).  Prefix pass: every unit is a group of
+  // `grp` sequences over one chunk of P positions of the prefix [0, pfx_len), and
+  // pfx_ml / pfx_acc receive each (sequence, query head) row's (max, sum, unnormalised
+  // output) over each of the pfx_chunks chunks.  Suffix pass: block_table points past
+  // the prefix's entries, `len_off` = pfx_len is taken off every context length, and each
+  // output merges the row's prefix results.
+  int len_off;
+  int pfx_len;
+  int pfx_chunks;
+  int grp;
+  float* pfx_ml;           // [S][Hq][pfx_chunks][2]
+  float* pfx_acc;          // [S][Hq][pfx_chunks][D]
 };
 
 // A context length clamped to what the launch can address.
@@ -108,7 +121,34 @@ __device__ __forceinline__ int clamp_len(const DecodeParams& a, int L, int BS) {
 }
 
 __device__ __forceinline__ int clamped_len(const DecodeParams& a, int s, int BS) {
-  return clamp_len(a, a.context_lens[s], BS);
+  return clamp_len(a, a.context_lens[s] - a.len_off, BS);
+}
+
+// Final output of one channel d of row `row` (sequence * Hq + query head) whose tokens gave
+// the running max M (log2 units), weight sum den and unnormalised value num: num / den, or
+// -- after a shared prefix -- the log-sum-exp merge with the (max, sum, value) of each of
+// the prefix's chunks for that row.  Nothing seen at all (M = -inf everywhere) gives 0.
+template <int D>
+__device__ __forceinline__ float finish_row(const DecodeParams& a, size_t row, int d, float M,
+                                            float den, float num) {
+  if (a.pfx_ml != nullptr) {
+    const int C = a.pfx_chunks;
+    const float* ml = a.pfx_ml + row * C * 2;
+    const float* ac = a.pfx_acc + row * C * D + d;
+    float Mx = M;
+    for (int c = 0; c < C; ++c) Mx = fmaxf(Mx, ml[2 * c]);
+    if (Mx == kNegInf) return 0.f;
+    const float fs = exp2_fast(M - Mx);                                 // 2^-inf = 0
+    num *= fs;
+    den *= fs;
+    for (int c = 0; c < C; ++c) {
+      const float f = exp2_fast(ml[2 * c] - Mx);
+      num += f * ac[(size_t)c * D];
+      den += f * ml[2 * c + 1];
+    }
+    return num / den;
+  }
+  return (M == kNegInf || den == 0.f) ? 0.f : num / den;
 }
 
 // Per-step shape constants for a query/output type T and a cache element type C (C = T,
@@ -187,9 +227,17 @@ using OrderArg = typename std::conditional<PAIRED, PairOrder, NoOrder>::type;
 // (identically), by counting for each sequence the sequences that are longer
 // (ties broken by index).  Used when each sequence is one partition;
 // otherwise a workgroup is one (kv head, sequence, partition).
-template <typename T, typename C, int D, int BS, int NW, int PIPE, bool PAIRED>
+//
+// Prefix pass (PREFIX): a workgroup takes one group of a.grp consecutive sequences that
+// share the first a.pfx_len positions (the same physical blocks) and computes, for all of
+// them at once, each (sequence, query head) row's attention statistics over that prefix:
+// the group's g-head query rows fill the columns of the MFMA operand (grp * g <= 16), so
+// each prefix K/V byte is read once per group instead of once per sequence.
+template <typename T, typename C, int D, int BS, int NW, int PIPE, bool PAIRED,
+          bool PREFIX = false>
 __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(PA_DECODE_OCC)))
 paged_decode_kernel(const DecodeParams a, const OrderArg<PAIRED> ord) {
+  static_assert(!(PAIRED && PREFIX), "the prefix pass is not paired");
   using Sh = StepShape<T, C, D>;
   constexpr bool kBf16 = Sh::kBf16;
   constexpr bool kFp8 = Sh::kFp8;
@@ -218,7 +266,7 @@ paged_decode_kernel(const DecodeParams a, const OrderArg<PAIRED> ord) {
   const int lens_words = PAIRED ? (a.S + 3) / 4 * 4 : 0;
   int* lens = reinterpret_cast<int*>(smem + 64 + 4 * D * sizeof(T));
   int* tbl = lens + lens_words;
-  const int tbl_words = ((PAIRED ? 2 : (a.wave_parts ? NW : 1)) * win + 3) / 4 * 4;
+  const int tbl_words = ((PAIRED ? 2 : (!PREFIX && a.wave_parts ? NW : 1)) * win + 3) / 4 * 4;
   float* red = reinterpret_cast<float*>(tbl + tbl_words);
 
   const int lane = threadIdx.x & 63;
@@ -237,6 +285,7 @@ paged_decode_kernel(const DecodeParams a, const OrderArg<PAIRED> ord) {
   int s, tok0 = 0, tok1 = 0, lw, nw, p = 0, nparts = 1, uidx = 0;
   int p0 = 0, seqL = 0;      // partition mode: the workgroup's first partition, the length
   int sA = 0, sB = -1, nA = NW;                             // PAIRED: the two sequences
+  int gseq = 1;                                             // PREFIX: sequences in the group
   int LA = 0, LB = 0;                                       // PAIRED: their lengths
   bool planned = false;                                     // PAIRED: pairs from the host
   bool onA = true;
@@ -254,8 +303,8 @@ paged_decode_kernel(const DecodeParams a, const OrderArg<PAIRED> ord) {
       nA = sB < 0 ? NW : min(max((int)(ey >> 24), 1), NW - 1);
       // the device lengths: both loads go out now and are first used after the
       // prologue's other loads (sA stands in for a missing second sequence)
-      LA = a.context_lens[sA];
-      LB = a.context_lens[sB >= 0 ? sB : sA];
+      LA = a.context_lens[sA] - a.len_off;
+      LB = a.context_lens[sB >= 0 ? sB : sA] - a.len_off;
     } else {
       // Sort keys: key_t = (L_t << 10) | (1023 - t), unique per sequence and ordered by
       // length, then by index for equal lengths (L_t <= P <= 8192 here, and S <= 512, so the
@@ -305,6 +354,18 @@ paged_decode_kernel(const DecodeParams a, const OrderArg<PAIRED> ord) {
     lw = onA ? wave : wave - nA;
     nw = onA ? nA : NW - nA;
     tblw = tbl + (onA ? 0 : win);
+  } else if constexpr (PREFIX) {
+    // group (fastest) and chunk p of P positions; the group's first sequence's table row
+    // holds the shared prefix's blocks
+    const int ngroups = (a.S + a.grp - 1) / a.grp;
+    s = (id % ngroups) * a.grp;
+    p = p0 = id / ngroups;
+    gseq = min(a.grp, a.S - s);
+    tok0 = p * a.P;
+    tok1 = min(a.pfx_len, tok0 + a.P);
+    seqL = a.pfx_len;
+    lw = wave;
+    nw = NW;
   } else if (a.wave_parts) {
     // NW consecutive partitions, one per wave: the workgroup stages one table window
     // for all of them and each wave streams its partition alone and writes its own
@@ -335,16 +396,19 @@ paged_decode_kernel(const DecodeParams a, const OrderArg<PAIRED> ord) {
   }
 
   const int g = a.g;
-  const int rows = kBf16 ? 2 * g : g;
+  // MFMA columns in use: the g heads (bf16: plus their lo copies), or in the prefix pass
+  // the g heads of each of the group's sequences
+  const int rows = PREFIX ? gseq * g : (kBf16 ? 2 * g : g);
   const int head = kvh * g + (n % g);
   const bool row_live = n < rows;
+  const int row_seq = PREFIX ? s + (row_live ? n / g : 0) : s;   // sequence of column n
 
   // Every load of the prologue is issued before the first wait on any of them: the
   // query operand, the new tokens and the block-table windows land in one round trip.
   //
   // Query operand: lane (n, j) holds head-row n's channels of the chunks it multiplies.
   // FP8: K chunk j + 4c' (16 channels) feeds MFMAs 2c' and 2c' + 1 (8 channels each).
-  const T* qrow = static_cast<const T*>(a.q) + ((size_t)s * a.Hq + head) * D;
+  const T* qrow = static_cast<const T*>(a.q) + ((size_t)row_seq * a.Hq + head) * D;
   u32x4 qop[kNq];
 #pragma unroll
   for (int c = 0; c < kNq; ++c) {
@@ -367,7 +431,7 @@ paged_decode_kernel(const DecodeParams a, const OrderArg<PAIRED> ord) {
         const int i = min(k * kThreads + (int)threadIdx.x, count - 1);
         int row = 0, col = 0, dst = 0;
         where(i, row, col, dst);
-        b[k] = static_cast<unsigned>(a.block_table[(size_t)row * a.MB + col]);
+        b[k] = static_cast<unsigned>(a.block_table[(size_t)row * a.tbl_stride + col]);
       }
     }
   };
@@ -780,6 +844,24 @@ paged_decode_kernel(const DecodeParams a, const OrderArg<PAIRED> ord) {
           acc[sl] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
               e4m3x8_to_bf16x8(b.v[sl][2 * h], b.v[sl][2 * h + 1]), pop, acc[sl], 0, 0, 0);
       }
+    } else if constexpr (kBf16 && PREFIX) {
+      // every column is a real row: the hi and lo weights go through two MFMAs into one
+      // accumulator
+      bf16x8 ph, pl;
+#pragma unroll
+      for (int v = 0; v < 8; ++v) {
+        const __bf16 hi = f32_to_bf16(pw[v]);
+        const __bf16 lo = f32_to_bf16(pw[v] - bf16_to_f32(hi));
+        ph[v] = row_live ? hi : f32_to_bf16(0.f);
+        pl[v] = row_live ? lo : f32_to_bf16(0.f);
+      }
+#pragma unroll
+      for (int sl = 0; sl < kNs; ++sl) {
+        acc[sl] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, b.v[sl]), ph,
+                                                          acc[sl], 0, 0, 0);
+        acc[sl] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, b.v[sl]), pl,
+                                                          acc[sl], 0, 0, 0);
+      }
     } else if constexpr (kBf16) {
       const bool is_hi = n < g;
       const bool is_lo = !is_hi && n < rows;
@@ -834,7 +916,7 @@ paged_decode_kernel(const DecodeParams a, const OrderArg<PAIRED> ord) {
   }
 
   // ---- merge the waves of the workgroup --------------------------------------------
-  if constexpr (kBf16 || kFp8) {
+  if constexpr ((kBf16 || kFp8) && !PREFIX) {
     // add the lo rows [g, 2g) into the hi rows [0, g)
 #pragma unroll
     for (int sl = 0; sl < kNs; ++sl)
@@ -843,6 +925,58 @@ paged_decode_kernel(const DecodeParams a, const OrderArg<PAIRED> ord) {
   }
   float lsum = sum_xor16(l_run);
   lsum = sum_xor32(lsum);
+  if constexpr (PREFIX) {
+    // Tree merge of the waves, lane by lane: lane (n, j) of every wave holds column n's
+    // max, sum and channels 16 sl + 4 j .. + 3, so half of the remaining waves hand their
+    // registers to the other half through LDS until wave 0 holds the workgroup's result.
+    constexpr int kLane = D / 4 + 2;                         // floats per lane
+    float* xb = red;                                         // [NW / 2][kLane][64]
+    for (int half = NW / 2; half >= 1; half /= 2) {
+      if (wave >= half && wave < 2 * half) {
+        float* dst = xb + (size_t)(wave - half) * kLane * 64 + lane;
+        dst[0] = m_run;
+        dst[64] = lsum;
+#pragma unroll
+        for (int sl = 0; sl < kNs; ++sl)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) dst[(2 + 4 * sl + e) * 64] = acc[sl][e];
+      }
+      __syncthreads();
+      if (wave < half) {
+        const float* src = xb + (size_t)wave * kLane * 64 + lane;
+        const float mb = src[0];
+        const float M = fmaxf(m_run, mb);
+        if (M != kNegInf) {
+          const float fa = exp2_fast(m_run - M), fb = exp2_fast(mb - M);
+          lsum = lsum * fa + src[64] * fb;
+#pragma unroll
+          for (int sl = 0; sl < kNs; ++sl)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              acc[sl][e] = acc[sl][e] * fa + src[(2 + 4 * sl + e) * 64] * fb;
+          m_run = M;
+        }
+      }
+      __syncthreads();
+    }
+    if (wave == 0 && row_live) {
+      // column n = head n % g of the group's sequence n / g; chunk p of the prefix
+      const size_t prow =
+          ((size_t)(s + n / g) * a.Hq + kvh * g + n % g) * a.pfx_chunks + p;
+#pragma unroll
+      for (int sl = 0; sl < kNs; ++sl) {
+        f32x4 v = acc[sl];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] *= a.v_scale;
+        *reinterpret_cast<f32x4*>(a.pfx_acc + prow * D + 16 * sl + 4 * j) = v;
+      }
+      if (j == 0) {
+        a.pfx_ml[prow * 2 + 0] = m_run;
+        a.pfx_ml[prow * 2 + 1] = lsum;
+      }
+    }
+    return;
+  }
   if (!PAIRED && a.wave_parts) {
     // one partition per wave: lane (n, j) holds row n's channels 16 sl + 4 j .. + 3;
     // the wave writes its partition's result itself (the output when the sequence has
@@ -854,8 +988,9 @@ paged_decode_kernel(const DecodeParams a, const OrderArg<PAIRED> ord) {
         for (int sl = 0; sl < kNs; ++sl)
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const float o = m_run == kNegInf ? 0.f : (acc[sl][e] * a.v_scale) / lsum;
-            const size_t at = row * D + 16 * sl + 4 * j + e;
+            const int d = 16 * sl + 4 * j + e;
+            const float o = finish_row<D>(a, row, d, m_run, lsum, acc[sl][e] * a.v_scale);
+            const size_t at = row * D + d;
             if constexpr (kBf16)
               static_cast<uint16_t*>(a.out)[at] = bf16_bits(o);
             else
@@ -878,9 +1013,10 @@ paged_decode_kernel(const DecodeParams a, const OrderArg<PAIRED> ord) {
     }
     return;
   }
+  const int rows_out = g;
   const int wstride = merge_words(D, g);
   float* wr = red + wave * wstride;
-  if (n < g) {
+  if (n < rows_out) {
     if (j == 0) {
       wr[n] = m_run;
       wr[16 + n] = lsum;
@@ -894,9 +1030,9 @@ paged_decode_kernel(const DecodeParams a, const OrderArg<PAIRED> ord) {
   // unit 0 = waves [0, nA) (all waves outside the paired mode), unit 1 = waves [nA, NW)
   const int nunits = (PAIRED && sB >= 0) ? 2 : 1;
   const bool single = nparts == 1;
-  for (int idx = threadIdx.x; idx < nunits * g * D; idx += kThreads) {
-    const int u = idx / (g * D);
-    const int h = (idx % (g * D)) / D;
+  for (int idx = threadIdx.x; idx < nunits * rows_out * D; idx += kThreads) {
+    const int u = idx / (rows_out * D);
+    const int h = (idx % (rows_out * D)) / D;
     const int d = idx % D;
     const int w0 = u ? nA : 0, w1 = u ? NW : nA;
     const int su = PAIRED ? (u ? sB : sA) : s;
@@ -914,7 +1050,7 @@ paged_decode_kernel(const DecodeParams a, const OrderArg<PAIRED> ord) {
     const size_t row = (size_t)su * a.Hq + kvh * g + h;
     num *= a.v_scale;
     if (single) {
-      const float o = (M == kNegInf) ? 0.f : num / den;
+      const float o = finish_row<D>(a, row, d, M, den, num);
       if constexpr (kBf16)
         static_cast<uint16_t*>(a.out)[row * D + d] = bf16_bits(o);
       else
@@ -978,7 +1114,7 @@ reduce_partitions_kernel(const DecodeParams a) {
   }
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
-    const float o = (M == kNegInf || den == 0.f) ? 0.f : num[i] / den;
+    const float o = finish_row<D>(a, row, lane + 64 * i, M, den, num[i]);
     const size_t idx = row * D + lane + 64 * i;
     if constexpr (ElemTraits<T>::kBf16)
       static_cast<uint16_t*>(a.out)[idx] = bf16_bits(o);
@@ -1016,7 +1152,7 @@ inline void order_on_host(const DecodeParams& a, int BS, int step, const int32_t
   const long cap = std::min((long)a.MB * BS, (long)a.P * a.Pmax);
   uint32_t key[kMaxPairedSeqs];
   for (int t = 0; t < a.S; ++t) {
-    const long L = std::min(std::max(0L, (long)host_lens[t]), cap);
+    const long L = std::min(std::max(0L, (long)host_lens[t] - a.len_off), cap);
     key[t] = (static_cast<uint32_t>(L) << 10) | static_cast<uint32_t>(1023 - t);
   }
   std::sort(key, key + a.S, [](uint32_t x, uint32_t y) { return x > y; });
@@ -1058,6 +1194,37 @@ hipError_t launch_decode(const DecodeParams& a, const int32_t* host_lens, hipStr
   hipLaunchKernelGGL((reduce_partitions_kernel<T, D, BS>), dim3((unsigned)((long)a.S * a.Hq)),
                      dim3(64), 0, stream, a);
   return hipGetLastError();
+}
+
+// The prefix pass: one workgroup per (kv head, group of a.grp sequences, chunk of the
+// prefix), kv head fastest, chunk slowest.
+constexpr int kPrefixWaves = 8;
+
+// LDS of a prefix-pass workgroup: control, new-token staging (unused), one table window of
+// P / BS entries, and the tree merge's exchange of NW / 2 waves' registers.
+inline size_t prefix_lds_bytes(int D, int BS, int P, int elt) {
+  const size_t tbl_words = ((size_t)(P / BS) + 3) / 4 * 4;
+  return 64 + 4 * (size_t)D * elt + 4 * (tbl_words + (kPrefixWaves / 2) * 64 * (D / 4 + 2));
+}
+
+template <typename T, int D, int BS>
+hipError_t launch_prefix(const DecodeParams& a, hipStream_t stream) {
+  const size_t lds = prefix_lds_bytes(D, BS, a.P, sizeof(T));
+  const long groups = (a.S + a.grp - 1) / a.grp;
+  hipLaunchKernelGGL((paged_decode_kernel<T, T, D, BS, kPrefixWaves, kPipe, false, true>),
+                     dim3((unsigned)((long)a.Hkv * groups * a.pfx_chunks)),
+                     dim3(kPrefixWaves * 64), lds, stream, a, NoOrder{});
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t dispatch_prefix(const DecodeParams& a, int D, int BS, hipStream_t stream) {
+#define PA_CASE(DD, BB) \
+  if (D == DD && BS == BB) return launch_prefix<T, DD, BB>(a, stream);
+  PA_CASE(64, 8) PA_CASE(64, 16) PA_CASE(64, 32)
+  PA_CASE(128, 8) PA_CASE(128, 16) PA_CASE(128, 32)
+#undef PA_CASE
+  return hipErrorInvalidValue;
 }
 
 template <typename T, typename C>
@@ -1169,6 +1336,17 @@ namespace {
 bool good_scale(float s) { return s > 0.f && s <= 3.4028234663852886e38f; }
 
 // fp8: the caches hold E4M3 codes read with k_scale / v_scale (query and out bf16).
+// The suffix pass of pa_decode_step_shared_prefix: positions before len_off are skipped
+// (block_table already points past their entries; rows are tbl_stride apart) and every
+// output merges the prefix pass's result of its row.
+struct SuffixArgs {
+  int len_off;
+  int tbl_stride;
+  int chunks;
+  float* pfx_ml;
+  float* pfx_acc;
+};
+
 pa_status run_decode(void* out, const void* query, const int32_t* block_table,
                      const int32_t* context_lens, const void* k_cache, const void* v_cache,
                      const void* new_k, const void* new_v, const int64_t* new_slot,
@@ -1176,7 +1354,8 @@ pa_status run_decode(void* out, const void* query, const int32_t* block_table,
                      int max_blocks_per_seq, int num_blocks, int max_context_len, float scale,
                      pa_dtype dtype, int partition_size, void* workspace, size_t workspace_bytes,
                      void* stream, const int32_t* host_lens, bool fp8 = false,
-                     float k_scale = 1.f, float v_scale = 1.f) {
+                     float k_scale = 1.f, float v_scale = 1.f,
+                     const SuffixArgs* sfx = nullptr) {
   pa_status st = check_shapes(num_heads, num_kv_heads, head_dim, block_size, dtype);
   if (st != PA_OK) return st;
   if (fp8 && dtype != PA_DTYPE_BF16) return PA_ERR_UNSUPPORTED;
@@ -1223,9 +1402,16 @@ pa_status run_decode(void* out, const void* query, const int32_t* block_table,
   a.Hkv = num_kv_heads;
   a.g = num_heads / num_kv_heads;
   a.MB = max_blocks_per_seq;
+  a.tbl_stride = sfx ? sfx->tbl_stride : max_blocks_per_seq;
   a.NB = num_blocks;
   a.P = P;
   a.Pmax = pmax;
+  a.len_off = sfx ? sfx->len_off : 0;
+  a.pfx_len = 0;
+  a.pfx_chunks = sfx ? sfx->chunks : 0;
+  a.grp = 0;
+  a.pfx_ml = sfx ? sfx->pfx_ml : nullptr;
+  a.pfx_acc = sfx ? sfx->pfx_acc : nullptr;
   // Short partitions: each wave of a workgroup owns one of kWaves consecutive
   // partitions, so one prologue serves them all and no cross-wave merge is needed --
   // when the workgroups still give every compute unit two.
@@ -1283,6 +1469,154 @@ extern "C" pa_status pa_decode_step(void* out, const void* query, const void* ke
                     num_seqs > 0 ? slot_mapping : nullptr, num_seqs, num_heads, num_kv_heads,
                     head_dim, block_size, max_blocks_per_seq, num_blocks, max_context_len, scale,
                     dtype, partition_size, workspace, workspace_bytes, stream, host_context_lens);
+}
+
+// ---------------------------------------------------------------------------
+// the decode step over a prefix that every sequence shares
+// ---------------------------------------------------------------------------
+namespace {
+
+// Workspace of pa_decode_step_shared_prefix: the prefix pass's (max, sum) [S][Hq][2] and
+// unnormalised outputs [S][Hq][D] (f32), then the suffix pass's partition workspace; each
+// region 256-byte aligned.
+struct PrefixLayout {
+  size_t ml, acc, part, total;
+  int P;                     // suffix partition length
+  int chunk, chunks;         // prefix pass: positions per chunk, chunks
+};
+
+// Sequences per prefix-pass group: their query rows fill the 16 columns of the MFMA.
+int prefix_group(int g) { return std::max(1, 16 / g); }
+
+PrefixLayout prefix_layout(int S, int Hq, int Hkv, int D, int pfx_len, int max_suffix_len,
+                           int partition_size, pa_dtype dtype) {
+  PrefixLayout w{0, 0, 0, 0, 0, 0, 0};
+  // The prefix is cut into chunks (multiples of 64 positions, at least 256 each) when the
+  // groups alone would leave compute units without a prefix-pass workgroup.
+  const long units = (long)Hkv * ((S + prefix_group(Hq / Hkv) - 1) / prefix_group(Hq / Hkv));
+  const long want = std::max(1L, ((long)device_cu_count() + units - 1) / units);
+  const long most = std::max(1L, (long)pfx_len / 256);
+  const long c = std::min(want, most);
+  w.chunk = (int)round_up((size_t)((pfx_len + c - 1) / c), 64);
+  w.chunks = (pfx_len + w.chunk - 1) / w.chunk;
+  const size_t rows = (size_t)S * Hq * w.chunks;
+  w.ml = 0;
+  w.acc = round_up(rows * 2 * sizeof(float), 256);
+  w.part = w.acc + round_up(rows * D * sizeof(float), 256);
+  w.P = partition_size ? partition_size
+                       : pa_default_partition_size(S, Hkv, max_suffix_len, dtype);
+  const int pmax = std::max(1, (max_suffix_len + w.P - 1) / w.P);
+  w.total = w.part + workspace_layout(S, Hq, D, pmax).total;
+  return w;
+}
+
+}  // namespace
+
+extern "C" size_t pa_shared_prefix_workspace_size(int num_seqs, int num_heads, int num_kv_heads,
+                                                  int head_dim, int max_context_len,
+                                                  int prefix_blocks, int block_size,
+                                                  int partition_size, pa_dtype dtype) {
+  if (num_seqs <= 0 || prefix_blocks <= 0) return 0;
+  if (check_shapes(num_heads, num_kv_heads, head_dim, block_size, dtype) != PA_OK) return 0;
+  const long pfx = (long)prefix_blocks * block_size;
+  if (pfx > kMaxPartition || max_context_len < pfx) return 0;
+  if (partition_size != 0 &&
+      (partition_size < 64 || partition_size > kMaxPartition || partition_size % 64))
+    return 0;
+  return prefix_layout(num_seqs, num_heads, num_kv_heads, head_dim, (int)pfx,
+                       max_context_len - (int)pfx, partition_size, dtype).total;
+}
+
+extern "C" pa_status pa_decode_step_shared_prefix(
+    void* out, const void* query, const void* key, const void* value,
+    const int64_t* slot_mapping, const int32_t* block_table, const int32_t* context_lens,
+    void* k_cache, void* v_cache, int num_seqs, int num_heads, int num_kv_heads, int head_dim,
+    int block_size, int max_blocks_per_seq, int num_blocks, int max_context_len,
+    int prefix_blocks, float scale, pa_dtype dtype, int partition_size, void* workspace,
+    size_t workspace_bytes, void* stream, const int32_t* host_context_lens) {
+  pa_status st = check_shapes(num_heads, num_kv_heads, head_dim, block_size, dtype);
+  if (st != PA_OK) return st;
+  if (num_seqs < 0 || max_blocks_per_seq <= 0 || num_blocks <= 0 || max_context_len < 0 ||
+      prefix_blocks < 0)
+    return PA_ERR_INVALID_ARG;
+  if (prefix_blocks == 0)
+    return num_seqs > 0 && (!key || !value || !slot_mapping)
+               ? PA_ERR_INVALID_ARG
+               : run_decode(out, query, block_table, context_lens, k_cache, v_cache, key, value,
+                            slot_mapping, num_seqs, num_heads, num_kv_heads, head_dim, block_size,
+                            max_blocks_per_seq, num_blocks, max_context_len, scale, dtype,
+                            partition_size, workspace, workspace_bytes, stream,
+                            host_context_lens);
+  const long pfx = (long)prefix_blocks * block_size;
+  if (pfx > kMaxPartition) return PA_ERR_UNSUPPORTED;
+  if (prefix_blocks >= max_blocks_per_seq || max_context_len < pfx ||
+      (long)max_context_len > (long)max_blocks_per_seq * block_size)
+    return PA_ERR_INVALID_ARG;
+  if (partition_size != 0 &&
+      (partition_size < 64 || partition_size > kMaxPartition || partition_size % 64))
+    return PA_ERR_INVALID_ARG;
+  if (num_seqs == 0) return PA_OK;
+  if (!out || !query || !block_table || !context_lens || !k_cache || !v_cache)
+    return PA_ERR_INVALID_ARG;
+  if (slot_mapping && (!key || !value)) return PA_ERR_INVALID_ARG;
+  if (!aligned(out, 16) || !aligned(query, 16) || !aligned(k_cache, 16) ||
+      !aligned(v_cache, 16) || !aligned(block_table, 4) || !aligned(context_lens, 4))
+    return PA_ERR_INVALID_ARG;
+  if (host_context_lens)
+    for (int t = 0; t < num_seqs; ++t)
+      if (host_context_lens[t] < pfx) return PA_ERR_INVALID_ARG;
+  const PrefixLayout wl = prefix_layout(num_seqs, num_heads, num_kv_heads, head_dim, (int)pfx,
+                                        max_context_len - (int)pfx, partition_size, dtype);
+  if (!workspace || workspace_bytes < wl.total || !aligned(workspace, 16))
+    return PA_ERR_WORKSPACE;
+  if ((long)num_kv_heads * wl.chunks *
+          ((num_seqs + prefix_group(num_heads / num_kv_heads) - 1) /
+           prefix_group(num_heads / num_kv_heads)) > 0x7FFFFFFFL)
+    return PA_ERR_INVALID_ARG;
+  char* ws = static_cast<char*>(workspace);
+  float* pml = reinterpret_cast<float*>(ws + wl.ml);
+  float* pacc = reinterpret_cast<float*>(ws + wl.acc);
+
+  // prefix pass: every group's rows over positions [0, pfx)
+  pa::DecodeParams a{};
+  a.q = query;
+  a.block_table = block_table;
+  a.context_lens = context_lens;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.S = num_seqs;
+  a.Hq = num_heads;
+  a.Hkv = num_kv_heads;
+  a.g = num_heads / num_kv_heads;
+  a.MB = max_blocks_per_seq;
+  a.tbl_stride = max_blocks_per_seq;
+  a.NB = num_blocks;
+  a.P = wl.chunk;                                // the table window holds one chunk
+  a.Pmax = wl.chunks;
+  a.wave_parts = 0;
+  a.scale_log2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
+  a.v_scale = 1.f;
+  a.k_quant = a.v_quant = 1.f;
+  a.len_off = 0;
+  a.pfx_len = (int)pfx;
+  a.pfx_chunks = wl.chunks;
+  a.grp = prefix_group(a.g);
+  a.pfx_ml = pml;
+  a.pfx_acc = pacc;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t err = dtype == PA_DTYPE_BF16
+                       ? pa::dispatch_prefix<uint16_t>(a, head_dim, block_size, s)
+                       : pa::dispatch_prefix<float>(a, head_dim, block_size, s);
+  if (err != hipSuccess) return PA_ERR_HIP;
+
+  // suffix pass: the decode step over positions [pfx, L), merged with the prefix results
+  const SuffixArgs sfx{(int)pfx, max_blocks_per_seq, wl.chunks, pml, pacc};
+  return run_decode(out, query, block_table + prefix_blocks, context_lens, k_cache, v_cache,
+                    slot_mapping ? key : nullptr, slot_mapping ? value : nullptr, slot_mapping,
+                    num_seqs, num_heads, num_kv_heads, head_dim, block_size,
+                    max_blocks_per_seq - prefix_blocks, num_blocks, max_context_len - (int)pfx,
+                    scale, dtype, wl.P, ws + wl.part, workspace_bytes - wl.part, stream,
+                    host_context_lens, false, 1.f, 1.f, &sfx);
 }
 
 // ---------------------------------------------------------------------------

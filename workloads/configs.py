@@ -304,7 +304,7 @@ def make_workload(*, name: str, context_lens, num_heads: int, num_kv_heads: int,
         new_records=np.asarray(new_records, dtype=np.int64),
         partition_size=partition_size,
         blocks_allocated=int(np.count_nonzero(pool.refcount)),
-        info={"seed": seed},
+        info={"seed": seed, "shared_prefix_len": int(shared_prefix_len)},
         cow_pairs=np.asarray(cow_pairs, dtype=np.int64).reshape(-1, 2),
         cow_records=np.nonzero(src >= 0)[0].astype(np.int64),
     )
