@@ -895,26 +895,22 @@ def main() -> int:
     step_name = "pa_decode_step: scatter of the new tokens + paged decode, one launch"
     if pfx_len and not args.plain_step:
         pfx_blocks = pfx_len // w.block_size
-        need_p = pk.shared_prefix_workspace_size(w.num_seqs, w.num_heads, w.num_kv_heads,
-                                                 w.head_dim, w.max_context_len, pfx_blocks,
-                                                 w.block_size, part, tdt)
-        ws_p = torch.empty(need_p, dtype=torch.uint8, device=dev)
         hl = host_lens if args.order == "host" else None
         shared = [pk.prepare_decode_step_shared_prefix(
             query, key_new, val_new, slot_new, table, lens, kc, vc, w.scale,
             prefix_blocks=pfx_blocks, max_context_len=w.max_context_len, out=out,
-            workspace=ws_p, partition_size=part, host_context_lens=hl) for kc, vc in pools]
+            host_context_lens=hl) for kc, vc in pools]
         run_fused(R, W, shared)
         wall_p, ev_p = timed(run_fused, R, K, shared)
         log(f"cold shared-prefix step: {wall_p / K * 1e6:.1f} us/step wall, "
-            f"{ev_p / K * 1e6:.1f} us/launch pair (events)")
+            f"{ev_p / K * 1e6:.1f} us/launch (events)")
         plain = {"step": "pa_decode_step", "us_per_step": round(wall / K * 1e6, 2),
                  "launch_us_events": round(ev_s / K * 1e6, 2),
                  "value": round(kv_unique / (wall / K) / 1e9, 2)}
         wall, ev_s = wall_p, ev_p
-        step_name = (f"pa_decode_step_shared_prefix ({pfx_blocks} shared blocks): the prefix "
-                     "pass once per group of sequences, then the scatter of the new tokens + "
-                     "paged decode of the private suffixes with the log-sum-exp merge")
+        step_name = (f"pa_decode_step_shared_prefix ({pfx_blocks} shared blocks), one launch: "
+                     "per group of sequences the shared prefix read once, the scatter of the "
+                     "new tokens + paged decode of the private suffixes, log-sum-exp merge")
 
     ms_step = wall / K * 1e3
     launch_avg_s = ev_s / K
@@ -972,8 +968,8 @@ def main() -> int:
                                       "value": round(kv_unique / (wall3 / K) / 1e9, 2)},
         "warm": warm,
         "plain_step": plain,
-        "roofline": {"kernel": (f"pa_decode_step_shared_prefix: prefix pass + {kernels}"
-                                if plain else f"pa_decode_step: {kernels}"),
+        "roofline": {"kernel": ("pa_decode_step_shared_prefix: paged_decode_kernel "
+                                "(shared-prefix mode)" if plain else f"pa_decode_step: {kernels}"),
                      "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic,

@@ -206,26 +206,25 @@ pa_status pa_decode_step(void* out, const void* query, const void* key, const vo
  * the first prefix_blocks entries of every block-table row name the same physical
  * blocks (one system prompt stored once and shared by reference: page "vLLM core
  * inference engine", section 2.2; prefix caching, page "vLLM core features", section
- * 4.6).  The result (out and both caches) is that of pa_decode_step; the attention over
- * the shared positions [0, P), P = prefix_blocks * block_size, is computed once per
- * group of sequences (their query heads side by side in one matrix product), so each
- * prefix block is read once per group rather than once per sequence.  The private
- * positions [P, L) go through the paged decode, and the two parts of each row are
- * combined with a log-sum-exp merge.
+ * 4.6).  The result (out and both caches) is that of pa_decode_step.  One launch; a
+ * workgroup takes a group of 1, 2 or 4 consecutive sequences (their query heads side by
+ * side fill at most the 16 columns of one matrix-core operand): half of its waves read
+ * the shared positions [0, P), P = prefix_blocks * block_size, once for the whole group,
+ * the other half the group's private positions [P, L), and the two parts of each row are
+ * combined with a log-sum-exp merge.  Each prefix block is read once per group instead of
+ * once per sequence.  Nothing is allocated and no workspace is needed.
  *
- *   prefix_blocks  shared leading blocks (0: exactly pa_decode_step); P <= 8192
- *                  tokens (else PA_ERR_UNSUPPORTED) and prefix_blocks <
- *                  max_blocks_per_seq
+ *   prefix_blocks  shared leading blocks, >= 1 and < max_blocks_per_seq
  *   slot_mapping   as in pa_decode_step, or NULL for decode attention alone (no token
  *                  appended; key and value are then ignored)
- *   workspace      pa_shared_prefix_workspace_size(...) bytes, 16-byte aligned; it
- *                  holds each row's prefix result and the suffix partitions
  *   dtype          PA_DTYPE_BF16 or PA_DTYPE_F32
- *   other arguments as in pa_decode_step; partition_size applies to the private
- *   suffixes (0: pa_default_partition_size of their longest length)
+ *   other arguments as in pa_decode_step
+ * P and the longest suffix, max_context_len - P, must each be at most 8192 tokens
+ * (PA_ERR_UNSUPPORTED otherwise: use pa_decode_step).
  * Preconditions (device side): every context_lens[s] >= P, and > P when a token is
  * appended for s (a new token goes to a private block).  With host_context_lens, a
- * length below P is rejected (PA_ERR_INVALID_ARG) before any launch.
+ * length below P or above max_context_len is rejected (PA_ERR_INVALID_ARG) before any
+ * launch.
  */
 pa_status pa_decode_step_shared_prefix(void* out, const void* query, const void* key,
                                        const void* value, const int64_t* slot_mapping,
@@ -234,14 +233,8 @@ pa_status pa_decode_step_shared_prefix(void* out, const void* query, const void*
                                        int num_heads, int num_kv_heads, int head_dim,
                                        int block_size, int max_blocks_per_seq, int num_blocks,
                                        int max_context_len, int prefix_blocks, float scale,
-                                       pa_dtype dtype, int partition_size, void* workspace,
-                                       size_t workspace_bytes, void* stream,
+                                       pa_dtype dtype, void* stream,
                                        const int32_t* host_context_lens);
-
-/* Workspace bytes of pa_decode_step_shared_prefix (0 for arguments it would reject). */
-size_t pa_shared_prefix_workspace_size(int num_seqs, int num_heads, int num_kv_heads,
-                                       int head_dim, int max_context_len, int prefix_blocks,
-                                       int block_size, int partition_size, pa_dtype dtype);
 
 /*
  * pa_decode_step for callers that cannot allocate device memory: code under

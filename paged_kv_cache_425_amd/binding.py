@@ -60,10 +60,7 @@ def load_library() -> ctypes.CDLL:
     lib.pa_decode_step_fp8.argtypes = [vp] * 9 + [i32] * 8 + [f32] * 3 + [i32, i32, vp, sz, vp,
                                                                           vp]
     lib.pa_decode_step_shared_prefix.restype = i32
-    lib.pa_decode_step_shared_prefix.argtypes = [vp] * 9 + [i32] * 9 + [f32, i32, i32, vp, sz,
-                                                                          vp, vp]
-    lib.pa_shared_prefix_workspace_size.restype = sz
-    lib.pa_shared_prefix_workspace_size.argtypes = [i32] * 9
+    lib.pa_decode_step_shared_prefix.argtypes = [vp] * 9 + [i32] * 9 + [f32, i32, vp, vp]
     lib.pa_read_probe.restype = i32
     lib.pa_read_probe.argtypes = [vp, vp, i32, i32, i32, i32, vp, vp]
     lib.pa_decode_step_noalloc.restype = i32
@@ -305,52 +302,9 @@ def decode_step_noalloc(query: torch.Tensor, key: torch.Tensor, value: torch.Ten
     return out
 
 
-def shared_prefix_workspace_size(num_seqs: int, num_heads: int, num_kv_heads: int,
-                                 head_dim: int, max_context_len: int, prefix_blocks: int,
-                                 block_size: int, partition_size: int = 0,
-                                 dtype: torch.dtype = torch.bfloat16) -> int:
-    return int(load_library().pa_shared_prefix_workspace_size(
-        num_seqs, num_heads, num_kv_heads, head_dim, max_context_len, prefix_blocks, block_size,
-        partition_size, _DTYPE_CODES[dtype]))
-
-
-def prepare_decode_step_shared_prefix(query, key, value, slot_mapping, block_table,
-                                      context_lens, k_cache, v_cache, scale, *,
-                                      prefix_blocks: int, max_context_len: int, out,
-                                      workspace, partition_size: int = 0, stream=None,
-                                      host_context_lens=None) -> PreparedCall:
-    """Check the arguments of decode_step_shared_prefix once (one checked call) and return
-    a re-launchable call."""
-    decode_step_shared_prefix(query, key, value, slot_mapping, block_table, context_lens,
-                              k_cache, v_cache, scale, prefix_blocks=prefix_blocks,
-                              max_context_len=max_context_len, out=out,
-                              partition_size=partition_size, workspace=workspace,
-                              stream=stream, host_context_lens=host_context_lens)
-    NB, Hkv, D, BS = _cache_dims(k_cache, v_cache)
-    S, Hq, _ = query.shape
-    hl, hold = _host_lens(host_context_lens, S)
-    args = (_ptr(out), _ptr(query), _ptr(key), _ptr(value), _ptr(slot_mapping),
-            _ptr(block_table), _ptr(context_lens), _ptr(k_cache), _ptr(v_cache), S, Hq, Hkv, D,
-            BS, block_table.shape[1], NB, int(max_context_len), int(prefix_blocks),
-            float(scale), _dtype_code(query), int(partition_size), _ptr(workspace),
-            workspace.numel() * workspace.element_size(), _stream(query.device, stream), hl)
-    return PreparedCall(load_library().pa_decode_step_shared_prefix, args,
-                        "pa_decode_step_shared_prefix",
-                        (query, key, value, slot_mapping, block_table, context_lens, k_cache,
-                         v_cache, out, workspace, hold))
-
-
-def decode_step_shared_prefix(query: torch.Tensor, key, value, slot_mapping,
-                              block_table: torch.Tensor, context_lens: torch.Tensor,
-                              k_cache: torch.Tensor, v_cache: torch.Tensor, scale: float, *,
-                              prefix_blocks: int, max_context_len: int,
-                              out: torch.Tensor | None = None, partition_size: int = 0,
-                              workspace: torch.Tensor | None = None, stream=None,
-                              host_context_lens=None) -> torch.Tensor:
-    """The fused decode step when every sequence's first `prefix_blocks` table entries
-    name the same shared blocks (pa_decode_step_shared_prefix).  key, value and
-    slot_mapping may all be None: decode attention alone."""
-    lib = load_library()
+def _shared_prefix_args(query, key, value, slot_mapping, block_table, context_lens, k_cache,
+                        v_cache, scale, prefix_blocks, max_context_len, out, stream,
+                        host_context_lens):
     dev = query.device
     _require(query, "query", dev)
     NB, Hkv, D, BS = _cache_dims(k_cache, v_cache)
@@ -379,24 +333,48 @@ def decode_step_shared_prefix(query: torch.Tensor, key, value, slot_mapping,
     _require(out, "out", dev, query.dtype)
     if tuple(out.shape) != tuple(query.shape):
         raise ValueError("out must have the shape of query")
-    need = shared_prefix_workspace_size(S, Hq, Hkv, D, max_context_len, prefix_blocks, BS,
-                                        partition_size, query.dtype)
-    if need and workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
-        made.append(workspace)
-    if workspace is not None:
-        _require(workspace, "workspace", dev)
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    hl, _hold = _host_lens(host_context_lens, S)
-    st = lib.pa_decode_step_shared_prefix(
-        _ptr(out), _ptr(query), _ptr(key), _ptr(value), _ptr(slot_mapping), _ptr(block_table),
-        _ptr(context_lens), _ptr(k_cache), _ptr(v_cache), S, Hq, Hkv, D, BS,
-        block_table.shape[1], NB, int(max_context_len), int(prefix_blocks), float(scale),
-        _dtype_code(query), int(partition_size), _ptr(workspace), ws_bytes,
-        _stream(dev, stream), hl)
-    _check(st, "pa_decode_step_shared_prefix")
+    hl, hold = _host_lens(host_context_lens, S)
+    args = (_ptr(out), _ptr(query), _ptr(key), _ptr(value), _ptr(slot_mapping),
+            _ptr(block_table), _ptr(context_lens), _ptr(k_cache), _ptr(v_cache), S, Hq, Hkv, D,
+            BS, block_table.shape[1], NB, int(max_context_len), int(prefix_blocks),
+            float(scale), _dtype_code(query), _stream(dev, stream), hl)
+    keep = (query, key, value, slot_mapping, block_table, context_lens, k_cache, v_cache, out,
+            hold)
+    return args, out, keep, made
+
+
+def decode_step_shared_prefix(query: torch.Tensor, key, value, slot_mapping,
+                              block_table: torch.Tensor, context_lens: torch.Tensor,
+                              k_cache: torch.Tensor, v_cache: torch.Tensor, scale: float, *,
+                              prefix_blocks: int, max_context_len: int,
+                              out: torch.Tensor | None = None, stream=None,
+                              host_context_lens=None) -> torch.Tensor:
+    """The fused decode step when every sequence's first `prefix_blocks` table entries
+    name the same shared blocks (pa_decode_step_shared_prefix).  key, value and
+    slot_mapping may all be None: decode attention alone."""
+    args, out, _, made = _shared_prefix_args(query, key, value, slot_mapping, block_table,
+                                             context_lens, k_cache, v_cache, scale,
+                                             prefix_blocks, max_context_len, out, stream,
+                                             host_context_lens)
+    _check(load_library().pa_decode_step_shared_prefix(*args), "pa_decode_step_shared_prefix")
     _record(stream, made)
     return out
+
+
+def prepare_decode_step_shared_prefix(query, key, value, slot_mapping, block_table,
+                                      context_lens, k_cache, v_cache, scale, *,
+                                      prefix_blocks: int, max_context_len: int, out,
+                                      stream=None, host_context_lens=None) -> PreparedCall:
+    """Check the arguments of decode_step_shared_prefix once and return a re-launchable
+    call (it runs once)."""
+    args, out, keep, _ = _shared_prefix_args(query, key, value, slot_mapping, block_table,
+                                             context_lens, k_cache, v_cache, scale,
+                                             prefix_blocks, max_context_len, out, stream,
+                                             host_context_lens)
+    call = PreparedCall(load_library().pa_decode_step_shared_prefix, args,
+                        "pa_decode_step_shared_prefix", keep)
+    call()
+    return call
 
 
 def reshape_and_cache(key: torch.Tensor, value: torch.Tensor, slot_mapping: torch.Tensor,

@@ -94,23 +94,14 @@ struct DecodeParams {
   const void* new_v;
   const int64_t* new_slot;
   int S, Hq, Hkv, g, MB, NB, P, Pmax;
-  int tbl_stride;          // entries per block-table row (MB, or more past a skipped prefix)
   int wave_parts;          // partition mode: 1 = each wave owns one partition of NW in a row
   float scale_log2;        // scale * log2(e) (* k_scale for FP8 K): base-2 logits
   float v_scale;           // output multiplier: 1, or the FP8 V scale
   float k_quant, v_quant;  // FP8 fused step: the scales the new token is quantised with
-  // Shared prefix (pa_decode_step_shared_prefix).  Prefix pass: every unit is a group of
-  // `grp` sequences over one chunk of P positions of the prefix [0, pfx_len), and
-  // pfx_ml / pfx_acc receive each (sequence, query head) row's (max, sum, unnormalised
-  // output) over each of the pfx_chunks chunks.  Suffix pass: block_table points past
-  // the prefix's entries, `len_off` = pfx_len is taken off every context length, and each
-  // output merges the row's prefix results.
-  int len_off;
+  // Shared-prefix mode (pa_decode_step_shared_prefix): every sequence's first pfx_len
+  // positions are the same blocks; a workgroup takes `grp` consecutive sequences.
   int pfx_len;
-  int pfx_chunks;
   int grp;
-  float* pfx_ml;           // [S][Hq][pfx_chunks][2]
-  float* pfx_acc;          // [S][Hq][pfx_chunks][D]
 };
 
 // A context length clamped to what the launch can address.
@@ -121,33 +112,12 @@ __device__ __forceinline__ int clamp_len(const DecodeParams& a, int L, int BS) {
 }
 
 __device__ __forceinline__ int clamped_len(const DecodeParams& a, int s, int BS) {
-  return clamp_len(a, a.context_lens[s] - a.len_off, BS);
+  return clamp_len(a, a.context_lens[s], BS);
 }
 
-// Final output of one channel d of row `row` (sequence * Hq + query head) whose tokens gave
-// the running max M (log2 units), weight sum den and unnormalised value num: num / den, or
-// -- after a shared prefix -- the log-sum-exp merge with the (max, sum, value) of each of
-// the prefix's chunks for that row.  Nothing seen at all (M = -inf everywhere) gives 0.
-template <int D>
-__device__ __forceinline__ float finish_row(const DecodeParams& a, size_t row, int d, float M,
-                                            float den, float num) {
-  if (a.pfx_ml != nullptr) {
-    const int C = a.pfx_chunks;
-    const float* ml = a.pfx_ml + row * C * 2;
-    const float* ac = a.pfx_acc + row * C * D + d;
-    float Mx = M;
-    for (int c = 0; c < C; ++c) Mx = fmaxf(Mx, ml[2 * c]);
-    if (Mx == kNegInf) return 0.f;
-    const float fs = exp2_fast(M - Mx);                                 // 2^-inf = 0
-    num *= fs;
-    den *= fs;
-    for (int c = 0; c < C; ++c) {
-      const float f = exp2_fast(ml[2 * c] - Mx);
-      num += f * ac[(size_t)c * D];
-      den += f * ml[2 * c + 1];
-    }
-    return num / den;
-  }
+// Final output of one channel of a row whose tokens gave the running max M (log2 units),
+// weight sum den and unnormalised value num; nothing seen (M = -inf) gives 0.
+__device__ __forceinline__ float finish_row(float M, float den, float num) {
   return (M == kNegInf || den == 0.f) ? 0.f : num / den;
 }
 
@@ -228,11 +198,14 @@ using OrderArg = typename std::conditional<PAIRED, PairOrder, NoOrder>::type;
 // (ties broken by index).  Used when each sequence is one partition;
 // otherwise a workgroup is one (kv head, sequence, partition).
 //
-// Prefix pass (PREFIX): a workgroup takes one group of a.grp consecutive sequences that
-// share the first a.pfx_len positions (the same physical blocks) and computes, for all of
-// them at once, each (sequence, query head) row's attention statistics over that prefix:
-// the group's g-head query rows fill the columns of the MFMA operand (grp * g <= 16), so
-// each prefix K/V byte is read once per group instead of once per sequence.
+// Shared-prefix mode (PREFIX, NW = 8): a workgroup takes one group of a.grp (1, 2 or 4)
+// consecutive sequences that share their first a.pfx_len positions (the same physical
+// blocks).  The first waves stream the shared prefix once for the whole group: the group's
+// g-head query rows fill the columns of the MFMA operand (grp * g <= 16), so each prefix
+// K/V byte is read once per group instead of once per sequence.  The other waves stream
+// the sequences' private suffixes; the split follows the units' steps.  Each unit's waves
+// are merged lane by lane in registers, and the prefix and suffix results of each row are
+// combined with a log-sum-exp merge before the output is written.
 template <typename T, typename C, int D, int BS, int NW, int PIPE, bool PAIRED,
           bool PREFIX = false>
 __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(PA_DECODE_OCC)))
@@ -259,14 +232,17 @@ paged_decode_kernel(const DecodeParams a, const OrderArg<PAIRED> ord) {
     __builtin_amdgcn_sched_barrier(0);
   }
 
+  static_assert(!PREFIX || NW == 8, "the shared-prefix mode splits 8 waves 4 + 4");
+  constexpr int kNewUnits = PREFIX ? 4 : 2;                 // new tokens staged in LDS
   extern __shared__ __align__(16) unsigned char smem[];
   int* ctrl = reinterpret_cast<int*>(smem);
   T* newkv = reinterpret_cast<T*>(smem + 64);                // [unit][K, V][D]
   const int win = a.P / BS;                                 // table entries per window
   const int lens_words = PAIRED ? (a.S + 3) / 4 * 4 : 0;
-  int* lens = reinterpret_cast<int*>(smem + 64 + 4 * D * sizeof(T));
+  int* lens = reinterpret_cast<int*>(smem + 64 + 2 * kNewUnits * D * sizeof(T));
   int* tbl = lens + lens_words;
-  const int tbl_words = ((PAIRED ? 2 : (!PREFIX && a.wave_parts ? NW : 1)) * win + 3) / 4 * 4;
+  const int tbl_words =
+      ((PAIRED ? 2 : (PREFIX ? 1 + a.grp : (a.wave_parts ? NW : 1))) * win + 3) / 4 * 4;
   float* red = reinterpret_cast<float*>(tbl + tbl_words);
 
   const int lane = threadIdx.x & 63;
@@ -285,7 +261,9 @@ paged_decode_kernel(const DecodeParams a, const OrderArg<PAIRED> ord) {
   int s, tok0 = 0, tok1 = 0, lw, nw, p = 0, nparts = 1, uidx = 0;
   int p0 = 0, seqL = 0;      // partition mode: the workgroup's first partition, the length
   int sA = 0, sB = -1, nA = NW;                             // PAIRED: the two sequences
-  int gseq = 1;                                             // PREFIX: sequences in the group
+  int gseq = 1, s0 = 0;                                     // PREFIX: the group's sequences
+  bool pfx_wave = false;                                    // PREFIX: a wave of the prefix
+  int part0 = 0;                                            // PREFIX: first wave of the unit
   int LA = 0, LB = 0;                                       // PAIRED: their lengths
   bool planned = false;                                     // PAIRED: pairs from the host
   bool onA = true;
@@ -303,8 +281,8 @@ paged_decode_kernel(const DecodeParams a, const OrderArg<PAIRED> ord) {
       nA = sB < 0 ? NW : min(max((int)(ey >> 24), 1), NW - 1);
       // the device lengths: both loads go out now and are first used after the
       // prologue's other loads (sA stands in for a missing second sequence)
-      LA = a.context_lens[sA] - a.len_off;
-      LB = a.context_lens[sB >= 0 ? sB : sA] - a.len_off;
+      LA = a.context_lens[sA];
+      LB = a.context_lens[sB >= 0 ? sB : sA];
     } else {
       // Sort keys: key_t = (L_t << 10) | (1023 - t), unique per sequence and ordered by
       // length, then by index for equal lengths (L_t <= P <= 8192 here, and S <= 512, so the
@@ -355,17 +333,49 @@ paged_decode_kernel(const DecodeParams a, const OrderArg<PAIRED> ord) {
     nw = onA ? nA : NW - nA;
     tblw = tbl + (onA ? 0 : win);
   } else if constexpr (PREFIX) {
-    // group (fastest) and chunk p of P positions; the group's first sequence's table row
-    // holds the shared prefix's blocks
-    const int ngroups = (a.S + a.grp - 1) / a.grp;
-    s = (id % ngroups) * a.grp;
-    p = p0 = id / ngroups;
-    gseq = min(a.grp, a.S - s);
-    tok0 = p * a.P;
-    tok1 = min(a.pfx_len, tok0 + a.P);
-    seqL = a.pfx_len;
-    lw = wave;
-    nw = NW;
+    // group id: sequences [s0, s0 + gseq); the first one's table row holds the prefix.
+    // The waves are split between the prefix (unit 0) and the group's private suffixes
+    // (units 1 .. gseq) in proportion to their steps -- the prefix's counted at half, as
+    // its blocks come from the L2 once the first group has read them -- with at least one
+    // and at most NW / 2 waves per unit (greedy: one more wave at a time to the unit with
+    // the most steps per wave).  Every wave computes the same split.
+    s0 = id * a.grp;
+    gseq = min(a.grp, a.S - s0);
+    const int cap = min(a.P / BS, a.MB - a.pfx_len / BS) * BS;   // suffix positions staged
+    int ust[5], uwv[5];
+    ust[0] = ((a.pfx_len + kStep - 1) / kStep + 1) / 2;
+#pragma unroll
+    for (int u = 1; u < 5; ++u) {
+      const int Lu = u <= gseq ? min(max(a.context_lens[s0 + u - 1] - a.pfx_len, 0), cap) : 0;
+      ust[u] = (Lu + kStep - 1) / kStep;
+    }
+    const int nunit = 1 + gseq;
+#pragma unroll
+    for (int u = 0; u < 5; ++u) uwv[u] = u < nunit ? 1 : 0;
+    for (int k = nunit; k < NW; ++k) {
+      int best = 0;
+#pragma unroll
+      for (int u = 1; u < 5; ++u)
+        if (u < nunit && uwv[u] < NW / 2 &&
+            (uwv[best] >= NW / 2 || ust[u] * uwv[best] > ust[best] * uwv[u]))
+          best = u;
+      uwv[best] += 1;
+    }
+    int u = 0, b = 0;
+#pragma unroll
+    for (int v = 0; v < 4; ++v)
+      if (u < nunit - 1 && wave >= b + uwv[u]) {
+        b += uwv[u];
+        u += 1;
+      }
+    pfx_wave = u == 0;
+    uidx = pfx_wave ? kNewUnits : u - 1;                    // the prefix has no new token
+    lw = __builtin_amdgcn_readfirstlane(wave - b);
+    nw = __builtin_amdgcn_readfirstlane(uwv[u]);
+    part0 = __builtin_amdgcn_readfirstlane(b);
+    s = pfx_wave ? s0 : s0 + uidx;
+    // prefix positions [0, pfx_len), or suffix positions [0, L - pfx_len)
+    tok1 = pfx_wave ? a.pfx_len : min(max(a.context_lens[s] - a.pfx_len, 0), cap);
   } else if (a.wave_parts) {
     // NW consecutive partitions, one per wave: the workgroup stages one table window
     // for all of them and each wave streams its partition alone and writes its own
@@ -396,12 +406,12 @@ paged_decode_kernel(const DecodeParams a, const OrderArg<PAIRED> ord) {
   }
 
   const int g = a.g;
-  // MFMA columns in use: the g heads (bf16: plus their lo copies), or in the prefix pass
-  // the g heads of each of the group's sequences
-  const int rows = PREFIX ? gseq * g : (kBf16 ? 2 * g : g);
+  // MFMA columns in use: the g heads (bf16: plus their lo copies), or for the prefix's
+  // waves the g heads of each of the group's sequences
+  const int rows = pfx_wave ? gseq * g : (kBf16 ? 2 * g : g);
   const int head = kvh * g + (n % g);
   const bool row_live = n < rows;
-  const int row_seq = PREFIX ? s + (row_live ? n / g : 0) : s;   // sequence of column n
+  const int row_seq = pfx_wave ? s + (row_live ? n / g : 0) : s;   // sequence of column n
 
   // Every load of the prologue is issued before the first wait on any of them: the
   // query operand, the new tokens and the block-table windows land in one round trip.
@@ -422,7 +432,8 @@ paged_decode_kernel(const DecodeParams a, const OrderArg<PAIRED> ord) {
   // loads go to registers first (lanes past the end re-read the last entry, so no load
   // sits in a divergent branch) and are written to LDS once the new tokens' loads are
   // out as well.  kPer entries per thread cover two windows of the longest partition.
-  constexpr int kPer = ((PAIRED ? 2 : 1) * (kMaxPartition / BS) + kThreads - 1) / kThreads;
+  constexpr int kPer =
+      ((PAIRED ? 2 : (PREFIX ? 5 : 1)) * (kMaxPartition / BS) + kThreads - 1) / kThreads;
   auto stage_load = [&](int count, unsigned (&b)[kPer], auto&& where) {
     const int iters = min(kPer, (count + kThreads - 1) / kThreads);       // uniform
 #pragma unroll
@@ -431,7 +442,7 @@ paged_decode_kernel(const DecodeParams a, const OrderArg<PAIRED> ord) {
         const int i = min(k * kThreads + (int)threadIdx.x, count - 1);
         int row = 0, col = 0, dst = 0;
         where(i, row, col, dst);
-        b[k] = static_cast<unsigned>(a.block_table[(size_t)row * a.tbl_stride + col]);
+        b[k] = static_cast<unsigned>(a.block_table[(size_t)row * a.MB + col]);
       }
     }
   };
@@ -458,7 +469,21 @@ paged_decode_kernel(const DecodeParams a, const OrderArg<PAIRED> ord) {
     col = p0 * win + i;
     dst = i;
   };
-  if constexpr (PAIRED) {
+  // shared-prefix mode: window 0 = the prefix's blocks (row s0), window 1 + u = the
+  // first cS suffix blocks of sequence s0 + u (whatever its length: entries past it are
+  // in the row and never used)
+  const int cP = PREFIX ? a.pfx_len / BS : 0;
+  const int cS = PREFIX ? min(win, a.MB - cP) : 1;             // >= 1: the host keeps cP < MB
+  auto where_grp = [&](int i, int& row, int& col, int& dst) {
+    const int k = i - cP;
+    const int u = k < 0 ? 0 : k / cS;
+    row = s0 + (k < 0 ? 0 : u);
+    col = k < 0 ? i : cP + k % cS;
+    dst = k < 0 ? i : (1 + u) * win + k % cS;
+  };
+  if constexpr (PREFIX) {
+    stage_load(cP + gseq * cS, tb, where_grp);
+  } else if constexpr (PAIRED) {
     // the host's block counts for a planned launch, else the lengths ranked above
     const uint32_t ey = static_cast<uint32_t>(plan_entry >> 32);
     cA = min(planned ? (int)(ey & 0xFFFu) : (LA + BS - 1) / BS, win);
@@ -485,7 +510,8 @@ paged_decode_kernel(const DecodeParams a, const OrderArg<PAIRED> ord) {
   constexpr int kCh = D / kSx;                              // 16-byte new-token chunks per head
   const bool fused = a.new_slot != nullptr;
   const bool last_part = nparts - 1 < p0 + (a.wave_parts ? NW : 1);    // holds the last
-  const int nun_new = !fused ? 0 : (PAIRED ? (sB >= 0 ? 2 : 1) : (last_part ? 1 : 0));
+  const int nun_new =
+      !fused ? 0 : (PAIRED ? (sB >= 0 ? 2 : 1) : (PREFIX ? gseq : (last_part ? 1 : 0)));
   u32x4 new_val = {0u, 0u, 0u, 0u};
   int64_t new_slot = -1;
   int new_u = 0;
@@ -494,7 +520,7 @@ paged_decode_kernel(const DecodeParams a, const OrderArg<PAIRED> ord) {
   const bool has_new = (int)threadIdx.x < nun_new * 2 * kCh;
   if (has_new) {
     new_u = threadIdx.x / (2 * kCh);
-    const int su = PAIRED ? (new_u ? sB : sA) : s;
+    const int su = PAIRED ? (new_u ? sB : sA) : (PREFIX ? s0 + new_u : s);
     const size_t src = ((size_t)su * a.Hkv + kvh) * D + (size_t)new_cc * kSx;
     new_val = load16(static_cast<const T*>(new_is_v ? a.new_v : a.new_k) + src);
     new_slot = a.new_slot[su];
@@ -520,6 +546,10 @@ paged_decode_kernel(const DecodeParams a, const OrderArg<PAIRED> ord) {
       }
     }
     tok1 = __builtin_amdgcn_readfirstlane(onA ? LA : LB);
+  } else if constexpr (PREFIX) {
+    stage_store(cP + gseq * cS, tb, where_grp);
+    tok1 = __builtin_amdgcn_readfirstlane(tok1);
+    if (!pfx_wave) tblw = tbl + (1 + uidx) * win;
   } else {
     stage_store(nblk, tb, where_part);
   }
@@ -554,7 +584,7 @@ paged_decode_kernel(const DecodeParams a, const OrderArg<PAIRED> ord) {
 
   // position this wave takes from LDS and writes back (-1: none)
   int lm1 = -1;
-  if (fused && uidx < nun_new && tok1 > tok0 && (PAIRED || p == nparts - 1)) {
+  if (fused && uidx < nun_new && tok1 > tok0 && (PAIRED || PREFIX || p == nparts - 1)) {
     const int64_t sl = a.new_slot[s];
     if (sl >= 0 && sl < nslots && sl == slot_of(tblw, tok0, tok1 - 1)) lm1 = tok1 - 1;
   }
@@ -562,9 +592,12 @@ paged_decode_kernel(const DecodeParams a, const OrderArg<PAIRED> ord) {
 
   // a new slot that is not where position L - 1 is read from: store it here
   if (new_slot >= 0 && new_slot < nslots) {
-    const int Lu = PAIRED ? (new_u ? LB : LA) : seqL;
+    int Lu = PAIRED ? (new_u ? LB : LA) : seqL;
+    if constexpr (PREFIX) Lu = min(max(a.context_lens[s0 + new_u] - a.pfx_len, 0), cS * BS);
     const int64_t loc =
-        Lu > 0 ? slot_of(PAIRED ? tbl + new_u * win : tbl, PAIRED ? 0 : p0 * a.P, Lu - 1) : -1;
+        Lu > 0 ? slot_of(PAIRED ? tbl + new_u * win : (PREFIX ? tbl + (1 + new_u) * win : tbl),
+                         (PAIRED || PREFIX) ? 0 : p0 * a.P, Lu - 1)
+               : -1;
     if (new_slot != loc && kFp8) {
       uint8_t* kcw = static_cast<uint8_t*>(const_cast<void*>(a.k_cache));
       uint8_t* vcw = static_cast<uint8_t*>(const_cast<void*>(a.v_cache));
@@ -844,38 +877,29 @@ paged_decode_kernel(const DecodeParams a, const OrderArg<PAIRED> ord) {
           acc[sl] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
               e4m3x8_to_bf16x8(b.v[sl][2 * h], b.v[sl][2 * h + 1]), pop, acc[sl], 0, 0, 0);
       }
-    } else if constexpr (kBf16 && PREFIX) {
-      // every column is a real row: the hi and lo weights go through two MFMAs into one
-      // accumulator
-      bf16x8 ph, pl;
-#pragma unroll
-      for (int v = 0; v < 8; ++v) {
-        const __bf16 hi = f32_to_bf16(pw[v]);
-        const __bf16 lo = f32_to_bf16(pw[v] - bf16_to_f32(hi));
-        ph[v] = row_live ? hi : f32_to_bf16(0.f);
-        pl[v] = row_live ? lo : f32_to_bf16(0.f);
-      }
-#pragma unroll
-      for (int sl = 0; sl < kNs; ++sl) {
-        acc[sl] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, b.v[sl]), ph,
-                                                          acc[sl], 0, 0, 0);
-        acc[sl] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, b.v[sl]), pl,
-                                                          acc[sl], 0, 0, 0);
-      }
     } else if constexpr (kBf16) {
-      const bool is_hi = n < g;
-      const bool is_lo = !is_hi && n < rows;
-      bf16x8 pop;
+      // Rows [0, g) carry the hi weights and rows [g, 2g) the lo weights in one MFMA; a
+      // wave of the shared prefix uses every column for a real row, so its hi and lo
+      // weights go through two MFMAs into one accumulator.
+      const bool two = PREFIX && pfx_wave;
+      const bool is_hi = two ? row_live : n < g;
+      const bool is_lo = !two && !is_hi && n < rows;
+      bf16x8 pop, plo;
 #pragma unroll
       for (int v = 0; v < 8; ++v) {
         const __bf16 hi = f32_to_bf16(pw[v]);
         const __bf16 lo = f32_to_bf16(pw[v] - bf16_to_f32(hi));
         pop[v] = is_hi ? hi : (is_lo ? lo : f32_to_bf16(0.f));
+        plo[v] = (two && row_live) ? lo : f32_to_bf16(0.f);
       }
 #pragma unroll
-      for (int sl = 0; sl < kNs; ++sl)
+      for (int sl = 0; sl < kNs; ++sl) {
         acc[sl] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, b.v[sl]), pop,
                                                           acc[sl], 0, 0, 0);
+        if (two)
+          acc[sl] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, b.v[sl]),
+                                                            plo, acc[sl], 0, 0, 0);
+      }
     } else {
 #pragma unroll
       for (int sl = 0; sl < kNs; ++sl)
@@ -916,7 +940,7 @@ paged_decode_kernel(const DecodeParams a, const OrderArg<PAIRED> ord) {
   }
 
   // ---- merge the waves of the workgroup --------------------------------------------
-  if constexpr ((kBf16 || kFp8) && !PREFIX) {
+  if ((kBf16 || kFp8) && !pfx_wave) {
     // add the lo rows [g, 2g) into the hi rows [0, g)
 #pragma unroll
     for (int sl = 0; sl < kNs; ++sl)
@@ -926,54 +950,61 @@ paged_decode_kernel(const DecodeParams a, const OrderArg<PAIRED> ord) {
   float lsum = sum_xor16(l_run);
   lsum = sum_xor32(lsum);
   if constexpr (PREFIX) {
-    // Tree merge of the waves, lane by lane: lane (n, j) of every wave holds column n's
-    // max, sum and channels 16 sl + 4 j .. + 3, so half of the remaining waves hand their
-    // registers to the other half through LDS until wave 0 holds the workgroup's result.
+    // Lane (n, j) of every wave holds column n's max and sum and its channels
+    // 16 sl + 4 j .. + 3, so waves merge lane by lane.  Tree merge within each unit (the
+    // prefix's waves, each suffix's): in round st the waves at odd multiples of st within
+    // their unit hand their registers through LDS (slot wave / 2; never two at once) to the
+    // wave st below.
     constexpr int kLane = D / 4 + 2;                         // floats per lane
     float* xb = red;                                         // [NW / 2][kLane][64]
-    for (int half = NW / 2; half >= 1; half /= 2) {
-      if (wave >= half && wave < 2 * half) {
-        float* dst = xb + (size_t)(wave - half) * kLane * 64 + lane;
-        dst[0] = m_run;
-        dst[64] = lsum;
+    const int rel = wave - part0;
+    auto put = [&](int slot) {
+      float* dst = xb + (size_t)slot * kLane * 64 + lane;
+      dst[0] = m_run;
+      dst[64] = lsum;
 #pragma unroll
-        for (int sl = 0; sl < kNs; ++sl)
+      for (int sl = 0; sl < kNs; ++sl)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) dst[(2 + 4 * sl + e) * 64] = acc[sl][e];
-      }
+        for (int e = 0; e < 4; ++e) dst[(2 + 4 * sl + e) * 64] = acc[sl][e];
+    };
+    // (max, sum, channels) of lane `from` in `slot`, merged with this lane's
+    auto take = [&](int slot, int from, float& M, float& L, f32x4 (&A)[kNs]) {
+      const float* src = xb + (size_t)slot * kLane * 64 + from;
+      const float mb = src[0];
+      const float Mx = fmaxf(M, mb);
+      if (Mx == kNegInf) return;
+      const float fa = exp2_fast(M - Mx), fb = exp2_fast(mb - Mx);
+      L = L * fa + src[64] * fb;
+#pragma unroll
+      for (int sl = 0; sl < kNs; ++sl)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) A[sl][e] = A[sl][e] * fa + src[(2 + 4 * sl + e) * 64] * fb;
+      M = Mx;
+    };
+    for (int st = 1; st < NW / 2; st *= 2) {
+      if (rel % (2 * st) == st) put(wave >> 1);
       __syncthreads();
-      if (wave < half) {
-        const float* src = xb + (size_t)wave * kLane * 64 + lane;
-        const float mb = src[0];
-        const float M = fmaxf(m_run, mb);
-        if (M != kNegInf) {
-          const float fa = exp2_fast(m_run - M), fb = exp2_fast(mb - M);
-          lsum = lsum * fa + src[64] * fb;
-#pragma unroll
-          for (int sl = 0; sl < kNs; ++sl)
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              acc[sl][e] = acc[sl][e] * fa + src[(2 + 4 * sl + e) * 64] * fb;
-          m_run = M;
-        }
-      }
+      if (rel % (2 * st) == 0 && rel + st < nw) take((wave + st) >> 1, lane, m_run, lsum, acc);
       __syncthreads();
     }
-    if (wave == 0 && row_live) {
-      // column n = head n % g of the group's sequence n / g; chunk p of the prefix
-      const size_t prow =
-          ((size_t)(s + n / g) * a.Hq + kvh * g + n % g) * a.pfx_chunks + p;
+    // wave 0 holds the prefix's result for every column of the group, the first wave of
+    // each suffix its rows: combine them per (sequence, head) and write the output
+    if (wave == 0) put(0);
+    __syncthreads();
+    if (!pfx_wave && lw == 0 && uidx < gseq && n < g) {
+      take(0, 16 * j + uidx * g + n, m_run, lsum, acc);
+      const size_t row = (size_t)s * a.Hq + kvh * g + n;
 #pragma unroll
-      for (int sl = 0; sl < kNs; ++sl) {
-        f32x4 v = acc[sl];
+      for (int sl = 0; sl < kNs; ++sl)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] *= a.v_scale;
-        *reinterpret_cast<f32x4*>(a.pfx_acc + prow * D + 16 * sl + 4 * j) = v;
-      }
-      if (j == 0) {
-        a.pfx_ml[prow * 2 + 0] = m_run;
-        a.pfx_ml[prow * 2 + 1] = lsum;
-      }
+        for (int e = 0; e < 4; ++e) {
+          const int d = 16 * sl + 4 * j + e;
+          const float o = m_run == kNegInf ? 0.f : (acc[sl][e] * a.v_scale) / lsum;
+          if constexpr (kBf16)
+            static_cast<uint16_t*>(a.out)[row * D + d] = bf16_bits(o);
+          else
+            static_cast<float*>(a.out)[row * D + d] = o;
+        }
     }
     return;
   }
@@ -989,7 +1020,7 @@ paged_decode_kernel(const DecodeParams a, const OrderArg<PAIRED> ord) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int d = 16 * sl + 4 * j + e;
-            const float o = finish_row<D>(a, row, d, m_run, lsum, acc[sl][e] * a.v_scale);
+            const float o = finish_row(m_run, lsum, acc[sl][e] * a.v_scale);
             const size_t at = row * D + d;
             if constexpr (kBf16)
               static_cast<uint16_t*>(a.out)[at] = bf16_bits(o);
@@ -1050,7 +1081,7 @@ paged_decode_kernel(const DecodeParams a, const OrderArg<PAIRED> ord) {
     const size_t row = (size_t)su * a.Hq + kvh * g + h;
     num *= a.v_scale;
     if (single) {
-      const float o = finish_row<D>(a, row, d, M, den, num);
+      const float o = finish_row(M, den, num);
       if constexpr (kBf16)
         static_cast<uint16_t*>(a.out)[row * D + d] = bf16_bits(o);
       else
@@ -1114,7 +1145,7 @@ reduce_partitions_kernel(const DecodeParams a) {
   }
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
-    const float o = finish_row<D>(a, row, lane + 64 * i, M, den, num[i]);
+    const float o = finish_row(M, den, num[i]);
     const size_t idx = row * D + lane + 64 * i;
     if constexpr (ElemTraits<T>::kBf16)
       static_cast<uint16_t*>(a.out)[idx] = bf16_bits(o);
@@ -1152,7 +1183,7 @@ inline void order_on_host(const DecodeParams& a, int BS, int step, const int32_t
   const long cap = std::min((long)a.MB * BS, (long)a.P * a.Pmax);
   uint32_t key[kMaxPairedSeqs];
   for (int t = 0; t < a.S; ++t) {
-    const long L = std::min(std::max(0L, (long)host_lens[t] - a.len_off), cap);
+    const long L = std::min(std::max(0L, (long)host_lens[t]), cap);
     key[t] = (static_cast<uint32_t>(L) << 10) | static_cast<uint32_t>(1023 - t);
   }
   std::sort(key, key + a.S, [](uint32_t x, uint32_t y) { return x > y; });
@@ -1200,20 +1231,23 @@ hipError_t launch_decode(const DecodeParams& a, const int32_t* host_lens, hipStr
 // prefix), kv head fastest, chunk slowest.
 constexpr int kPrefixWaves = 8;
 
-// LDS of a prefix-pass workgroup: control, new-token staging (unused), one table window of
-// P / BS entries, and the tree merge's exchange of NW / 2 waves' registers.
-inline size_t prefix_lds_bytes(int D, int BS, int P, int elt) {
-  const size_t tbl_words = ((size_t)(P / BS) + 3) / 4 * 4;
-  return 64 + 4 * (size_t)D * elt + 4 * (tbl_words + (kPrefixWaves / 2) * 64 * (D / 4 + 2));
+// LDS of a shared-prefix workgroup: control, the new tokens of up to 4 sequences, the
+// table windows (the prefix, then one per sequence of the group) of P / BS entries, and
+// the exchange of NW / 2 waves' registers for the merges.
+inline size_t prefix_lds_bytes(int D, int BS, int P, int grp, int elt) {
+  const size_t tbl_words = ((size_t)(1 + grp) * (P / BS) + 3) / 4 * 4;
+  return 64 + 2 * 4 * (size_t)D * elt +
+         4 * (tbl_words + (kPrefixWaves / 2) * 64 * (size_t)(D / 4 + 2));
 }
 
+// One workgroup per (kv head, group of a.grp sequences), kv head fastest.
 template <typename T, int D, int BS>
 hipError_t launch_prefix(const DecodeParams& a, hipStream_t stream) {
-  const size_t lds = prefix_lds_bytes(D, BS, a.P, sizeof(T));
+  const size_t lds = prefix_lds_bytes(D, BS, a.P, a.grp, sizeof(T));
   const long groups = (a.S + a.grp - 1) / a.grp;
   hipLaunchKernelGGL((paged_decode_kernel<T, T, D, BS, kPrefixWaves, kPipe, false, true>),
-                     dim3((unsigned)((long)a.Hkv * groups * a.pfx_chunks)),
-                     dim3(kPrefixWaves * 64), lds, stream, a, NoOrder{});
+                     dim3((unsigned)((long)a.Hkv * groups)), dim3(kPrefixWaves * 64), lds,
+                     stream, a, NoOrder{});
   return hipGetLastError();
 }
 
@@ -1336,17 +1370,6 @@ namespace {
 bool good_scale(float s) { return s > 0.f && s <= 3.4028234663852886e38f; }
 
 // fp8: the caches hold E4M3 codes read with k_scale / v_scale (query and out bf16).
-// The suffix pass of pa_decode_step_shared_prefix: positions before len_off are skipped
-// (block_table already points past their entries; rows are tbl_stride apart) and every
-// output merges the prefix pass's result of its row.
-struct SuffixArgs {
-  int len_off;
-  int tbl_stride;
-  int chunks;
-  float* pfx_ml;
-  float* pfx_acc;
-};
-
 pa_status run_decode(void* out, const void* query, const int32_t* block_table,
                      const int32_t* context_lens, const void* k_cache, const void* v_cache,
                      const void* new_k, const void* new_v, const int64_t* new_slot,
@@ -1354,8 +1377,7 @@ pa_status run_decode(void* out, const void* query, const int32_t* block_table,
                      int max_blocks_per_seq, int num_blocks, int max_context_len, float scale,
                      pa_dtype dtype, int partition_size, void* workspace, size_t workspace_bytes,
                      void* stream, const int32_t* host_lens, bool fp8 = false,
-                     float k_scale = 1.f, float v_scale = 1.f,
-                     const SuffixArgs* sfx = nullptr) {
+                     float k_scale = 1.f, float v_scale = 1.f) {
   pa_status st = check_shapes(num_heads, num_kv_heads, head_dim, block_size, dtype);
   if (st != PA_OK) return st;
   if (fp8 && dtype != PA_DTYPE_BF16) return PA_ERR_UNSUPPORTED;
@@ -1402,16 +1424,11 @@ pa_status run_decode(void* out, const void* query, const int32_t* block_table,
   a.Hkv = num_kv_heads;
   a.g = num_heads / num_kv_heads;
   a.MB = max_blocks_per_seq;
-  a.tbl_stride = sfx ? sfx->tbl_stride : max_blocks_per_seq;
   a.NB = num_blocks;
   a.P = P;
   a.Pmax = pmax;
-  a.len_off = sfx ? sfx->len_off : 0;
   a.pfx_len = 0;
-  a.pfx_chunks = sfx ? sfx->chunks : 0;
   a.grp = 0;
-  a.pfx_ml = sfx ? sfx->pfx_ml : nullptr;
-  a.pfx_acc = sfx ? sfx->pfx_acc : nullptr;
   // Short partitions: each wave of a workgroup owns one of kWaves consecutive
   // partitions, so one prologue serves them all and no cross-wave merge is needed --
   // when the workgroups still give every compute unit two.
@@ -1476,147 +1493,79 @@ extern "C" pa_status pa_decode_step(void* out, const void* query, const void* ke
 // ---------------------------------------------------------------------------
 namespace {
 
-// Workspace of pa_decode_step_shared_prefix: the prefix pass's (max, sum) [S][Hq][2] and
-// unnormalised outputs [S][Hq][D] (f32), then the suffix pass's partition workspace; each
-// region 256-byte aligned.
-struct PrefixLayout {
-  size_t ml, acc, part, total;
-  int P;                     // suffix partition length
-  int chunk, chunks;         // prefix pass: positions per chunk, chunks
-};
-
-// Sequences per prefix-pass group: their query rows fill the 16 columns of the MFMA.
-int prefix_group(int g) { return std::max(1, 16 / g); }
-
-PrefixLayout prefix_layout(int S, int Hq, int Hkv, int D, int pfx_len, int max_suffix_len,
-                           int partition_size, pa_dtype dtype) {
-  PrefixLayout w{0, 0, 0, 0, 0, 0, 0};
-  // The prefix is cut into chunks (multiples of 64 positions, at least 256 each) when the
-  // groups alone would leave compute units without a prefix-pass workgroup.
-  const long units = (long)Hkv * ((S + prefix_group(Hq / Hkv) - 1) / prefix_group(Hq / Hkv));
-  const long want = std::max(1L, ((long)device_cu_count() + units - 1) / units);
-  const long most = std::max(1L, (long)pfx_len / 256);
-  const long c = std::min(want, most);
-  w.chunk = (int)round_up((size_t)((pfx_len + c - 1) / c), 64);
-  w.chunks = (pfx_len + w.chunk - 1) / w.chunk;
-  const size_t rows = (size_t)S * Hq * w.chunks;
-  w.ml = 0;
-  w.acc = round_up(rows * 2 * sizeof(float), 256);
-  w.part = w.acc + round_up(rows * D * sizeof(float), 256);
-  w.P = partition_size ? partition_size
-                       : pa_default_partition_size(S, Hkv, max_suffix_len, dtype);
-  const int pmax = std::max(1, (max_suffix_len + w.P - 1) / w.P);
-  w.total = w.part + workspace_layout(S, Hq, D, pmax).total;
-  return w;
+// Sequences per workgroup: their g query heads fill at most the 16 columns of the MFMA,
+// and the 4 suffix waves split evenly among them (1, 2 or 4 sequences).
+int prefix_group(int g) {
+  const int most = std::min(4, 16 / g);
+  return most >= 4 ? 4 : (most >= 2 ? 2 : 1);
 }
 
 }  // namespace
-
-extern "C" size_t pa_shared_prefix_workspace_size(int num_seqs, int num_heads, int num_kv_heads,
-                                                  int head_dim, int max_context_len,
-                                                  int prefix_blocks, int block_size,
-                                                  int partition_size, pa_dtype dtype) {
-  if (num_seqs <= 0 || prefix_blocks <= 0) return 0;
-  if (check_shapes(num_heads, num_kv_heads, head_dim, block_size, dtype) != PA_OK) return 0;
-  const long pfx = (long)prefix_blocks * block_size;
-  if (pfx > kMaxPartition || max_context_len < pfx) return 0;
-  if (partition_size != 0 &&
-      (partition_size < 64 || partition_size > kMaxPartition || partition_size % 64))
-    return 0;
-  return prefix_layout(num_seqs, num_heads, num_kv_heads, head_dim, (int)pfx,
-                       max_context_len - (int)pfx, partition_size, dtype).total;
-}
 
 extern "C" pa_status pa_decode_step_shared_prefix(
     void* out, const void* query, const void* key, const void* value,
     const int64_t* slot_mapping, const int32_t* block_table, const int32_t* context_lens,
     void* k_cache, void* v_cache, int num_seqs, int num_heads, int num_kv_heads, int head_dim,
     int block_size, int max_blocks_per_seq, int num_blocks, int max_context_len,
-    int prefix_blocks, float scale, pa_dtype dtype, int partition_size, void* workspace,
-    size_t workspace_bytes, void* stream, const int32_t* host_context_lens) {
+    int prefix_blocks, float scale, pa_dtype dtype, void* stream,
+    const int32_t* host_context_lens) {
   pa_status st = check_shapes(num_heads, num_kv_heads, head_dim, block_size, dtype);
   if (st != PA_OK) return st;
   if (num_seqs < 0 || max_blocks_per_seq <= 0 || num_blocks <= 0 || max_context_len < 0 ||
-      prefix_blocks < 0)
+      prefix_blocks <= 0)
     return PA_ERR_INVALID_ARG;
-  if (prefix_blocks == 0)
-    return num_seqs > 0 && (!key || !value || !slot_mapping)
-               ? PA_ERR_INVALID_ARG
-               : run_decode(out, query, block_table, context_lens, k_cache, v_cache, key, value,
-                            slot_mapping, num_seqs, num_heads, num_kv_heads, head_dim, block_size,
-                            max_blocks_per_seq, num_blocks, max_context_len, scale, dtype,
-                            partition_size, workspace, workspace_bytes, stream,
-                            host_context_lens);
   const long pfx = (long)prefix_blocks * block_size;
-  if (pfx > kMaxPartition) return PA_ERR_UNSUPPORTED;
   if (prefix_blocks >= max_blocks_per_seq || max_context_len < pfx ||
       (long)max_context_len > (long)max_blocks_per_seq * block_size)
     return PA_ERR_INVALID_ARG;
-  if (partition_size != 0 &&
-      (partition_size < 64 || partition_size > kMaxPartition || partition_size % 64))
-    return PA_ERR_INVALID_ARG;
+  // one table window holds the prefix, another each private suffix
+  const long window = std::max(pfx, (long)max_context_len - pfx);
+  if (window > kMaxPartition) return PA_ERR_UNSUPPORTED;
   if (num_seqs == 0) return PA_OK;
   if (!out || !query || !block_table || !context_lens || !k_cache || !v_cache)
     return PA_ERR_INVALID_ARG;
   if (slot_mapping && (!key || !value)) return PA_ERR_INVALID_ARG;
   if (!aligned(out, 16) || !aligned(query, 16) || !aligned(k_cache, 16) ||
-      !aligned(v_cache, 16) || !aligned(block_table, 4) || !aligned(context_lens, 4))
+      !aligned(v_cache, 16) || !aligned(block_table, 4) || !aligned(context_lens, 4) ||
+      (slot_mapping && (!aligned(key, 16) || !aligned(value, 16) || !aligned(slot_mapping, 8))))
     return PA_ERR_INVALID_ARG;
   if (host_context_lens)
     for (int t = 0; t < num_seqs; ++t)
-      if (host_context_lens[t] < pfx) return PA_ERR_INVALID_ARG;
-  const PrefixLayout wl = prefix_layout(num_seqs, num_heads, num_kv_heads, head_dim, (int)pfx,
-                                        max_context_len - (int)pfx, partition_size, dtype);
-  if (!workspace || workspace_bytes < wl.total || !aligned(workspace, 16))
-    return PA_ERR_WORKSPACE;
-  if ((long)num_kv_heads * wl.chunks *
-          ((num_seqs + prefix_group(num_heads / num_kv_heads) - 1) /
-           prefix_group(num_heads / num_kv_heads)) > 0x7FFFFFFFL)
-    return PA_ERR_INVALID_ARG;
-  char* ws = static_cast<char*>(workspace);
-  float* pml = reinterpret_cast<float*>(ws + wl.ml);
-  float* pacc = reinterpret_cast<float*>(ws + wl.acc);
+      if (host_context_lens[t] < pfx || host_context_lens[t] > max_context_len)
+        return PA_ERR_INVALID_ARG;
+  const int g = num_heads / num_kv_heads;
+  const int grp = prefix_group(g);
+  if ((long)num_kv_heads * ((num_seqs + grp - 1) / grp) > 0x7FFFFFFFL) return PA_ERR_INVALID_ARG;
 
-  // prefix pass: every group's rows over positions [0, pfx)
   pa::DecodeParams a{};
+  a.out = out;
   a.q = query;
   a.block_table = block_table;
   a.context_lens = context_lens;
   a.k_cache = k_cache;
   a.v_cache = v_cache;
+  a.new_k = slot_mapping ? key : nullptr;
+  a.new_v = slot_mapping ? value : nullptr;
+  a.new_slot = slot_mapping;
   a.S = num_seqs;
   a.Hq = num_heads;
   a.Hkv = num_kv_heads;
-  a.g = num_heads / num_kv_heads;
+  a.g = g;
   a.MB = max_blocks_per_seq;
-  a.tbl_stride = max_blocks_per_seq;
   a.NB = num_blocks;
-  a.P = wl.chunk;                                // the table window holds one chunk
-  a.Pmax = wl.chunks;
+  a.P = (int)round_up((size_t)window, 64);
+  a.Pmax = 1;
   a.wave_parts = 0;
   a.scale_log2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
   a.v_scale = 1.f;
   a.k_quant = a.v_quant = 1.f;
-  a.len_off = 0;
   a.pfx_len = (int)pfx;
-  a.pfx_chunks = wl.chunks;
-  a.grp = prefix_group(a.g);
-  a.pfx_ml = pml;
-  a.pfx_acc = pacc;
+  a.grp = grp;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t err = dtype == PA_DTYPE_BF16
-                       ? pa::dispatch_prefix<uint16_t>(a, head_dim, block_size, s)
-                       : pa::dispatch_prefix<float>(a, head_dim, block_size, s);
-  if (err != hipSuccess) return PA_ERR_HIP;
-
-  // suffix pass: the decode step over positions [pfx, L), merged with the prefix results
-  const SuffixArgs sfx{(int)pfx, max_blocks_per_seq, wl.chunks, pml, pacc};
-  return run_decode(out, query, block_table + prefix_blocks, context_lens, k_cache, v_cache,
-                    slot_mapping ? key : nullptr, slot_mapping ? value : nullptr, slot_mapping,
-                    num_seqs, num_heads, num_kv_heads, head_dim, block_size,
-                    max_blocks_per_seq - prefix_blocks, num_blocks, max_context_len - (int)pfx,
-                    scale, dtype, wl.P, ws + wl.part, workspace_bytes - wl.part, stream,
-                    host_context_lens, false, 1.f, 1.f, &sfx);
+  const hipError_t err = dtype == PA_DTYPE_BF16
+                             ? pa::dispatch_prefix<uint16_t>(a, head_dim, block_size, s)
+                             : pa::dispatch_prefix<float>(a, head_dim, block_size, s);
+  return err == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
 // ---------------------------------------------------------------------------

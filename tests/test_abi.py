@@ -35,7 +35,7 @@ def test_header_declares_the_boundary():
         "pa_gather_kv", "pa_decode_step", "pa_copy_blocks", "pa_paged_prefill",
         "pa_reshape_and_cache_fp8", "pa_paged_attention_fp8", "pa_decode_step_fp8",
         "pa_swap_blocks", "pa_decode_step_noalloc", "pa_read_probe",
-        "pa_decode_step_shared_prefix", "pa_shared_prefix_workspace_size"])
+        "pa_decode_step_shared_prefix"])
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -160,8 +160,8 @@ def test_decode_step_noalloc_rejects_before_launch(lib):
 
 def test_shared_prefix_step_rejects_before_launch(lib):
     f = lib.pa_decode_step_shared_prefix
-    #       out..v_cache  S  Hq Hkv  D  BS MB  NB  maxL pfx scale dt P  ws  wsb strm hl
-    base = [FAKE] * 9 + [4, 32, 8, 128, 16, 8, 64, 128, 2, 0.1, 1, 0, FAKE, 1 << 30, None, None]
+    #       out..v_cache  S  Hq Hkv  D  BS MB  NB  maxL pfx scale dt strm hl
+    base = [FAKE] * 9 + [4, 32, 8, 128, 16, 8, 64, 128, 2, 0.1, 1, None, None]
 
     def call(over):
         a = list(base)
@@ -170,17 +170,14 @@ def test_shared_prefix_step_rejects_before_launch(lib):
         return f(*a)
     assert call({12: 96}) == 2                  # head size
     assert call({17: 513, 14: 600, 16: 9000}) == 2    # prefix past 8192 tokens
+    assert call({17: 2, 14: 600, 16: 8300}) == 2      # a suffix past 8192 tokens
     assert call({17: 8}) == 1                   # prefix takes every table column
+    assert call({17: 0}) == 1                   # no prefix
     assert call({16: 20}) == 1                  # longest context shorter than the prefix
     assert call({4: None, 2: None, 3: None, 9: 0}) == 0   # empty batch
     assert call({2: None}) == 1                 # slot_mapping without key
-    assert call({21: None}) == 3                # no workspace
-    assert call({22: 64}) == 3                  # workspace too small
-    need = lib.pa_shared_prefix_workspace_size(4, 32, 8, 128, 128, 2, 16, 0, 1)
-    assert need >= 4 * 32 * 130 * 4
-    assert lib.pa_shared_prefix_workspace_size(4, 32, 8, 128, 20, 2, 16, 0, 1) == 0
     lens = (ctypes.c_int32 * 4)(40, 40, 31, 40)          # a host length below the prefix
-    assert call({24: ctypes.cast(lens, ctypes.c_void_p)}) == 1
+    assert call({21: ctypes.cast(lens, ctypes.c_void_p)}) == 1
 
 
 def test_read_probe_rejects_before_launch(lib):

@@ -30,7 +30,7 @@ def say(msg: str) -> None:
     sys.stdout.flush()
 
 
-def run_step(w, prefix_blocks, part=0, append=True, host=True):
+def run_step(w, prefix_blocks, append=True, host=True):
     """(output, K pool, V pool) of the shared-prefix step; the new token of every sequence
     (its record at position L - 1) is appended when `append`."""
     new = np.array([w.seq_records[s][-1] for s in range(w.num_seqs)], dtype=np.int64)
@@ -44,14 +44,14 @@ def run_step(w, prefix_blocks, part=0, append=True, host=True):
     out = pk.decode_step_shared_prefix(inp["query"], key, val, slot, inp["block_table"],
                                        inp["context_lens"], kc, vc, w.scale,
                                        prefix_blocks=prefix_blocks,
-                                       max_context_len=w.max_context_len, partition_size=part,
+                                       max_context_len=w.max_context_len,
                                        host_context_lens=w.context_lens if host else None)
     torch.cuda.synchronize()
     return out, kc, vc
 
 
-def check_step(w, prefix_blocks, part=0, append=True, host=True, what=""):
-    out, kc, vc = run_step(w, prefix_blocks, part, append, host)
+def check_step(w, prefix_blocks, append=True, host=True, what=""):
+    out, kc, vc = run_step(w, prefix_blocks, append, host)
     ref_k, ref_v = build_pools(w)
     assert np.array_equal(bits(kc), ref_k.view(bits(kc).dtype)), f"{what}: K pool"
     assert np.array_equal(bits(vc), ref_v.view(bits(vc).dtype)), f"{what}: V pool"
@@ -72,17 +72,17 @@ SUFFIXES = (1, 2, 7, 31, 32, 33, 63, 64, 65, 130, 257, 511, 700)
                                      ("f32", 16)])
 @pytest.mark.parametrize("D,BS", [(128, 16), (64, 8), (128, 32)])
 def test_shared_prefix_variants(dtype, g, D, BS):
-    """Ragged suffixes over a prefix of a few blocks; the groups of the prefix pass do not
-    divide the batch evenly; paired suffixes, partitions with the merge kernel and one
-    partition per wave; with and without the host's copy of the lengths."""
+    """Ragged suffixes (one token to 700) over a prefix of a few blocks, and over a prefix
+    longer than every suffix; groups of 1, 2 or 4 sequences that do not divide the batch
+    evenly; with and without the host's copy of the lengths."""
     Hkv = 2
-    prefix = 3 * BS if BS > 8 else 5 * BS
-    w = prefixed(dtype, prefix, SUFFIXES, g * Hkv, Hkv, D, BS, seed=1300 + 16 * g + D + BS,
-                 scale=0.6 / np.sqrt(D) * 4)
-    for part, host in ((0, True), (0, False), (64, True), (768, False)):
-        say(f"shared prefix {dtype} g={g} D={D} BS={BS} prefix={prefix} P={part} host={host}")
-        check_step(w, prefix // BS, part, host=host,
-                   what=f"prefix/{dtype}/g{g}/{D}/{BS}/{part}/{host}")
+    for prefix in ((3 * BS if BS > 8 else 5 * BS), 1024):
+        w = prefixed(dtype, prefix, SUFFIXES, g * Hkv, Hkv, D, BS,
+                     seed=1300 + 16 * g + D + BS + prefix, scale=0.6 / np.sqrt(D) * 4)
+        for host in (True, False):
+            say(f"shared prefix {dtype} g={g} D={D} BS={BS} prefix={prefix} host={host}")
+            check_step(w, prefix // BS, host=host,
+                       what=f"prefix/{dtype}/g{g}/{D}/{BS}/{prefix}/{host}")
 
 
 def test_shared_prefix_decode_alone_and_empty_suffixes():
@@ -92,11 +92,10 @@ def test_shared_prefix_decode_alone_and_empty_suffixes():
     lens = w.context_lens.copy()
     lens[0] = lens[3] = 64                         # the new token is not there yet
     w.context_lens = lens
-    for part in (0, 64):
-        say(f"shared prefix, decode alone, empty suffixes, P={part}")
-        out, kc, vc = run_step(w, 4, part, append=False)
-        kr, vr = build_pools(w)
-        check_close(to_f64(out), oracle_out(w, kr, vr), "bf16", f"prefix-alone/{part}")
+    say("shared prefix, decode alone, empty suffixes")
+    out, kc, vc = run_step(w, 4, append=False)
+    kr, vr = build_pools(w)
+    check_close(to_f64(out), oracle_out(w, kr, vr), "bf16", "prefix-alone")
 
 
 def test_shared_prefix_long_prefix_and_many_groups():
@@ -110,8 +109,7 @@ def test_shared_prefix_long_prefix_and_many_groups():
 
 def test_shared_prefix_named_workload_every_sequence():
     """The prefix-sharing workload (128 sequences, one 1024-token prefix, private suffixes
-    of 32-512 tokens), every sequence against the oracle; the output also agrees with
-    pa_decode_step's within the bar."""
+    of 32-512 tokens), every sequence against the oracle."""
     w = make_config(3)
     say(f"shared prefix {w.name}: S={w.num_seqs}")
     stats = check_step(w, 1024 // w.block_size, what=w.name)
@@ -134,3 +132,7 @@ def test_shared_prefix_rejections():
         pk.decode_step_shared_prefix(inp["query"], None, None, None, wide, inp["context_lens"],
                                      kc, vc, w.scale, prefix_blocks=513,
                                      max_context_len=9000)
+    with pytest.raises(NotImplementedError):        # a suffix of 8268 tokens
+        pk.decode_step_shared_prefix(inp["query"], None, None, None, wide, inp["context_lens"],
+                                     kc, vc, w.scale, prefix_blocks=2,
+                                     max_context_len=8300)
