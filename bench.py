@@ -50,14 +50,17 @@ def parse_args():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--op", default="step",
-                    choices=["step", "copy_blocks", "prefill", "fp8", "swap", "ceiling"],
+                    choices=["step", "copy_blocks", "prefill", "fp8", "swap", "ceiling",
+                             "math"],
                     help="step: the decode step (default); copy_blocks: the copy-on-write "
                          "copies of the parallel-sampling workload; prefill: paged prefill; "
                          "fp8: the decode step over FP8 (E4M3) K/V pools; swap: swapping a "
                          "quarter of the sequences' blocks out to pinned host memory and back; "
                          "ceiling: the read-bandwidth probe over the workload's KV bytes, "
                          "streaming and as a gather of scattered 4 KB tiles, every launch "
-                         "shape of the sweep")
+                         "shape of the sweep; math: the fused step of the Llama-3-8B "
+                         "batch with its two products on the matrix cores and on the vector "
+                         "ALU, at group sizes 1, 2 and 4 over the same KV")
     ap.add_argument("--prefill-case", default="prefix-cache-prefill",
                     choices=["prefix-cache-prefill", "chunked-prefill-llama3-8b"])
     ap.add_argument("--config", type=int, default=1, choices=[0, 1, 2, 3, 4])
@@ -80,6 +83,12 @@ def parse_args():
                     help="skip the read-probe sweep beside the step (e.g. under a profiler)")
     ap.add_argument("--warm", action="store_true",
                     help="also time K steps over one pool copy (Infinity Cache warm)")
+    ap.add_argument("--math", choices=["both", "mfma", "valu"], default="both",
+                    help="--op math: the forms to time (one form alone under a profiler)")
+    ap.add_argument("--groups", default="1,2,4",
+                    help="--op math: query heads per kv head to time")
+    ap.add_argument("--rounds", type=int, default=3,
+                    help="--op math: alternating rounds of the forms")
     ap.add_argument("--cpu-budget", type=float, default=10.0,
                     help="seconds of oracle work in the CPU baseline")
     return ap.parse_args()
@@ -748,6 +757,89 @@ def cpu_baseline_swap(w, blocks: np.ndarray, budget_s: float) -> dict:
                        f"{dt:.1f} s (one thread: NumPy copies)")}
 
 
+def bench_math(args) -> int:
+    """The fused decode step of the Llama-3-8B batch (64 sequences, lengths 128-2048, 8 kv
+    heads, D 128, BS 16, bf16) with its products on the matrix cores and on the vector ALU
+    (pa_set_decode_math), at 8 g query heads for each g of --groups: the K/V bytes are the
+    same at every g, only the query rows differ.  The forms alternate over --rounds
+    rounds on the same pools; each round times K steps after W of warm-up, and the
+    median round is reported."""
+    import torch
+
+    import paged_kv_cache_425_amd as pk
+    from workloads import make_config, make_workload
+    dev = torch.device("cuda:0")
+    base = make_config(1, seed=args.seed)
+    forms = ["mfma", "valu"] if args.math == "both" else [args.math]
+    K, W = args.steps, args.warmup
+    rows = []
+    for g in [int(x) for x in args.groups.split(",")]:
+        w = base if g == 4 else make_workload(
+            name=f"{base.name}-g{g}", context_lens=base.context_lens, num_heads=8 * g,
+            num_kv_heads=8, head_dim=128, block_size=16, dtype="bf16", seed=base.info["seed"],
+            max_blocks_per_seq=base.block_table.shape[1])
+        new = np.array([w.seq_records[s][-1] for s in range(w.num_seqs)], dtype=np.int64)
+        hist = np.setdiff1d(np.arange(len(w.rec_slot)), new)
+
+        def up(a):
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(
+                torch.bfloat16).to(dev)
+        kshape = pk.k_cache_shape(w.num_blocks, 8, 128, 16, torch.bfloat16)
+        vshape = pk.v_cache_shape(w.num_blocks, 8, 128, 16, torch.bfloat16)
+        kc0 = torch.full(kshape, float("nan"), dtype=torch.bfloat16, device=dev)
+        vc0 = torch.full(vshape, float("nan"), dtype=torch.bfloat16, device=dev)
+        pk.reshape_and_cache(up(w.rec_key[hist]), up(w.rec_value[hist]),
+                             torch.from_numpy(w.rec_slot[hist]).to(dev), kc0, vc0)
+        pools = [(kc0, vc0)] + [(kc0.clone(), vc0.clone())
+                                for _ in range(max(1, args.replicas) - 1)]
+        query, table = up(w.query), torch.from_numpy(w.block_table).to(dev)
+        lens = torch.from_numpy(w.context_lens).to(dev)
+        key, val = up(w.rec_key[new]), up(w.rec_value[new])
+        slot = torch.from_numpy(w.rec_slot[new]).to(dev)
+        out = torch.empty_like(query)
+        ws = torch.empty(1, dtype=torch.uint8, device=dev)
+        calls = [pk.prepare_decode_step(query, key, val, slot, table, lens, kc, vc, w.scale,
+                                        max_context_len=w.max_context_len, out=out,
+                                        workspace=ws, host_context_lens=w.context_lens)
+                 for kc, vc in pools]
+        kv = unique_kv_bytes(w)
+        times = {f: [] for f in forms}
+        for _ in range(max(1, args.rounds)):
+            for f in forms:
+                pk.set_decode_math(f)
+                for i in range(W):
+                    calls[i % len(calls)]()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                torch.cuda.synchronize()
+                e0.record()
+                for i in range(K):
+                    calls[i % len(calls)]()
+                e1.record()
+                torch.cuda.synchronize()
+                times[f].append(e0.elapsed_time(e1) * 1e3 / K)
+        pk.set_decode_math("mfma")
+        row = {"g": g, "workload": w.name, "num_heads": w.num_heads, "kv_bytes": kv}
+        for f in forms:
+            us = float(np.median(times[f]))
+            row[f] = {"us_per_launch": round(us, 2), "rounds_us": [round(t, 2) for t in times[f]],
+                      "GB/s": round(kv / (us * 1e-6) / 1e9, 1),
+                      "hbm_frac": round(kv / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+        if len(forms) == 2:
+            row["valu_over_mfma"] = round(row["valu"]["us_per_launch"] /
+                                          row["mfma"]["us_per_launch"], 4)
+        log(f"g={g}: " + ", ".join(f"{f} {row[f]['us_per_launch']} us" for f in forms))
+        rows.append(row)
+        del pools, kc0, vc0
+        torch.cuda.empty_cache()
+    print(json.dumps({"metric": "fused decode step, matrix cores vs vector ALU", "unit": "us",
+                      "steps": K, "warmup": W, "rounds": args.rounds, "dtype": "bf16",
+                      "higher_is_better": False, "data": "synthetic",
+                      "config": {"workload": f"{base.name} at g = {args.groups}",
+                                 "pool_replicas": max(1, args.replicas)},
+                      "rows": rows}), flush=True)
+    return 0
+
+
 def main() -> int:
     args = parse_args()
     if args.gpus != 1:
@@ -773,6 +865,8 @@ def main() -> int:
         return bench_swap(args)
     if args.op == "ceiling":
         return bench_ceiling(args)
+    if args.op == "math":
+        return bench_math(args)
     dev = torch.device("cuda:0")
 
     t = time.perf_counter()

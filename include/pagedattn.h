@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define PA_ABI_VERSION 3
+#define PA_ABI_VERSION 4
 
 typedef enum {
     PA_OK = 0,
@@ -75,6 +75,11 @@ typedef enum {
     PA_DTYPE_FP8_E4M3 = 2     /* FP8 pools (uint8 codes): pa_copy_blocks and pa_swap_blocks
                                  only; the FP8 calls below name their pool type themselves */
 } pa_dtype;
+
+typedef enum {
+    PA_MATH_MFMA = 0,         /* matrix cores (the default)                             */
+    PA_MATH_VALU = 1          /* vector ALU: v_dot2_f32_bf16 scores, float32 FMA P.V    */
+} pa_math;
 
 /* Version of this ABI (PA_ABI_VERSION of the build). */
 int pa_abi_version(void);
@@ -427,6 +432,22 @@ pa_status pa_gather_kv(void* k_out, void* v_out, const int64_t* seq_offsets,
                        const void* k_cache, const void* v_cache, int num_seqs,
                        int num_kv_heads, int head_dim, int block_size, int max_blocks_per_seq,
                        int num_blocks, int max_context_len, pa_dtype dtype, void* stream);
+
+/*
+ * Arithmetic of the bf16 decode (process-wide; for measurement and diagnostics).
+ * The attention of "core architecture" section 2.2.2 needs two small products per
+ * step of a (block, kv head): the g query rows of a group against the step's K rows,
+ * and the softmax weights against its V rows.  With PA_MATH_MFMA (the default) both
+ * run on the matrix cores; with PA_MATH_VALU they run on the vector ALU (bf16 dot
+ * products for the scores, float32 FMAs with unsplit weights for P.V), with the same
+ * loads, partitioning and merges.  The VALU form serves pa_paged_attention,
+ * pa_decode_step and pa_decode_step_noalloc on bf16 pools with group size 1, 2 or 4;
+ * every other call and shape runs on the matrix cores whatever is set.  Both forms
+ * meet the same accuracy bound; their results differ in rounding only.  A call takes
+ * the value set when it is made.  Returns PA_ERR_INVALID_ARG for another value.
+ */
+pa_status pa_set_decode_math(pa_math math);
+pa_math pa_get_decode_math(void);
 
 /*
  * Diagnostic read-bandwidth probe (not a step of the decode path).  A paged decode

@@ -3,7 +3,8 @@
 The work runs in hand-written HIP kernels behind a C ABI (include/pagedattn.h);
 this package only marshals torch tensors to it.
 """
-from .binding import (LIB_PATH, PreparedCall, chunk_elems, copy_blocks, decode_step,
+from .binding import (LIB_PATH, PreparedCall, chunk_elems, copy_blocks, decode_math,
+                      decode_step, get_decode_math, set_decode_math,
                       decode_step_noalloc, decode_step_shared_prefix, read_probe,
                       prepare_decode_step_shared_prefix,
                       decode_step_fp8, default_partition_size, gather_kv, k_cache_shape,
@@ -13,7 +14,8 @@ from .binding import (LIB_PATH, PreparedCall, chunk_elems, copy_blocks, decode_s
                       prepare_reshape_and_cache, prepare_reshape_and_cache_fp8, reshape_and_cache,
                       reshape_and_cache_fp8, v_cache_shape, workspace_size)
 
-__all__ = ["LIB_PATH", "PreparedCall", "chunk_elems", "copy_blocks", "decode_step",
+__all__ = ["LIB_PATH", "PreparedCall", "chunk_elems", "copy_blocks", "decode_math",
+           "decode_step", "get_decode_math", "set_decode_math",
            "decode_step_noalloc", "decode_step_shared_prefix", "read_probe",
            "prepare_decode_step_shared_prefix",
            "decode_step_fp8", "prepare_decode_step_fp8", "prepare_swap_blocks", "swap_blocks",

@@ -7,6 +7,7 @@ not built it raises -- there is no other implementation to fall back on.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 
@@ -68,6 +69,10 @@ def load_library() -> ctypes.CDLL:
     lib.pa_paged_attention_fp8.restype = i32
     lib.pa_paged_attention_fp8.argtypes = [vp] * 6 + [i32] * 8 + [f32] * 3 + [i32, i32, vp, sz,
                                                                               vp, vp]
+    lib.pa_set_decode_math.restype = i32
+    lib.pa_set_decode_math.argtypes = [i32]
+    lib.pa_get_decode_math.restype = i32
+    lib.pa_get_decode_math.argtypes = []
     _lib = lib
     return lib
 
@@ -680,6 +685,33 @@ def read_probe(buf: torch.Tensor, piece_offsets: torch.Tensor, piece_bytes: int,
     _check(load_library().pa_read_probe(_ptr(buf), _ptr(piece_offsets), n, int(piece_bytes),
                                         int(workgroups), int(in_flight), _ptr(sink),
                                         _stream(dev, stream)), "pa_read_probe")
+
+
+DECODE_MATH = {"mfma": 0, "valu": 1}
+
+
+def set_decode_math(math: str) -> None:
+    """Arithmetic of the bf16 decode calls from now on (pa_set_decode_math): "mfma"
+    (matrix cores, the default) or "valu" (vector ALU; group sizes 1, 2 and 4)."""
+    if math not in DECODE_MATH:
+        raise ValueError(f"decode math must be one of {sorted(DECODE_MATH)}")
+    _check(load_library().pa_set_decode_math(DECODE_MATH[math]), "pa_set_decode_math")
+
+
+def get_decode_math() -> str:
+    code = load_library().pa_get_decode_math()
+    return {v: k for k, v in DECODE_MATH.items()}[code]
+
+
+@contextlib.contextmanager
+def decode_math(math: str):
+    """Run the enclosed calls with the given decode arithmetic, then restore it."""
+    before = get_decode_math()
+    set_decode_math(math)
+    try:
+        yield
+    finally:
+        set_decode_math(before)
 
 
 # ---------------------------------------------------------------------------

@@ -57,6 +57,44 @@ __device__ __forceinline__ float sum_xor32(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Reductions across the 16 lanes of each row with DPP moves: after quad_perm xor 1 and
+// xor 2 every lane of a quad holds its quad's result, the half-row mirror (lane i reads
+// lane 7 - i of its half-row) pairs the two quads of each half-row and the row mirror
+// (lane i reads lane 15 - i) the two halves.  Each step combines a lane with its partner
+// symmetrically, so all 16 lanes end with the same bits.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+constexpr int kDppXor1 = 0xB1;          // quad_perm(1, 0, 3, 2)
+constexpr int kDppXor2 = 0x4E;          // quad_perm(2, 3, 0, 1)
+constexpr int kDppHalfMirror = 0x141;
+constexpr int kDppMirror = 0x140;
+__device__ __forceinline__ float row_max16(float x) {
+  x = fmaxf(x, dpp_f32<kDppXor1>(x));
+  x = fmaxf(x, dpp_f32<kDppXor2>(x));
+  x = fmaxf(x, dpp_f32<kDppHalfMirror>(x));
+  return fmaxf(x, dpp_f32<kDppMirror>(x));
+}
+__device__ __forceinline__ float row_sum16(float x) {
+  x += dpp_f32<kDppXor1>(x);
+  x += dpp_f32<kDppXor2>(x);
+  x += dpp_f32<kDppHalfMirror>(x);
+  return x + dpp_f32<kDppMirror>(x);
+}
+
+// Word w of a 16-byte chunk as a pair of bf16.  The word is copied out first: clang
+// lowers __builtin_bit_cast of an ext_vector element subscript (v[w]) to element 0.
+__device__ __forceinline__ bf16x2 bf16_pair(u32x4 v, int w) {
+  const uint32_t u = v[w];
+  return __builtin_bit_cast(bf16x2, u);
+}
+
+// x of lane `src` (0..63) of the wave (ds_bpermute: no LDS storage is used).
+__device__ __forceinline__ float lane_read(float x, int src) {
+  return __int_as_float(__builtin_amdgcn_ds_bpermute(4 * src, __float_as_int(x)));
+}
+
 // bfloat16 <-> float32 (round to nearest even on the way down).
 __device__ __forceinline__ float bf16_to_f32(__bf16 h) { return static_cast<float>(h); }
 __device__ __forceinline__ __bf16 f32_to_bf16(float x) { return static_cast<__bf16>(x); }

@@ -207,10 +207,12 @@ using OrderArg = typename std::conditional<PAIRED, PairOrder, NoOrder>::type;
 // are merged lane by lane in registers, and the prefix and suffix results of each row are
 // combined with a log-sum-exp merge before the output is written.
 template <typename T, typename C, int D, int BS, int NW, int PIPE, bool PAIRED,
-          bool PREFIX = false>
+          bool PREFIX = false, int VG = 0>
 __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(PA_DECODE_OCC)))
 paged_decode_kernel(const DecodeParams a, const OrderArg<PAIRED> ord) {
   static_assert(!(PAIRED && PREFIX), "the prefix pass is not paired");
+  static_assert(VG == 0 || (ElemTraits<T>::kBf16 && sizeof(C) == 2 && !PREFIX),
+                "the VALU math serves bf16 pools outside the shared-prefix mode");
   using Sh = StepShape<T, C, D>;
   constexpr bool kBf16 = Sh::kBf16;
   constexpr bool kFp8 = Sh::kFp8;
@@ -420,11 +422,21 @@ paged_decode_kernel(const DecodeParams a, const OrderArg<PAIRED> ord) {
   // FP8: K chunk j + 4c' (16 channels) feeds MFMAs 2c' and 2c' + 1 (8 channels each).
   const T* qrow = static_cast<const T*>(a.q) + ((size_t)row_seq * a.Hq + head) * D;
   u32x4 qop[kNq];
+  // VALU math: lane (n, j) holds the same channels of every head of the group
+  u32x4 qv[VG > 0 ? VG : 1][kNc];
+  if constexpr (VG > 0) {
+    const T* qg = static_cast<const T*>(a.q) + ((size_t)s * a.Hq + kvh * VG) * D;
 #pragma unroll
-  for (int c = 0; c < kNq; ++c) {
-    const u32x4 z = {0u, 0u, 0u, 0u};
-    const int off = kFp8 ? 16 * (j + 4 * (c >> 1)) + 8 * (c & 1) : kX * (4 * c + j);
-    qop[c] = row_live ? load16(qrow + off) : z;
+    for (int h = 0; h < VG; ++h)
+#pragma unroll
+      for (int c = 0; c < kNc; ++c) qv[h][c] = load16(qg + (size_t)h * D + kX * (4 * c + j));
+  } else {
+#pragma unroll
+    for (int c = 0; c < kNq; ++c) {
+      const u32x4 z = {0u, 0u, 0u, 0u};
+      const int off = kFp8 ? 16 * (j + 4 * (c >> 1)) + 8 * (c & 1) : kX * (4 * c + j);
+      qop[c] = row_live ? load16(qrow + off) : z;
+    }
   }
 
   // Block-table windows: entry i of `count` is column col(i) of row row(i), staged at
@@ -679,6 +691,17 @@ paged_decode_kernel(const DecodeParams a, const OrderArg<PAIRED> ord) {
   f32x4 acc[kNs];
 #pragma unroll
   for (int i = 0; i < kNs; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // VALU math: per head, the running max and the lane's partial sum and output (lane
+  // (n, j): channel 16 sl + n over the tokens of row j)
+  constexpr int kVG = VG > 0 ? VG : 1;
+  float mv[kVG], lv[kVG], accv[kVG][kNs];
+#pragma unroll
+  for (int h = 0; h < kVG; ++h) {
+    mv[h] = kNegInf;
+    lv[h] = 0.f;
+#pragma unroll
+    for (int sl = 0; sl < kNs; ++sl) accv[h][sl] = 0.f;
+  }
 
   // ---- math of one step ---------------------------------------------------------
   auto compute_step = [&](int st, StepData<T, C, D>& b) {
@@ -787,6 +810,64 @@ paged_decode_kernel(const DecodeParams a, const OrderArg<PAIRED> ord) {
 #pragma unroll
         for (int sl = 0; sl < kNs; ++sl) b.v[sl][w] &= mask;
       }
+    }
+
+    if constexpr (VG > 0) {
+      // Q.K^T on the VALU: lane (n, j) dots its channel chunks j + 4c of K row n (token
+      // 8 (n / 4) + 4t + n % 4 of the step) with the same channels of each head's query
+      // (v_dot2_f32_bf16: exact products, float32 sums); the four rows' partial dots are
+      // then summed, so every row holds the step's 32 scores.
+      float yv[kVG][2], mx[kVG];
+#pragma unroll
+      for (int h = 0; h < VG; ++h) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          float part[kNc];
+#pragma unroll
+          for (int c = 0; c < kNc; ++c) {
+            float x = 0.f;
+#pragma unroll
+            for (int w = 0; w < 4; ++w)
+              x = __builtin_amdgcn_fdot2_f32_bf16(bf16_pair(b.k[t][c], w), bf16_pair(qv[h][c], w),
+                                                  x, false);
+            part[c] = x;
+          }
+          float x = part[0];
+#pragma unroll
+          for (int c = 1; c < kNc; ++c) x += part[c];
+          x = sum_xor32(sum_xor16(x));
+          const int tok = base + 8 * (n >> 2) + 4 * t + (n & 3);
+          yv[h][t] = (!tail || tok < tok1) ? x * a.scale_log2 : kNegInf;
+        }
+        mx[h] = row_max16(fmaxf(yv[h][0], yv[h][1]));
+      }
+      // online softmax per head, then P.V in float32: lane (n, j) takes the weights of
+      // its V tokens 8j + i from lane 4j + i % 4 of its row (tile i / 4) and accumulates
+      // them against its channels with FMAs (the weights need no bf16 split)
+#pragma unroll
+      for (int h = 0; h < VG; ++h) {
+        const float m_new = fmaxf(mv[h], mx[h]);
+        const float m_use = (m_new == kNegInf) ? 0.f : m_new;
+        const float alpha = exp2_fast(mv[h] - m_use);
+        const float p0 = exp2_fast(yv[h][0] - m_use);
+        const float p1 = exp2_fast(yv[h][1] - m_use);
+        lv[h] = lv[h] * alpha + (p0 + p1);
+        mv[h] = m_new;
+        float pw[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) pw[i] = lane_read(i < 4 ? p0 : p1, 20 * j + (i & 3));
+#pragma unroll
+        for (int sl = 0; sl < kNs; ++sl) {
+          float x = accv[h][sl] * alpha;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const uint32_t w = b.v[sl][i >> 1];
+            x = fmaf(pw[i], __uint_as_float((i & 1) ? (w & 0xFFFF0000u) : (w << 16)), x);
+          }
+          accv[h][sl] = x;
+        }
+      }
+      return;
     }
 
     // scores
@@ -937,6 +1018,37 @@ paged_decode_kernel(const DecodeParams a, const OrderArg<PAIRED> ord) {
       load_step(st, b0);
       compute_step(st, b0);
     }
+  }
+
+  if constexpr (VG > 0) {
+    // Back to the MFMA path's register layout, which the merges below read: lane (n, j)
+    // with n < g holds head n's max, a share of its sum (the whole sum in row 0, so that
+    // the sum over rows is the total) and its channels 16 sl + 4j .. + 3; the other lanes
+    // hold nothing (zero outputs, so the lo-row fold below adds nothing).
+#pragma unroll
+    for (int h = 0; h < VG; ++h) {
+#pragma unroll
+      for (int sl = 0; sl < kNs; ++sl) accv[h][sl] = sum_xor32(sum_xor16(accv[h][sl]));
+      lv[h] = row_sum16(lv[h]);
+    }
+#pragma unroll
+    for (int h = 0; h < VG; ++h)
+      if (n == h) {
+        m_run = mv[h];
+        l_run = j == 0 ? lv[h] : 0.f;
+      }
+#pragma unroll
+    for (int sl = 0; sl < kNs; ++sl)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float v = 0.f;
+#pragma unroll
+        for (int h = 0; h < VG; ++h) {
+          const float x = lane_read(accv[h][sl], 4 * j + e);
+          v = n == h ? x : v;
+        }
+        acc[sl][e] = v;
+      }
   }
 
   // ---- merge the waves of the workgroup --------------------------------------------
@@ -1200,7 +1312,7 @@ inline void order_on_host(const DecodeParams& a, int BS, int step, const int32_t
   }
 }
 
-template <typename T, typename C, int D, int BS>
+template <typename T, typename C, int D, int BS, int VG = 0>
 hipError_t launch_decode(const DecodeParams& a, const int32_t* host_lens, hipStream_t stream) {
   constexpr int elt = sizeof(T);
   if (use_paired(a, D, BS, elt)) {
@@ -1210,7 +1322,7 @@ hipError_t launch_decode(const DecodeParams& a, const int32_t* host_lens, hipStr
       order_on_host(a, BS, StepShape<T, C, D>::kStep, host_lens, ord);
     else
       for (int r = 0; r < (a.S + 1) / 2; ++r) ord.pair[r] = make_uint2(kNoPlan, 0u);
-    hipLaunchKernelGGL((paged_decode_kernel<T, C, D, BS, kPairWaves, kPipe, true>),
+    hipLaunchKernelGGL((paged_decode_kernel<T, C, D, BS, kPairWaves, kPipe, true, false, VG>),
                        dim3((unsigned)a.Hkv, (unsigned)((a.S + 1) / 2)), dim3(kPairWaves * 64),
                        lds, stream, a, ord);
     return hipGetLastError();
@@ -1218,8 +1330,8 @@ hipError_t launch_decode(const DecodeParams& a, const int32_t* host_lens, hipStr
   const size_t lds = decode_lds_bytes(false, kWaves, a.S, D, BS, a.P, a.g, elt, a.wave_parts);
   const long groups = a.wave_parts ? (a.Pmax + kWaves - 1) / kWaves : a.Pmax;
   const long grid = (long)a.Hkv * groups * a.S;
-  hipLaunchKernelGGL((paged_decode_kernel<T, C, D, BS, kWaves, kPipe, false>), dim3((unsigned)grid),
-                     dim3(kWaves * 64), lds, stream, a, NoOrder{});
+  hipLaunchKernelGGL((paged_decode_kernel<T, C, D, BS, kWaves, kPipe, false, false, VG>),
+                     dim3((unsigned)grid), dim3(kWaves * 64), lds, stream, a, NoOrder{});
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || a.Pmax == 1) return err;
   hipLaunchKernelGGL((reduce_partitions_kernel<T, D, BS>), dim3((unsigned)((long)a.S * a.Hq)),
@@ -1261,9 +1373,28 @@ hipError_t dispatch_prefix(const DecodeParams& a, int D, int BS, hipStream_t str
   return hipErrorInvalidValue;
 }
 
+// Arithmetic of the bf16 decode kernels (pa_set_decode_math).
+std::atomic<int> g_decode_math{PA_MATH_MFMA};
+
+// Group sizes the VALU math is built for.
+inline bool valu_group(int g) { return g == 1 || g == 2 || g == 4; }
+
 template <typename T, typename C>
 hipError_t dispatch_decode(const DecodeParams& a, int D, int BS, const int32_t* host_lens,
                            hipStream_t stream) {
+  if constexpr (std::is_same<T, uint16_t>::value && std::is_same<C, uint16_t>::value) {
+    if (g_decode_math.load(std::memory_order_relaxed) == PA_MATH_VALU && valu_group(a.g)) {
+#define PA_VCASE(DD, BB)                                                                    \
+  if (D == DD && BS == BB)                                                                  \
+    return a.g == 1   ? launch_decode<T, C, DD, BB, 1>(a, host_lens, stream)                \
+           : a.g == 2 ? launch_decode<T, C, DD, BB, 2>(a, host_lens, stream)                \
+                      : launch_decode<T, C, DD, BB, 4>(a, host_lens, stream);
+      PA_VCASE(64, 8) PA_VCASE(64, 16) PA_VCASE(64, 32)
+      PA_VCASE(128, 8) PA_VCASE(128, 16) PA_VCASE(128, 32)
+#undef PA_VCASE
+      return hipErrorInvalidValue;
+    }
+  }
 #define PA_CASE(DD, BB) \
   if (D == DD && BS == BB) return launch_decode<T, C, DD, BB>(a, host_lens, stream);
   PA_CASE(64, 8) PA_CASE(64, 16) PA_CASE(64, 32)
@@ -1456,6 +1587,16 @@ pa_status run_decode(void* out, const void* query, const int32_t* block_table,
 }
 
 }  // namespace
+
+extern "C" pa_status pa_set_decode_math(pa_math math) {
+  if (math != PA_MATH_MFMA && math != PA_MATH_VALU) return PA_ERR_INVALID_ARG;
+  pa::g_decode_math.store(math, std::memory_order_relaxed);
+  return PA_OK;
+}
+
+extern "C" pa_math pa_get_decode_math(void) {
+  return static_cast<pa_math>(pa::g_decode_math.load(std::memory_order_relaxed));
+}
 
 extern "C" pa_status pa_paged_attention(void* out, const void* query, const int32_t* block_table,
                                         const int32_t* context_lens, const void* k_cache,

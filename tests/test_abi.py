@@ -35,7 +35,7 @@ def test_header_declares_the_boundary():
         "pa_gather_kv", "pa_decode_step", "pa_copy_blocks", "pa_paged_prefill",
         "pa_reshape_and_cache_fp8", "pa_paged_attention_fp8", "pa_decode_step_fp8",
         "pa_swap_blocks", "pa_decode_step_noalloc", "pa_read_probe",
-        "pa_decode_step_shared_prefix"])
+        "pa_decode_step_shared_prefix", "pa_set_decode_math", "pa_get_decode_math"])
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -44,7 +44,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.pa_abi_version() == 3
+    assert lib.pa_abi_version() == 4
     for code in range(5):
         assert lib.pa_status_string(code).decode().startswith("PA_")
     assert b"unknown" in lib.pa_status_string(99)
@@ -178,6 +178,24 @@ def test_shared_prefix_step_rejects_before_launch(lib):
     assert call({2: None}) == 1                 # slot_mapping without key
     lens = (ctypes.c_int32 * 4)(40, 40, 31, 40)          # a host length below the prefix
     assert call({21: ctypes.cast(lens, ctypes.c_void_p)}) == 1
+
+
+def test_decode_math_selector(lib):
+    """The selector is process-wide state with no device work: MFMA by default, VALU on
+    request, anything else refused and the setting kept."""
+    assert lib.pa_get_decode_math() == 0
+    try:
+        assert lib.pa_set_decode_math(1) == 0
+        assert lib.pa_get_decode_math() == 1
+        assert lib.pa_set_decode_math(2) == 1 and lib.pa_set_decode_math(-1) == 1
+        assert lib.pa_get_decode_math() == 1
+        with pk.decode_math("mfma"):
+            assert pk.get_decode_math() == "mfma"
+        assert pk.get_decode_math() == "valu"
+        with pytest.raises(ValueError):
+            pk.set_decode_math("dot")
+    finally:
+        assert lib.pa_set_decode_math(0) == 0
 
 
 def test_read_probe_rejects_before_launch(lib):
