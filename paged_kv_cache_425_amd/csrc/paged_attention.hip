@@ -48,6 +48,11 @@
 //   the pair is ~2^-17 p) and the head group occupies 2g of the 16 MFMA rows:
 //   rows [0, g) carry hi, rows [g, 2g) carry lo, and the two are added at the
 //   end.  The rows are there anyway (g <= 8 < 16), so this costs no extra MFMA.
+//   A vector-ALU form of both products (VG > 0: bf16, g = 1, 2, 4; selected with
+//   pa_set_decode_math) uses the same loads: bf16 dot products per lane, summed across
+//   the lanes that hold a K row, and float32 FMAs for P.V with unsplit weights.  It is
+//   kept for measurement: on the Llama-3-8B batch the matrix cores are faster at every
+//   group size (equal within 1% at g = 1, twice as fast at g = 4).
 //
 // FP8 pools (cache element C = uint8_t, E4M3 codes; queries bf16)
 //   The cache element type is a template parameter.  With 1-byte codes a 16-byte
