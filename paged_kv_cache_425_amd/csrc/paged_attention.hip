@@ -212,7 +212,7 @@ using OrderArg = typename std::conditional<PAIRED, PairOrder, NoOrder>::type;
 // are merged lane by lane in registers, and the prefix and suffix results of each row are
 // combined with a log-sum-exp merge before the output is written.
 template <typename T, typename C, int D, int BS, int NW, int PIPE, bool PAIRED,
-          bool PREFIX = false, int VG = 0>
+          bool PREFIX = false, int VG = 0, bool NT = false>
 __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(PA_DECODE_OCC)))
 paged_decode_kernel(const DecodeParams a, const OrderArg<PAIRED> ord) {
   static_assert(!(PAIRED && PREFIX), "the prefix pass is not paired");
@@ -651,6 +651,8 @@ paged_decode_kernel(const DecodeParams a, const OrderArg<PAIRED> ord) {
   const size_t head_elems = (size_t)D * BS;          // elements of one (block, kv head)
 
   // ---- loads of one step ------------------------------------------------------
+  // K/V loads: the nt (streaming) policy when the launch asks for it, else the default
+  auto kv_load = [&](const C* p) { return NT ? load16_nt(p) : load16(p); };
   auto load_step = [&](int st, StepData<T, C, D>& b) {
     const int base = tok0 + st * kStep;
 #pragma unroll
@@ -666,7 +668,7 @@ paged_decode_kernel(const DecodeParams a, const OrderArg<PAIRED> ord) {
       // 16-byte chunks j, j + 4, ...
       const C* kp = kc + (((size_t)phys * a.Hkv + kvh) * BS + tok % BS) * D + (size_t)j * kX;
 #pragma unroll
-      for (int c = 0; c < kNc; ++c) b.k[t][c] = load16(kp + 4 * c * kX);
+      for (int c = 0; c < kNc; ++c) b.k[t][c] = kv_load(kp + 4 * c * kX);
     }
     // V operand of slice sl: channel 16*sl + n, tokens base + kTpl*j .. + kTpl - 1.  A group
     // wholly past the end reads the group of the last live token (in bounds; it is zeroed
@@ -681,13 +683,15 @@ paged_decode_kernel(const DecodeParams a, const OrderArg<PAIRED> ord) {
       const C* vp2 = vc + ((size_t)physv2 * a.Hkv + kvh) * head_elems + (size_t)n * BS;
 #pragma unroll
       for (int sl = 0; sl < kNs; ++sl) {
-        const uint2 lo = *reinterpret_cast<const uint2*>(vp + (size_t)16 * sl * BS);
-        const uint2 hi = *reinterpret_cast<const uint2*>(vp2 + (size_t)16 * sl * BS);
+        const uint2 lo = NT ? load8_nt(vp + (size_t)16 * sl * BS)
+                            : *reinterpret_cast<const uint2*>(vp + (size_t)16 * sl * BS);
+        const uint2 hi = NT ? load8_nt(vp2 + (size_t)16 * sl * BS)
+                            : *reinterpret_cast<const uint2*>(vp2 + (size_t)16 * sl * BS);
         b.v[sl] = u32x4{lo.x, lo.y, hi.x, hi.y};
       }
     } else {
 #pragma unroll
-      for (int sl = 0; sl < kNs; ++sl) b.v[sl] = load16(vp + (size_t)16 * sl * BS);
+      for (int sl = 0; sl < kNs; ++sl) b.v[sl] = kv_load(vp + (size_t)16 * sl * BS);
     }
   };
 
@@ -1317,6 +1321,22 @@ inline void order_on_host(const DecodeParams& a, int BS, int step, const int32_t
   }
 }
 
+// Compute units of the current device (queried once per device; concurrent first calls
+// may both query, and store the same value).
+int device_cu_count() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+      n = 256;
+    cache[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
 template <typename T, typename C, int D, int BS, int VG = 0>
 hipError_t launch_decode(const DecodeParams& a, const int32_t* host_lens, hipStream_t stream) {
   constexpr int elt = sizeof(T);
@@ -1327,9 +1347,18 @@ hipError_t launch_decode(const DecodeParams& a, const int32_t* host_lens, hipStr
       order_on_host(a, BS, StepShape<T, C, D>::kStep, host_lens, ord);
     else
       for (int r = 0; r < (a.S + 1) / 2; ++r) ord.pair[r] = make_uint2(kNoPlan, 0u);
-    hipLaunchKernelGGL((paged_decode_kernel<T, C, D, BS, kPairWaves, kPipe, true, false, VG>),
-                       dim3((unsigned)a.Hkv, (unsigned)((a.S + 1) / 2)), dim3(kPairWaves * 64),
-                       lds, stream, a, ord);
+    // Streaming (nt) K/V loads when every workgroup of the launch is resident at once (one
+    // per compute unit or fewer): measured faster there (the Llama-3-8B batch: 56.6 ->
+    // 54.5 us), and slower when compute units run several workgroups in turn (the
+    // continuous-batching mix: 156.7 -> 164.7 us).
+    const dim3 grid((unsigned)a.Hkv, (unsigned)((a.S + 1) / 2));
+    const bool nt = VG == 0 && (long)grid.x * grid.y <= device_cu_count();
+    if (nt)
+      hipLaunchKernelGGL((paged_decode_kernel<T, C, D, BS, kPairWaves, kPipe, true, false, 0, true>),
+                         grid, dim3(kPairWaves * 64), lds, stream, a, ord);
+    else
+      hipLaunchKernelGGL((paged_decode_kernel<T, C, D, BS, kPairWaves, kPipe, true, false, VG>),
+                         grid, dim3(kPairWaves * 64), lds, stream, a, ord);
     return hipGetLastError();
   }
   const size_t lds = decode_lds_bytes(false, kWaves, a.S, D, BS, a.P, a.g, elt, a.wave_parts);
@@ -1448,21 +1477,6 @@ WorkspaceLayout workspace_layout(int S, int Hq, int D, int pmax) {
   return w;
 }
 
-// Compute units of the current device (queried once per device; concurrent first calls
-// may both query, and store the same value).
-int device_cu_count() {
-  static std::atomic<int> cache[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  int n = cache[dev].load(std::memory_order_relaxed);
-  if (n == 0) {
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        n <= 0)
-      n = 256;
-    cache[dev].store(n, std::memory_order_relaxed);
-  }
-  return n;
-}
 
 using pa::kMaxPartition;
 static_assert(kMaxPartition <= (1 << 20), "a paired-mode sort key holds the length in 21 bits");
@@ -1478,7 +1492,7 @@ extern "C" int pa_default_partition_size(int num_seqs, int num_kv_heads, int max
   (void)dtype;
   const long units = std::max(1L, (long)num_seqs * std::max(1, num_kv_heads));
   const long whole = std::max(64L, ((long)std::max(0, max_context_len) + 63) / 64 * 64);
-  const long cus = device_cu_count();
+  const long cus = pa::device_cu_count();
   if (whole <= kMaxPartition && units >= 2 * cus) return (int)whole;
   const long want_parts = std::max(1L, (4 * cus + units - 1) / units);
   long P = ((long)std::max(0, max_context_len) + want_parts - 1) / want_parts;
@@ -1571,7 +1585,7 @@ pa_status run_decode(void* out, const void* query, const int32_t* block_table,
   {
     const long groups = (pmax + pa::kWaves - 1) / pa::kWaves;
     a.wave_parts = pmax >= 2 && (long)P * pa::kWaves <= pa::kMaxPartition &&
-                   (long)num_kv_heads * num_seqs * groups >= 2L * device_cu_count();
+                   (long)num_kv_heads * num_seqs * groups >= 2L * pa::device_cu_count();
   }
   a.scale_log2 = static_cast<float>(static_cast<double>(scale) * (fp8 ? k_scale : 1.0) *
                                     1.4426950408889634);

@@ -120,11 +120,14 @@ paged_prefill_kernel(const PrefillParams a) {
   const int nsteps = (kmax + kStep - 1) / kStep;
   const int nblk = (kmax + BS - 1) / BS;                     // <= MB
 
-  // block-table window 0 .. nblk - 1, in chunks of 1024 entries (refilled per 1024 blocks)
+  // block-table window 0 .. nblk - 1, in chunks of 1024 entries (refilled per 1024 blocks).
+  // Entries past the last block with a seen key repeat that block, so the last step's
+  // loads past kmax need no clamp (in bounds; those keys are masked, their V zeroed).
   const int* bt = a.block_table + (size_t)s * a.MB;
   auto load_table = [&](int first) {
-    for (int i = threadIdx.x; i < 1024 && first + i < nblk; i += kThreads) {
-      const unsigned b = static_cast<unsigned>(bt[first + i]);
+    const int end = min(1024, nblk + kStep / BS + 1 - first);
+    for (int i = threadIdx.x; i < end; i += kThreads) {
+      const unsigned b = static_cast<unsigned>(bt[min(first + i, nblk - 1)]);
       tbl_lds[i] = static_cast<int>(min(b, static_cast<unsigned>(a.NB - 1)));
     }
   };
@@ -172,6 +175,8 @@ paged_prefill_kernel(const PrefillParams a) {
   // also adds its own offset inside the block.  Blocks past the last one with a seen key
   // are clamped to it (in bounds; those keys are masked, their V zeroed).
   static_assert(kStep % BS == 0 || BS % kStep == 0, "steps and blocks must nest");
+  static_assert(Sh::kKChunks % kThreads == 0 && Sh::kVChunks % kThreads == 0,
+                "every thread stages whole chunks of K and V");
   int k_blk[kLoadsK], v_blk[kLoadsV];                       // block offset within the step
   int k_off[kLoadsK], v_off[kLoadsV];                       // element offset in the tile
 #pragma unroll
@@ -188,28 +193,31 @@ paged_prefill_kernel(const PrefillParams a) {
     v_blk[i] = grp * kX / BS;
     v_off[i] = ch * BS + grp * kX % BS;
   }
-  const int last_blk = (kmax - 1) / BS;                     // last block with a seen key
-  const size_t blk_stride = (size_t)a.Hkv * head_elems;      // elements per physical block
-  const T* kbase = kc + (size_t)kvh * head_elems;
-  const T* vbase = vc + (size_t)kvh * head_elems;
+  // bytes per physical block (all kv heads), < 2^32: Hkv * D * BS * elt
+  const uint32_t blk_bytes = static_cast<uint32_t>((size_t)a.Hkv * head_elems * sizeof(T));
+  // each chunk's address is its fixed place within (block, kv head) plus block * blk_bytes
+  const unsigned char* kp[kLoadsK];
+  const unsigned char* vp[kLoadsV];
+#pragma unroll
+  for (int i = 0; i < kLoadsK; ++i)
+    kp[i] = reinterpret_cast<const unsigned char*>(kc + (size_t)kvh * head_elems + k_off[i]);
+#pragma unroll
+  for (int i = 0; i < kLoadsV; ++i)
+    vp[i] = reinterpret_cast<const unsigned char*>(vc + (size_t)kvh * head_elems + v_off[i]);
+  auto at = [&](const unsigned char* p, int phys) {
+    return p + (uint64_t)static_cast<uint32_t>(phys) * blk_bytes;
+  };
   auto fetch = [&](int st) {
     const int b0 = st * kStep / BS;                          // first block of the step
-    const int boff = st * kStep % BS;                        // 0 unless kStep < BS
     const int tb0 = b0 / 1024 * 1024;                        // its table window
+    // kStep < BS (f32, BS 32): the step's offset inside its block
+    const size_t boff = kStep < BS ? (size_t)(st * kStep % BS) * sizeof(T) : 0;
 #pragma unroll
-    for (int i = 0; i < kLoadsK; ++i) {
-      const int phys = tbl_lds[min(b0 + k_blk[i], last_blk) - tb0];
-      const u32x4 z = {0u, 0u, 0u, 0u};
-      kreg[i] = threadIdx.x + i * kThreads < Sh::kKChunks
-                    ? load16(kbase + (size_t)phys * blk_stride + k_off[i] + boff * D) : z;
-    }
+    for (int i = 0; i < kLoadsK; ++i)
+      kreg[i] = load16(at(kp[i], tbl_lds[b0 - tb0 + k_blk[i]]) + boff * D);
 #pragma unroll
-    for (int i = 0; i < kLoadsV; ++i) {
-      const int phys = tbl_lds[min(b0 + v_blk[i], last_blk) - tb0];
-      const u32x4 z = {0u, 0u, 0u, 0u};
-      vreg[i] = threadIdx.x + i * kThreads < Sh::kVChunks
-                    ? load16(vbase + (size_t)phys * blk_stride + v_off[i] + boff) : z;
-    }
+    for (int i = 0; i < kLoadsV; ++i)
+      vreg[i] = load16(at(vp[i], tbl_lds[b0 - tb0 + v_blk[i]]) + boff);
   };
   auto stage = [&](int st, int buf) {
     const int base = st * kStep;
@@ -218,32 +226,31 @@ paged_prefill_kernel(const PrefillParams a) {
 #pragma unroll
     for (int i = 0; i < kLoadsK; ++i) {
       const int cid = threadIdx.x + i * kThreads;
-      if (cid < Sh::kKChunks) {
-        const int q = cid % (D / kX), key = cid / (D / kX);
-        *reinterpret_cast<u32x4*>(kb + (krow(key) * Sh::kKRow + q) * 16) = kreg[i];
+      const int q = cid % (D / kX), key = cid / (D / kX);
+      *reinterpret_cast<u32x4*>(kb + (krow(key) * Sh::kKRow + q) * 16) = kreg[i];
+    }
+    if (__builtin_expect(base + kStep > kmax, 0)) {          // the step ends past kmax
+      // zero positions >= L (kmax <= L): weight 0 must not meet NaN
+#pragma unroll
+      for (int i = 0; i < kLoadsV; ++i) {
+        const int grp = (threadIdx.x + i * kThreads) % (kStep / kX);
+        const int nv = min(max(kmax - (base + grp * kX), 0), kX);
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          uint32_t mask;
+          if (kBf16)
+            mask = (2 * w + 1 < nv) ? 0xFFFFFFFFu : ((2 * w < nv) ? 0x0000FFFFu : 0u);
+          else
+            mask = (w < nv) ? 0xFFFFFFFFu : 0u;
+          vreg[i][w] &= mask;
+        }
       }
     }
 #pragma unroll
     for (int i = 0; i < kLoadsV; ++i) {
       const int cid = threadIdx.x + i * kThreads;
-      if (cid < Sh::kVChunks) {
-        const int ch = cid / (kStep / kX), grp = cid % (kStep / kX);
-        u32x4 v = vreg[i];
-        if (base + kStep > kmax) {                           // the step ends past kmax
-          // zero positions >= L (kmax <= L): weight 0 must not meet NaN
-          const int nv = min(max(kmax - (base + grp * kX), 0), kX);
-#pragma unroll
-          for (int w = 0; w < 4; ++w) {
-            uint32_t mask;
-            if (kBf16)
-              mask = (2 * w + 1 < nv) ? 0xFFFFFFFFu : ((2 * w < nv) ? 0x0000FFFFu : 0u);
-            else
-              mask = (w < nv) ? 0xFFFFFFFFu : 0u;
-            v[w] &= mask;
-          }
-        }
-        *reinterpret_cast<u32x4*>(vb + (ch * Sh::kVRow + grp) * 16) = v;
-      }
+      const int ch = cid / (kStep / kX), grp = cid % (kStep / kX);
+      *reinterpret_cast<u32x4*>(vb + (ch * Sh::kVRow + grp) * 16) = vreg[i];
     }
   };
 

@@ -487,6 +487,30 @@ def test_prefill_variants_ragged(dtype, D, BS, g):
     check_close(to_f64(got), ref, dtype, f"prefill/{dtype}/{D}/{BS}/{g}")
 
 
+@pytest.mark.parametrize("D,BS,g", [(128, 16, 4), (64, 8, 1), (128, 32, 2)])
+def test_prefill_with_large_v_magnitudes(D, BS, g):
+    """Large V magnitudes: V of every third physical block scaled by 16 (exact in bf16) and
+    one element set to 2^17 (beyond fp16's range).  The weights' hi + lo split keeps P.V
+    exact to ~2^-16 of each weight whatever V holds; the result must meet the bar against
+    the oracle."""
+    Hkv = 2
+    w = tiny("bf16", PREFILL_LENS, g * Hkv, Hkv, D, BS, seed=75 + D + BS + g,
+             scale=0.6 / np.sqrt(D) * 4)
+    pb = make_prefill(w, [1, 5, 17, 33, 64, 40, 200, 129], 75)
+    kc, vc = build_pools(w)
+    v = (vc.astype(np.uint32) << 16).view(np.float32).copy()      # bf16 bits -> values
+    v[::3] *= 16.0
+    b, kvh = int(w.block_table[6, 2]), 1                            # a block sequence 6 reads
+    v[b, kvh, 5, 3] = 2.0 ** 17
+    vc = (v.view(np.uint32) >> 16).astype(np.uint16)
+    assert np.abs(np.nan_to_num(v)).max() > 65504
+    say(f"prefill with large V, D={D} BS={BS} g={g}")
+    got = run_prefill(w, pb, kc, vc)
+    ref = oracle.paged_prefill(pb.query, pb.query_start_loc, w.block_table, w.context_lens,
+                               kc, vc, w.scale, "bf16")
+    check_close(to_f64(got), ref, "bf16", f"prefill-large-v/{D}/{BS}/{g}")
+
+
 def test_prefill_long_context_reloads_the_table_window():
     """More than 1024 blocks before the chunk (BS 8, 9000 tokens)."""
     w = tiny("bf16", (9000, 40), 8, 2, 128, 8, seed=75)
