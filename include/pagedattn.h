@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define PA_ABI_VERSION 4
+#define PA_ABI_VERSION 5
 
 typedef enum {
     PA_OK = 0,
@@ -466,13 +466,15 @@ pa_math pa_get_decode_math(void);
  *                  workgroups * in_flight pieces further on, and so on
  *   in_flight      4, 8 or 16: pieces whose 16-byte loads each thread issues
  *                  before using any of them
+ *   nontemporal    0: default-policy loads; 1: streaming (nt) loads, the policy the
+ *                  paged decode uses when its workgroups are all resident at once
  *   sink           [workgroups * 256] uint32, device: written with checksums
  * Returns PA_ERR_INVALID_ARG / PA_ERR_UNSUPPORTED for bad arguments (nothing
  * launched).
  */
 pa_status pa_read_probe(const void* buf, const int64_t* piece_offsets, int num_pieces,
-                        int piece_bytes, int workgroups, int in_flight, uint32_t* sink,
-                        void* stream);
+                        int piece_bytes, int workgroups, int in_flight, int nontemporal,
+                        uint32_t* sink, void* stream);
 
 #ifdef __cplusplus
 }

@@ -63,7 +63,7 @@ def load_library() -> ctypes.CDLL:
     lib.pa_decode_step_shared_prefix.restype = i32
     lib.pa_decode_step_shared_prefix.argtypes = [vp] * 9 + [i32] * 9 + [f32, i32, vp, vp]
     lib.pa_read_probe.restype = i32
-    lib.pa_read_probe.argtypes = [vp, vp, i32, i32, i32, i32, vp, vp]
+    lib.pa_read_probe.argtypes = [vp, vp, i32, i32, i32, i32, i32, vp, vp]
     lib.pa_decode_step_noalloc.restype = i32
     lib.pa_decode_step_noalloc.argtypes = [vp] * 9 + [i32] * 8 + [f32, i32, i32, vp, vp]
     lib.pa_paged_attention_fp8.restype = i32
@@ -669,9 +669,11 @@ def gather_kv(block_table: torch.Tensor, context_lens: torch.Tensor, k_cache: to
 
 
 def read_probe(buf: torch.Tensor, piece_offsets: torch.Tensor, piece_bytes: int,
-               workgroups: int, in_flight: int, sink: torch.Tensor, stream=None) -> None:
+               workgroups: int, in_flight: int, sink: torch.Tensor, stream=None,
+               nontemporal: bool = False) -> None:
     """Read-bandwidth probe (pa_read_probe): read the pieces of `buf` at `piece_offsets`
-    (int64 byte offsets) and leave checksums in `sink` (int32, workgroups * 256)."""
+    (int64 byte offsets) and leave checksums in `sink` (int32, workgroups * 256), with
+    default-policy or streaming (nt) loads."""
     dev = buf.device
     _require(buf, "buf", dev)
     _require(piece_offsets, "piece_offsets", dev, torch.int64)
@@ -683,8 +685,8 @@ def read_probe(buf: torch.Tensor, piece_offsets: torch.Tensor, piece_bytes: int,
     if n and piece_bytes > size:
         raise ValueError("pieces larger than the buffer")
     _check(load_library().pa_read_probe(_ptr(buf), _ptr(piece_offsets), n, int(piece_bytes),
-                                        int(workgroups), int(in_flight), _ptr(sink),
-                                        _stream(dev, stream)), "pa_read_probe")
+                                        int(workgroups), int(in_flight), int(bool(nontemporal)),
+                                        _ptr(sink), _stream(dev, stream)), "pa_read_probe")
 
 
 DECODE_MATH = {"mfma": 0, "valu": 1}

@@ -5,8 +5,8 @@
 // scattered through the pool -- 4 KB each at block size 16, bf16, head size 128.
 // This kernel reads such pieces (at offsets the caller lists: in order, for a
 // streaming read, or shuffled, for the paged gather) and keeps only a checksum, so
-// its rate is the ceiling the decode's loads can reach on this part.  It is a
-// diagnostic next to the decode path, not a step of it.
+// its rate is the ceiling the decode's loads can reach on this part, with default or
+// streaming (nt) loads.  It is a diagnostic next to the decode path, not a step of it.
 #include "common.h"
 
 namespace pa {
@@ -16,7 +16,7 @@ constexpr int kProbeThreads = 256;
 // Workgroup b takes pieces [U*b, U*b + U), then [U*(b + grid), ...), and so on.  For a
 // group of U pieces each thread loads its 16-byte chunk of every piece before it uses
 // any of them, so U loads per thread are in flight.  Pieces past the end are skipped.
-template <int U>
+template <int U, bool NT>
 __global__ void __launch_bounds__(kProbeThreads)
 read_probe_kernel(const unsigned char* __restrict__ buf, const int64_t* __restrict__ offs,
                   int npieces, int piece_bytes, uint32_t* __restrict__ sink) {
@@ -29,7 +29,8 @@ read_probe_kernel(const unsigned char* __restrict__ buf, const int64_t* __restri
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const long p = p0 + (u < live ? u : 0);
-        v[u] = load16(buf + offs[p] + (size_t)c * 16);
+        const unsigned char* a = buf + offs[p] + (size_t)c * 16;
+        v[u] = NT ? load16_nt(a) : load16(a);
       }
 #pragma unroll
       for (int u = 0; u < U; ++u) acc ^= v[u];
@@ -40,10 +41,24 @@ read_probe_kernel(const unsigned char* __restrict__ buf, const int64_t* __restri
 
 }  // namespace pa
 
+namespace {
+template <int U>
+void launch_probe(bool nt, int workgroups, hipStream_t s, const unsigned char* b,
+                  const int64_t* offs, int n, int piece_bytes, uint32_t* sink) {
+  if (nt)
+    hipLaunchKernelGGL((pa::read_probe_kernel<U, true>), dim3(workgroups), dim3(pa::kProbeThreads),
+                       0, s, b, offs, n, piece_bytes, sink);
+  else
+    hipLaunchKernelGGL((pa::read_probe_kernel<U, false>), dim3(workgroups),
+                       dim3(pa::kProbeThreads), 0, s, b, offs, n, piece_bytes, sink);
+}
+}  // namespace
+
 extern "C" pa_status pa_read_probe(const void* buf, const int64_t* piece_offsets, int num_pieces,
                                    int piece_bytes, int workgroups, int in_flight,
-                                   uint32_t* sink, void* stream) {
-  if (num_pieces < 0 || workgroups <= 0 || piece_bytes <= 0 || piece_bytes % 4096)
+                                   int nontemporal, uint32_t* sink, void* stream) {
+  if (num_pieces < 0 || workgroups <= 0 || piece_bytes <= 0 || piece_bytes % 4096 ||
+      (nontemporal != 0 && nontemporal != 1))
     return PA_ERR_INVALID_ARG;
   if (in_flight != 4 && in_flight != 8 && in_flight != 16) return PA_ERR_UNSUPPORTED;
   if (num_pieces == 0) return PA_OK;
@@ -53,14 +68,12 @@ extern "C" pa_status pa_read_probe(const void* buf, const int64_t* piece_offsets
     return PA_ERR_INVALID_ARG;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const unsigned char* b = static_cast<const unsigned char*>(buf);
+  const bool nt = nontemporal == 1;
   if (in_flight == 4)
-    hipLaunchKernelGGL(pa::read_probe_kernel<4>, dim3(workgroups), dim3(pa::kProbeThreads), 0, s,
-                       b, piece_offsets, num_pieces, piece_bytes, sink);
+    launch_probe<4>(nt, workgroups, s, b, piece_offsets, num_pieces, piece_bytes, sink);
   else if (in_flight == 8)
-    hipLaunchKernelGGL(pa::read_probe_kernel<8>, dim3(workgroups), dim3(pa::kProbeThreads), 0, s,
-                       b, piece_offsets, num_pieces, piece_bytes, sink);
+    launch_probe<8>(nt, workgroups, s, b, piece_offsets, num_pieces, piece_bytes, sink);
   else
-    hipLaunchKernelGGL(pa::read_probe_kernel<16>, dim3(workgroups), dim3(pa::kProbeThreads), 0,
-                       s, b, piece_offsets, num_pieces, piece_bytes, sink);
+    launch_probe<16>(nt, workgroups, s, b, piece_offsets, num_pieces, piece_bytes, sink);
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
 }

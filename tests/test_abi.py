@@ -44,7 +44,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.pa_abi_version() == 4
+    assert lib.pa_abi_version() == 5
     for code in range(5):
         assert lib.pa_status_string(code).decode().startswith("PA_")
     assert b"unknown" in lib.pa_status_string(99)
@@ -200,7 +200,7 @@ def test_decode_math_selector(lib):
 
 def test_read_probe_rejects_before_launch(lib):
     f = lib.pa_read_probe
-    base = [FAKE, FAKE, 16, 4096, 64, 8, FAKE, None]
+    base = [FAKE, FAKE, 16, 4096, 64, 8, 0, FAKE, None]
 
     def call(over):
         a = list(base)
@@ -211,7 +211,9 @@ def test_read_probe_rejects_before_launch(lib):
     assert call({5: 6}) == 2                    # in-flight count not built
     assert call({4: 0}) == 1                    # no workgroups
     assert call({0: FAKE + 4}) == 1             # buffer misaligned
+    assert call({6: 2}) == 1                    # load policy is 0 or 1
     assert call({2: 0}) == 0                    # nothing to read
+    assert call({2: 0, 6: 1}) == 0
 
 
 def test_reshape_and_cache_rejects_before_launch(lib):
