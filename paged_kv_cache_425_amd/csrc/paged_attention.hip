@@ -51,8 +51,8 @@
 //   A vector-ALU form of both products (VG > 0: bf16, g = 1, 2, 4; selected with
 //   pa_set_decode_math) uses the same loads: bf16 dot products per lane, summed across
 //   the lanes that hold a K row, and float32 FMAs for P.V with unsplit weights.  It is
-//   kept for measurement: on the Llama-3-8B batch the matrix cores are faster at every
-//   group size (equal within 1% at g = 1, twice as fast at g = 4).
+//   kept for measurement: on the Llama-3-8B batch, with the same loads, the two tie at
+//   g = 1 and the matrix cores are twice as fast at g = 4.
 //
 // FP8 pools (cache element C = uint8_t, E4M3 codes; queries bf16)
 //   The cache element type is a template parameter.  With 1-byte codes a 16-byte
@@ -1352,9 +1352,9 @@ hipError_t launch_decode(const DecodeParams& a, const int32_t* host_lens, hipStr
     // 54.5 us), and slower when compute units run several workgroups in turn (the
     // continuous-batching mix: 156.7 -> 164.7 us).
     const dim3 grid((unsigned)a.Hkv, (unsigned)((a.S + 1) / 2));
-    const bool nt = VG == 0 && (long)grid.x * grid.y <= device_cu_count();
+    const bool nt = (long)grid.x * grid.y <= device_cu_count();
     if (nt)
-      hipLaunchKernelGGL((paged_decode_kernel<T, C, D, BS, kPairWaves, kPipe, true, false, 0, true>),
+      hipLaunchKernelGGL((paged_decode_kernel<T, C, D, BS, kPairWaves, kPipe, true, false, VG, true>),
                          grid, dim3(kPairWaves * 64), lds, stream, a, ord);
     else
       hipLaunchKernelGGL((paged_decode_kernel<T, C, D, BS, kPairWaves, kPipe, true, false, VG>),
