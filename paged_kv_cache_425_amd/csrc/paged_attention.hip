@@ -212,7 +212,7 @@ using OrderArg = typename std::conditional<PAIRED, PairOrder, NoOrder>::type;
 // are merged lane by lane in registers, and the prefix and suffix results of each row are
 // combined with a log-sum-exp merge before the output is written.
 template <typename T, typename C, int D, int BS, int NW, int PIPE, bool PAIRED,
-          bool PREFIX = false, int VG = 0, bool NT = false>
+          bool PREFIX = false, int VG = 0>
 __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(PA_DECODE_OCC)))
 paged_decode_kernel(const DecodeParams a, const OrderArg<PAIRED> ord) {
   static_assert(!(PAIRED && PREFIX), "the prefix pass is not paired");
@@ -651,8 +651,14 @@ paged_decode_kernel(const DecodeParams a, const OrderArg<PAIRED> ord) {
   const size_t head_elems = (size_t)D * BS;          // elements of one (block, kv head)
 
   // ---- loads of one step ------------------------------------------------------
-  // K/V loads: the nt (streaming) policy when the launch asks for it, else the default
-  auto kv_load = [&](const C* p) { return NT ? load16_nt(p) : load16(p); };
+  // Load policy.  Each K load instruction reads 64 bytes of each of 16 rows, half of each
+  // 128-byte line, and the next instruction reads the other half: K keeps the default
+  // policy, so that half comes from the cache.  V instructions read whole lines (16
+  // channel rows of a block, contiguous) and stream with the nt policy, which gathers
+  // scattered 4 KB tiles ~15% faster on gfx950 -- except in the waves of a shared prefix,
+  // whose blocks every group of the launch reads again from L2.
+  const bool v_stream = !(PREFIX && pfx_wave);
+  auto v_load = [&](const C* p) { return v_stream ? load16_nt(p) : load16(p); };
   auto load_step = [&](int st, StepData<T, C, D>& b) {
     const int base = tok0 + st * kStep;
 #pragma unroll
@@ -668,7 +674,7 @@ paged_decode_kernel(const DecodeParams a, const OrderArg<PAIRED> ord) {
       // 16-byte chunks j, j + 4, ...
       const C* kp = kc + (((size_t)phys * a.Hkv + kvh) * BS + tok % BS) * D + (size_t)j * kX;
 #pragma unroll
-      for (int c = 0; c < kNc; ++c) b.k[t][c] = kv_load(kp + 4 * c * kX);
+      for (int c = 0; c < kNc; ++c) b.k[t][c] = load16(kp + 4 * c * kX);
     }
     // V operand of slice sl: channel 16*sl + n, tokens base + kTpl*j .. + kTpl - 1.  A group
     // wholly past the end reads the group of the last live token (in bounds; it is zeroed
@@ -683,15 +689,13 @@ paged_decode_kernel(const DecodeParams a, const OrderArg<PAIRED> ord) {
       const C* vp2 = vc + ((size_t)physv2 * a.Hkv + kvh) * head_elems + (size_t)n * BS;
 #pragma unroll
       for (int sl = 0; sl < kNs; ++sl) {
-        const uint2 lo = NT ? load8_nt(vp + (size_t)16 * sl * BS)
-                            : *reinterpret_cast<const uint2*>(vp + (size_t)16 * sl * BS);
-        const uint2 hi = NT ? load8_nt(vp2 + (size_t)16 * sl * BS)
-                            : *reinterpret_cast<const uint2*>(vp2 + (size_t)16 * sl * BS);
+        const uint2 lo = load8_nt(vp + (size_t)16 * sl * BS);
+        const uint2 hi = load8_nt(vp2 + (size_t)16 * sl * BS);
         b.v[sl] = u32x4{lo.x, lo.y, hi.x, hi.y};
       }
     } else {
 #pragma unroll
-      for (int sl = 0; sl < kNs; ++sl) b.v[sl] = kv_load(vp + (size_t)16 * sl * BS);
+      for (int sl = 0; sl < kNs; ++sl) b.v[sl] = v_load(vp + (size_t)16 * sl * BS);
     }
   };
 
@@ -1347,18 +1351,9 @@ hipError_t launch_decode(const DecodeParams& a, const int32_t* host_lens, hipStr
       order_on_host(a, BS, StepShape<T, C, D>::kStep, host_lens, ord);
     else
       for (int r = 0; r < (a.S + 1) / 2; ++r) ord.pair[r] = make_uint2(kNoPlan, 0u);
-    // Streaming (nt) K/V loads when every workgroup of the launch is resident at once (one
-    // per compute unit or fewer): measured faster there (the Llama-3-8B batch: 56.6 ->
-    // 54.5 us), and slower when compute units run several workgroups in turn (the
-    // continuous-batching mix: 156.7 -> 164.7 us).
-    const dim3 grid((unsigned)a.Hkv, (unsigned)((a.S + 1) / 2));
-    const bool nt = (long)grid.x * grid.y <= device_cu_count();
-    if (nt)
-      hipLaunchKernelGGL((paged_decode_kernel<T, C, D, BS, kPairWaves, kPipe, true, false, VG, true>),
-                         grid, dim3(kPairWaves * 64), lds, stream, a, ord);
-    else
-      hipLaunchKernelGGL((paged_decode_kernel<T, C, D, BS, kPairWaves, kPipe, true, false, VG>),
-                         grid, dim3(kPairWaves * 64), lds, stream, a, ord);
+    hipLaunchKernelGGL((paged_decode_kernel<T, C, D, BS, kPairWaves, kPipe, true, false, VG>),
+                       dim3((unsigned)a.Hkv, (unsigned)((a.S + 1) / 2)), dim3(kPairWaves * 64),
+                       lds, stream, a, ord);
     return hipGetLastError();
   }
   const size_t lds = decode_lds_bytes(false, kWaves, a.S, D, BS, a.P, a.g, elt, a.wave_parts);
