@@ -165,13 +165,34 @@ static_assert(kMaxPairedSeqs <= 1024, "a sort key holds 10 bits of sequence inde
 // Paired mode: waves of the first unit, so that the busier unit's waves finish together.
 // With a second sequence each unit keeps at least one wave (even an empty one), so that
 // a split made from the host lengths never leaves a sequence without waves.
+// Paired mode: waves are ranked 0, NW/2, 1, NW/2 + 1, ... (rank r = wave w gives w =
+// r / 2 + (r % 2) * NW / 2).  The two waves on a SIMD progress at different rates (the first
+// half of the workgroup's waves ~1.5x faster than the second on gfx950), so a wave of the first
+// half (even rank) takes 3 steps for every 2 of a wave of the second half (odd rank).
+__host__ __device__ constexpr int rank_weight(int rank) { return rank % 2 == 0 ? 3 : 2; }
+__host__ __device__ inline int rank_capacity(int r0, int r1) {
+  int c = 0;
+  for (int r = r0; r < r1; ++r) c += rank_weight(r);
+  return c;
+}
+
+// Paired mode: waves (ranks [0, nA)) of the first unit, chosen so that the two units' steps per
+// unit of capacity are as even as possible (exact integer comparisons, so that the host and the
+// kernel choose alike).  With a second sequence each unit keeps at least one wave (even an empty
+// one), so that a split made from the host lengths never leaves a sequence without waves.
 __host__ __device__ inline int split_waves(int nw, int stA, int stB, bool two) {
   if (!two) return nw;
-  int nA = 1, best = 1 << 30;
+  int nA = 1;
+  long long bn = -1, bd = 1;                                 // best max(stA/capA, stB/capB)
   for (int c = 1; c < nw; ++c) {
-    const int tA = (stA + c - 1) / c, tB = (stB + nw - c - 1) / (nw - c);
-    const int t = tA > tB ? tA : tB;
-    if (t < best) { best = t; nA = c; }
+    const long long capA = rank_capacity(0, c), capB = rank_capacity(c, nw);
+    const bool a_max = (long long)stA * capB >= (long long)stB * capA;
+    const long long tn = a_max ? stA : stB, td = a_max ? capA : capB;
+    if (bn < 0 || tn * bd < bn * td) {
+      bn = tn;
+      bd = td;
+      nA = c;
+    }
   }
   return nA;
 }
@@ -333,10 +354,14 @@ paged_decode_kernel(const DecodeParams a, const OrderArg<PAIRED> ord) {
       nA = split_waves(NW, (LA + kStep - 1) / kStep, (LB + kStep - 1) / kStep, sB >= 0);
     }
     nA = __builtin_amdgcn_readfirstlane(nA);
-    onA = wave < nA;
+    // The two halves of the workgroup's waves share the SIMDs (wave w and w + NW / 2 on one)
+    // and progress at different rates, so the units take waves alternately from the two
+    // halves: unit A the first nA of waves 0, NW/2, 1, NW/2 + 1, ...
+    const int rank = (wave % (NW / 2)) * 2 + wave / (NW / 2);
+    onA = rank < nA;
     uidx = onA ? 0 : 1;
     s = onA ? sA : sB;
-    lw = onA ? wave : wave - nA;
+    lw = onA ? rank : rank - nA;
     nw = onA ? nA : NW - nA;
     tblw = tbl + (onA ? 0 : win);
   } else if constexpr (PREFIX) {
@@ -1004,9 +1029,39 @@ paged_decode_kernel(const DecodeParams a, const OrderArg<PAIRED> ord) {
     }
   };
 
-  // ---- the wave's steps: st = lw, lw + nw, ... ----------------------------------------
+  // ---- the wave's steps ----------------------------------------------------------------
+  // Paired mode: the unit's steps are dealt in rounds of its waves' total weight, each wave
+  // taking a run of rank_weight(rank) consecutive steps per round.  Other modes: st = lw,
+  // lw + nw, ...
   const int nsteps = (tok1 - tok0 + kStep - 1) / kStep;
-  if constexpr (PIPE == 2) {
+  if constexpr (PAIRED && PIPE == 2) {
+    const int r0 = onA ? 0 : nA;                             // the unit's first rank
+    const int cw = rank_weight(r0 + lw);                     // this wave's steps per round
+    const int round = __builtin_amdgcn_readfirstlane(rank_capacity(r0, r0 + nw));
+    const int pre = __builtin_amdgcn_readfirstlane(rank_capacity(r0, r0 + lw));
+    auto step_of = [&](int k) { return (k / cw) * round + pre + k % cw; };
+    StepData<T, C, D> b0, b1;
+    int k = 0;
+    int cur = step_of(0);                                    // the step in b0
+    if (cur < nsteps) {
+      load_step(cur, b0);
+      int nxt = step_of(1);                                  // the step prefetched next
+      for (;;) {
+        load_step(nxt < nsteps ? nxt : cur, b1);
+        __builtin_amdgcn_sched_barrier(0);
+        compute_step(cur, b0);
+        if (nxt >= nsteps) break;
+        cur = nxt;
+        nxt = step_of(++k + 1);
+        load_step(nxt < nsteps ? nxt : cur, b0);
+        __builtin_amdgcn_sched_barrier(0);
+        compute_step(cur, b1);
+        if (nxt >= nsteps) break;
+        cur = nxt;
+        nxt = step_of(++k + 1);
+      }
+    }
+  } else if constexpr (PIPE == 2) {
     StepData<T, C, D> b0, b1;
     int st = lw;
     if (st < nsteps) {
@@ -1190,13 +1245,18 @@ paged_decode_kernel(const DecodeParams a, const OrderArg<PAIRED> ord) {
     const int u = idx / (rows_out * D);
     const int h = (idx % (rows_out * D)) / D;
     const int d = idx % D;
-    const int w0 = u ? nA : 0, w1 = u ? NW : nA;
+    // the unit's waves (paired mode: ranks [0, nA) are unit A, as assigned above)
+    auto in_unit = [&](int w) {
+      return !PAIRED || (((w % (NW / 2)) * 2 + w / (NW / 2)) < nA) == (u == 0);
+    };
     const int su = PAIRED ? (u ? sB : sA) : s;
     float M = kNegInf;
-    for (int w = w0; w < w1; ++w) M = fmaxf(M, red[w * wstride + h]);
+    for (int w = 0; w < NW; ++w)
+      if (in_unit(w)) M = fmaxf(M, red[w * wstride + h]);
     float num = 0.f, den = 0.f;
     if (M != kNegInf) {
-      for (int w = w0; w < w1; ++w) {
+      for (int w = 0; w < NW; ++w) {
+        if (!in_unit(w)) continue;
         const float* r = red + w * wstride;
         const float f = exp2_fast(r[h] - M);
         den += f * r[16 + h];
