@@ -524,7 +524,7 @@ def bench_fp8(args) -> int:
     new = np.array([w.seq_records[s][-1] for s in range(w.num_seqs)], dtype=np.int64)
     hist = np.setdiff1d(np.arange(len(w.rec_slot)), new)
     kshape = pk.k_cache_shape(w.num_blocks, w.num_kv_heads, w.head_dim, w.block_size)
-    vshape = (w.num_blocks, w.num_kv_heads, w.head_dim, w.block_size)
+    vshape = pk.v_cache_shape(w.num_blocks, w.num_kv_heads, w.head_dim, w.block_size, torch.uint8)
     kc0 = torch.full(kshape, 0x7F, dtype=torch.uint8, device=dev)     # NaN codes
     vc0 = torch.full(vshape, 0x7F, dtype=torch.uint8, device=dev)
     pk.reshape_and_cache_fp8(up(w.rec_key[hist]), up(w.rec_value[hist]),

@@ -37,12 +37,14 @@
  * Cache layout (one K pool and one V pool):
  *   k_cache: [num_blocks][num_kv_heads][BS][D]   (token-major: a token's K row of
  *            one kv head is D contiguous elements)
- *   v_cache: [num_blocks][num_kv_heads][D][BS]   (channel-major: one channel's BS
- *            tokens are contiguous)
+ *   v_cache: [num_blocks][num_kv_heads][BS / X][D][X]   (token groups: X =
+ *            min(16 / element bytes, BS) consecutive tokens of one channel are
+ *            one contiguous 16-byte chunk, the groups channel-major)
+ * X is 8 for bf16, 4 for f32 and 16 for FP8 codes (8 at BS 8).
  * Token t of a sequence with block-table row `bt` lives in physical block
  * b = bt[t / BS] at offset o = t % BS; its K channel d is k_cache[b][h][o][d] and
- * its V channel d is v_cache[b][h][d][o].  One (block, kv head) tile of either
- * pool is BS * D contiguous elements.  A slot is b * BS + o.
+ * its V channel d is v_cache[b][h][o / X][d][o % X].  One (block, kv head) tile
+ * of either pool is BS * D contiguous elements.  A slot is b * BS + o.
  *
  * Device-side preconditions (not checked by the library; violating them gives
  * wrong results but no access outside the buffers passed in):
@@ -59,7 +61,7 @@
 extern "C" {
 #endif
 
-#define PA_ABI_VERSION 5
+#define PA_ABI_VERSION 6
 
 typedef enum {
     PA_OK = 0,
@@ -339,7 +341,7 @@ pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_mapp
  *
  * Layout: the pools above with 1-byte elements:
  *   k_cache: [num_blocks][num_kv_heads][BS][D] uint8
- *   v_cache: [num_blocks][num_kv_heads][D][BS] uint8
+ *   v_cache: [num_blocks][num_kv_heads][BS / X][D][X] uint8, X = min(16, BS)
  */
 
 /*

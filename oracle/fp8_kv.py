@@ -28,9 +28,9 @@ plainest reading of an FP8 K/V cache:
   4 + 24 significant bits, so float64 holds it exactly.
 * Attention over an FP8 cache is attention over the dequantised K and V.
 
-Cache layout: the boundary's layout with 1-byte elements, so X = 16:
-k_cache uint8 [num_blocks, Hkv, block_size, D], v_cache uint8
-[num_blocks, Hkv, D, block_size].
+Cache layout: the boundary's layout with 1-byte elements, so a V group is
+min(16, block_size) tokens: k_cache uint8 [num_blocks, Hkv, block_size, D],
+v_cache uint8 [num_blocks, Hkv, block_size / X, D, X].
 
 Pins (in the test suite): the code values the OCP specification lists
 (0, min subnormal, min normal, 1, 448, NaN), the format's monotone order,
@@ -114,8 +114,9 @@ def quantize_bf16(x_bits: np.ndarray, scale: float) -> np.ndarray:
 def empty_fp8_pools(num_blocks: int, num_kv_heads: int, head_dim: int, block_size: int,
                     fill: int = 0x7F):
     """FP8 pools filled with one code (NaN by default, so stray reads show)."""
+    X = min(16, block_size)
     ks = (num_blocks, num_kv_heads, block_size, head_dim)
-    vs = (num_blocks, num_kv_heads, head_dim, block_size)
+    vs = (num_blocks, num_kv_heads, block_size // X, head_dim, X)
     return np.full(ks, fill, dtype=np.uint8), np.full(vs, fill, dtype=np.uint8)
 
 

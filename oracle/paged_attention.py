@@ -33,9 +33,11 @@ Cache layout (the library's boundary format; the pages show only that a
 physical block yields its k and v):
 * k_cache: [num_blocks, Hkv, block_size, D] (token-major: one token's K row of
   one kv head is contiguous);
-* v_cache: [num_blocks, Hkv, D, block_size] (channel-major).
+* v_cache: [num_blocks, Hkv, block_size / X, D, X] with X = min(16 bytes / element,
+  block_size): the block's tokens in groups of X, each group channel-major (X
+  consecutive tokens of one channel are one 16-byte chunk).
 Element (token t, kv head h, channel d) of sequence s lives at
-``k_cache[b, h, t % BS, d]`` and ``v_cache[b, h, d, t % BS]`` with
+``k_cache[b, h, t % BS, d]`` and ``v_cache[b, h, (t % BS) // X, d, t % X]`` with
 ``b = block_table[s, t // BS]``.
 
 Precision: inputs are float32 arrays or bfloat16 bit patterns (uint16);
@@ -84,9 +86,15 @@ def k_cache_shape(num_blocks: int, num_kv_heads: int, head_dim: int, block_size:
     return (num_blocks, num_kv_heads, block_size, head_dim)
 
 
+def v_group(block_size: int, element_bytes: int) -> int:
+    """Tokens per V group: one 16-byte chunk of a channel, at most the block."""
+    return min(16 // element_bytes, block_size)
+
+
 def v_cache_shape(num_blocks: int, num_kv_heads: int, head_dim: int, block_size: int,
                   dtype: str) -> tuple:
-    return (num_blocks, num_kv_heads, head_dim, block_size)
+    X = v_group(block_size, ELEMENT_BYTES[dtype])
+    return (num_blocks, num_kv_heads, block_size // X, head_dim, X)
 
 
 # ---------------------------------------------------------------------------
@@ -106,9 +114,10 @@ def reshape_and_cache(key: np.ndarray, value: np.ndarray, slot_mapping: np.ndarr
     live = np.nonzero(slots >= 0)[0]
     assert len(np.unique(slots[live])) == len(live), "slots of one call must be distinct"
     assert (slots[live] < NB * BS).all(), "slot outside the pool"
+    X = v_cache.shape[4]
     blk, off = slots[live] // BS, slots[live] % BS
     k_new[blk, :, off, :] = key[live]
-    v_new[blk, :, :, off] = value[live]
+    v_new[blk, :, off // X, :, off % X] = value[live]
     return k_new, v_new
 
 
@@ -177,7 +186,8 @@ def gather_sequence(block_table_row: np.ndarray, context_len: int,
     n = -(-L // BS)
     blocks = np.asarray(block_table_row[:n], dtype=np.int64)
     k = k_cache[blocks].transpose(0, 2, 1, 3).reshape(n * BS, Hkv, D)[:L]
-    v = v_cache[blocks].transpose(0, 3, 1, 2).reshape(n * BS, Hkv, D)[:L]
+    # [n, Hkv, BS / X, D, X] -> [n, BS / X, X, Hkv, D]: token (group, x) = group * X + x
+    v = v_cache[blocks].transpose(0, 2, 4, 1, 3).reshape(n * BS, Hkv, D)[:L]
     return k, v
 
 

@@ -12,7 +12,7 @@ from .binding import (LIB_PATH, PreparedCall, chunk_elems, copy_blocks, decode_m
                       prepare_swap_blocks, swap_blocks, paged_attention_fp8, paged_prefill, prepare_copy_blocks,
                       prepare_decode_step, prepare_paged_attention, prepare_paged_attention_fp8,
                       prepare_reshape_and_cache, prepare_reshape_and_cache_fp8, reshape_and_cache,
-                      reshape_and_cache_fp8, v_cache_shape, workspace_size)
+                      reshape_and_cache_fp8, v_cache_shape, v_group, workspace_size)
 
 __all__ = ["LIB_PATH", "PreparedCall", "chunk_elems", "copy_blocks", "decode_math",
            "decode_step", "get_decode_math", "set_decode_math",
@@ -23,4 +23,4 @@ __all__ = ["LIB_PATH", "PreparedCall", "chunk_elems", "copy_blocks", "decode_mat
            "paged_attention", "paged_attention_fp8", "paged_prefill", "prepare_copy_blocks",
            "prepare_decode_step", "prepare_paged_attention", "prepare_paged_attention_fp8",
            "prepare_reshape_and_cache", "prepare_reshape_and_cache_fp8", "reshape_and_cache",
-           "reshape_and_cache_fp8", "v_cache_shape", "workspace_size"]
+           "reshape_and_cache_fp8", "v_cache_shape", "v_group", "workspace_size"]

@@ -146,17 +146,25 @@ def k_cache_shape(num_blocks, num_kv_heads, head_dim, block_size, dtype=None) ->
     return (num_blocks, num_kv_heads, block_size, head_dim)
 
 
-def v_cache_shape(num_blocks, num_kv_heads, head_dim, block_size, dtype=None) -> tuple:
-    """V pool shape: channel-major [NB, Hkv, D, BS]."""
-    return (num_blocks, num_kv_heads, head_dim, block_size)
+def v_group(block_size: int, dtype: torch.dtype) -> int:
+    """Tokens per V group: one 16-byte chunk of a channel, at most the block."""
+    return min(chunk_elems(dtype), block_size)
+
+
+def v_cache_shape(num_blocks, num_kv_heads, head_dim, block_size, dtype) -> tuple:
+    """V pool shape: token groups of X = v_group(block_size, dtype) tokens, channel-major
+    within a group: [NB, Hkv, BS / X, D, X]."""
+    X = v_group(block_size, dtype)
+    return (num_blocks, num_kv_heads, block_size // X, head_dim, X)
 
 
 def _cache_dims(k_cache: torch.Tensor, v_cache: torch.Tensor):
-    if k_cache.dim() != 4 or v_cache.dim() != 4:
-        raise ValueError("k_cache must be [NB, Hkv, BS, D] and v_cache [NB, Hkv, D, BS]")
+    if k_cache.dim() != 4 or v_cache.dim() != 5:
+        raise ValueError("k_cache must be [NB, Hkv, BS, D] and v_cache [NB, Hkv, BS / X, D, X]")
     NB, Hkv, BS, D = k_cache.shape
-    if tuple(v_cache.shape) != (NB, Hkv, D, BS) or v_cache.dtype != k_cache.dtype:
-        raise ValueError(f"v_cache must be {(NB, Hkv, D, BS)} of {k_cache.dtype}, got "
+    want = v_cache_shape(NB, Hkv, D, BS, k_cache.dtype)
+    if tuple(v_cache.shape) != want or v_cache.dtype != k_cache.dtype:
+        raise ValueError(f"v_cache must be {want} of {k_cache.dtype}, got "
                          f"{tuple(v_cache.shape)} of {v_cache.dtype}")
     return NB, Hkv, D, BS
 

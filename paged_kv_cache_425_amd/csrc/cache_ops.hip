@@ -7,8 +7,8 @@
 // (page "vLLM core architecture", section 2.2.2) as plain copies.
 //
 // Both are bit-exact copies; K moves in 16-byte chunks (a token's K row is
-// contiguous in the token-major K pool), V element by element (its cache rows
-// run along tokens).
+// contiguous in the token-major K pool), V element by element (a token holds one
+// element of each channel's 16-byte token group).
 #include "common.h"
 
 namespace pa {
@@ -17,7 +17,7 @@ constexpr int kCopyThreads = 256;
 
 // One workgroup per token.  Thread c moves 16-byte chunk c of the token's K
 // (c < Hkv*D/X) or V (the rest): K chunks land whole in the cache, V chunks
-// are split into X single-element stores along the cache's token axis.  The
+// are split into X single-element stores, one per channel's token group.  The
 // source chunk is loaded before the slot is looked at, so the two loads are
 // in flight together.
 template <typename T>
@@ -43,10 +43,11 @@ reshape_and_cache_kernel(const T* __restrict__ key, const T* __restrict__ value,
     if (!is_v) {
       store16(k_cache + (((size_t)blk * Hkv + h) * BS + off) * D + (size_t)dc * X, val);
     } else {
-      T* dst = v_cache + (((size_t)blk * Hkv + h) * D + (size_t)dc * X) * BS + off;
+      const int Xv = v_group<T>(BS);
+      T* dst = v_cache + ((size_t)blk * Hkv + h) * D * BS + v_offset(off, dc * X, D, Xv);
       const T* e = reinterpret_cast<const T*>(&val);
 #pragma unroll
-      for (int k = 0; k < X; ++k) dst[(size_t)k * BS] = e[k];
+      for (int k = 0; k < X; ++k) dst[(size_t)k * Xv] = e[k];
     }
   }
 }
@@ -84,7 +85,8 @@ gather_kv_kernel(T* __restrict__ k_out, T* __restrict__ v_out,
     const int r = e % (Hkv * D);
     const int h = r / D;
     const int d = r % D;
-    v_out[((row0 + o) * Hkv + h) * D + d] = v_cache[((phys * Hkv + h) * D + d) * BS + o];
+    v_out[((row0 + o) * Hkv + h) * D + d] =
+        v_cache[(phys * Hkv + h) * D * BS + v_offset(o, d, D, v_group<T>(BS))];
   }
 }
 

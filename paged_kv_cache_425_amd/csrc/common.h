@@ -137,6 +137,19 @@ struct ElemTraits<uint8_t> {             // OCP FP8 E4M3 codes (K/V cache storag
   static constexpr bool kBf16 = false;
 };
 
+// V cache tile of one (block, kv head): the block's BS tokens in groups of
+// Xv = min(elements per 16 bytes, BS) tokens, each group channel-major, so that Xv
+// consecutive tokens of one channel are one 16-byte chunk (an appended token touches one
+// 16-byte chunk per channel, 8 channels per 128-byte line).  Element (token o, channel d)
+// sits at ((o / Xv) * D + d) * Xv + o % Xv.
+template <typename T>
+__host__ __device__ constexpr int v_group(int BS) {
+  return ElemTraits<T>::kX < BS ? ElemTraits<T>::kX : BS;
+}
+__host__ __device__ inline size_t v_offset(int o, int d, int D, int Xv) {
+  return ((size_t)(o / Xv) * D + d) * Xv + o % Xv;
+}
+
 // ---- FP8 E4M3 (OCP): 1 sign, 4 exponent bits (bias 7), 3 mantissa bits; exponent field 0
 // holds subnormals m * 2^-9; S.1111.111 is NaN; no infinities; largest finite 448. ----
 

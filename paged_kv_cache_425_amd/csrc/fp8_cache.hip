@@ -38,7 +38,7 @@ __device__ __forceinline__ void load8_elems(const T* p, float (&x)[8]) {
 
 // One workgroup per token.  Thread c quantises 8 consecutive channels of the token's K
 // (c < Hkv*D/8) or V (the rest): K codes are one 8-byte store into the token's K row,
-// V codes are 8 byte stores along the cache's token axis.
+// V codes are 8 byte stores, one into each channel's token group.
 template <typename T>
 __global__ void __launch_bounds__(kFp8Threads)
 reshape_and_cache_fp8_kernel(const T* __restrict__ key, const T* __restrict__ value,
@@ -73,10 +73,11 @@ reshape_and_cache_fp8_kernel(const T* __restrict__ key, const T* __restrict__ va
       uint8_t* dst = k_cache + (((size_t)blk * Hkv + h) * BS + off) * D + d0;
       *reinterpret_cast<uint2*>(dst) = make_uint2(codes[0], codes[1]);
     } else {
-      uint8_t* dst = v_cache + (((size_t)blk * Hkv + h) * D + (size_t)d0) * BS + off;
+      const int Xv = v_group<uint8_t>(BS);
+      uint8_t* dst = v_cache + ((size_t)blk * Hkv + h) * D * BS + v_offset(off, d0, D, Xv);
 #pragma unroll
       for (int k = 0; k < 8; ++k)
-        dst[(size_t)k * BS] = static_cast<uint8_t>(codes[k >> 2] >> (8 * (k & 3)));
+        dst[(size_t)k * Xv] = static_cast<uint8_t>(codes[k >> 2] >> (8 * (k & 3)));
     }
   }
 }

@@ -249,6 +249,8 @@ paged_decode_kernel(const DecodeParams a, const OrderArg<PAIRED> ord) {
   constexpr int kNq = Sh::kNq;
   constexpr int kNs = Sh::kNs;
   constexpr int kThreads = NW * 64;
+  constexpr int kXv = v_group<C>(BS);                      // tokens per V group
+  static_assert(kXv == kTpl || (kFp8 && BS == 8), "a lane's V tokens are one group");
 
   // LDS: [ctrl: 16 ints][new K/V: 2 units x 2 x D elements][sort keys: S ints, PAIRED only]
   //      [tables: 1 or 2 windows of P/BS][merge]
@@ -650,10 +652,10 @@ paged_decode_kernel(const DecodeParams a, const OrderArg<PAIRED> ord) {
         uint8_t* dst = kcw + ((blk * a.Hkv + kvh) * BS + off) * D + d0;
         *reinterpret_cast<uint2*>(dst) = make_uint2(new_val[0], new_val[1]);
       } else {
-        uint8_t* dst = vcw + ((blk * a.Hkv + kvh) * D + (size_t)d0) * BS + off;
+        uint8_t* dst = vcw + (blk * a.Hkv + kvh) * D * BS + v_offset(off, d0, D, kXv);
 #pragma unroll
         for (int k = 0; k < 8; ++k)
-          dst[(size_t)k * BS] = static_cast<uint8_t>(new_val[k >> 2] >> (8 * (k & 3)));
+          dst[(size_t)k * kXv] = static_cast<uint8_t>(new_val[k >> 2] >> (8 * (k & 3)));
       }
     } else if (new_slot != loc) {
       T* kcw = const_cast<T*>(static_cast<const T*>(a.k_cache));
@@ -663,10 +665,10 @@ paged_decode_kernel(const DecodeParams a, const OrderArg<PAIRED> ord) {
       if (!new_is_v) {
         store16(kcw + ((blk * a.Hkv + kvh) * BS + off) * D + (size_t)new_cc * kSx, new_val);
       } else {
-        T* dst = vcw + ((blk * a.Hkv + kvh) * D + (size_t)new_cc * kX) * BS + off;
+        T* dst = vcw + (blk * a.Hkv + kvh) * D * BS + v_offset(off, new_cc * kX, D, kXv);
         const T* e = reinterpret_cast<const T*>(&new_val);
 #pragma unroll
-        for (int k = 0; k < kX; ++k) dst[(size_t)k * BS] = e[k];
+        for (int k = 0; k < kX; ++k) dst[(size_t)k * kXv] = e[k];
       }
     }
   }
@@ -701,26 +703,27 @@ paged_decode_kernel(const DecodeParams a, const OrderArg<PAIRED> ord) {
 #pragma unroll
       for (int c = 0; c < kNc; ++c) b.k[t][c] = load16(kp + 4 * c * kX);
     }
-    // V operand of slice sl: channel 16*sl + n, tokens base + kTpl*j .. + kTpl - 1.  A group
-    // wholly past the end reads the group of the last live token (in bounds; it is zeroed
-    // before use).
+    // V operand of slice sl: channel 16*sl + n, tokens base + kTpl*j .. + kTpl - 1 -- one
+    // 16-byte token group of the channel, so the 16 lanes of a row read 256 contiguous
+    // bytes.  A group wholly past the end reads the group of the last live token (in
+    // bounds; it is zeroed before use).
     const int tokv = min(base + kTpl * j, (tok1 - 1) / kTpl * kTpl);
     const int physv = tblw[(tokv - tok0) / BS];
-    const C* vp = vc + ((size_t)physv * a.Hkv + kvh) * head_elems + (size_t)n * BS + (tokv % BS);
+    const C* vp = vc + ((size_t)physv * a.Hkv + kvh) * head_elems + v_offset(tokv % BS, n, D, kXv);
     if constexpr (kFp8 && BS < 16) {
-      // 16 tokens span two blocks of 8: two 8-byte halves (the second clamped like tokv)
+      // 16 tokens span two blocks of 8: two 8-byte groups (the second clamped like tokv)
       const int tokv2 = min(tokv + 8, (tok1 - 1) / 8 * 8);
       const int physv2 = tblw[(tokv2 - tok0) / BS];
-      const C* vp2 = vc + ((size_t)physv2 * a.Hkv + kvh) * head_elems + (size_t)n * BS;
+      const C* vp2 = vc + ((size_t)physv2 * a.Hkv + kvh) * head_elems + v_offset(0, n, D, kXv);
 #pragma unroll
       for (int sl = 0; sl < kNs; ++sl) {
-        const uint2 lo = load8_nt(vp + (size_t)16 * sl * BS);
-        const uint2 hi = load8_nt(vp2 + (size_t)16 * sl * BS);
+        const uint2 lo = load8_nt(vp + (size_t)16 * sl * kXv);
+        const uint2 hi = load8_nt(vp2 + (size_t)16 * sl * kXv);
         b.v[sl] = u32x4{lo.x, lo.y, hi.x, hi.y};
       }
     } else {
 #pragma unroll
-      for (int sl = 0; sl < kNs; ++sl) b.v[sl] = v_load(vp + (size_t)16 * sl * BS);
+      for (int sl = 0; sl < kNs; ++sl) b.v[sl] = v_load(vp + (size_t)16 * sl * kXv);
     }
   };
 
@@ -771,8 +774,8 @@ paged_decode_kernel(const DecodeParams a, const OrderArg<PAIRED> ord) {
           // 16 tokens per lane; at BS 8 they are two 8-byte halves in two blocks
           const int half_tok = BS < 16 ? tokv + (e & 8) : tokv;
           const int physv = tblw[(half_tok - tok0) / BS];
-          uint8_t* vp = vcw + ((size_t)physv * a.Hkv + kvh) * head_elems + (size_t)n * BS +
-                        (BS < 16 ? 0 : tokv % BS);
+          uint8_t* vp = vcw + ((size_t)physv * a.Hkv + kvh) * head_elems +
+                        v_offset(BS < 16 ? 0 : tokv % BS, n, D, kXv);
 #pragma unroll
           for (int sl = 0; sl < kNs; ++sl) {
             const uint32_t code = nv[16 * sl + n];
@@ -780,10 +783,10 @@ paged_decode_kernel(const DecodeParams a, const OrderArg<PAIRED> ord) {
             b.v[sl][e >> 2] = (b.v[sl][e >> 2] & ~(0xFFu << sh)) | (code << sh);
             if constexpr (BS < 16) {
               const int h = e >> 3;
-              *reinterpret_cast<uint2*>(vp + (size_t)16 * sl * BS) =
+              *reinterpret_cast<uint2*>(vp + (size_t)16 * sl * kXv) =
                   make_uint2(b.v[sl][2 * h], b.v[sl][2 * h + 1]);
             } else {
-              store16(vp + (size_t)16 * sl * BS, b.v[sl]);
+              store16(vp + (size_t)16 * sl * kXv, b.v[sl]);
             }
           }
         }
@@ -811,7 +814,7 @@ paged_decode_kernel(const DecodeParams a, const OrderArg<PAIRED> ord) {
       const int e = lm1 - tokv;
       if (e >= 0 && e < kTpl) {
         const int physv = tblw[(tokv - tok0) / BS];
-        T* vp = vcw + ((size_t)physv * a.Hkv + kvh) * head_elems + (size_t)n * BS + (tokv % BS);
+        T* vp = vcw + ((size_t)physv * a.Hkv + kvh) * head_elems + v_offset(tokv % BS, n, D, kXv);
 #pragma unroll
         for (int sl = 0; sl < kNs; ++sl) {
           const T val = nv[16 * sl + n];
@@ -824,7 +827,7 @@ paged_decode_kernel(const DecodeParams a, const OrderArg<PAIRED> ord) {
           } else {
             b.v[sl][e] = __builtin_bit_cast(uint32_t, val);
           }
-          store16(vp + (size_t)16 * sl * BS, b.v[sl]);
+          store16(vp + (size_t)16 * sl * kXv, b.v[sl]);
         }
       }
     }

@@ -167,7 +167,8 @@ paged_prefill_kernel(const PrefillParams a) {
   };
 
   // chunk ids: K id = key * (D / kX) + q (q = 16-byte chunk of the key's row in the
-  // token-major K pool), V id = channel * (kStep / kX) + group; consecutive threads read
+  // token-major K pool), V id = group * D + channel (a V chunk is one channel's group of
+  // kX tokens, and the groups of a block are channel-major); consecutive threads read
   // consecutive addresses within a block.
   // A step is kStep keys starting at a multiple of kStep.  When BS divides kStep, each
   // chunk's block within the step and its offset inside the block are fixed per thread
@@ -175,6 +176,7 @@ paged_prefill_kernel(const PrefillParams a) {
   // also adds its own offset inside the block.  Blocks past the last one with a seen key
   // are clamped to it (in bounds; those keys are masked, their V zeroed).
   static_assert(kStep % BS == 0 || BS % kStep == 0, "steps and blocks must nest");
+  static_assert(v_group<T>(BS) == kX, "a V chunk is one token group");
   static_assert(Sh::kKChunks % kThreads == 0 && Sh::kVChunks % kThreads == 0,
                 "every thread stages whole chunks of K and V");
   int k_blk[kLoadsK], v_blk[kLoadsV];                       // block offset within the step
@@ -189,9 +191,9 @@ paged_prefill_kernel(const PrefillParams a) {
 #pragma unroll
   for (int i = 0; i < kLoadsV; ++i) {
     const int cid = threadIdx.x + i * kThreads;
-    const int ch = cid / (kStep / kX), grp = cid % (kStep / kX);
+    const int ch = cid % D, grp = cid / D;
     v_blk[i] = grp * kX / BS;
-    v_off[i] = ch * BS + grp * kX % BS;
+    v_off[i] = (int)v_offset(grp * kX % BS, ch, D, kX);
   }
   // bytes per physical block (all kv heads), < 2^32: Hkv * D * BS * elt
   const uint32_t blk_bytes = static_cast<uint32_t>((size_t)a.Hkv * head_elems * sizeof(T));
@@ -210,14 +212,15 @@ paged_prefill_kernel(const PrefillParams a) {
   auto fetch = [&](int st) {
     const int b0 = st * kStep / BS;                          // first block of the step
     const int tb0 = b0 / 1024 * 1024;                        // its table window
-    // kStep < BS (f32, BS 32): the step's offset inside its block
+    // kStep < BS (f32, BS 32): the step's offset inside its block, D * elt bytes per token
+    // in both pools (a V group of kX tokens spans D chunks)
     const size_t boff = kStep < BS ? (size_t)(st * kStep % BS) * sizeof(T) : 0;
 #pragma unroll
     for (int i = 0; i < kLoadsK; ++i)
       kreg[i] = load16(at(kp[i], tbl_lds[b0 - tb0 + k_blk[i]]) + boff * D);
 #pragma unroll
     for (int i = 0; i < kLoadsV; ++i)
-      vreg[i] = load16(at(vp[i], tbl_lds[b0 - tb0 + v_blk[i]]) + boff);
+      vreg[i] = load16(at(vp[i], tbl_lds[b0 - tb0 + v_blk[i]]) + boff * D);
   };
   auto stage = [&](int st, int buf) {
     const int base = st * kStep;
@@ -233,7 +236,7 @@ paged_prefill_kernel(const PrefillParams a) {
       // zero positions >= L (kmax <= L): weight 0 must not meet NaN
 #pragma unroll
       for (int i = 0; i < kLoadsV; ++i) {
-        const int grp = (threadIdx.x + i * kThreads) % (kStep / kX);
+        const int grp = (threadIdx.x + i * kThreads) / D;
         const int nv = min(max(kmax - (base + grp * kX), 0), kX);
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
@@ -249,7 +252,7 @@ paged_prefill_kernel(const PrefillParams a) {
 #pragma unroll
     for (int i = 0; i < kLoadsV; ++i) {
       const int cid = threadIdx.x + i * kThreads;
-      const int ch = cid / (kStep / kX), grp = cid % (kStep / kX);
+      const int ch = cid % D, grp = cid / D;
       *reinterpret_cast<u32x4*>(vb + (ch * Sh::kVRow + grp) * 16) = vreg[i];
     }
   };

@@ -44,7 +44,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.pa_abi_version() == 5
+    assert lib.pa_abi_version() == 6
     for code in range(5):
         assert lib.pa_status_string(code).decode().startswith("PA_")
     assert b"unknown" in lib.pa_status_string(99)

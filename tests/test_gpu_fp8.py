@@ -149,7 +149,7 @@ def test_every_code_decodes_exactly():
     codes = np.resize(rng.permutation(np.tile(finite, 2)), (S, Hkv, D))
     for s in range(S):
         b = int(w.block_table[s, 0])
-        vc[b, :, :, 0] = codes[s]
+        vc[b, :, 0, :, 0] = codes[s]                      # token 0, every channel
     say("attention_fp8 every code")
     got = run_attention(w, kc, vc, 1.0, 1.0)
     want = oracle.e4m3_decode(codes)                       # [S, Hkv, D]
@@ -183,8 +183,8 @@ def _device_pools_of(w, recs):
     """FP8 pools (NaN codes elsewhere) holding records ``recs``, written by the library."""
     kshape = (w.num_blocks, w.num_kv_heads, w.block_size, w.head_dim)
     kd = torch.full(kshape, 0x7F, dtype=torch.uint8, device=DEV)
-    vd = torch.full((w.num_blocks, w.num_kv_heads, w.head_dim, w.block_size), 0x7F,
-                    dtype=torch.uint8, device=DEV)
+    vd = torch.full(pk.v_cache_shape(w.num_blocks, w.num_kv_heads, w.head_dim, w.block_size,
+                                     torch.uint8), 0x7F, dtype=torch.uint8, device=DEV)
     step = 1 << 16
     for r0 in range(0, len(recs), step):
         r = recs[r0:r0 + step]

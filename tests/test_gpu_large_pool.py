@@ -53,7 +53,7 @@ def test_fused_step_and_prefill_beyond_4gib(setup):
     new = np.array([w.seq_records[s][-1] for s in range(w.num_seqs)], dtype=np.int64)
     hist = np.setdiff1d(np.arange(len(w.rec_slot)), new)
     ks = (HIGH, w.num_kv_heads, w.block_size, w.head_dim)
-    vs = (HIGH, w.num_kv_heads, w.head_dim, w.block_size)
+    vs = pk.v_cache_shape(HIGH, w.num_kv_heads, w.head_dim, w.block_size, torch.bfloat16)
     say("large pool: bf16 pools of 4.6 GB each")
     kd = torch.full(ks, float("nan"), dtype=torch.bfloat16, device=DEV)
     vd = torch.full(vs, float("nan"), dtype=torch.bfloat16, device=DEV)
@@ -110,7 +110,7 @@ def test_fp8_beyond_4gib(setup):
     new = np.array([w.seq_records[s][-1] for s in range(w.num_seqs)], dtype=np.int64)
     hist = np.setdiff1d(np.arange(len(w.rec_slot)), new)
     ks = (HIGH8, w.num_kv_heads, w.block_size, w.head_dim)
-    vs = (HIGH8, w.num_kv_heads, w.head_dim, w.block_size)
+    vs = pk.v_cache_shape(HIGH8, w.num_kv_heads, w.head_dim, w.block_size, torch.uint8)
     say("large pool: FP8 pools of 4.6 GB each")
     kd = torch.full(ks, 0x7F, dtype=torch.uint8, device=DEV)
     vd = torch.full(vs, 0x7F, dtype=torch.uint8, device=DEV)

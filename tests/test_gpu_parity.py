@@ -501,7 +501,7 @@ def test_prefill_with_large_v_magnitudes(D, BS, g):
     v = (vc.astype(np.uint32) << 16).view(np.float32).copy()      # bf16 bits -> values
     v[::3] *= 16.0
     b, kvh = int(w.block_table[6, 2]), 1                            # a block sequence 6 reads
-    v[b, kvh, 5, 3] = 2.0 ** 17
+    v[b, kvh, 0, 5, 3] = 2.0 ** 17                                 # token 3, channel 5
     vc = (v.view(np.uint32) >> 16).astype(np.uint16)
     assert np.abs(np.nan_to_num(v)).max() > 65504
     say(f"prefill with large V, D={D} BS={BS} g={g}")

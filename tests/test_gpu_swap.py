@@ -35,7 +35,8 @@ def say(msg: str) -> None:
 
 
 def shapes(nb, Hkv, D, BS, dtype):
-    return (nb, Hkv, BS, D), (nb, Hkv, D, BS)
+    X = min(16 // np.dtype(NP[dtype]).itemsize, BS)          # tokens per V group
+    return (nb, Hkv, BS, D), (nb, Hkv, BS // X, D, X)
 
 
 def random_pools(rng, nb, Hkv, D, BS, dtype):
@@ -182,7 +183,7 @@ def test_pageable_host_memory_is_refused_before_launch():
     lib = pk.load_library()
     pageable = np.zeros((4, 2, 16, 64), dtype=np.uint16)      # not pinned, not mapped
     dk = torch.zeros((4, 2, 16, 64), dtype=torch.bfloat16, device=DEV)
-    dv = torch.zeros((4, 2, 64, 16), dtype=torch.bfloat16, device=DEV)
+    dv = torch.zeros((4, 2, 2, 64, 8), dtype=torch.bfloat16, device=DEV)
     mapping = torch.tensor([[0, 1]], dtype=torch.int64, device=DEV)
     say("swap with pageable host memory: refused")
     st = lib.pa_swap_blocks(ctypes.c_void_p(pageable.ctypes.data), dk.data_ptr(),
@@ -191,10 +192,10 @@ def test_pageable_host_memory_is_refused_before_launch():
     assert st == 1
     with pytest.raises(ValueError):
         pk.swap_blocks(torch.zeros((4, 2, 16, 64), dtype=torch.bfloat16), dv.new_zeros(
-            (4, 2, 64, 16)).cpu(), dk, dv, mapping)
+            (4, 2, 2, 64, 8)).cpu(), dk, dv, mapping)
     # the refused call leaves no error behind: the next call goes through
     hk = torch.zeros((4, 2, 16, 64), dtype=torch.bfloat16, pin_memory=True)
-    hv = torch.zeros((4, 2, 64, 16), dtype=torch.bfloat16, pin_memory=True)
+    hv = torch.zeros((4, 2, 2, 64, 8), dtype=torch.bfloat16, pin_memory=True)
     dk.fill_(1.5)
     pk.swap_blocks(dk, dv, hk, hv, mapping)
     torch.cuda.synchronize()

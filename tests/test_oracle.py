@@ -90,7 +90,10 @@ def _golden():
         return np.array(x, dtype=object).astype(float).astype(np.float32)
 
     nanify = lambda x: np.where(np.array(x, dtype=object) == None, np.nan, x).astype(np.float32)  # noqa: E711,E731
-    return g, nanify(g["k_cache"]), nanify(g["v_cache"]), arr
+    # The fixture lists V as [block][kv_head][d][offset].  With 2-token blocks of f32 a block
+    # is a single V group, so the pool's [block][kv_head][group][d][offset in group] holds the
+    # same numbers with a unit group axis.
+    return g, nanify(g["k_cache"]), nanify(g["v_cache"])[:, :, None, :, :], arr
 
 
 def test_golden_layout_shapes():
@@ -126,7 +129,7 @@ def test_golden_append_then_attention():
     changed_v = ~((vc2 == vc) | (np.isnan(vc2) & np.isnan(vc)))
     # slot 1 = physical block 0, offset 1: only those elements changed
     assert changed_k.sum() == 8 and changed_k[0, :, 1, :].all()
-    assert changed_v.sum() == 8 and changed_v[0, :, :, 1].all()
+    assert changed_v.sum() == 8 and changed_v[0, :, 0, :, 1].all()   # group 0, offset 1
     out = oracle.paged_attention(arr(g["query"]), np.array(g["block_table"]),
                                  np.array(a["context_lens_after"]), kc2, vc2, g["scale"], "f32")
     np.testing.assert_allclose(out[0], np.array(a["expected_out_seq0"], dtype=float),
@@ -150,14 +153,16 @@ def test_gather_matches_flat_index_loop_and_never_paged_records(dtype, BS, D):
         # the never-paged sequence the pool was filled from
         assert np.array_equal(k, w.rec_key[w.seq_records[s]])
         assert np.array_equal(v, w.rec_value[w.seq_records[s]])
-        # one element at a time, flat offsets written out by hand
+        # one element at a time, flat offsets written out by hand (V: groups of X tokens,
+        # X = min(16 bytes / element, BS), each group channel-major)
+        X = min(16 // (4 if dtype == "f32" else 2), BS)
         for t in range(int(w.context_lens[s])):
             b = int(w.block_table[s, t // BS])
             o = t % BS
             for h in range(Hkv):
                 for d in range(D):
                     ko = ((b * Hkv + h) * BS + o) * D + d
-                    vo = ((b * Hkv + h) * D + d) * BS + o
+                    vo = (((b * Hkv + h) * (BS // X) + o // X) * D + d) * X + o % X
                     assert k[t, h, d] == kflat[ko]
                     assert v[t, h, d] == vflat[vo]
 
@@ -175,8 +180,9 @@ def test_scatter_touches_only_its_slots_and_skips_negative():
         if slot < 0:
             assert np.array_equal(kc2[blk, :, off, :], kc[blk, :, off, :])
             continue
+        X = vc.shape[4]
         kc2[blk, :, off, :] = kc[blk, :, off, :]
-        vc2[blk, :, :, off] = vc[blk, :, :, off]
+        vc2[blk, :, off // X, :, off % X] = vc[blk, :, off // X, :, off % X]
     assert np.array_equal(kc2, kc) and np.array_equal(vc2, vc)  # nothing else changed
 
 
@@ -450,7 +456,8 @@ def test_swap_blocks_matches_element_loop(dtype):
 
     def pool(nb):
         k = rng.integers(0, 255, size=shape_k(nb)).astype(np_t)
-        v = rng.integers(0, 255, size=(nb, Hkv, D, BS)).astype(np_t)
+        X = min(16 // np.dtype(np_t).itemsize, BS)
+        v = rng.integers(0, 255, size=(nb, Hkv, BS // X, D, X)).astype(np_t)
         return k, v
 
     sk, sv = pool(10)

@@ -189,7 +189,7 @@ def test_nan_codes_poison_only_their_reader(bad):
     kc, vc = _fp8_pools(w, 1.0, 1.0)
     s = 3                                        # longest sequence
     b = int(w.block_table[s, 0])
-    vc[b, 0, 5, 0] = bad
+    vc[b, 0, 0, 5, 0] = bad                      # token 0 of the block, kv head 0, channel 5
     out = oracle.paged_attention_fp8(w.query, w.block_table, w.context_lens, kc, vc, w.scale,
                                      1.0, 1.0, "bf16")
     g = w.num_heads // w.num_kv_heads
