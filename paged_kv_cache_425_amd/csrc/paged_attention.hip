@@ -99,6 +99,7 @@ struct DecodeParams {
   const void* new_v;
   const int64_t* new_slot;
   int S, Hq, Hkv, g, MB, NB, P, Pmax;
+  int max_len;             // the caller's max_context_len (host-side launch choices only)
   int wave_parts;          // partition mode: 1 = each wave owns one partition of NW in a row
   float scale_log2;        // scale * log2(e) (* k_scale for FP8 K): base-2 logits
   float v_scale;           // output multiplier: 1, or the FP8 V scale
@@ -166,13 +167,16 @@ static_assert(kMaxPairedSeqs <= 1024, "a sort key holds 10 bits of sequence inde
 // With a second sequence each unit keeps at least one wave (even an empty one), so that
 // a split made from the host lengths never leaves a sequence without waves.
 // Paired mode: waves are ranked 0, NW/2, 1, NW/2 + 1, ... (rank r = wave w gives w =
-// r / 2 + (r % 2) * NW / 2).  The two waves on a SIMD progress at different rates (the first
-// half of the workgroup's waves ~1.5x faster than the second on gfx950), so a wave of the first
-// half (even rank) takes 3 steps for every 2 of a wave of the second half (odd rank).
-__host__ __device__ constexpr int rank_weight(int rank) { return rank % 2 == 0 ? 3 : 2; }
-__host__ __device__ inline int rank_capacity(int r0, int r1) {
+// r / 2 + (r % 2) * NW / 2).  With 8 waves, two share each SIMD and progress at different
+// rates (the first half of the workgroup's waves ~1.5x faster than the second on gfx950), so
+// a wave of the first half (even rank) takes 3 steps for every 2 of a wave of the second half
+// (odd rank).  With 4 waves (one per SIMD of the workgroup) every wave takes 1.
+__host__ __device__ constexpr int rank_weight(int rank, int nw) {
+  return nw == 8 ? (rank % 2 == 0 ? 3 : 2) : 1;
+}
+__host__ __device__ inline int rank_capacity(int r0, int r1, int nw) {
   int c = 0;
-  for (int r = r0; r < r1; ++r) c += rank_weight(r);
+  for (int r = r0; r < r1; ++r) c += rank_weight(r, nw);
   return c;
 }
 
@@ -185,7 +189,7 @@ __host__ __device__ inline int split_waves(int nw, int stA, int stB, bool two) {
   int nA = 1;
   long long bn = -1, bd = 1;                                 // best max(stA/capA, stB/capB)
   for (int c = 1; c < nw; ++c) {
-    const long long capA = rank_capacity(0, c), capB = rank_capacity(c, nw);
+    const long long capA = rank_capacity(0, c, nw), capB = rank_capacity(c, nw, nw);
     const bool a_max = (long long)stA * capB >= (long long)stB * capA;
     const long long tn = a_max ? stA : stB, td = a_max ? capA : capB;
     if (bn < 0 || tn * bd < bn * td) {
@@ -326,7 +330,7 @@ paged_decode_kernel(const DecodeParams a, const OrderArg<PAIRED> ord) {
       // nparts-th slice (x / S) of the keys and leaves a partial count in the merge area
       // (free until the end), and thread t then adds its partial counts.
       int* part_rank = reinterpret_cast<int*>(red);           // [nparts][S]
-      const int nparts = max(1, kThreads / a.S);              // S <= kThreads here
+      const int nparts = max(1, kThreads / a.S);              // 1 when S >= kThreads
       const int nq = lens_words / 4;                          // int4 groups of keys
       const int per = (nq + nparts - 1) / nparts;
       for (int x = threadIdx.x; x < nparts * a.S; x += kThreads) {
@@ -1039,9 +1043,9 @@ paged_decode_kernel(const DecodeParams a, const OrderArg<PAIRED> ord) {
   const int nsteps = (tok1 - tok0 + kStep - 1) / kStep;
   if constexpr (PAIRED && PIPE == 2) {
     const int r0 = onA ? 0 : nA;                             // the unit's first rank
-    const int cw = rank_weight(r0 + lw);                     // this wave's steps per round
-    const int round = __builtin_amdgcn_readfirstlane(rank_capacity(r0, r0 + nw));
-    const int pre = __builtin_amdgcn_readfirstlane(rank_capacity(r0, r0 + lw));
+    const int cw = rank_weight(r0 + lw, NW);                 // this wave's steps per round
+    const int round = __builtin_amdgcn_readfirstlane(rank_capacity(r0, r0 + nw, NW));
+    const int pre = __builtin_amdgcn_readfirstlane(rank_capacity(r0, r0 + lw, NW));
     auto step_of = [&](int k) { return (k / cw) * round + pre + k % cw; };
     StepData<T, C, D> b0, b1;
     int k = 0;
@@ -1343,7 +1347,7 @@ reduce_partitions_kernel(const DecodeParams a) {
 }
 
 constexpr int kWaves = PA_DECODE_WAVES;     // waves per workgroup, partition mode
-constexpr int kPairWaves = 8;               // waves per workgroup, paired mode
+constexpr int kPairWaves = 8;               // waves per workgroup, paired mode (at most)
 constexpr int kPipe = PA_DECODE_PIPE;
 constexpr size_t kMaxLds = 64 * 1024;
 
@@ -1353,8 +1357,11 @@ inline size_t decode_lds_bytes(bool paired, int nw, int S, int D, int BS, int P,
   const size_t lens_words = paired ? (size_t)(S + 3) / 4 * 4 : 0;
   const size_t tbl_words =
       ((size_t)(paired ? 2 : (wave_parts ? nw : 1)) * (P / BS) + 3) / 4 * 4;
-  return 64 + 4 * (size_t)D * elt +
-         4 * (lens_words + tbl_words + (size_t)nw * merge_words(D, g));
+  // the merge area also holds the paired ranking's partial counts, [max(1, threads / S)][S]
+  // ints <= max(S, threads)
+  const size_t merge = std::max((size_t)nw * merge_words(D, g),
+                                paired ? (size_t)std::max(S, nw * 64) : (size_t)0);
+  return 64 + 4 * (size_t)D * elt + 4 * (lens_words + tbl_words + merge);
 }
 
 // Paired mode when every sequence is one partition, there are at least two
@@ -1366,8 +1373,8 @@ inline bool use_paired(const DecodeParams& a, int D, int BS, int elt) {
 
 // The paired mode's order of the sequences from a host copy of the lengths: the same
 // keys the kernel ranks (clamped length, then lower index first), sorted on the host.
-inline void order_on_host(const DecodeParams& a, int BS, int step, const int32_t* host_lens,
-                          PairOrder& ord) {
+inline void order_on_host(const DecodeParams& a, int BS, int step, int nw,
+                          const int32_t* host_lens, PairOrder& ord) {
   const long cap = std::min((long)a.MB * BS, (long)a.P * a.Pmax);
   uint32_t key[kMaxPairedSeqs];
   for (int t = 0; t < a.S; ++t) {
@@ -1382,7 +1389,7 @@ inline void order_on_host(const DecodeParams& a, int BS, int step, const int32_t
     const uint32_t sB = r == a.S - 1 - r ? 0xFFFFu : 1023u - (kB & 1023u);
     const int LA = (int)(kA >> 10), LB = sB == 0xFFFFu ? 0 : (int)(kB >> 10);
     const uint32_t bA = (LA + BS - 1) / BS, bB = (LB + BS - 1) / BS;
-    const uint32_t nA = split_waves(kPairWaves, (LA + step - 1) / step, (LB + step - 1) / step,
+    const uint32_t nA = split_waves(nw, (LA + step - 1) / step, (LB + step - 1) / step,
                                     sB != 0xFFFFu);
     ord.pair[r] = make_uint2(sA | sB << 16, bA | bB << 12 | nA << 24);
   }
@@ -1404,20 +1411,39 @@ int device_cu_count() {
   return n;
 }
 
+// Paired mode's waves per workgroup.  8 (two per SIMD) keep a compute unit's loads in
+// flight from one workgroup.  When the pairs outnumber the compute units and are short --
+// the two longest sequences together within 32 steps -- 4 waves do better: two workgroups
+// share a compute unit, so one's prologue and merge run under the other's loads
+// (parallel-sampling batch: 22.5 against 26.4 us; the others slower).  The choice uses only
+// max_context_len, not the host lengths, so that a call with and without them runs alike.
+inline int pair_waves(const DecodeParams& a, int step, int max_context_len) {
+  const long wgs = (long)(a.S + 1) / 2 * a.Hkv;
+  return wgs > device_cu_count() && 2L * max_context_len <= 32L * step ? 4 : kPairWaves;
+}
+
+template <typename T, typename C, int D, int BS, int VG, int NW>
+hipError_t launch_paired(const DecodeParams& a, const int32_t* host_lens, hipStream_t stream) {
+  constexpr int elt = sizeof(T);
+  const size_t lds = decode_lds_bytes(true, NW, a.S, D, BS, a.P, a.g, elt);
+  PairOrder ord;
+  if (host_lens)
+    order_on_host(a, BS, StepShape<T, C, D>::kStep, NW, host_lens, ord);
+  else
+    for (int r = 0; r < (a.S + 1) / 2; ++r) ord.pair[r] = make_uint2(kNoPlan, 0u);
+  hipLaunchKernelGGL((paged_decode_kernel<T, C, D, BS, NW, kPipe, true, false, VG>),
+                     dim3((unsigned)a.Hkv, (unsigned)((a.S + 1) / 2)), dim3(NW * 64), lds,
+                     stream, a, ord);
+  return hipGetLastError();
+}
+
 template <typename T, typename C, int D, int BS, int VG = 0>
 hipError_t launch_decode(const DecodeParams& a, const int32_t* host_lens, hipStream_t stream) {
   constexpr int elt = sizeof(T);
   if (use_paired(a, D, BS, elt)) {
-    const size_t lds = decode_lds_bytes(true, kPairWaves, a.S, D, BS, a.P, a.g, elt);
-    PairOrder ord;
-    if (host_lens)
-      order_on_host(a, BS, StepShape<T, C, D>::kStep, host_lens, ord);
-    else
-      for (int r = 0; r < (a.S + 1) / 2; ++r) ord.pair[r] = make_uint2(kNoPlan, 0u);
-    hipLaunchKernelGGL((paged_decode_kernel<T, C, D, BS, kPairWaves, kPipe, true, false, VG>),
-                       dim3((unsigned)a.Hkv, (unsigned)((a.S + 1) / 2)), dim3(kPairWaves * 64),
-                       lds, stream, a, ord);
-    return hipGetLastError();
+    if (pair_waves(a, StepShape<T, C, D>::kStep, a.max_len) == 4)
+      return launch_paired<T, C, D, BS, VG, 4>(a, host_lens, stream);
+    return launch_paired<T, C, D, BS, VG, kPairWaves>(a, host_lens, stream);
   }
   const size_t lds = decode_lds_bytes(false, kWaves, a.S, D, BS, a.P, a.g, elt, a.wave_parts);
   const long groups = a.wave_parts ? (a.Pmax + kWaves - 1) / kWaves : a.Pmax;
@@ -1635,6 +1661,7 @@ pa_status run_decode(void* out, const void* query, const int32_t* block_table,
   a.NB = num_blocks;
   a.P = P;
   a.Pmax = pmax;
+  a.max_len = max_context_len;
   a.pfx_len = 0;
   a.grp = 0;
   // Short partitions: each wave of a workgroup owns one of kWaves consecutive
