@@ -51,7 +51,7 @@ def parse_args():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--op", default="step",
                     choices=["step", "copy_blocks", "prefill", "fp8", "swap", "ceiling",
-                             "math"],
+                             "math", "balance", "coexec"],
                     help="step: the decode step (default); copy_blocks: the copy-on-write "
                          "copies of the parallel-sampling workload; prefill: paged prefill; "
                          "fp8: the decode step over FP8 (E4M3) K/V pools; swap: swapping a "
@@ -60,7 +60,10 @@ def parse_args():
                          "streaming and as a gather of scattered 4 KB tiles, every launch "
                          "shape of the sweep; math: the fused step of the Llama-3-8B "
                          "batch with its two products on the matrix cores and on the vector "
-                         "ALU, at group sizes 1, 2 and 4 over the same KV")
+                         "ALU, at group sizes 1, 2 and 4 over the same KV; balance: the "
+                         "fused step of the Llama-3-8B batch against batches of the same "
+                         "bytes whose pairs are exactly balanced or whose lengths are equal; "
+                         "coexec: the MFMA / VALU co-execution probe")
     ap.add_argument("--prefill-case", default="prefix-cache-prefill",
                     choices=["prefix-cache-prefill", "chunked-prefill-llama3-8b"])
     ap.add_argument("--config", type=int, default=1, choices=[0, 1, 2, 3, 4])
@@ -848,6 +851,127 @@ def bench_math(args) -> int:
     return 0
 
 
+def balanced_pair_lengths(lens: np.ndarray) -> np.ndarray:
+    """The same lengths spread, rearranged so that the paired mode's pairs (r-th longest with
+    r-th shortest) all hold the same tokens: the r-th shortest becomes 2 * mean - r-th
+    longest (at least 1)."""
+    s = np.sort(lens)[::-1].astype(np.int64)
+    n = len(s)
+    total = 2 * int(round(float(lens.mean())))
+    out = s.copy()
+    for r in range(n // 2):
+        out[n - 1 - r] = max(1, total - int(s[r]))
+    return out
+
+
+def bench_balance(args) -> int:
+    """The fused step of the Llama-3-8B batch and of two batches with (about) the same KV
+    bytes: one whose pairs (longest with shortest) hold exactly the mean tokens, one with
+    every length equal to the mean.  If the pairs' imbalance set the step's time, the
+    balanced batches would run faster by the imbalance."""
+    import torch
+
+    import paged_kv_cache_425_amd as pk
+    from workloads import make_config, make_workload
+
+    dev = torch.device("cuda:0")
+    base = make_config(1, seed=args.seed)
+    L = base.context_lens
+    variants = [("llama3-8b-decode-bf16", base),
+                ("balanced-pairs", make_workload(
+                    name="balanced-pairs", context_lens=balanced_pair_lengths(L),
+                    num_heads=base.num_heads, num_kv_heads=base.num_kv_heads,
+                    head_dim=base.head_dim, block_size=base.block_size, dtype="bf16", seed=1)),
+                ("equal-lengths", make_workload(
+                    name="equal-lengths", context_lens=np.full(len(L), int(round(float(L.mean())))),
+                    num_heads=base.num_heads, num_kv_heads=base.num_kv_heads,
+                    head_dim=base.head_dim, block_size=base.block_size, dtype="bf16", seed=1))]
+    up = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)  # noqa: E731
+    K, W, R = args.steps, args.warmup, max(4, args.replicas)
+    rows = {}
+    for name, w in variants:
+        tdt = torch.bfloat16
+        new = np.array([w.seq_records[s][-1] for s in range(w.num_seqs)], dtype=np.int64)
+        hist = np.setdiff1d(np.arange(len(w.rec_slot)), new)
+        kc0 = torch.full(pk.k_cache_shape(w.num_blocks, w.num_kv_heads, w.head_dim, w.block_size,
+                                          tdt), float("nan"), dtype=tdt, device=dev)
+        vc0 = torch.full(pk.v_cache_shape(w.num_blocks, w.num_kv_heads, w.head_dim, w.block_size,
+                                          tdt), float("nan"), dtype=tdt, device=dev)
+        pk.reshape_and_cache(up(w.rec_key[hist]), up(w.rec_value[hist]),
+                             torch.from_numpy(w.rec_slot[hist]).to(dev), kc0, vc0)
+        pools = [(kc0, vc0)] + [(kc0.clone(), vc0.clone()) for _ in range(R - 1)]
+        q, kn, vn = up(w.query), up(w.rec_key[new]), up(w.rec_value[new])
+        sl = torch.from_numpy(w.rec_slot[new]).to(dev)
+        tb = torch.from_numpy(w.block_table).to(dev)
+        ln = torch.from_numpy(w.context_lens).to(dev)
+        out = torch.empty_like(q)
+        calls = [pk.prepare_decode_step(q, kn, vn, sl, tb, ln, kc, vc, w.scale,
+                                        max_context_len=w.max_context_len, out=out,
+                                        host_context_lens=w.context_lens.copy())
+                 for kc, vc in pools]
+        for i in range(W):
+            calls[i % R]()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(K):
+            calls[i % R]()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / K
+        s = np.sort(w.context_lens)[::-1].astype(np.int64)
+        pairs = [int(s[r] + (s[len(s) - 1 - r] if len(s) - 1 - r != r else 0))
+                 for r in range((len(s) + 1) // 2)]
+        kv = int(w.context_lens.astype(np.int64).sum()) * 2 * w.num_kv_heads * w.head_dim * 2
+        rows[name] = {"launch_us_events": round(us, 2), "kv_bytes": kv,
+                      "pair_tokens_max": max(pairs), "pair_tokens_mean": round(float(np.mean(pairs)), 1),
+                      "tokens": int(w.context_lens.sum())}
+        log(f"{name}: {us:.2f} us/launch, pair tokens max {max(pairs)} mean {np.mean(pairs):.1f}")
+        del pools, calls
+        torch.cuda.empty_cache()
+    print(json.dumps({"metric": "fused decode step us/launch, Llama-3-8B batch vs balanced batches",
+                      "unit": "us", "n_gpus": 1, "steps": K, "warmup": W, "pool_replicas": R,
+                      "higher_is_better": False, "dtype": "bf16", "data": "synthetic",
+                      "config": {"workload": "llama3-8b-decode-bf16 and two length variants"},
+                      "rows": rows}), flush=True)
+    return 0
+
+
+def bench_coexec(args) -> int:
+    """The co-execution probe (pa_coexec_probe) at one workgroup per compute unit: MFMA work
+    only, VALU work only, both interleaved in every wave, and split between the two waves of
+    each SIMD; best of 5 launches each."""
+    import torch
+
+    import paged_kv_cache_425_amd as pk
+    dev = torch.device("cuda:0")
+    wgs = torch.cuda.get_device_properties(dev).multi_processor_count
+    iters = 4096
+    out = torch.empty(wgs * 8 * 64, dtype=torch.float32, device=dev)
+    cases = [("mfma", 4), ("valu", 4), ("interleaved", 4), ("mfma", 8), ("valu", 8),
+             ("split", 8), ("interleaved", 8)]
+    rows = []
+    for mode, waves in cases:
+        best = None
+        for _ in range(5):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            pk.coexec_probe(mode, wgs, waves, iters, out)
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1)
+            best = ms if best is None else min(best, ms)
+        rows.append({"mode": mode, "waves_per_workgroup": waves, "best_ms": round(best, 4)})
+        log(f"{mode:12s} {waves} waves/WG: {best:.4f} ms")
+    print(json.dumps({"metric": "MFMA / VALU co-execution probe, ms per launch (best of 5)",
+                      "unit": "ms", "n_gpus": 1, "higher_is_better": False, "data": "synthetic",
+                      "config": {"workload": "coexec probe", "workgroups": wgs,
+                                 "iterations_per_wave": iters,
+                                 "work_per_iteration": "8 MFMA 16x16x32 bf16 and/or 32 FMA"},
+                      "rows": rows}), flush=True)
+    return 0
+
+
 def main() -> int:
     args = parse_args()
     if args.gpus != 1:
@@ -875,6 +999,10 @@ def main() -> int:
         return bench_ceiling(args)
     if args.op == "math":
         return bench_math(args)
+    if args.op == "balance":
+        return bench_balance(args)
+    if args.op == "coexec":
+        return bench_coexec(args)
     dev = torch.device("cuda:0")
 
     t = time.perf_counter()

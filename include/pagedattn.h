@@ -468,8 +468,8 @@ pa_math pa_get_decode_math(void);
  *                  workgroups * in_flight pieces further on, and so on
  *   in_flight      4, 8 or 16: pieces whose 16-byte loads each thread issues
  *                  before using any of them
- *   nontemporal    0: default-policy loads; 1: streaming (nt) loads, the policy the
- *                  paged decode uses when its workgroups are all resident at once
+ *   nontemporal    0: default-policy loads; 1: streaming (nt) loads, the policy of
+ *                  the paged decode's V loads
  *   sink           [workgroups * 256] uint32, device: written with checksums
  * Returns PA_ERR_INVALID_ARG / PA_ERR_UNSUPPORTED for bad arguments (nothing
  * launched).
@@ -477,6 +477,26 @@ pa_math pa_get_decode_math(void);
 pa_status pa_read_probe(const void* buf, const int64_t* piece_offsets, int num_pieces,
                         int piece_bytes, int workgroups, int in_flight, int nontemporal,
                         uint32_t* sink, void* stream);
+
+/*
+ * Diagnostic co-execution probe (not a step of any path).  A SIMD of gfx950 can run
+ * matrix-core (MFMA) and vector-ALU work at once; this call shows when.  Every wave
+ * runs `iters` iterations of its work -- MFMA work: 8 independent chains of 16x16x32
+ * bf16 MFMAs; VALU work: 32 fused multiply-adds over 8 independent chains -- and the
+ * launch's time (events on `stream`) is the answer:
+ *   mode 0  MFMA work only            mode 1  VALU work only
+ *   mode 2  both in every wave, one MFMA then four FMAs
+ *   mode 3  MFMA work in the even waves, VALU work in the odd ones (waves w and w + 4
+ *           of a workgroup share a SIMD)
+ *   workgroups           >= 1
+ *   waves_per_workgroup  4 (one wave per SIMD) or 8 (two)
+ *   iters                1 .. 2^20
+ *   out                  [workgroups * waves_per_workgroup * 64] float, device:
+ *                        written with one value per thread
+ * Returns PA_ERR_INVALID_ARG for bad arguments (nothing launched).
+ */
+pa_status pa_coexec_probe(int mode, int workgroups, int waves_per_workgroup, int iters,
+                          float* out, void* stream);
 
 #ifdef __cplusplus
 }

@@ -64,6 +64,8 @@ def load_library() -> ctypes.CDLL:
     lib.pa_decode_step_shared_prefix.argtypes = [vp] * 9 + [i32] * 9 + [f32, i32, vp, vp]
     lib.pa_read_probe.restype = i32
     lib.pa_read_probe.argtypes = [vp, vp, i32, i32, i32, i32, i32, vp, vp]
+    lib.pa_coexec_probe.restype = i32
+    lib.pa_coexec_probe.argtypes = [i32, i32, i32, i32, vp, vp]
     lib.pa_decode_step_noalloc.restype = i32
     lib.pa_decode_step_noalloc.argtypes = [vp] * 9 + [i32] * 8 + [f32, i32, i32, vp, vp]
     lib.pa_paged_attention_fp8.restype = i32
@@ -695,6 +697,24 @@ def read_probe(buf: torch.Tensor, piece_offsets: torch.Tensor, piece_bytes: int,
     _check(load_library().pa_read_probe(_ptr(buf), _ptr(piece_offsets), n, int(piece_bytes),
                                         int(workgroups), int(in_flight), int(bool(nontemporal)),
                                         _ptr(sink), _stream(dev, stream)), "pa_read_probe")
+
+
+COEXEC_MODES = {"mfma": 0, "valu": 1, "interleaved": 2, "split": 3}
+
+
+def coexec_probe(mode: str, workgroups: int, waves_per_workgroup: int, iters: int,
+                 out: torch.Tensor, stream=None) -> None:
+    """Co-execution probe (pa_coexec_probe): MFMA work, VALU work, both interleaved in
+    every wave, or split between the two waves of each SIMD; time it with events."""
+    dev = out.device
+    _require(out, "out", dev, torch.float32)
+    if mode not in COEXEC_MODES:
+        raise ValueError(f"mode must be one of {sorted(COEXEC_MODES)}")
+    if out.numel() < workgroups * waves_per_workgroup * 64:
+        raise ValueError(f"out must hold {workgroups * waves_per_workgroup * 64} floats")
+    _check(load_library().pa_coexec_probe(COEXEC_MODES[mode], int(workgroups),
+                                          int(waves_per_workgroup), int(iters), _ptr(out),
+                                          _stream(dev, stream)), "pa_coexec_probe")
 
 
 DECODE_MATH = {"mfma": 0, "valu": 1}

@@ -7,6 +7,11 @@
 // streaming read, or shuffled, for the paged gather) and keeps only a checksum, so
 // its rate is the ceiling the decode's loads can reach on this part, with default or
 // streaming (nt) loads.  It is a diagnostic next to the decode path, not a step of it.
+//
+// A second diagnostic, the co-execution probe, times matrix-core and vector-ALU work on
+// one SIMD: whether the VALU instructions of one wave run while the MFMAs of the same
+// wave, or of another wave on the SIMD, are in flight.  It decides how a kernel whose
+// steps alternate the two (the paged prefill) can overlap them.
 #include "common.h"
 
 namespace pa {
@@ -37,6 +42,66 @@ read_probe_kernel(const unsigned char* __restrict__ buf, const int64_t* __restri
     }
   }
   sink[(size_t)blockIdx.x * kProbeThreads + threadIdx.x] = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
+}
+
+// Co-execution probe.  Every wave runs `iters` iterations of its work: MFMA work is 8
+// independent chains of v_mfma_f32_16x16x32_bf16 (one MFMA each per iteration), VALU work
+// is 32 fused multiply-adds over 8 independent chains.  Mode 0: MFMA work only; 1: VALU
+// work only; 2: both in every wave, one MFMA then four FMAs (held in that order by
+// scheduling barriers); 3: MFMA work in the even waves of the workgroup and VALU work in
+// the odd ones (a workgroup's waves w and w + 4 share a SIMD).  One float per thread is
+// written so that no work is removed.
+constexpr int kCoexecMaxThreads = 512;
+
+__global__ void __launch_bounds__(kCoexecMaxThreads)
+coexec_probe_kernel(int mode, int iters, float seed, float* __restrict__ out) {
+  const int wave = threadIdx.x >> 6;
+  bool do_m = mode == 0 || mode == 2, do_v = mode == 1 || mode == 2;
+  if (mode == 3) {
+    do_m = (wave & 1) == 0;
+    do_v = !do_m;
+  }
+  bf16x8 a, b;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    a[i] = static_cast<__bf16>(seed * static_cast<float>(threadIdx.x + i));
+    b[i] = static_cast<__bf16>(seed - static_cast<float>(i));
+  }
+  f32x4 acc[8];
+  float v[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    acc[k] = f32x4{seed, seed, seed, seed};
+    v[k] = seed * static_cast<float>(k + 1) + static_cast<float>(threadIdx.x);
+  }
+  const float mul = 0.999f + seed * 1e-7f, add = 1e-3f * seed;
+  if (do_m && do_v) {
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        __builtin_amdgcn_sched_barrier(0);
+        acc[k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[k], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v[(k + q) & 7] = fmaf(v[(k + q) & 7], mul, add);
+      }
+    }
+  } else if (do_m) {
+    for (int it = 0; it < iters; ++it)
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        acc[k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[k], 0, 0, 0);
+  } else {
+    for (int it = 0; it < iters; ++it)
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v[(k + q) & 7] = fmaf(v[(k + q) & 7], mul, add);
+  }
+  float sum = 0.f;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) sum += acc[k][0] + acc[k][1] + acc[k][2] + acc[k][3] + v[k];
+  out[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = sum;
 }
 
 }  // namespace pa
@@ -75,5 +140,17 @@ extern "C" pa_status pa_read_probe(const void* buf, const int64_t* piece_offsets
     launch_probe<8>(nt, workgroups, s, b, piece_offsets, num_pieces, piece_bytes, sink);
   else
     launch_probe<16>(nt, workgroups, s, b, piece_offsets, num_pieces, piece_bytes, sink);
+  return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+extern "C" pa_status pa_coexec_probe(int mode, int workgroups, int waves_per_workgroup,
+                                     int iters, float* out, void* stream) {
+  if (mode < 0 || mode > 3 || workgroups <= 0 || iters <= 0 || iters > (1 << 20) ||
+      (waves_per_workgroup != 4 && waves_per_workgroup != 8))
+    return PA_ERR_INVALID_ARG;
+  if (!out || reinterpret_cast<uintptr_t>(out) % 4) return PA_ERR_INVALID_ARG;
+  hipLaunchKernelGGL(pa::coexec_probe_kernel, dim3((unsigned)workgroups),
+                     dim3((unsigned)(waves_per_workgroup * 64)), 0,
+                     static_cast<hipStream_t>(stream), mode, iters, 1.0f, out);
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
 }

@@ -28,13 +28,27 @@ def lib():
     return pk.load_library()
 
 
+def test_coexec_probe_rejects_before_launch(lib):
+    f = lib.pa_coexec_probe
+    f.restype = ctypes.c_int
+    f.argtypes = [ctypes.c_int] * 4 + [ctypes.c_void_p] * 2
+    assert f(4, 256, 8, 16, FAKE, None) == 1         # no such mode
+    assert f(-1, 256, 8, 16, FAKE, None) == 1
+    assert f(0, 0, 8, 16, FAKE, None) == 1           # no workgroups
+    assert f(0, 256, 6, 16, FAKE, None) == 1         # 4 or 8 waves only
+    assert f(0, 256, 8, 0, FAKE, None) == 1          # no iterations
+    assert f(0, 256, 8, (1 << 20) + 1, FAKE, None) == 1
+    assert f(0, 256, 8, 16, None, None) == 1         # no output
+    assert f(0, 256, 8, 16, FAKE + 2, None) == 1     # output misaligned
+
+
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted([
         "pa_abi_version", "pa_status_string", "pa_default_partition_size",
         "pa_paged_attention_workspace_size", "pa_paged_attention", "pa_reshape_and_cache",
         "pa_gather_kv", "pa_decode_step", "pa_copy_blocks", "pa_paged_prefill",
         "pa_reshape_and_cache_fp8", "pa_paged_attention_fp8", "pa_decode_step_fp8",
-        "pa_swap_blocks", "pa_decode_step_noalloc", "pa_read_probe",
+        "pa_swap_blocks", "pa_decode_step_noalloc", "pa_read_probe", "pa_coexec_probe",
         "pa_decode_step_shared_prefix", "pa_set_decode_math", "pa_get_decode_math"])
 
 
