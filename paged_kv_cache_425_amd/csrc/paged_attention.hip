@@ -41,8 +41,8 @@
 //   [D x tokens] . [tokens x head-rows]: dense contractions, run on
 //   v_mfma_f32_16x16x32_bf16 (bf16) or v_mfma_f32_16x16x4_f32 (f32).
 //   With the cache layout of pagedattn.h every MFMA operand is one 16-byte
-//   load per lane straight from HBM: K rows of 8 channels for Q.K^T, V rows of
-//   8 (bf16) or 4 (f32) consecutive tokens for P.V.
+//   load per lane straight from HBM: K rows of 8 channels for Q.K^T, one V token
+//   group -- 8 (bf16) or 4 (f32) consecutive tokens of one channel -- for P.V.
 //   For bf16 the softmax weights must enter the P.V product in bf16.  To keep
 //   float32 accuracy each weight is split p = hi + lo (both bf16, the error of
 //   the pair is ~2^-17 p) and the head group occupies 2g of the 16 MFMA rows:
@@ -56,7 +56,7 @@
 //
 // FP8 pools (cache element C = uint8_t, E4M3 codes; queries bf16)
 //   The cache element type is a template parameter.  With 1-byte codes a 16-byte
-//   load holds 16 channels of a K row or 16 tokens of a V row, so a step is 64
+//   load holds 16 channels of a K row or a 16-token V group, so a step is 64
 //   tokens (four 16-row K tiles) at the register cost of a 32-token bf16 step.
 //   Codes are widened to bf16 in registers (v_cvt_scalef32_pk_bf16_fp8 at scale 1,
 //   exact: every E4M3 value is a bf16 value) and go through the same bf16 MFMAs;
@@ -218,7 +218,8 @@ struct NoOrder {};
 template <bool PAIRED>
 using OrderArg = typename std::conditional<PAIRED, PairOrder, NoOrder>::type;
 
-// Pair-balanced mode (PAIRED): a workgroup of NW waves takes two
+// Pair-balanced mode (PAIRED): a workgroup of NW waves (8, or 4 for short pairs that
+// outnumber the compute units) takes two
 // (sequence, kv head) units -- the r-th longest and the r-th shortest
 // sequence -- and splits its waves between them in proportion to their steps,
 // so that every workgroup carries about the same number of tokens.  The order
