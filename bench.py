@@ -51,7 +51,7 @@ def parse_args():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--op", default="step",
                     choices=["step", "copy_blocks", "prefill", "fp8", "swap", "ceiling",
-                             "math", "balance", "coexec"],
+                             "math", "balance", "coexec", "writes"],
                     help="step: the decode step (default); copy_blocks: the copy-on-write "
                          "copies of the parallel-sampling workload; prefill: paged prefill; "
                          "fp8: the decode step over FP8 (E4M3) K/V pools; swap: swapping a "
@@ -63,7 +63,9 @@ def parse_args():
                          "ALU, at group sizes 1, 2 and 4 over the same KV; balance: the "
                          "fused step of the Llama-3-8B batch against batches of the same "
                          "bytes whose pairs are exactly balanced or whose lengths are equal; "
-                         "coexec: the MFMA / VALU co-execution probe")
+                         "coexec: the MFMA / VALU co-execution probe; writes: the decode of "
+                         "the continuous-batching mix after a scatter of N of its new tokens, "
+                         "against the two apart (what dirty cache lines cost the reads)")
     ap.add_argument("--prefill-case", default="prefix-cache-prefill",
                     choices=["prefix-cache-prefill", "chunked-prefill-llama3-8b"])
     ap.add_argument("--config", type=int, default=1, choices=[0, 1, 2, 3, 4])
@@ -972,6 +974,77 @@ def bench_coexec(args) -> int:
     return 0
 
 
+def bench_writes(args) -> int:
+    """What the append's writes cost the decode's reads: the decode of the continuous-batching
+    mix (BS 16; pa_paged_attention, host order) timed alone, a scatter of the first N of its
+    new tokens (pa_reshape_and_cache) timed alone, and the two alternating; the extra time
+    of the pair over the sum is the cost of the scatter's dirty lines to the reads."""
+    import torch
+
+    import paged_kv_cache_425_amd as pk
+    from workloads import make_config
+
+    dev = torch.device("cuda:0")
+    w = make_config(2, seed=args.seed, block_size=16)
+    tdt = torch.bfloat16
+    up = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(tdt).to(dev)  # noqa: E731
+    allr = np.arange(len(w.rec_slot))
+    new = np.array([w.seq_records[s][-1] for s in range(w.num_seqs)], dtype=np.int64)
+    kc0 = torch.zeros(pk.k_cache_shape(w.num_blocks, w.num_kv_heads, w.head_dim, w.block_size,
+                                       tdt), dtype=tdt, device=dev)
+    vc0 = torch.zeros(pk.v_cache_shape(w.num_blocks, w.num_kv_heads, w.head_dim, w.block_size,
+                                       tdt), dtype=tdt, device=dev)
+    pk.reshape_and_cache(up(w.rec_key[allr]), up(w.rec_value[allr]),
+                         torch.from_numpy(w.rec_slot[allr]).to(dev), kc0, vc0)
+    R = max(4, args.replicas)
+    pools = [(kc0, vc0)] + [(kc0.clone(), vc0.clone()) for _ in range(R - 1)]
+    q, out = up(w.query), torch.empty_like(up(w.query))
+    table = torch.from_numpy(w.block_table).to(dev)
+    lens = torch.from_numpy(w.context_lens).to(dev)
+    K, W = args.steps, args.warmup
+
+    def timed(calls):
+        for i in range(W):
+            calls[i % len(calls)]()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(K):
+            calls[i % len(calls)]()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / K
+
+    dec = [pk.prepare_paged_attention(q, table, lens, kc, vc, w.scale,
+                                      max_context_len=w.max_context_len, out=out,
+                                      host_context_lens=w.context_lens.copy())
+           for kc, vc in pools]
+    t_dec = timed(dec)
+    rows = []
+    for ntok in (8, 32, 64, 128, 256):
+        sel = new[:ntok]
+        key, val = up(w.rec_key[sel]), up(w.rec_value[sel])
+        slot = torch.from_numpy(w.rec_slot[sel]).to(dev)
+        sc = [pk.prepare_reshape_and_cache(key, val, slot, kc, vc) for kc, vc in pools]
+        both = []
+        for i in range(R):
+            both += [sc[i], dec[i]]
+        t_sc = timed(sc)
+        t_both = 2 * timed(both)
+        rows.append({"tokens_scattered": ntok,
+                     "dirty_lines_at_most": ntok * w.num_kv_heads * (2 + w.head_dim // 8),
+                     "scatter_us": round(t_sc, 2), "scatter_then_decode_us": round(t_both, 2),
+                     "extra_us": round(t_both - t_sc - t_dec, 2)})
+        log(f"{ntok} tokens: scatter {t_sc:.2f}, scatter+decode {t_both:.2f}, "
+            f"extra {t_both - t_sc - t_dec:.2f} us (decode alone {t_dec:.2f})")
+    print(json.dumps({"metric": "decode us after a scatter of N new tokens, continuous-batching mix",
+                      "unit": "us", "n_gpus": 1, "steps": K, "warmup": W, "pool_replicas": R,
+                      "higher_is_better": False, "dtype": "bf16", "data": "synthetic",
+                      "config": {"workload": w.name, "new_tokens": int(len(new))},
+                      "decode_alone_us": round(t_dec, 2), "rows": rows}), flush=True)
+    return 0
+
+
 def main() -> int:
     args = parse_args()
     if args.gpus != 1:
@@ -1003,6 +1076,8 @@ def main() -> int:
         return bench_balance(args)
     if args.op == "coexec":
         return bench_coexec(args)
+    if args.op == "writes":
+        return bench_writes(args)
     dev = torch.device("cuda:0")
 
     t = time.perf_counter()
