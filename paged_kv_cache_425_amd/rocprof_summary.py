@@ -186,7 +186,10 @@ def main() -> None:
     f = sub.add_parser("traffic")
     f.add_argument("--fetch", required=True)
     f.add_argument("--write", required=True)
-    f.add_argument("--kernel", required=True)
+    f.add_argument("--kernel", required=True,
+                   help="substring of the kernel's name that selects its dispatches")
+    f.add_argument("--label", default="",
+                   help="name of the kernel in the summary (default: --kernel)")
     f.add_argument("--copy-bytes", type=int, required=True)
     f.add_argument("--algorithmic-bytes", type=int, required=True)
     f.add_argument("--workload", required=True)
@@ -239,7 +242,8 @@ def main() -> None:
     with open(a.out_json, "w") as fh:
         json.dump(rec, fh, indent=1)
         fh.write("\n")
-    text = f"""# HBM traffic of `{a.kernel}` ({a.workload})
+    label = a.label or a.kernel
+    text = f"""# HBM traffic of `{label}` ({a.workload})
 
 Commands (from the repository root on the GPU box), one counter per run:
 
@@ -253,7 +257,7 @@ K/V pools, {a.copy_bytes} bytes each.  FETCH_SIZE reads {fread:.1f} KiB for them
 (median of {fn}), so its scale is {ff:.4f}; WRITE_SIZE reads {wread:.1f} KiB
 (median of {wn}), scale {wf:.4f}.
 
-| per launch of `{a.kernel}` | bytes |
+| per launch of `{label}` | bytes |
 |---|---|
 | FETCH_SIZE x scale (median of launches {a.start}..{a.start + len(fk) - 1}) | {fetch_b:,.0f} |
 | WRITE_SIZE x scale (median of launches {a.start}..{a.start + len(wk) - 1}) | {write_b:,.0f} |
