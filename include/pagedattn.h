@@ -480,7 +480,8 @@ pa_status pa_read_probe(const void* buf, const int64_t* piece_offsets, int num_p
 
 /*
  * Diagnostic co-execution probe (not a step of any path).  A SIMD of gfx950 can run
- * matrix-core (MFMA) and vector-ALU work at once; this call shows when.  Every wave
+ * matrix-core (MFMA) and vector-ALU work at once; this call measures how much of the
+ * two overlaps, within a wave and between the waves of a SIMD.  Every wave
  * runs `iters` iterations of its work -- MFMA work: 8 independent chains of 16x16x32
  * bf16 MFMAs; VALU work: 32 fused multiply-adds over 8 independent chains -- and the
  * launch's time (events on `stream`) is the answer:

@@ -9,9 +9,9 @@
 // streaming (nt) loads.  It is a diagnostic next to the decode path, not a step of it.
 //
 // A second diagnostic, the co-execution probe, times matrix-core and vector-ALU work on
-// one SIMD: whether the VALU instructions of one wave run while the MFMAs of the same
-// wave, or of another wave on the SIMD, are in flight.  It decides how a kernel whose
-// steps alternate the two (the paged prefill) can overlap them.
+// one SIMD: how far the VALU instructions of one wave run while the MFMAs of the same
+// wave, or of another wave on the SIMD, are in flight.  It bounds what a kernel whose
+// steps alternate the two (the paged prefill) can gain from overlapping them.
 #include "common.h"
 
 namespace pa {
