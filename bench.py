@@ -940,20 +940,35 @@ def bench_balance(args) -> int:
 
 
 def bench_coexec(args) -> int:
-    """The co-execution probe (pa_coexec_probe) at one workgroup per compute unit: MFMA work
-    only, VALU work only, both interleaved in every wave, and split between the two waves of
-    each SIMD; best of 5 launches each."""
+    """The co-execution probe (pa_coexec_probe): MFMA work only, VALU work only, both
+    interleaved in every wave, and split between the two waves of each SIMD, at one to four
+    waves per SIMD (4- or 8-wave workgroups, one to three of them per compute unit, all
+    launched together); best of 5 launches each.  `ms_per_unit` divides a row's time by the
+    units of work each SIMD does (one unit: one wave's iterations of its kind of work; M + V
+    for the interleaved and split rows)."""
     import torch
 
     import paged_kv_cache_425_amd as pk
     dev = torch.device("cuda:0")
-    wgs = torch.cuda.get_device_properties(dev).multi_processor_count
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
     iters = 4096
-    out = torch.empty(wgs * 8 * 64, dtype=torch.float32, device=dev)
-    cases = [("mfma", 4), ("valu", 4), ("interleaved", 4), ("mfma", 8), ("valu", 8),
-             ("split", 8), ("interleaved", 8)]
+    # (mode, waves per workgroup, workgroups per compute unit)
+    cases = [("mfma", 4, 1), ("valu", 4, 1), ("interleaved", 4, 1), ("mfma", 8, 1),
+             ("valu", 8, 1), ("split", 8, 1), ("interleaved", 8, 1),
+             ("mfma", 4, 3), ("valu", 4, 3), ("interleaved", 4, 3),
+             ("mfma", 8, 2), ("valu", 8, 2), ("split", 8, 2), ("interleaved", 8, 2)]
+    out = torch.empty(3 * cus * 8 * 64, dtype=torch.float32, device=dev)
+    # where the waves run: the split rows need waves w and w + 4 of a workgroup on one SIMD
+    pk.coexec_probe("placement", cus, 8, 1, out)
+    torch.cuda.synchronize()
+    simd = out[:cus * 8 * 64].view(cus, 8, 64)[:, :, 0].cpu()
+    paired = bool((simd[:, :4] == simd[:, 4:]).all())
+    log(f"placement: waves w and w + 4 share a SIMD in every workgroup: {paired}")
     rows = []
-    for mode, waves in cases:
+    for mode, waves, per_cu in cases:
+        wgs = cus * per_cu
+        per_simd = waves // 4 * per_cu
+        units = per_simd // 2 if mode == "split" else per_simd
         best = None
         for _ in range(5):
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -963,11 +978,15 @@ def bench_coexec(args) -> int:
             torch.cuda.synchronize()
             ms = e0.elapsed_time(e1)
             best = ms if best is None else min(best, ms)
-        rows.append({"mode": mode, "waves_per_workgroup": waves, "best_ms": round(best, 4)})
-        log(f"{mode:12s} {waves} waves/WG: {best:.4f} ms")
+        rows.append({"mode": mode, "waves_per_workgroup": waves, "workgroups": wgs,
+                     "waves_per_simd": per_simd, "best_ms": round(best, 4),
+                     "ms_per_unit": round(best / units, 4)})
+        log(f"{mode:12s} {waves} waves/WG x {wgs} WGs ({per_simd}/SIMD): {best:.4f} ms, "
+            f"{best / units:.4f} ms per unit")
     print(json.dumps({"metric": "MFMA / VALU co-execution probe, ms per launch (best of 5)",
                       "unit": "ms", "n_gpus": 1, "higher_is_better": False, "data": "synthetic",
-                      "config": {"workload": "coexec probe", "workgroups": wgs,
+                      "config": {"workload": "coexec probe", "compute_units": cus,
+                                 "waves_w_and_w_plus_4_share_a_simd": paired,
                                  "iterations_per_wave": iters,
                                  "work_per_iteration": "8 MFMA 16x16x32 bf16 and/or 32 FMA"},
                       "rows": rows}), flush=True)

@@ -487,8 +487,11 @@ pa_status pa_read_probe(const void* buf, const int64_t* piece_offsets, int num_p
  * launch's time (events on `stream`) is the answer:
  *   mode 0  MFMA work only            mode 1  VALU work only
  *   mode 2  both in every wave, one MFMA then four FMAs
- *   mode 3  MFMA work in the even waves, VALU work in the odd ones (waves w and w + 4
- *           of a workgroup share a SIMD)
+ *   mode 3  MFMA work in the first half of the workgroup's waves, VALU work in the
+ *           second half (wave w runs on SIMD w % 4, so at 8 waves per workgroup every
+ *           SIMD runs one wave of each kind)
+ *   mode 4  placement check: no work; every thread writes the index (0..3) of the SIMD
+ *           its wave runs on, so that the placement mode 3 relies on can be seen
  *   workgroups           >= 1
  *   waves_per_workgroup  4 (one wave per SIMD) or 8 (two)
  *   iters                1 .. 2^20

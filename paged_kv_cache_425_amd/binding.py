@@ -699,13 +699,14 @@ def read_probe(buf: torch.Tensor, piece_offsets: torch.Tensor, piece_bytes: int,
                                         _ptr(sink), _stream(dev, stream)), "pa_read_probe")
 
 
-COEXEC_MODES = {"mfma": 0, "valu": 1, "interleaved": 2, "split": 3}
+COEXEC_MODES = {"mfma": 0, "valu": 1, "interleaved": 2, "split": 3, "placement": 4}
 
 
 def coexec_probe(mode: str, workgroups: int, waves_per_workgroup: int, iters: int,
                  out: torch.Tensor, stream=None) -> None:
     """Co-execution probe (pa_coexec_probe): MFMA work, VALU work, both interleaved in
-    every wave, or split between the two waves of each SIMD; time it with events."""
+    every wave, or split between the two waves of each SIMD; time it with events.  Mode
+    "placement" does no work and writes, per thread, the SIMD its wave runs on."""
     dev = out.device
     _require(out, "out", dev, torch.float32)
     if mode not in COEXEC_MODES:

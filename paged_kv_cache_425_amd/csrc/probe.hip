@@ -48,17 +48,25 @@ read_probe_kernel(const unsigned char* __restrict__ buf, const int64_t* __restri
 // independent chains of v_mfma_f32_16x16x32_bf16 (one MFMA each per iteration), VALU work
 // is 32 fused multiply-adds over 8 independent chains.  Mode 0: MFMA work only; 1: VALU
 // work only; 2: both in every wave, one MFMA then four FMAs (held in that order by
-// scheduling barriers); 3: MFMA work in the even waves of the workgroup and VALU work in
-// the odd ones (a workgroup's waves w and w + 4 share a SIMD).  One float per thread is
+// scheduling barriers); 3: MFMA work in the first half of the workgroup's waves and VALU
+// work in the second half.  A workgroup's waves go to the compute unit's four SIMDs in
+// turn (wave w to SIMD w % 4), so at 8 waves every SIMD runs one wave of each kind; mode
+// 4 checks that placement: no work, and every thread writes the SIMD its wave runs on
+// (bits 5:4 of the hardware wave id register, HW_ID).  Otherwise one float per thread is
 // written so that no work is removed.
 constexpr int kCoexecMaxThreads = 512;
 
 __global__ void __launch_bounds__(kCoexecMaxThreads)
 coexec_probe_kernel(int mode, int iters, float seed, float* __restrict__ out) {
   const int wave = threadIdx.x >> 6;
+  if (mode == 4) {
+    const unsigned hw_id = __builtin_amdgcn_s_getreg(4 | (0 << 6) | (31 << 11));
+    out[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = static_cast<float>((hw_id >> 4) & 3u);
+    return;
+  }
   bool do_m = mode == 0 || mode == 2, do_v = mode == 1 || mode == 2;
   if (mode == 3) {
-    do_m = (wave & 1) == 0;
+    do_m = 2 * wave < (int)(blockDim.x >> 6);
     do_v = !do_m;
   }
   bf16x8 a, b;
@@ -145,7 +153,7 @@ extern "C" pa_status pa_read_probe(const void* buf, const int64_t* piece_offsets
 
 extern "C" pa_status pa_coexec_probe(int mode, int workgroups, int waves_per_workgroup,
                                      int iters, float* out, void* stream) {
-  if (mode < 0 || mode > 3 || workgroups <= 0 || iters <= 0 || iters > (1 << 20) ||
+  if (mode < 0 || mode > 4 || workgroups <= 0 || iters <= 0 || iters > (1 << 20) ||
       (waves_per_workgroup != 4 && waves_per_workgroup != 8))
     return PA_ERR_INVALID_ARG;
   if (!out || reinterpret_cast<uintptr_t>(out) % 4) return PA_ERR_INVALID_ARG;

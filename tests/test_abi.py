@@ -32,7 +32,7 @@ def test_coexec_probe_rejects_before_launch(lib):
     f = lib.pa_coexec_probe
     f.restype = ctypes.c_int
     f.argtypes = [ctypes.c_int] * 4 + [ctypes.c_void_p] * 2
-    assert f(4, 256, 8, 16, FAKE, None) == 1         # no such mode
+    assert f(5, 256, 8, 16, FAKE, None) == 1         # no such mode
     assert f(-1, 256, 8, 16, FAKE, None) == 1
     assert f(0, 0, 8, 16, FAKE, None) == 1           # no workgroups
     assert f(0, 256, 6, 16, FAKE, None) == 1         # 4 or 8 waves only

@@ -4,7 +4,9 @@
   XOR of every 32-bit word of the pieces, computed on the host, for the in-order and the
   shuffled piece lists and both load policies.
 * pa_coexec_probe runs every mode at 4 and 8 waves per workgroup, writes one finite value
-  per thread, and gives the same values on a second launch.
+  per thread, and gives the same values on a second launch.  Its placement mode shows the
+  placement the split mode relies on: the four waves 0..3 of an 8-wave workgroup run on
+  four different SIMDs, and wave w + 4 on the SIMD of wave w.
 """
 from __future__ import annotations
 
@@ -58,3 +60,18 @@ def test_coexec_probe_runs_every_mode(waves):
         torch.cuda.synchronize()
         assert torch.isfinite(a).all()
         assert torch.equal(a, b)
+
+
+def test_coexec_probe_placement():
+    wgs, waves = 16, 8
+    say(f"coexec probe placement workgroups={wgs} waves={waves}")
+    out = torch.full((wgs * waves * 64,), -1.0, dtype=torch.float32, device=DEV)
+    pk.coexec_probe("placement", wgs, waves, 1, out)
+    torch.cuda.synchronize()
+    simd = out.cpu().numpy().reshape(wgs, waves, 64)
+    assert (simd == simd[:, :, :1]).all()              # one SIMD per wave
+    first = simd[:, :, 0].astype(np.int64)
+    assert set(np.unique(first)) <= {0, 1, 2, 3}
+    for w in first:
+        assert sorted(w[:4]) == [0, 1, 2, 3]
+        assert (w[4:] == w[:4]).all()
