@@ -285,6 +285,10 @@ paged_decode_kernel(const DecodeParams a, const OrderArg<PAIRED> ord) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15;
   const int j = lane >> 4;
+  // position that row n of K tile t holds, in the step starting at position `base`
+  auto step_row = [&](int base, int t) {
+    return Sh::kTiles == 1 ? base + n : base + kTpl * (n >> 2) + 4 * t + (n & 3);
+  };
 
   // paired mode: a 2-D grid (kv head, pair), so that the pair's plan entry can be
   // read together with the parameters; otherwise kv head fastest in a 1-D grid
@@ -300,6 +304,7 @@ paged_decode_kernel(const DecodeParams a, const OrderArg<PAIRED> ord) {
   bool pfx_wave = false;                                    // PREFIX: a wave of the prefix
   int part0 = 0;                                            // PREFIX: first wave of the unit
   int LA = 0, LB = 0;                                       // PAIRED: their lengths
+  int blkA = 0, blkB = 0;                                   // PAIRED: their blocks
   bool planned = false;                                     // PAIRED: pairs from the host
   bool onA = true;
   const int* tblw = tbl;
@@ -318,6 +323,8 @@ paged_decode_kernel(const DecodeParams a, const OrderArg<PAIRED> ord) {
       // prologue's other loads (sA stands in for a missing second sequence)
       LA = a.context_lens[sA];
       LB = a.context_lens[sB >= 0 ? sB : sA];
+      blkA = (int)(ey & 0xFFFu);                            // the host's block counts
+      blkB = (int)((ey >> 12) & 0xFFFu);
     } else {
       // Sort keys: key_t = (L_t << 10) | (1023 - t), unique per sequence and ordered by
       // length, then by index for equal lengths (L_t <= P <= 8192 here, and S <= 512, so the
@@ -359,6 +366,8 @@ paged_decode_kernel(const DecodeParams a, const OrderArg<PAIRED> ord) {
       LA = lens[sA] >> 10;
       LB = sB >= 0 ? lens[sB] >> 10 : 0;
       nA = split_waves(NW, (LA + kStep - 1) / kStep, (LB + kStep - 1) / kStep, sB >= 0);
+      blkA = (LA + BS - 1) / BS;
+      blkB = (LB + BS - 1) / BS;
     }
     nA = __builtin_amdgcn_readfirstlane(nA);
     // The two halves of the workgroup's waves share the SIMDs (wave w and w + NW / 2 on one)
@@ -453,6 +462,94 @@ paged_decode_kernel(const DecodeParams a, const OrderArg<PAIRED> ord) {
   const bool row_live = n < rows;
   const int row_seq = pfx_wave ? s + (row_live ? n / g : 0) : s;   // sequence of column n
 
+  const C* kc = static_cast<const C*>(a.k_cache);
+  const C* vc = static_cast<const C*>(a.v_cache);
+  const size_t head_elems = (size_t)D * BS;          // elements of one (block, kv head)
+
+  // ---- loads of one step ------------------------------------------------------
+  // Load policy.  Each K load instruction reads 64 bytes of each of 16 rows, half of each
+  // 128-byte line, and the next instruction reads the other half: K keeps the default
+  // policy, so that half comes from the cache.  V instructions read whole lines (16
+  // channel rows of a block, contiguous) and stream with the nt policy, which gathers
+  // scattered 4 KB tiles ~15% faster on gfx950 -- except in the waves of a shared prefix,
+  // whose blocks every group of the launch reads again from L2.
+  const bool v_stream = !(PREFIX && pfx_wave);
+  auto v_load = [&](const C* p) { return v_stream ? load16_nt(p) : load16(p); };
+  // Loads of step st, with positions clamped below `end` and the block of a position
+  // given by phys_k(t, pos) (K tile t) and phys_v(h, pos) (V group h).
+  auto load_step_from = [&](int st, StepData<T, C, D>& b, int end, auto&& phys_k,
+                            auto&& phys_v) {
+    const int base = tok0 + st * kStep;
+#pragma unroll
+    for (int t = 0; t < Sh::kTiles; ++t) {
+      // K-tile row n: bf16/FP8 rows interleave the step as kTpl*(n/4) + 4*t + n%4 so
+      // that the score of lane (n, j), register 4t + e is token kTpl*j + 4*t + e; f32
+      // rows are tokens n.  Rows past the partition's end read the last live token
+      // instead (in bounds; their logits are masked to -inf).
+      const int tok = min(step_row(base, t), end - 1);
+      const int phys = phys_k(t, tok);
+      // token-major K: the row of token `tok` is D contiguous elements; lane j takes its
+      // 16-byte chunks j, j + 4, ...
+      const C* kp = kc + (((size_t)phys * a.Hkv + kvh) * BS + tok % BS) * D + (size_t)j * kX;
+#pragma unroll
+      for (int c = 0; c < kNc; ++c) b.k[t][c] = load16(kp + 4 * c * kX);
+    }
+    // V operand of slice sl: channel 16*sl + n, tokens base + kTpl*j .. + kTpl - 1 -- one
+    // 16-byte token group of the channel, so the 16 lanes of a row read 256 contiguous
+    // bytes.  A group wholly past the end reads the group of the last live token (in
+    // bounds; it is zeroed before use).
+    const int tokv = min(base + kTpl * j, (end - 1) / kTpl * kTpl);
+    const int physv = phys_v(0, tokv);
+    const C* vp = vc + ((size_t)physv * a.Hkv + kvh) * head_elems + v_offset(tokv % BS, n, D, kXv);
+    if constexpr (kFp8 && BS < 16) {
+      // 16 tokens span two blocks of 8: two 8-byte groups (the second clamped like tokv)
+      const int tokv2 = min(tokv + 8, (end - 1) / 8 * 8);
+      const int physv2 = phys_v(1, tokv2);
+      const C* vp2 = vc + ((size_t)physv2 * a.Hkv + kvh) * head_elems + v_offset(0, n, D, kXv);
+#pragma unroll
+      for (int sl = 0; sl < kNs; ++sl) {
+        const uint2 lo = load8_nt(vp + (size_t)16 * sl * kXv);
+        const uint2 hi = load8_nt(vp2 + (size_t)16 * sl * kXv);
+        b.v[sl] = u32x4{lo.x, lo.y, hi.x, hi.y};
+      }
+    } else {
+#pragma unroll
+      for (int sl = 0; sl < kNs; ++sl) b.v[sl] = v_load(vp + (size_t)16 * sl * kXv);
+    }
+  };
+  auto window = [&](int, int pos) { return tblw[(pos - tok0) / BS]; };
+  auto load_step = [&](int st, StepData<T, C, D>& b) {
+    load_step_from(st, b, tok1, window, window);
+  };
+
+  // Paired mode over FP8 pools: each wave's first step is loaded before the table windows
+  // reach LDS, from table entries its lanes read themselves, so that its K/V loads wait
+  // for neither the windows nor the barrier and run while the prologue encodes the new
+  // tokens to E4M3 (bf16 pools have no such work there, and gained nothing from it).  The
+  // entries are read before the prologue's other loads, so that waiting for them waits for
+  // no other load: the columns of the step's own positions and the column of the unit's
+  // last block (by the host's block count for a planned launch).  By the time they land,
+  // so has the length: positions past the end are clamped to its last position, as in
+  // every other step, and read the last block's entry -- or, if the host's count was
+  // stale, their own column's, which is in bounds (the column clamped to the row, the
+  // block id to the pool) and masked.
+  constexpr bool kEarly = PAIRED && PIPE == 2 && kFp8;
+  int first_st = 0, first_last = 0;
+  unsigned first_k[Sh::kTiles], first_v[2], first_lb = 0;
+  StepData<T, C, D> first_b;
+  if constexpr (kEarly) {
+    first_st = __builtin_amdgcn_readfirstlane(rank_capacity(onA ? 0 : nA, (onA ? 0 : nA) + lw, NW));
+    const int base = tok0 + first_st * kStep;
+    const int32_t* row = a.block_table + (size_t)s * a.MB;
+#pragma unroll
+    for (int t = 0; t < Sh::kTiles; ++t) first_k[t] = row[min(step_row(base, t) / BS, a.MB - 1)];
+    first_v[0] = row[min((base + kTpl * j) / BS, a.MB - 1)];
+    if constexpr (kFp8 && BS < 16) first_v[1] = row[min((base + kTpl * j + 8) / BS, a.MB - 1)];
+    first_last = max(min(onA ? blkA : blkB, a.MB) - 1, 0);
+    first_lb = row[first_last];
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
   // Every load of the prologue is issued before the first wait on any of them: the
   // query operand, the new tokens and the block-table windows land in one round trip.
   //
@@ -535,9 +632,8 @@ paged_decode_kernel(const DecodeParams a, const OrderArg<PAIRED> ord) {
     stage_load(cP + gseq * cS, tb, where_grp);
   } else if constexpr (PAIRED) {
     // the host's block counts for a planned launch, else the lengths ranked above
-    const uint32_t ey = static_cast<uint32_t>(plan_entry >> 32);
-    cA = min(planned ? (int)(ey & 0xFFFu) : (LA + BS - 1) / BS, win);
-    cB = sB < 0 ? 0 : min(planned ? (int)((ey >> 12) & 0xFFFu) : (LB + BS - 1) / BS, win);
+    cA = min(blkA, win);
+    cB = sB < 0 ? 0 : min(blkB, win);
     if (cA + cB > 0) stage_load(cA + cB, tb, where_pair);
   } else {
     // the window of the workgroup's partitions (one, or NW with one per wave)
@@ -577,6 +673,21 @@ paged_decode_kernel(const DecodeParams a, const OrderArg<PAIRED> ord) {
   }
 
   if constexpr (PAIRED) {
+    if constexpr (kEarly) {
+      // the unit's length (device lengths: loaded before the entries, so here by now)
+      const int end = max(clamp_len(a, onA ? LA : LB, BS), 1);
+      const int base = tok0 + first_st * kStep;
+      const bool last_known = (end - 1) / BS == first_last;
+      auto entry = [&](unsigned own, int own_pos, int pos) {
+        const unsigned e = pos != own_pos && last_known && pos / BS == first_last ? first_lb : own;
+        return (int)min(e, (unsigned)(a.NB - 1));
+      };
+      auto first_kb = [&](int t, int pos) { return entry(first_k[t], step_row(base, t), pos); };
+      auto first_vb = [&](int h, int pos) {
+        return entry(first_v[h], base + kTpl * j + 8 * h, pos);
+      };
+      load_step_from(first_st, first_b, end, first_kb, first_vb);
+    }
     stage_store(cA + cB, tb, where_pair);
     if (planned) {
       LA = clamp_len(a, LA, BS);
@@ -678,60 +789,6 @@ paged_decode_kernel(const DecodeParams a, const OrderArg<PAIRED> ord) {
       }
     }
   }
-
-  const C* kc = static_cast<const C*>(a.k_cache);
-  const C* vc = static_cast<const C*>(a.v_cache);
-  const size_t head_elems = (size_t)D * BS;          // elements of one (block, kv head)
-
-  // ---- loads of one step ------------------------------------------------------
-  // Load policy.  Each K load instruction reads 64 bytes of each of 16 rows, half of each
-  // 128-byte line, and the next instruction reads the other half: K keeps the default
-  // policy, so that half comes from the cache.  V instructions read whole lines (16
-  // channel rows of a block, contiguous) and stream with the nt policy, which gathers
-  // scattered 4 KB tiles ~15% faster on gfx950 -- except in the waves of a shared prefix,
-  // whose blocks every group of the launch reads again from L2.
-  const bool v_stream = !(PREFIX && pfx_wave);
-  auto v_load = [&](const C* p) { return v_stream ? load16_nt(p) : load16(p); };
-  auto load_step = [&](int st, StepData<T, C, D>& b) {
-    const int base = tok0 + st * kStep;
-#pragma unroll
-    for (int t = 0; t < Sh::kTiles; ++t) {
-      // K-tile row n: bf16/FP8 rows interleave the step as kTpl*(n/4) + 4*t + n%4 so
-      // that the score of lane (n, j), register 4t + e is token kTpl*j + 4*t + e; f32
-      // rows are tokens n.  Rows past the partition's end read the last live token
-      // instead (in bounds; their logits are masked to -inf).
-      const int tok =
-          min(Sh::kTiles == 1 ? base + n : base + kTpl * (n >> 2) + 4 * t + (n & 3), tok1 - 1);
-      const int phys = tblw[(tok - tok0) / BS];
-      // token-major K: the row of token `tok` is D contiguous elements; lane j takes its
-      // 16-byte chunks j, j + 4, ...
-      const C* kp = kc + (((size_t)phys * a.Hkv + kvh) * BS + tok % BS) * D + (size_t)j * kX;
-#pragma unroll
-      for (int c = 0; c < kNc; ++c) b.k[t][c] = load16(kp + 4 * c * kX);
-    }
-    // V operand of slice sl: channel 16*sl + n, tokens base + kTpl*j .. + kTpl - 1 -- one
-    // 16-byte token group of the channel, so the 16 lanes of a row read 256 contiguous
-    // bytes.  A group wholly past the end reads the group of the last live token (in
-    // bounds; it is zeroed before use).
-    const int tokv = min(base + kTpl * j, (tok1 - 1) / kTpl * kTpl);
-    const int physv = tblw[(tokv - tok0) / BS];
-    const C* vp = vc + ((size_t)physv * a.Hkv + kvh) * head_elems + v_offset(tokv % BS, n, D, kXv);
-    if constexpr (kFp8 && BS < 16) {
-      // 16 tokens span two blocks of 8: two 8-byte groups (the second clamped like tokv)
-      const int tokv2 = min(tokv + 8, (tok1 - 1) / 8 * 8);
-      const int physv2 = tblw[(tokv2 - tok0) / BS];
-      const C* vp2 = vc + ((size_t)physv2 * a.Hkv + kvh) * head_elems + v_offset(0, n, D, kXv);
-#pragma unroll
-      for (int sl = 0; sl < kNs; ++sl) {
-        const uint2 lo = load8_nt(vp + (size_t)16 * sl * kXv);
-        const uint2 hi = load8_nt(vp2 + (size_t)16 * sl * kXv);
-        b.v[sl] = u32x4{lo.x, lo.y, hi.x, hi.y};
-      }
-    } else {
-#pragma unroll
-      for (int sl = 0; sl < kNs; ++sl) b.v[sl] = v_load(vp + (size_t)16 * sl * kXv);
-    }
-  };
 
   float m_run = kNegInf;
   float l_run = 0.f;
@@ -1049,11 +1106,12 @@ paged_decode_kernel(const DecodeParams a, const OrderArg<PAIRED> ord) {
     const int round = __builtin_amdgcn_readfirstlane(rank_capacity(r0, r0 + nw, NW));
     const int pre = __builtin_amdgcn_readfirstlane(rank_capacity(r0, r0 + lw, NW));
     auto step_of = [&](int k) { return (k / cw) * round + pre + k % cw; };
-    StepData<T, C, D> b0, b1;
+    StepData<T, C, D>& b0 = first_b;                         // FP8: the first step, loaded above
+    StepData<T, C, D> b1;
     int k = 0;
     int cur = step_of(0);                                    // the step in b0
     if (cur < nsteps) {
-      load_step(cur, b0);
+      if constexpr (!kEarly) load_step(cur, b0);
       int nxt = step_of(1);                                  // the step prefetched next
       for (;;) {
         load_step(nxt < nsteps ? nxt : cur, b1);

@@ -10,7 +10,10 @@ as the in-kernel ranking, so:
   differently but every sequence is still computed once: the output still meets
   the oracle bar and the caches are still bit-exact;
 * launches that do not use the paired mode (several partitions per sequence)
-  ignore the copy.
+  ignore the copy;
+* over FP8 pools, whose first step per wave is read with the host's block count, a
+  stale copy (a block short or long, or unrelated) still gives the oracle's caches and
+  an output within the bar.
 """
 from __future__ import annotations
 
@@ -180,3 +183,53 @@ def test_fp8_step_with_host_lengths_is_bitwise_unchanged(D, BS, g):
                                      w.scale, K_SCALE, V_SCALE, "bf16")
     out1 = res[1][0].view(np.uint16).astype(np.uint32) << 16
     check_close(out1.view(np.float32).astype(np.float64), ref, "bf16", "fp8-host-order")
+
+
+STALE = ["reversed", "shuffled", "zeros", "too-long", "one-block-short", "one-block-long"]
+
+
+@pytest.mark.parametrize("D,BS,g", [(128, 16, 4), (64, 8, 8)])
+@pytest.mark.parametrize("how", STALE)
+def test_fp8_stale_host_lengths_still_meet_the_bar(how, D, BS, g):
+    """FP8 pools read each wave's first step from table entries taken before the lengths
+    are known, among them the entry of the last block by the host's block count: with a
+    stale copy (shorter or longer by a block, or unrelated) the caches must still be the
+    oracle's and the output within the bar."""
+    w = tiny("bf16", LENS + (1500, 9, 48, 49), 2 * g, 2, D, BS, seed=450 + D + BS + g)
+    rng = np.random.default_rng(451)
+    host = w.context_lens.copy()
+    if how == "reversed":
+        host = host[::-1].copy()
+    elif how == "shuffled":
+        host = rng.permutation(host)
+    elif how == "zeros":
+        host[:] = 0
+    elif how == "too-long":
+        host[:] = 10 ** 6
+    elif how == "one-block-short":
+        host = np.maximum(host - BS, 0)
+    else:
+        host = host + BS
+    kc_np, vc_np = oracle.empty_fp8_pools(w.num_blocks, w.num_kv_heads, w.head_dim,
+                                          w.block_size)
+    hist = w.history_records
+    oracle.reshape_and_cache_fp8(w.rec_key[hist], w.rec_value[hist], w.rec_slot[hist], kc_np,
+                                 vc_np, w.dtype, K_SCALE, V_SCALE, inplace=True)
+    new = np.array([w.seq_records[s][-1] for s in range(w.num_seqs)], dtype=np.int64)
+    inp = upload_inputs(w, DEV)
+    kc = torch.from_numpy(kc_np.copy()).to(DEV)
+    vc = torch.from_numpy(vc_np.copy()).to(DEV)
+    say(f"host order: FP8 fused step, stale host copy ({how}) D={D} BS={BS} g={g}")
+    out = pk.decode_step_fp8(inp["query"], to_dev(w.rec_key[new], w.dtype, DEV),
+                             to_dev(w.rec_value[new], w.dtype, DEV),
+                             torch.from_numpy(w.rec_slot[new]).to(DEV), inp["block_table"],
+                             inp["context_lens"], kc, vc, w.scale, K_SCALE, V_SCALE,
+                             max_context_len=w.max_context_len, host_context_lens=host)
+    torch.cuda.synchronize()
+    oracle.reshape_and_cache_fp8(w.rec_key[new], w.rec_value[new], w.rec_slot[new], kc_np,
+                                 vc_np, w.dtype, K_SCALE, V_SCALE, inplace=True)
+    assert np.array_equal(kc.cpu().numpy(), kc_np) and np.array_equal(vc.cpu().numpy(), vc_np)
+    ref = oracle.paged_attention_fp8(w.query, w.block_table, w.context_lens, kc_np, vc_np,
+                                     w.scale, K_SCALE, V_SCALE, "bf16")
+    got = bits(out).view(np.uint16).astype(np.uint32) << 16
+    say(f"  {check_close(got.view(np.float32).astype(np.float64), ref, 'bf16', how)}")
