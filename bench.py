@@ -51,7 +51,7 @@ def parse_args():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--op", default="step",
                     choices=["step", "copy_blocks", "prefill", "fp8", "swap", "ceiling",
-                             "math", "balance", "coexec", "writes"],
+                             "math", "balance", "coexec", "writes", "suffixes"],
                     help="step: the decode step (default); copy_blocks: the copy-on-write "
                          "copies of the parallel-sampling workload; prefill: paged prefill; "
                          "fp8: the decode step over FP8 (E4M3) K/V pools; swap: swapping a "
@@ -65,7 +65,9 @@ def parse_args():
                          "bytes whose pairs are exactly balanced or whose lengths are equal; "
                          "coexec: the MFMA / VALU co-execution probe; writes: the decode of "
                          "the continuous-batching mix after a scatter of N of its new tokens, "
-                         "against the two apart (what dirty cache lines cost the reads)")
+                         "against the two apart (what dirty cache lines cost the reads); "
+                         "suffixes: the prefix-sharing step against the fused step of its "
+                         "private suffixes alone (a floor for any way of adding the prefix)")
     ap.add_argument("--prefill-case", default="prefix-cache-prefill",
                     choices=["prefix-cache-prefill", "chunked-prefill-llama3-8b"])
     ap.add_argument("--config", type=int, default=1, choices=[0, 1, 2, 3, 4])
@@ -939,6 +941,84 @@ def bench_balance(args) -> int:
     return 0
 
 
+def bench_suffixes(args) -> int:
+    """The prefix-sharing batch (128 sequences over one shared 1024-token prefix) against
+    the same sequences' private suffixes alone: pa_decode_step_shared_prefix on the batch,
+    pa_decode_step on a batch of the suffix lengths (the same heads, block size and new
+    tokens' shape).  The suffixes' step is a floor for any way of adding the prefix."""
+    import torch
+
+    import paged_kv_cache_425_amd as pk
+    from workloads import make_config, make_workload
+
+    dev = torch.device("cuda:0")
+    base = make_config(3, seed=args.seed)
+    pfx_len = int(base.info["shared_prefix_len"])
+    suffix = make_workload(name="prefix-sharing-suffixes", context_lens=base.context_lens - pfx_len,
+                           num_heads=base.num_heads, num_kv_heads=base.num_kv_heads,
+                           head_dim=base.head_dim, block_size=base.block_size, dtype="bf16",
+                           seed=base.info["seed"])
+    up = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)  # noqa: E731
+    K, W, R = args.steps, args.warmup, max(4, args.replicas)
+    rows = {}
+    for name, w, shared in (("prefix-sharing-bf16-prefix", base, True),
+                            ("suffixes-alone", suffix, False)):
+        tdt = torch.bfloat16
+        new = np.array([w.seq_records[s][-1] for s in range(w.num_seqs)], dtype=np.int64)
+        hist = np.setdiff1d(np.arange(len(w.rec_slot)), new)
+        kc0 = torch.full(pk.k_cache_shape(w.num_blocks, w.num_kv_heads, w.head_dim, w.block_size,
+                                          tdt), float("nan"), dtype=tdt, device=dev)
+        vc0 = torch.full(pk.v_cache_shape(w.num_blocks, w.num_kv_heads, w.head_dim, w.block_size,
+                                          tdt), float("nan"), dtype=tdt, device=dev)
+        pk.reshape_and_cache(up(w.rec_key[hist]), up(w.rec_value[hist]),
+                             torch.from_numpy(w.rec_slot[hist]).to(dev), kc0, vc0)
+        pools = [(kc0, vc0)] + [(kc0.clone(), vc0.clone()) for _ in range(R - 1)]
+        q, kn, vn = up(w.query), up(w.rec_key[new]), up(w.rec_value[new])
+        sl = torch.from_numpy(w.rec_slot[new]).to(dev)
+        tb = torch.from_numpy(w.block_table).to(dev)
+        ln = torch.from_numpy(w.context_lens).to(dev)
+        out = torch.empty_like(q)
+        if shared:
+            calls = [pk.prepare_decode_step_shared_prefix(
+                q, kn, vn, sl, tb, ln, kc, vc, w.scale, prefix_blocks=pfx_len // w.block_size,
+                max_context_len=w.max_context_len, out=out, host_context_lens=w.context_lens.copy())
+                for kc, vc in pools]
+        else:
+            calls = [pk.prepare_decode_step(q, kn, vn, sl, tb, ln, kc, vc, w.scale,
+                                            max_context_len=w.max_context_len, out=out,
+                                            host_context_lens=w.context_lens.copy())
+                     for kc, vc in pools]
+        for i in range(W):
+            calls[i % R]()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(K):
+            calls[i % R]()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / K
+        # unique KV bytes: the shared prefix counted once
+        tokens = int(w.context_lens.sum()) - (pfx_len * (w.num_seqs - 1) if shared else 0)
+        kv = tokens * 2 * w.num_kv_heads * w.head_dim * 2
+        rows[name] = {"launch_us_events": round(us, 2), "kv_unique_bytes": kv,
+                      "tokens_unique": tokens}
+        log(f"{name}: {us:.2f} us/launch, {kv / 1e6:.1f} MB of unique KV")
+        del pools, calls
+        torch.cuda.empty_cache()
+    whole = rows["prefix-sharing-bf16-prefix"]
+    floor_us = rows["suffixes-alone"]["launch_us_events"]
+    rows["floor"] = {"roofline_frac_at_floor": round(whole["kv_unique_bytes"] / (floor_us * 1e-6) / 8e12, 3),
+                     "roofline_frac": round(whole["kv_unique_bytes"] / (whole["launch_us_events"] * 1e-6) / 8e12, 3)}
+    print(json.dumps({"metric": "prefix-sharing step vs its private suffixes alone, us/launch",
+                      "unit": "us", "n_gpus": 1, "steps": K, "warmup": W, "pool_replicas": R,
+                      "higher_is_better": False, "dtype": "bf16", "data": "synthetic",
+                      "config": {"workload": "prefix-sharing-bf16-prefix and its suffixes alone",
+                                 "shared_prefix_len": pfx_len},
+                      "rows": rows}), flush=True)
+    return 0
+
+
 def bench_coexec(args) -> int:
     """The co-execution probe (pa_coexec_probe): MFMA work only, VALU work only, both
     interleaved in every wave, and split between the two waves of each SIMD, at one to four
@@ -1091,6 +1171,8 @@ def main() -> int:
         return bench_ceiling(args)
     if args.op == "math":
         return bench_math(args)
+    if args.op == "suffixes":
+        return bench_suffixes(args)
     if args.op == "balance":
         return bench_balance(args)
     if args.op == "coexec":
