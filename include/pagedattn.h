@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define PA_ABI_VERSION 6
+#define PA_ABI_VERSION 7
 
 typedef enum {
     PA_OK = 0,
@@ -501,6 +501,32 @@ pa_status pa_read_probe(const void* buf, const int64_t* piece_offsets, int num_p
  */
 pa_status pa_coexec_probe(int mode, int workgroups, int waves_per_workgroup, int iters,
                           float* out, void* stream);
+
+/*
+ * The paired mode's plan made on the host (diagnostic; no GPU work, callable without a
+ * GPU).  When every sequence of a decode call is one partition, a workgroup takes the r-th
+ * longest and the r-th shortest sequence of a kv head and splits its waves between the
+ * two in proportion to their steps, so that every workgroup carries about the same tokens.
+ * The pages define the attention (page "vLLM core architecture", section 2.2.2); this
+ * pairing is the library's own schedule of it.  With host_context_lens the decode calls
+ * make exactly this plan; without it the kernel derives the same pairs from context_lens.
+ *   host_lens    [num_seqs] int32, host memory; each clamped to [0, max_len]
+ *   num_seqs     2 .. 512
+ *   block_size   8, 16 or 32
+ *   max_len      the clamp, 0 .. 8192 (the decode uses the partition size)
+ *   step_tokens  positions per step of the kernel (32 for bf16, 16 for f32, 64 for FP8)
+ *   waves        4 or 8 per workgroup (rank r of a workgroup's waves takes 3 steps for
+ *                every 2 of rank r + 1 at 8 waves when r is even, 1 each at 4)
+ *   pairs        [2 * ((num_seqs + 1) / 2)] uint32, host memory, written: for pair r,
+ *                pairs[2r] = sA | sB << 16 (sA the r-th longest sequence, sB the r-th
+ *                shortest, ties to the lower index; sB = 0xFFFF for the middle sequence
+ *                of an odd count) and pairs[2r + 1] = blocks of sA | blocks of sB << 12 |
+ *                waves of sA << 24 (the split that evens the two units' steps per unit of
+ *                wave weight; each unit of a pair keeps at least one wave)
+ * Returns PA_ERR_INVALID_ARG for bad arguments (nothing written).
+ */
+pa_status pa_plan_pairs(const int32_t* host_lens, int num_seqs, int block_size, int max_len,
+                        int step_tokens, int waves, uint32_t* pairs);
 
 #ifdef __cplusplus
 }

@@ -6,7 +6,7 @@ this package only marshals torch tensors to it.
 from .binding import (LIB_PATH, PreparedCall, chunk_elems, copy_blocks, decode_math,
                       decode_step, get_decode_math, set_decode_math,
                       decode_step_noalloc, decode_step_shared_prefix, read_probe, coexec_probe,
-                      prepare_decode_step_shared_prefix,
+                      plan_pairs, prepare_decode_step_shared_prefix,
                       decode_step_fp8, default_partition_size, gather_kv, k_cache_shape,
                       load_library, prepare_decode_step_fp8, paged_attention,
                       prepare_swap_blocks, swap_blocks, paged_attention_fp8, paged_prefill, prepare_copy_blocks,
@@ -17,7 +17,7 @@ from .binding import (LIB_PATH, PreparedCall, chunk_elems, copy_blocks, decode_m
 __all__ = ["LIB_PATH", "PreparedCall", "chunk_elems", "copy_blocks", "decode_math",
            "decode_step", "get_decode_math", "set_decode_math",
            "decode_step_noalloc", "decode_step_shared_prefix", "read_probe", "coexec_probe",
-           "prepare_decode_step_shared_prefix",
+           "plan_pairs", "prepare_decode_step_shared_prefix",
            "decode_step_fp8", "prepare_decode_step_fp8", "prepare_swap_blocks", "swap_blocks",
            "default_partition_size", "gather_kv", "k_cache_shape", "load_library",
            "paged_attention", "paged_attention_fp8", "paged_prefill", "prepare_copy_blocks",

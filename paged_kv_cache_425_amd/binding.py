@@ -11,6 +11,7 @@ import contextlib
 import ctypes
 import os
 
+import numpy as np
 import torch
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpagedattn.so")
@@ -66,6 +67,8 @@ def load_library() -> ctypes.CDLL:
     lib.pa_read_probe.argtypes = [vp, vp, i32, i32, i32, i32, i32, vp, vp]
     lib.pa_coexec_probe.restype = i32
     lib.pa_coexec_probe.argtypes = [i32, i32, i32, i32, vp, vp]
+    lib.pa_plan_pairs.restype = i32
+    lib.pa_plan_pairs.argtypes = [vp, i32, i32, i32, i32, i32, vp]
     lib.pa_decode_step_noalloc.restype = i32
     lib.pa_decode_step_noalloc.argtypes = [vp] * 9 + [i32] * 8 + [f32, i32, i32, vp, vp]
     lib.pa_paged_attention_fp8.restype = i32
@@ -716,6 +719,20 @@ def coexec_probe(mode: str, workgroups: int, waves_per_workgroup: int, iters: in
     _check(load_library().pa_coexec_probe(COEXEC_MODES[mode], int(workgroups),
                                           int(waves_per_workgroup), int(iters), _ptr(out),
                                           _stream(dev, stream)), "pa_coexec_probe")
+
+
+def plan_pairs(host_lens, block_size: int, max_len: int, step_tokens: int,
+               waves: int) -> np.ndarray:
+    """The paired mode's host plan (pa_plan_pairs; no GPU work): uint32 [pairs, 2] of
+    (sA | sB << 16, blocks of sA | blocks of sB << 12 | waves of sA << 24)."""
+    lens = np.ascontiguousarray(np.asarray(host_lens, dtype=np.int32))
+    if lens.ndim != 1:
+        raise ValueError("host_lens must be one-dimensional")
+    out = np.zeros(((lens.size + 1) // 2, 2), dtype=np.uint32)
+    _check(load_library().pa_plan_pairs(lens.ctypes.data, int(lens.size), int(block_size),
+                                        int(max_len), int(step_tokens), int(waves),
+                                        out.ctypes.data), "pa_plan_pairs")
+    return out
 
 
 DECODE_MATH = {"mfma": 0, "valu": 1}

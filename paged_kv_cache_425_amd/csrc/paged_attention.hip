@@ -1433,26 +1433,31 @@ inline bool use_paired(const DecodeParams& a, int D, int BS, int elt) {
 
 // The paired mode's order of the sequences from a host copy of the lengths: the same
 // keys the kernel ranks (clamped length, then lower index first), sorted on the host.
-inline void order_on_host(const DecodeParams& a, int BS, int step, int nw,
-                          const int32_t* host_lens, PairOrder& ord) {
-  const long cap = std::min((long)a.MB * BS, (long)a.P * a.Pmax);
+// Lengths are clamped to [0, cap], as the kernel clamps them (clamp_len).
+inline void plan_pairs(int S, long cap, int BS, int step, int nw, const int32_t* host_lens,
+                       PairOrder& ord) {
   uint32_t key[kMaxPairedSeqs];
-  for (int t = 0; t < a.S; ++t) {
+  for (int t = 0; t < S; ++t) {
     const long L = std::min(std::max(0L, (long)host_lens[t]), cap);
     key[t] = (static_cast<uint32_t>(L) << 10) | static_cast<uint32_t>(1023 - t);
   }
-  std::sort(key, key + a.S, [](uint32_t x, uint32_t y) { return x > y; });
-  const int npairs = (a.S + 1) / 2;
+  std::sort(key, key + S, [](uint32_t x, uint32_t y) { return x > y; });
+  const int npairs = (S + 1) / 2;
   for (int r = 0; r < npairs; ++r) {
-    const uint32_t kA = key[r], kB = key[a.S - 1 - r];
+    const uint32_t kA = key[r], kB = key[S - 1 - r];
     const uint32_t sA = 1023u - (kA & 1023u);
-    const uint32_t sB = r == a.S - 1 - r ? 0xFFFFu : 1023u - (kB & 1023u);
+    const uint32_t sB = r == S - 1 - r ? 0xFFFFu : 1023u - (kB & 1023u);
     const int LA = (int)(kA >> 10), LB = sB == 0xFFFFu ? 0 : (int)(kB >> 10);
     const uint32_t bA = (LA + BS - 1) / BS, bB = (LB + BS - 1) / BS;
     const uint32_t nA = split_waves(nw, (LA + step - 1) / step, (LB + step - 1) / step,
                                     sB != 0xFFFFu);
     ord.pair[r] = make_uint2(sA | sB << 16, bA | bB << 12 | nA << 24);
   }
+}
+
+inline void order_on_host(const DecodeParams& a, int BS, int step, int nw,
+                          const int32_t* host_lens, PairOrder& ord) {
+  plan_pairs(a.S, std::min((long)a.MB * BS, (long)a.P * a.Pmax), BS, step, nw, host_lens, ord);
 }
 
 // Compute units of the current device (queried once per device; concurrent first calls
@@ -1965,4 +1970,22 @@ extern "C" pa_status pa_decode_step_fp8(void* out, const void* query, const void
                     head_dim, block_size, max_blocks_per_seq, num_blocks, max_context_len, scale,
                     dtype, partition_size, workspace, workspace_bytes, stream, host_context_lens,
                     true, k_scale, v_scale);
+}
+
+// ---------------------------------------------------------------------------
+// the paired mode's host plan, for inspection
+// ---------------------------------------------------------------------------
+extern "C" pa_status pa_plan_pairs(const int32_t* host_lens, int num_seqs, int block_size,
+                                   int max_len, int step_tokens, int waves, uint32_t* pairs) {
+  if (!host_lens || !pairs || num_seqs < 2 || num_seqs > pa::kMaxPairedSeqs ||
+      (block_size != 8 && block_size != 16 && block_size != 32) || max_len < 0 ||
+      max_len > pa::kMaxPartition || step_tokens <= 0 || (waves != 4 && waves != 8))
+    return PA_ERR_INVALID_ARG;
+  pa::PairOrder ord;
+  pa::plan_pairs(num_seqs, max_len, block_size, step_tokens, waves, host_lens, ord);
+  for (int r = 0; r < (num_seqs + 1) / 2; ++r) {
+    pairs[2 * r] = ord.pair[r].x;
+    pairs[2 * r + 1] = ord.pair[r].y;
+  }
+  return PA_OK;
 }

@@ -42,6 +42,22 @@ def test_coexec_probe_rejects_before_launch(lib):
     assert f(0, 256, 8, 16, FAKE + 2, None) == 1     # output misaligned
 
 
+def test_plan_pairs_rejects_before_writing(lib):
+    f = lib.pa_plan_pairs
+    f.restype = ctypes.c_int
+    f.argtypes = [ctypes.c_void_p] + [ctypes.c_int] * 5 + [ctypes.c_void_p]
+    lens = (ctypes.c_int32 * 4)(1, 2, 3, 4)
+    out = (ctypes.c_uint32 * 4)(*([7] * 4))
+    assert f(None, 4, 16, 8192, 32, 8, out) == 1             # no lengths
+    assert f(lens, 4, 16, 8192, 32, 8, None) == 1            # no output
+    assert f(lens, 1, 16, 8192, 32, 8, out) == 1             # fewer than two sequences
+    assert f(lens, 4, 24, 8192, 32, 8, out) == 1             # block size
+    assert f(lens, 4, 16, 9000, 32, 8, out) == 1             # clamp past 8192
+    assert f(lens, 4, 16, 8192, 32, 5, out) == 1             # 4 or 8 waves only
+    assert list(out) == [7] * 4                                # nothing written
+    assert f(lens, 4, 16, 8192, 32, 8, out) == 0
+
+
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted([
         "pa_abi_version", "pa_status_string", "pa_default_partition_size",
@@ -49,7 +65,8 @@ def test_header_declares_the_boundary():
         "pa_gather_kv", "pa_decode_step", "pa_copy_blocks", "pa_paged_prefill",
         "pa_reshape_and_cache_fp8", "pa_paged_attention_fp8", "pa_decode_step_fp8",
         "pa_swap_blocks", "pa_decode_step_noalloc", "pa_read_probe", "pa_coexec_probe",
-        "pa_decode_step_shared_prefix", "pa_set_decode_math", "pa_get_decode_math"])
+        "pa_decode_step_shared_prefix", "pa_set_decode_math", "pa_get_decode_math",
+        "pa_plan_pairs"])
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -58,7 +75,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.pa_abi_version() == 6
+    assert lib.pa_abi_version() == 7
     for code in range(5):
         assert lib.pa_status_string(code).decode().startswith("PA_")
     assert b"unknown" in lib.pa_status_string(99)
